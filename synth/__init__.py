@@ -1,0 +1,164 @@
+"""Seeded synthetic decode-step inputs shared by the tests, the smoke check and
+the benchmark.
+
+This module only draws inputs. It holds none of the attention arithmetic: no
+score, softmax, merge or dequantisation. The fp8 workload's quantiser lives
+here because its codes and scales are inputs that both the GPU path and the
+oracle consume unchanged.
+
+Recipe (every workload):
+  * ``g = torch.Generator().manual_seed(seed)`` on the CPU.
+  * context lengths: fixed, or ``torch.randint(lo, hi + 1)`` (inclusive).
+  * pages needed by sequence b: ceil(L_b / P); pool = 2 x total needed pages
+    (the tiny workload: exactly the needed pages).
+  * ``perm = torch.randperm(pool)``; block_table rows take consecutive entries
+    of ``perm`` in batch order; unused entries are -1.
+  * q, then the K rows of every needed page, then the V rows: ``randn`` in
+    fp32, rounded to bf16 (round to nearest even).
+  * pages that no block_table row names are filled with NaN (bf16) or the
+    NaN code 0x7F (fp8, with NaN scales), so that any read of them shows up.
+  * fp8 workload: each (token, kv head) row of K and of V gets
+    scale = absmax(row) / 448 (fp32; 1 for an all-zero row) and
+    code = e4m3fn(round-to-nearest-even(x / scale)) clamped to +-448.
+"""
+from dataclasses import dataclass
+import math
+
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "kv_bytes"]
+
+E4M3_MAX = 448.0
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    description: str
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    lens: tuple            # ("fixed", (L0, L1, ...)) or ("uniform", lo, hi)
+    kv_dtype: str = "bf16"  # "bf16" or "fp8_e4m3"
+    pool: str = "2x"        # "2x" or "exact"
+    seed: int = 1000
+
+    def with_(self, **kw):
+        d = dict(self.__dict__)
+        d.update(kw)
+        return Workload(**d)
+
+
+WORKLOADS = {
+    "tiny": Workload(
+        "tiny", "paged GQA decode B1, 8 q / 2 kv heads, d64, L256, P16, 16-page pool",
+        1, 8, 2, 64, 16, ("fixed", (256,)), pool="exact", seed=1001),
+    "llama3_8b": Workload(
+        "llama3_8b", "Llama-3-8B-shaped paged GQA decode B32, 32 q / 8 kv heads, d128, "
+        "L~U[512,4096], P16", 32, 32, 8, 128, 16, ("uniform", 512, 4096), seed=1002),
+    "long_ctx": Workload(
+        "long_ctx", "long-context paged GQA decode B4, 64 q / 8 kv heads, d128, "
+        "L in {32K,64K,96K,128K}, P64", 4, 64, 8, 128, 64,
+        ("fixed", (32768, 65536, 98304, 131072)), seed=1003),
+    "many_short": Workload(
+        "many_short", "many-short-sequence paged GQA decode B256, 32 q / 8 kv heads, d128, "
+        "L~U[16,512], P16", 256, 32, 8, 128, 16, ("uniform", 16, 512), seed=1004),
+    "fp8_kv": Workload(
+        "fp8_kv", "FP8-e4m3 KV paged GQA decode B32, 32 q / 8 kv heads, d128, "
+        "L~U[1024,8192], P16, per-token fp32 scales", 32, 32, 8, 128, 16,
+        ("uniform", 1024, 8192), kv_dtype="fp8_e4m3", seed=1005),
+}
+
+
+def _lens(w: Workload, g: torch.Generator) -> torch.Tensor:
+    kind = w.lens[0]
+    if kind == "fixed":
+        vals = tuple(w.lens[1])
+        if len(vals) != w.batch:
+            raise ValueError("fixed lens must give one length per sequence")
+        return torch.tensor(vals, dtype=torch.int32)
+    if kind == "uniform":
+        lo, hi = int(w.lens[1]), int(w.lens[2])
+        return torch.randint(lo, hi + 1, (w.batch,), generator=g, dtype=torch.int64).to(torch.int32)
+    raise ValueError(f"unknown lens kind {kind!r}")
+
+
+def quantize_rows_e4m3(x: torch.Tensor):
+    """Per-row (last axis) absmax fp8 quantiser for the fp8 workload's inputs.
+
+    Returns (codes float8_e4m3fn, scale float32 with the last axis dropped)."""
+    x = x.to(torch.float32)
+    amax = x.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    y = (x / scale[..., None]).clamp(-E4M3_MAX, E4M3_MAX)
+    return y.to(torch.float8_e4m3fn), scale
+
+
+def make_inputs(w, *, seed=None, unused="nan"):
+    """Draw one decode step's inputs on the CPU.
+
+    Returns a dict: q [B,Hq,d] bf16; k_pages, v_pages [num_pages,P,Hkv,d]
+    (bf16 or float8_e4m3fn); k_scale, v_scale [num_pages,P,Hkv] fp32 or None;
+    block_table [B,max_pages] int32 (-1 where unused); context_lens [B] int32;
+    workload; scale (1/sqrt(d)).
+    """
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    seed = w.seed if seed is None else seed
+    g = torch.Generator().manual_seed(int(seed))
+    B, Hq, Hkv, D, P = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size
+    lens = _lens(w, g)
+    needed = [(int(L) + P - 1) // P for L in lens.tolist()]
+    total_needed = sum(needed)
+    pool = total_needed if w.pool == "exact" else 2 * total_needed
+    pool = max(pool, 1)
+    max_pages = max(max(needed) if needed else 0, 1)
+    perm = torch.randperm(pool, generator=g).to(torch.int32)
+    block_table = torch.full((B, max_pages), -1, dtype=torch.int32)
+    used_pages = perm[:total_needed].to(torch.int64)
+    off = 0
+    for b, n in enumerate(needed):
+        block_table[b, :n] = perm[off:off + n]
+        off += n
+    q = torch.randn((B, Hq, D), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    k_rows = torch.randn((total_needed, P, Hkv, D), generator=g, dtype=torch.float32)
+    v_rows = torch.randn((total_needed, P, Hkv, D), generator=g, dtype=torch.float32)
+    k_scale = v_scale = None
+    if w.kv_dtype == "bf16":
+        fill = float("nan") if unused == "nan" else 0.0
+        k_pages = torch.full((pool, P, Hkv, D), fill, dtype=torch.bfloat16)
+        v_pages = torch.full((pool, P, Hkv, D), fill, dtype=torch.bfloat16)
+        k_pages[used_pages] = k_rows.to(torch.bfloat16)
+        v_pages[used_pages] = v_rows.to(torch.bfloat16)
+    elif w.kv_dtype == "fp8_e4m3":
+        kc, ks = quantize_rows_e4m3(k_rows)
+        vc, vs = quantize_rows_e4m3(v_rows)
+        code_fill = 0x7F if unused == "nan" else 0x00
+        k_pages = torch.full((pool, P, Hkv, D), code_fill, dtype=torch.uint8).view(torch.float8_e4m3fn)
+        v_pages = torch.full((pool, P, Hkv, D), code_fill, dtype=torch.uint8).view(torch.float8_e4m3fn)
+        sfill = float("nan") if unused == "nan" else 1.0
+        k_scale = torch.full((pool, P, Hkv), sfill, dtype=torch.float32)
+        v_scale = torch.full((pool, P, Hkv), sfill, dtype=torch.float32)
+        k_pages.view(torch.uint8)[used_pages] = kc.view(torch.uint8)
+        v_pages.view(torch.uint8)[used_pages] = vc.view(torch.uint8)
+        k_scale[used_pages] = ks
+        v_scale[used_pages] = vs
+    else:
+        raise ValueError(f"unknown kv dtype {w.kv_dtype!r}")
+    return dict(q=q, k_pages=k_pages, v_pages=v_pages, k_scale=k_scale, v_scale=v_scale,
+                block_table=block_table, context_lens=lens, workload=w,
+                scale=1.0 / math.sqrt(D))
+
+
+def kv_bytes(w, context_lens) -> int:
+    """Algorithmic KV bytes of one decode step: every K and V element of every
+    valid (token, kv head) once, plus the two fp32 scales per (token, kv head)
+    for an fp8 pool."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    tokens = int(torch.as_tensor(context_lens).to(torch.int64).sum())
+    esize = 2 if w.kv_dtype == "bf16" else 1
+    per = 2 * w.head_dim * esize + (8 if w.kv_dtype == "fp8_e4m3" else 0)
+    return tokens * w.num_kv_heads * per

@@ -1,0 +1,164 @@
+/*
+ * pdattn.h -- paged split-KV grouped-query decode attention for AMD Instinct
+ * MI355X (gfx950). C ABI; every pointer is a plain host or device address.
+ *
+ * The operation (FlashQuant wiki "CUDA Kernels": flash_attention.cu Online
+ * Softmax and GQA Support, paged_decode.cu Page Table Addressing and Partial
+ * Output, split_k_reduce.cu Algorithm; AstrAI "CUDA Kernels": Python
+ * Wrappers; OASR "Kernel Layer": Fused attention and FP8 KV variants):
+ *
+ *   for each sequence b < B and query head h < Hq, with G = Hq / Hkv,
+ *   kv head kvh = h / G and L = context_lens[b]:
+ *     page(t) = block_table[b * max_pages_per_seq + t / P],  slot(t) = t mod P
+ *     s_t = scale * sum_d q[b][h][d] * K[page(t)][slot(t)][kvh][d],  t < L
+ *     out[b][h][:] = sum_t softmax(s)_t * V[page(t)][slot(t)][kvh][:]
+ *     lse[b][h]    = ln sum_t exp(s_t)            (natural log)
+ *   L == 0 gives out = 0 and lse = -inf.
+ *
+ * The KV sequence of every (b, kvh) is cut into splits of plan.split_tokens
+ * tokens (flash-decoding). One workgroup computes one split for all G query
+ * heads of one kv head with an online softmax (running max and sum in base 2,
+ * fp32 accumulators) and, for a sequence with more than one split, writes
+ * (m, l, acc) partials to the workspace; pdattn_reduce merges them with the
+ * log-sum-exp rule. A sequence that fits in one split is written to `out`
+ * directly by pdattn_decode.
+ *
+ * Layouts (all contiguous, row-major):
+ *   q            bf16 [B][Hq][d]
+ *   k_pages,     bf16 or OCP e4m3fn bytes [num_pages][P][Hkv][d]
+ *   v_pages
+ *   k_scale,     fp32 [num_pages][P][Hkv], fp8 pools only (NULL for bf16):
+ *   v_scale      the stored value of element d is e4m3fn(code) * scale
+ *   block_table  int32 [B][max_pages_per_seq]; only entries < ceil(L_b / P)
+ *                are read; a page may appear in several rows
+ *   context_lens int32 [B], device copy, read by the kernels
+ *   out          fp32 [B][Hq][d]
+ *   lse          fp32 [B][Hq], optional (NULL to skip)
+ *
+ * Supported: d in {64, 128}; G in {1, 2, 4, 8, 16}; P a power of two in
+ * [8, 128]; q / k / v / out bases 16-byte aligned; B <= 65535.
+ *
+ * Ownership and execution: the caller allocates and owns every buffer,
+ * including the workspace (size from the plan). The library allocates
+ * nothing, keeps no device state and never synchronises; decode and reduce
+ * are enqueued on the caller's stream and are safe to capture in a graph
+ * (no allocation, no memset, no capture-dependent choice).
+ *
+ * Errors: every call validates its arguments before launching anything and
+ * returns a status; an invalid call enqueues no work. The last error message
+ * of the calling thread is available from pdattn_last_error(). On the
+ * device, a context length beyond the plan's capacity or beyond the block
+ * table, and a block_table entry outside [0, num_pages), are not read
+ * through: the affected (b, h) outputs are set to NaN instead.
+ */
+#ifndef PDATTN_H
+#define PDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PDATTN_API __attribute__((visibility("default")))
+
+typedef enum pdattn_status {
+  PDATTN_OK = 0,
+  PDATTN_ERR_INVALID_ARGUMENT = 1, /* null or misaligned pointer, bad shape or length */
+  PDATTN_ERR_UNSUPPORTED = 2,      /* head_dim, group size, page size or dtype not built */
+  PDATTN_ERR_WORKSPACE = 3,        /* workspace missing or smaller than plan->workspace_bytes */
+  PDATTN_ERR_PLAN_MISMATCH = 4,    /* plan not produced by pdattn_plan */
+  PDATTN_ERR_DEVICE = 5            /* HIP runtime error; detail in pdattn_last_error() */
+} pdattn_status;
+
+typedef enum pdattn_kv_dtype {
+  PDATTN_KV_BF16 = 0,
+  PDATTN_KV_FP8_E4M3 = 1 /* OCP e4m3fn codes with one fp32 scale per (token, kv head) */
+} pdattn_kv_dtype;
+
+/* The problem shape (AstrAI "CUDA Kernels", Python Wrappers: blhd layout,
+ * scale 1/sqrt(head_dim); OASR "Kernel Layer", Fused attention: paged mode
+ * takes block_table and per-sequence lengths). */
+typedef struct pdattn_problem {
+  int32_t batch;             /* B */
+  int32_t num_q_heads;       /* Hq */
+  int32_t num_kv_heads;      /* Hkv; Hq % Hkv == 0 */
+  int32_t head_dim;          /* d */
+  int32_t page_size;         /* P */
+  int32_t max_pages_per_seq; /* block_table row stride, in entries */
+  int32_t num_pages;         /* pool size, in pages */
+  int32_t kv_dtype;          /* pdattn_kv_dtype */
+  float scale;               /* softmax scale; <= 0 selects 1/sqrt(head_dim) */
+} pdattn_problem;
+
+/* A launch plan: a pure function of the problem, the host copy of the
+ * context lengths and the compute-unit count (OASR "Kernel Layer", Fused
+ * attention: the split count depends on shape and machine only; Atlas
+ * "CUDA Kernel Engineering", kernel inventory: adaptive split count). */
+typedef struct pdattn_plan_t {
+  pdattn_problem problem;   /* copy of the problem, scale resolved */
+  int32_t split_tokens;     /* tokens per split, a multiple of 16 */
+  int32_t max_splits;       /* largest number of splits of any sequence */
+  int32_t num_cus;          /* compute units the plan was sized for */
+  int32_t num_work_items;   /* sum over sequences of splits, times Hkv */
+  int64_t max_context_len;  /* largest host context length planned for */
+  uint64_t workspace_bytes; /* 0 when max_splits == 1 */
+  uint32_t magic;           /* set by pdattn_plan; checked by decode / reduce */
+  uint32_t reserved;
+} pdattn_plan_t;
+
+/*
+ * Plan one decode step.
+ *   problem            shape; validated here (supported set above)
+ *   context_lens_host  host int32 [batch]; each 0 <= L <= max_pages_per_seq * P
+ *   num_cus            compute units to size for; 0 queries the current device
+ *   force_split_tokens 0 = adaptive; > 0 forces this split length (rounded up
+ *                      to a multiple of 16; used by tests)
+ *   out                receives the plan (caller-owned POD)
+ * Pure host computation apart from the optional device query.
+ */
+PDATTN_API pdattn_status pdattn_plan(const pdattn_problem* problem, const int32_t* context_lens_host,
+                                     int32_t num_cus, int32_t force_split_tokens, pdattn_plan_t* out);
+
+/*
+ * Enqueue the split-KV partial pass on `stream` (a hipStream_t; NULL = the
+ * null stream). Pointers and layouts as described above; k_scale / v_scale
+ * must be NULL for bf16 pools and non-NULL for fp8 pools. `workspace` may be
+ * NULL only when plan->workspace_bytes == 0. Writes `out` (and `lse`) for
+ * every sequence with at most one split; writes workspace partials for the
+ * others, which pdattn_reduce completes.
+ */
+PDATTN_API pdattn_status pdattn_decode(const pdattn_plan_t* plan, const void* q, const void* k_pages,
+                                       const void* v_pages, const float* k_scale, const float* v_scale,
+                                       const int32_t* block_table, const int32_t* context_lens,
+                                       void* workspace, uint64_t workspace_bytes, float* out, float* lse,
+                                       void* stream);
+
+/*
+ * Enqueue the split reduce (FlashQuant wiki "CUDA Kernels", split_k_reduce.cu
+ * Algorithm and Numerical Stability) on `stream`: for each sequence with
+ * more than one split, out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
+ * with M = max_s m_s, and lse = ln 2 * (M + log2 sum_s 2^(m_s - M) l_s).
+ * Must follow pdattn_decode with the same plan, workspace and context_lens
+ * on the same stream. Enqueues nothing when plan->max_splits == 1.
+ */
+PDATTN_API pdattn_status pdattn_reduce(const pdattn_plan_t* plan, const void* workspace,
+                                       uint64_t workspace_bytes, const int32_t* context_lens, float* out,
+                                       float* lse, void* stream);
+
+/* Static description of a status code. */
+PDATTN_API const char* pdattn_status_string(pdattn_status status);
+
+/* The last error message of the calling thread ("" if none). */
+PDATTN_API const char* pdattn_last_error(void);
+
+/* sizeof(pdattn_problem) and sizeof(pdattn_plan_t), for binding checks. */
+PDATTN_API uint64_t pdattn_problem_size(void);
+PDATTN_API uint64_t pdattn_plan_size(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PDATTN_H */

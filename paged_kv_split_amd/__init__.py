@@ -1,0 +1,155 @@
+"""Python binding of libpdattn.so: paged split-KV GQA decode attention on
+MI355X (gfx950).
+
+The functions below keep the C-ABI names (``plan``, ``decode``, ``reduce``)
+and only marshal arguments: torch tensors in, device pointers and the
+current HIP stream out. Every step of the computation runs in the library's
+kernels; there is no other code path. Importing this module fails loudly when
+the library has not been built (``python -m paged_kv_split_amd.build``).
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = ["Problem", "Plan", "PdattnError", "plan", "decode", "reduce", "paged_decode",
+           "KV_BF16", "KV_FP8_E4M3", "library_path"]
+
+KV_BF16 = 0
+KV_FP8_E4M3 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libpdattn.so")
+
+if not os.path.exists(library_path):
+    raise ImportError(f"{library_path} is missing: build it with `python -m paged_kv_split_amd.build`")
+
+_lib = ctypes.CDLL(library_path)
+
+
+class Problem(ctypes.Structure):
+    """Mirror of ``pdattn_problem``."""
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
+class Plan(ctypes.Structure):
+    """Mirror of ``pdattn_plan_t``."""
+    _fields_ = [
+        ("problem", Problem),
+        ("split_tokens", ctypes.c_int32),
+        ("max_splits", ctypes.c_int32),
+        ("num_cus", ctypes.c_int32),
+        ("num_work_items", ctypes.c_int32),
+        ("max_context_len", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_uint64),
+        ("magic", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+    ]
+
+
+_P = ctypes.c_void_p
+_lib.pdattn_plan.restype = ctypes.c_int
+_lib.pdattn_plan.argtypes = [ctypes.POINTER(Problem), _P, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(Plan)]
+_lib.pdattn_decode.restype = ctypes.c_int
+_lib.pdattn_decode.argtypes = [ctypes.POINTER(Plan), _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint64, _P, _P, _P]
+_lib.pdattn_reduce.restype = ctypes.c_int
+_lib.pdattn_reduce.argtypes = [ctypes.POINTER(Plan), _P, ctypes.c_uint64, _P, _P, _P, _P]
+_lib.pdattn_status_string.restype = ctypes.c_char_p
+_lib.pdattn_status_string.argtypes = [ctypes.c_int]
+_lib.pdattn_last_error.restype = ctypes.c_char_p
+_lib.pdattn_last_error.argtypes = []
+_lib.pdattn_problem_size.restype = ctypes.c_uint64
+_lib.pdattn_plan_size.restype = ctypes.c_uint64
+
+if _lib.pdattn_problem_size() != ctypes.sizeof(Problem) or _lib.pdattn_plan_size() != ctypes.sizeof(Plan):
+    raise ImportError("libpdattn.so struct layout does not match the binding")
+
+
+class PdattnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = _lib.pdattn_status_string(status).decode()
+        detail = _lib.pdattn_last_error().decode()
+        super().__init__(f"{where}: {msg}" + (f" ({detail})" if detail else ""))
+
+
+def _check(status, where):
+    if status != 0:
+        raise PdattnError(status, where)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def plan(*, batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq, num_pages,
+         kv_dtype=KV_BF16, scale=0.0, context_lens_host, num_cus=0, force_split_tokens=0) -> Plan:
+    """``pdattn_plan``: context_lens_host is a CPU int32 tensor (or sequence)."""
+    lens = torch.as_tensor(context_lens_host, dtype=torch.int32).cpu().contiguous()
+    prob = Problem(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq, num_pages,
+                   kv_dtype, float(scale))
+    out = Plan()
+    _check(_lib.pdattn_plan(ctypes.byref(prob), _ptr(lens), int(num_cus), int(force_split_tokens),
+                            ctypes.byref(out)), "pdattn_plan")
+    return out
+
+
+def decode(pl: Plan, q, k_pages, v_pages, k_scale, v_scale, block_table, context_lens, workspace,
+           out, lse=None, stream=None):
+    """``pdattn_decode`` on device tensors (workspace: a uint8 tensor or None)."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.pdattn_decode(ctypes.byref(pl), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
+                              _ptr(v_scale), _ptr(block_table), _ptr(context_lens), _ptr(workspace),
+                              ws_bytes, _ptr(out), _ptr(lse), _stream(stream)), "pdattn_decode")
+
+
+def reduce(pl: Plan, workspace, context_lens, out, lse=None, stream=None):
+    """``pdattn_reduce`` on device tensors."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.pdattn_reduce(ctypes.byref(pl), _ptr(workspace), ws_bytes, _ptr(context_lens), _ptr(out),
+                              _ptr(lse), _stream(stream)), "pdattn_reduce")
+
+
+def paged_decode(q, k_pages, v_pages, block_table, context_lens, *, context_lens_host=None,
+                 k_scale=None, v_scale=None, scale=None, num_cus=0, force_split_tokens=0,
+                 return_lse=True):
+    """Plan, allocate (torch) and run one decode step; returns (out, lse).
+
+    q: bf16 [B,Hq,d]; k_pages/v_pages: bf16 or float8_e4m3fn [num_pages,P,Hkv,d];
+    block_table int32 [B,max_pages]; context_lens int32 [B] on the device.
+    """
+    B, Hq, D = q.shape
+    num_pages, P, Hkv, _ = k_pages.shape
+    if context_lens_host is None:
+        context_lens_host = context_lens.cpu()
+    kv = KV_FP8_E4M3 if k_pages.dtype == torch.float8_e4m3fn else KV_BF16
+    pl = plan(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=P,
+              max_pages_per_seq=block_table.shape[1], num_pages=num_pages, kv_dtype=kv,
+              scale=0.0 if scale is None else scale, context_lens_host=context_lens_host,
+              num_cus=num_cus, force_split_tokens=force_split_tokens)
+    dev = q.device
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if return_lse else None
+    ws = torch.empty(max(int(pl.workspace_bytes), 16), dtype=torch.uint8, device=dev) \
+        if pl.workspace_bytes else None
+    decode(pl, q, k_pages, v_pages, k_scale, v_scale, block_table, context_lens, ws, out, lse)
+    reduce(pl, ws, context_lens, out, lse)
+    return out, lse

@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark: one paged GQA decode step per timed step.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 20] [--workload llama3_8b]
+
+A step is one pass of the whole hot path, pdattn_decode + pdattn_reduce, over
+one batch of seeded synthetic input already resident in HBM. Before every
+timed step (outside its events) a 512 MiB buffer is rewritten, which evicts
+the L2s and the 256 MB Infinity Cache, so the KV pages are read from HBM.
+
+Prints ONE JSON line. value = KV algorithmic bytes (every K and V element of
+every valid (token, kv head) once, plus the fp8 scales) / mean step time, in
+GB/s. roofline = the same bytes / the mean duration of the partial kernel
+alone (events around that launch on its stream), against MI355X's 8 TB/s HBM
+peak. traffic = measured HBM bytes per launch of that kernel from the
+committed rocprofv3 counter summary, or null when the kernel source has
+changed since the counters were taken. cpu_baseline = the CPU fp64 oracle
+timed on this host's cores on the same step's inputs.
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_split_amd", "csrc", "decode_kernels.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "partial_kernel_llama3_8b_hbm_traffic.txt")
+METRIC = "decode-attn achieved HBM GB/s + µs/call, Llama-3-8B shape, 1×MI355X"
+
+
+def source_digest():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(workload):
+    """Bytes per launch from the committed counter summary, if it still
+    describes the current kernel source and this workload."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    vals = {}
+    with open(TRAFFIC_SUMMARY) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != source_digest() or vals.get("workload") != workload:
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama3_8b")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU time budget of the oracle baseline (0 skips it)")
+    ap.add_argument("--no-flush", action="store_true", help="time with warm caches")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, run 3 device copies of 256 MiB (a plain copy kernel of known "
+                         "size, for scaling the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode "
+              "(each GPU would run the same kernel on its own shard of sequences or kv heads)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import paged_kv_split_amd as pk
+
+    w = synth.WORKLOADS[args.workload]
+    inp = synth.make_inputs(w)
+    dev = torch.device("cuda:0")
+    d = {k: (inp[k].to(dev) if inp[k] is not None else None)
+         for k in ("q", "k_pages", "v_pages", "k_scale", "v_scale", "block_table", "context_lens")}
+    kv_bytes = synth.kv_bytes(w, inp["context_lens"])
+    t0 = time.perf_counter()
+    pl = pk.plan(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                 head_dim=w.head_dim, page_size=w.page_size,
+                 max_pages_per_seq=inp["block_table"].shape[1], num_pages=inp["k_pages"].shape[0],
+                 kv_dtype=pk.KV_BF16 if w.kv_dtype == "bf16" else pk.KV_FP8_E4M3,
+                 context_lens_host=inp["context_lens"])
+    plan_us = (time.perf_counter() - t0) * 1e6
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(int(pl.workspace_bytes), 16), dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def step():
+        pk.decode(pl, d["q"], d["k_pages"], d["v_pages"], d["k_scale"], d["v_scale"], d["block_table"],
+                  d["context_lens"], ws, out, lse)
+        pk.reduce(pl, ws, d["context_lens"], out, lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush.fill_(i & 0xFF)
+        ev[i][0].record()
+        pk.decode(pl, d["q"], d["k_pages"], d["v_pages"], d["k_scale"], d["v_scale"], d["block_table"],
+                  d["context_lens"], ws, out, lse)
+        ev[i][1].record()
+        pk.reduce(pl, ws, d["context_lens"], out, lse)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_us = [e[0].elapsed_time(e[2]) * 1e3 for e in ev]
+    dec_us = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
+    red_us = [e[1].elapsed_time(e[2]) * 1e3 for e in ev]
+    mean_step = statistics.fmean(step_us)
+    mean_dec = statistics.fmean(dec_us)
+    qs = statistics.quantiles(step_us, n=10)
+
+    # warm-cache figure (secondary): same steps without the flush
+    warm = []
+    for _ in range(10):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        torch.cuda.synchronize()
+        warm.append(a.elapsed_time(b) * 1e3)
+    ok = bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
+    if args.calibrate_copy:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            flush.fill_(0)
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        times = []
+        threads = 0
+        start = time.perf_counter()
+        while True:
+            t = time.perf_counter()
+            _, _, threads = oracle.decode(inp["q"], inp["k_pages"], inp["v_pages"], inp["block_table"],
+                                          inp["context_lens"], k_scale=inp["k_scale"],
+                                          v_scale=inp["v_scale"], return_threads=True)
+            times.append(time.perf_counter() - t)
+            if time.perf_counter() - start >= args.cpu_seconds:
+                break
+        per_call = statistics.median(times)
+        cpu = {"value": round(kv_bytes / per_call / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"the full {w.name} step ({w.batch} sequences) repeated {len(times)} times "
+                         f"({sum(times):.1f} s); median {per_call * 1e6:.0f} us/call"}
+
+    traffic = read_traffic(w.name)
+    achieved = kv_bytes / (mean_dec * 1e-6) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": round(kv_bytes / (mean_step * 1e-6) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean_step / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": w.description, "batch": w.batch, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
+                   "context_lens": list(w.lens[1:]) if w.lens[0] == "uniform" else list(w.lens[1]),
+                   "seed": w.seed, "split_tokens": pl.split_tokens, "max_splits": pl.max_splits,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+        "us_per_call": round(mean_step, 2),
+        "us_per_call_p10_p50_p90": [round(qs[0], 2), round(statistics.median(step_us), 2), round(qs[-1], 2)],
+        "partial_kernel_us": round(mean_dec, 2),
+        "reduce_kernel_us": round(statistics.fmean(red_us), 2),
+        "warm_cache_us_per_call": round(statistics.median(warm), 2),
+        "kv_bytes_per_call": kv_bytes,
+        "plan_host_us": round(plan_us, 1),
+        "timed_wall_s": round(wall, 4),
+        "cache_flush_between_steps": not args.no_flush,
+        "outputs_finite": ok,
+        "device": torch.cuda.get_device_name(0),
+        "kernel_source_sha256_16": source_digest(),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -109,28 +109,173 @@ __device__ __forceinline__ uint32_t dword(const T& x, int w) {
   }
 }
 
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8), followed by a
+// compiler barrier so that no LDS access is moved across it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most `ahead` tiles of C loads each are still in flight.
+template <int C, int S>
+__device__ __forceinline__ void wait_tiles(int ahead) {
+  if constexpr (S >= 4) {
+    if (ahead >= 3) { wait_vmcnt<3 * C>(); return; }
+  }
+  if constexpr (S >= 3) {
+    if (ahead >= 2) { wait_vmcnt<2 * C>(); return; }
+  }
+  if (ahead >= 1) { wait_vmcnt<C>(); return; }
+  wait_vmcnt<0>();
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Cache policy of the K/V stream: non-temporal. Each KV byte is read once
+// per call, so it is not kept in L2 or the Infinity Cache; on MI355X this
+// lifts a streaming read from about 4.7 to about 6.9 TB/s.
+constexpr int kStreamPolicy = 2;  // nt
+
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, kStreamPolicy);
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 4, 0, kStreamPolicy);
+}
+
+// LDS byte address of a generic pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Read one ring stage into registers: the lane's K fragments (kf), its four
+// V chunks (V rows row + 4 j; vp points at row `row`) and, for fp8, the k / v
+// scales of its four tokens. One inline-assembly block issues the reads and
+// waits for them (lgkmcnt(0)), so every destination is defined only once
+// its data has landed and no use or copy can be scheduled earlier; the
+// compiler also adds no wait of its own for the ring's direct-to-LDS loads
+// (the caller has waited for them with wait_tiles).
+template <int D, bool FP8, typename VVec, int K_LD>
+__device__ __forceinline__ void read_stage(const unsigned char* kp, const unsigned char* vp, const unsigned char* sp,
+                                           u32x4 (&kf)[K_LD], VVec (&vf)[4], float (&ks)[4], float (&vs)[4]) {
+  const uint32_t ka = lds_addr(kp), va = lds_addr(vp), sa = lds_addr(sp);
+  if constexpr (!FP8 && D == 128) {  // row 256 B: 4 K fragments, V rows 1024 B apart
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b128 %2, %8 offset:2048\n\t"
+        "ds_read_b128 %3, %8 offset:3072\n\t"
+        "ds_read_b128 %4, %9\n\t"
+        "ds_read_b128 %5, %9 offset:1024\n\t"
+        "ds_read_b128 %6, %9 offset:2048\n\t"
+        "ds_read_b128 %7, %9 offset:3072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3]), "=&v"(vf[0]), "=&v"(vf[1]), "=&v"(vf[2]),
+          "=&v"(vf[3])
+        : "v"(ka), "v"(va)
+        : "memory");
+  } else if constexpr (!FP8 && D == 64) {  // row 128 B: 2 K fragments, 8-byte V chunks 512 B apart
+    asm volatile(
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %6 offset:1024\n\t"
+        "ds_read_b64 %2, %7\n\t"
+        "ds_read_b64 %3, %7 offset:512\n\t"
+        "ds_read_b64 %4, %7 offset:1024\n\t"
+        "ds_read_b64 %5, %7 offset:1536\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(vf[0]), "=&v"(vf[1]), "=&v"(vf[2]), "=&v"(vf[3])
+        : "v"(ka), "v"(va)
+        : "memory");
+  } else if constexpr (FP8 && D == 128) {  // row 128 B, plus two scale quads
+    f32x4 a, c;
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b64 %2, %9\n\t"
+        "ds_read_b64 %3, %9 offset:512\n\t"
+        "ds_read_b64 %4, %9 offset:1024\n\t"
+        "ds_read_b64 %5, %9 offset:1536\n\t"
+        "ds_read_b128 %6, %10\n\t"
+        "ds_read_b128 %7, %10 offset:64\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(vf[0]), "=&v"(vf[1]), "=&v"(vf[2]), "=&v"(vf[3]), "=&v"(a), "=&v"(c)
+        : "v"(ka), "v"(va), "v"(sa)
+        : "memory");
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      ks[v] = a[v];
+      vs[v] = c[v];
+    }
+  } else {  // fp8, D == 64: row 64 B: 1 K fragment, 4-byte V chunks 256 B apart
+    static_assert(FP8 && D == 64, "layout");
+    f32x4 a, c;
+    asm volatile(
+        "ds_read_b128 %0, %7\n\t"
+        "ds_read_b32 %1, %8\n\t"
+        "ds_read_b32 %2, %8 offset:256\n\t"
+        "ds_read_b32 %3, %8 offset:512\n\t"
+        "ds_read_b32 %4, %8 offset:768\n\t"
+        "ds_read_b128 %5, %9\n\t"
+        "ds_read_b128 %6, %9 offset:64\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kf[0]), "=&v"(vf[0]), "=&v"(vf[1]), "=&v"(vf[2]), "=&v"(vf[3]), "=&v"(a), "=&v"(c)
+        : "v"(ka), "v"(va), "v"(sa)
+        : "memory");
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      ks[v] = a[v];
+      vs[v] = c[v];
+    }
+  }
+}
+
+// Token order inside a 16-token tile. MFMA A-row m carries token
+// tile_token(m) = m / 4 + 4 (m mod 4), so the result row 4 r + v held by
+// 16-lane row r is token r + 4 v: every 16-lane row owns the tokens
+// congruent to r mod 4, for the scores as well as for the V rows it reads.
+__device__ __forceinline__ int tile_token(int m) { return (m >> 2) + 4 * (m & 3); }
+
 template <int D, int G, bool FP8>
 __global__ __launch_bounds__(kWaves * 64) void partial_kernel(DecodeParams p) {
-  constexpr int ESZ = FP8 ? 1 : 2;           // bytes per stored element
-  constexpr int ROW_BYTES = D * ESZ;         // one (token, kv head) row
-  constexpr int KSTEPS = D / 32;             // MFMA k-steps over head_dim
-  constexpr int K_LD = ROW_BYTES / 64;       // 16-byte K loads per lane per tile
-  constexpr int VE = D / 16;                 // V elements per lane per row
-  constexpr int VB = VE * ESZ;               // V bytes per lane per row
+  constexpr int ESZ = FP8 ? 1 : 2;             // bytes per stored element
+  constexpr int ROW_BYTES = D * ESZ;           // one (token, kv head) row
+  constexpr int KSTEPS = D / 32;               // MFMA k-steps over head_dim
+  constexpr int K_LD = ROW_BYTES / 64;         // 16-byte loads per lane per tile, K
+  constexpr int V_LD = ROW_BYTES / 64;         // and V (a tile is 16 rows)
+  constexpr int C = K_LD + V_LD + (FP8 ? 1 : 0);  // DMA instructions per tile
+  constexpr int VE = D / 16;                   // V elements per lane per row
+  constexpr int VB = VE * ESZ;                 // V bytes per lane per row
   constexpr int NT = kWaves * 64;
+  constexpr int S = kStages;
+  // one ring stage: K tile in MFMA-operand lane order, V tile row-major,
+  // then (fp8) 64 scale slots: k scales 0..15, v scales 16..31
+  constexpr int K_TILE = kTileTokens * ROW_BYTES;
+  constexpr int V_TILE = kTileTokens * ROW_BYTES;
+  constexpr int STAGE = K_TILE + V_TILE + (FP8 ? 256 : 0);
+  constexpr int RING = kWaves * S * STAGE;
+  constexpr int MERGE = kWaves * G * (D + 2) * 4;
+  constexpr int UNION = RING > MERGE ? RING : MERGE;
   using VVec = typename VChunk<VB>::type;
   static_assert(K_LD >= 1 && (D == 64 || D == 128), "head_dim");
   static_assert(G >= 1 && G <= 16, "group size");
+  static_assert(C * (S - 1) < 64, "vmcnt range");
 
-  // LDS: the split's block-table slice, then the per-wave softmax states.
+  // LDS: per-wave load rings (reused for the cross-wave merge after the tile
+  // loop), then the split's block-table slice.
+  __shared__ __attribute__((aligned(16))) unsigned char s_mem[UNION];
   __shared__ int s_pages[kMaxPageList];
-  __shared__ float s_m[kWaves][G];
-  __shared__ float s_l[kWaves][G];
-  __shared__ float s_acc[kWaves][G][D];  // row-major [wave][head][d]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int col = lane & 15;   // MFMA column / V chunk index
   const int row = lane >> 4;   // 16-lane row
 
@@ -151,7 +296,7 @@ __global__ __launch_bounds__(kWaves * 64) void partial_kernel(DecodeParams p) {
   const int lp = p.page_log2;
   const int P = 1 << lp;
 
-  const int L = p.context_lens[b];
+  const int L = __builtin_amdgcn_readfirstlane(p.context_lens[b]);
   const int64_t cap = (int64_t)p.max_pages_per_seq << lp;
   const int nsplit = L > 0 ? (int)(((int64_t)L + p.split_tokens - 1) / p.split_tokens) : 0;
   if (L <= 0 || (int64_t)L > cap || nsplit > p.max_splits) {
@@ -209,44 +354,51 @@ __global__ __launch_bounds__(kWaves * 64) void partial_kernel(DecodeParams p) {
   }
   __syncthreads();
 
-  struct Tile {
-    u32x4 k[K_LD];
-    VVec v[4];
-    float ks[4];
-    float vs[4];
-  };
-
   auto page_of = [&](int pos) -> int {
     const int idx = min((pos >> lp) - pg0, kMaxPageList - 1);
     return s_pages[idx];
   };
+  // (token, kv head) row index of sequence position pos
+  auto row_of = [&](int pos) -> int64_t {
+    return ((((int64_t)page_of(pos)) << lp) + (pos & (P - 1))) * Hkv + kvh;
+  };
 
-  // Issue the loads of tile i into registers T. Rows past the split's last
-  // token are clamped onto that token (finite data, masked in the softmax).
-  auto load_tile = [&](Tile& T, int i) {
-    const int tb = s0 + i * kTileTokens;
+  unsigned char* ring = s_mem + wave * (S * STAGE);
+  // this wave's tiles: i = wave + k * kWaves, k < nk
+  const int nk = wave < ntiles ? (ntiles - 1 - wave) / kWaves + 1 : 0;
+
+  // Issue the C direct-to-LDS loads of local tile k into stage k % S. Rows
+  // past the split's last token are clamped onto that token (finite data,
+  // masked in the softmax).
+  auto issue = [&](int k) {
+    unsigned char* st = ring + (k % S) * STAGE;
+    const int tb = s0 + (wave + k * kWaves) * kTileTokens;
     {
-      const int pos = min(tb + col, s1 - 1);
-      const int64_t r = ((((int64_t)page_of(pos)) << lp) + (pos & (P - 1))) * Hkv + kvh;
-      const uint8_t* src = p.k + r * ROW_BYTES + row * 16;
+      // K: lane (row, col) fetches bytes [j*64 + row*16, +16) of token
+      // tile_token(col); it lands at j*1024 + lane*16, the lane's own
+      // A-operand fragment for k-steps 2j, 2j+1 (fp8) or j (bf16).
+      const int pos = min(tb + tile_token(col), s1 - 1);
+      const unsigned char* src = p.k + row_of(pos) * ROW_BYTES + row * 16;
 #pragma unroll
-      for (int j = 0; j < K_LD; ++j) T.k[j] = *reinterpret_cast<const u32x4*>(src + j * 64);
+      for (int j = 0; j < K_LD; ++j) dma16(src + j * 64, st + j * 1024 + lane * 16);
     }
     {
-      // tokens tb + 4 row + j, j < 4, lie in one aligned 4-token block and
-      // so in one page (P >= 8)
-      const int base = min(tb + 4 * row, s1 - 1);
-      const int64_t pr = ((int64_t)page_of(base)) << lp;
+      // V: row-major tile, 64 lanes x 16 bytes per load
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int pos = min(tb + 4 * row + j, s1 - 1);
-        const int64_t r = (pr + (pos & (P - 1))) * Hkv + kvh;
-        T.v[j] = *reinterpret_cast<const VVec*>(p.v + r * ROW_BYTES + col * VB);
-        if constexpr (FP8) {
-          T.ks[j] = p.k_scale[r];
-          T.vs[j] = p.v_scale[r];
-        }
+      for (int j = 0; j < V_LD; ++j) {
+        const int byte = j * 1024 + lane * 16;
+        const int r = byte / ROW_BYTES;
+        const int pos = min(tb + r, s1 - 1);
+        dma16(p.v + row_of(pos) * ROW_BYTES + (byte % ROW_BYTES), st + K_TILE + j * 1024 + lane * 16);
       }
+    }
+    if constexpr (FP8) {
+      // scale slot m < 16 holds k_scale of token tile_token(m); slot 16 + m
+      // holds its v_scale; lanes 32..63 repeat lanes 0..31
+      const int m = lane & 15;
+      const int pos = min(tb + tile_token(m), s1 - 1);
+      const float* src = ((lane & 16) ? p.v_scale : p.k_scale) + row_of(pos);
+      dma4(src, st + K_TILE + V_TILE + lane * 4);
     }
   };
 
@@ -258,27 +410,44 @@ __global__ __launch_bounds__(kWaves * 64) void partial_kernel(DecodeParams p) {
 #pragma unroll
     for (int e = 0; e < VE; ++e) acc[g][e] = 0.0f;
 
-  auto compute_tile = [&](const Tile& T, int i) {
-    const int tb = s0 + i * kTileTokens;
-    // S[t][g] for t = 4 row + v, g = col
-    f32x4 S = {0.0f, 0.0f, 0.0f, 0.0f};
+  // prologue: fill the ring
+#pragma unroll
+  for (int k = 0; k < S; ++k)
+    if (k < nk) issue(k);
+
+  for (int k = 0; k < nk; ++k) {
+    // tiles k+1 .. min(k+S-1, nk-1) may stay in flight
+    wait_tiles<C, S>(min(S - 1, nk - 1 - k));
+    const unsigned char* st = ring + (k % S) * STAGE;
+    u32x4 kf[K_LD];
+    VVec vf_raw[4];
+    float ks[4], vs[4];
+    read_stage<D, FP8>(
+        st + lane * 16, st + K_TILE + row * ROW_BYTES + col * VB, st + K_TILE + V_TILE + row * 16, kf, vf_raw,
+        ks, vs);
+    // the stage's reads have returned (read_stage waits for them): refill it
+    if (k + S < nk) issue(k + S);
+
+    const int tb = s0 + (wave + k * kWaves) * kTileTokens;
+    // S[t][g]: lane (row, col) holds head col for tokens row + 4 v
+    f32x4 Sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       u32x4 kw;
       if constexpr (FP8) {
-        const u32x4& c = T.k[kk >> 1];
+        const u32x4& c = kf[kk >> 1];
         kw = fp8x8_to_bf16x8(c[(kk & 1) * 2], c[(kk & 1) * 2 + 1]);
       } else {
-        kw = T.k[kk];
+        kw = kf[kk];
       }
-      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw), qop[kk], S, 0, 0, 0);
+      Sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw), qop[kk], Sacc, 0, 0, 0);
     }
     float s[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      float x = S[v] * p.qk_scale_log2;
-      if constexpr (FP8) x *= T.ks[v];
-      s[v] = (tb + 4 * row + v < s1) ? x : -__builtin_inff();
+      float x = Sacc[v] * p.qk_scale_log2;
+      if constexpr (FP8) x *= ks[v];
+      s[v] = (tb + row + 4 * v < s1) ? x : -__builtin_inff();
     }
     float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -301,15 +470,16 @@ __global__ __launch_bounds__(kWaves * 64) void partial_kernel(DecodeParams p) {
     }
     if constexpr (FP8) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) pr[v] *= T.vs[v];
+      for (int v = 0; v < 4; ++v) pr[v] *= vs[v];
     }
+    // p . V: lane (row, col) takes V row (token) row + 4 j, d-chunk col
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float vf[VE];
       if constexpr (FP8) {
 #pragma unroll
         for (int w = 0; w < VB / 4; ++w) {
-          const uint32_t x = dword(T.v[j], w);
+          const uint32_t x = dword(vf_raw[j], w);
           auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(x, false);
           auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(x, true);
           vf[4 * w + 0] = lo[0];
@@ -320,7 +490,7 @@ __global__ __launch_bounds__(kWaves * 64) void partial_kernel(DecodeParams p) {
       } else {
 #pragma unroll
         for (int w = 0; w < VB / 4; ++w) {
-          const uint32_t x = dword(T.v[j], w);
+          const uint32_t x = dword(vf_raw[j], w);
           vf[2 * w + 0] = bf16_lo(x);
           vf[2 * w + 1] = bf16_hi(x);
         }
@@ -332,24 +502,6 @@ __global__ __launch_bounds__(kWaves * 64) void partial_kernel(DecodeParams p) {
 #pragma unroll
         for (int e = 0; e < VE; ++e) acc[g][e] = fmaf(pg, vf[e], acc[g][e]);
       });
-    }
-  };
-
-  // Two register sets: the next tile's loads are in flight while the
-  // current tile is computed.
-  {
-    Tile t0, t1;
-    int i = wave;
-    if (i < ntiles) load_tile(t0, i);
-    while (i < ntiles) {
-      const int i1 = i + kWaves;
-      if (i1 < ntiles) load_tile(t1, i1);
-      compute_tile(t0, i);
-      if (i1 >= ntiles) break;
-      const int i2 = i1 + kWaves;
-      if (i2 < ntiles) load_tile(t0, i2);
-      compute_tile(t1, i1);
-      i = i2;
     }
   }
 
@@ -365,14 +517,20 @@ __global__ __launch_bounds__(kWaves * 64) void partial_kernel(DecodeParams p) {
       a += __shfl_xor(a, 32);
       acc[g][e] = a;
     }
+  // every wave has drained its ring (the last wait was vmcnt(0)); the ring
+  // memory now holds the per-wave states: acc [wave][g][D], m, l [wave][g]
+  __syncthreads();
+  float* s_acc = reinterpret_cast<float*>(s_mem);
+  float* s_m = s_acc + kWaves * G * D;
+  float* s_l = s_m + kWaves * G;
   if (row == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int e = 0; e < VE; ++e) s_acc[wave][g][col * VE + e] = acc[g][e];
+      for (int e = 0; e < VE; ++e) s_acc[(wave * G + g) * D + col * VE + e] = acc[g][e];
     if (col < G) {
-      s_m[wave][col] = m_run;
-      s_l[wave][col] = l_run;
+      s_m[wave * G + col] = m_run;
+      s_l[wave * G + col] = l_run;
     }
   }
   const int any_bad = __syncthreads_or(bad);
@@ -383,13 +541,13 @@ __global__ __launch_bounds__(kWaves * 64) void partial_kernel(DecodeParams p) {
     const int d = idx % D;
     float M = -__builtin_inff();
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][g]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w * G + g]);
     float A = 0.0f, Ls = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float f = __builtin_amdgcn_exp2f(s_m[w][g] - M);
-      A = fmaf(f, s_acc[w][g][d], A);
-      Ls = fmaf(f, s_l[w][g], Ls);
+      const float f = __builtin_amdgcn_exp2f(s_m[w * G + g] - M);
+      A = fmaf(f, s_acc[(w * G + g) * D + d], A);
+      Ls = fmaf(f, s_l[w * G + g], Ls);
     }
     const int64_t bh = (int64_t)b * Hq + h0 + g;
     const float nan = __builtin_nanf("");

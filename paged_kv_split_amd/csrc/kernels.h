@@ -15,6 +15,8 @@ constexpr int kMaxPageList = 1024;
 constexpr int kWaves = 4;
 // Tokens per tile: the M extent of one 16x16x32 MFMA.
 constexpr int kTileTokens = 16;
+// Stages of each wave's direct-to-LDS load ring (tiles in flight).
+constexpr int kStages = 2;
 
 struct DecodeParams {
   const uint16_t* q;          // bf16 bits [B][Hq][D]

@@ -96,13 +96,13 @@ def main():
     plan_us = (time.perf_counter() - t0) * 1e6
     out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
     lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(int(pl.workspace_bytes), 16), dtype=torch.uint8, device=dev)
+    ws = pk.workspace(pl, dev)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
     def step():
         pk.decode(pl, d["q"], d["k_pages"], d["v_pages"], d["k_scale"], d["v_scale"], d["block_table"],
                   d["context_lens"], ws, out, lse)
-        pk.reduce(pl, ws, d["context_lens"], out, lse)
+        pk.reduce(pl, ws, out, lse)
 
     for _ in range(args.warmup):
         step()
@@ -118,7 +118,7 @@ def main():
         pk.decode(pl, d["q"], d["k_pages"], d["v_pages"], d["k_scale"], d["v_scale"], d["block_table"],
                   d["context_lens"], ws, out, lse)
         ev[i][1].record()
-        pk.reduce(pl, ws, d["context_lens"], out, lse)
+        pk.reduce(pl, ws, out, lse)
         ev[i][2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -186,7 +186,7 @@ def main():
         "config": {"workload": w.description, "batch": w.batch, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
                    "context_lens": list(w.lens[1:]) if w.lens[0] == "uniform" else list(w.lens[1]),
-                   "seed": w.seed, "split_tokens": pl.split_tokens, "max_splits": pl.max_splits,
+                   "seed": w.seed, "workers": pl.num_workers, "workgroups": pl.num_workgroups,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},

@@ -15,13 +15,14 @@
  *     lse[b][h]    = ln sum_t exp(s_t)            (natural log)
  *   L == 0 gives out = 0 and lse = -inf.
  *
- * The KV sequence of every (b, kvh) is cut into splits of plan.split_tokens
- * tokens (flash-decoding). One workgroup computes one split for all G query
- * heads of one kv head with an online softmax (running max and sum in base 2,
- * fp32 accumulators) and, for a sequence with more than one split, writes
- * (m, l, acc) partials to the workspace; pdattn_reduce merges them with the
- * log-sum-exp rule. A sequence that fits in one split is written to `out`
- * directly by pdattn_decode.
+ * Work decomposition (flash-decoding): the (b, kvh) pairs are laid end to
+ * end, each cut into 16-token tiles, and a persistent grid of
+ * plan->num_workers waves takes equal contiguous ranges of that tile list.
+ * A wave computes all G query heads of a kv head with an online softmax
+ * (running max and sum in base 2, fp32 accumulators). A pair covered by one
+ * wave is written to `out` by pdattn_decode; a pair cut by wave boundaries
+ * leaves per-piece (m, l, acc) partials in the workspace, which
+ * pdattn_reduce merges with the log-sum-exp rule.
  *
  * Layouts (all contiguous, row-major):
  *   q            bf16 [B][Hq][d]
@@ -47,9 +48,9 @@
  * Errors: every call validates its arguments before launching anything and
  * returns a status; an invalid call enqueues no work. The last error message
  * of the calling thread is available from pdattn_last_error(). On the
- * device, a context length beyond the plan's capacity or beyond the block
- * table, and a block_table entry outside [0, num_pages), are not read
- * through: the affected (b, h) outputs are set to NaN instead.
+ * device, a context length that is negative or beyond the block table
+ * (max_pages_per_seq * P), and a block_table entry outside [0, num_pages),
+ * are not read through: the affected outputs are set to NaN instead.
  */
 #ifndef PDATTN_H
 #define PDATTN_H
@@ -95,17 +96,20 @@ typedef struct pdattn_problem {
 /* A launch plan: a pure function of the problem, the host copy of the
  * context lengths and the compute-unit count (OASR "Kernel Layer", Fused
  * attention: the split count depends on shape and machine only; Atlas
- * "CUDA Kernel Engineering", kernel inventory: adaptive split count). */
+ * "CUDA Kernel Engineering", kernel inventory: adaptive split count). The
+ * kernels re-derive the split points from the device context_lens, so the
+ * workspace size does not depend on the lengths. */
 typedef struct pdattn_plan_t {
   pdattn_problem problem;   /* copy of the problem, scale resolved */
-  int32_t split_tokens;     /* tokens per split, a multiple of 16 */
-  int32_t max_splits;       /* largest number of splits of any sequence */
   int32_t num_cus;          /* compute units the plan was sized for */
-  int32_t num_work_items;   /* sum over sequences of splits, times Hkv */
+  int32_t num_workgroups;   /* grid of the decode kernel (4 waves each) */
+  int32_t num_workers;      /* waves that own tile ranges, <= 4 * num_workgroups */
+  int32_t reserved0;
+  int64_t total_tiles;      /* Hkv * sum_b ceil(L_b / 16) over the host lengths */
   int64_t max_context_len;  /* largest host context length planned for */
-  uint64_t workspace_bytes; /* 0 when max_splits == 1 */
+  uint64_t workspace_bytes; /* partial records and merge descriptors */
   uint32_t magic;           /* set by pdattn_plan; checked by decode / reduce */
-  uint32_t reserved;
+  uint32_t reserved1;
 } pdattn_plan_t;
 
 /*
@@ -113,21 +117,23 @@ typedef struct pdattn_plan_t {
  *   problem            shape; validated here (supported set above)
  *   context_lens_host  host int32 [batch]; each 0 <= L <= max_pages_per_seq * P
  *   num_cus            compute units to size for; 0 queries the current device
- *   force_split_tokens 0 = adaptive; > 0 forces this split length (rounded up
- *                      to a multiple of 16; used by tests)
+ *   force_workers      0 = adaptive (fill the device's resident capacity, at
+ *                      least 4 tiles per worker); > 0 forces this number of
+ *                      worker waves (tests use it to move the split points)
  *   out                receives the plan (caller-owned POD)
  * Pure host computation apart from the optional device query.
  */
 PDATTN_API pdattn_status pdattn_plan(const pdattn_problem* problem, const int32_t* context_lens_host,
-                                     int32_t num_cus, int32_t force_split_tokens, pdattn_plan_t* out);
+                                     int32_t num_cus, int32_t force_workers, pdattn_plan_t* out);
 
 /*
  * Enqueue the split-KV partial pass on `stream` (a hipStream_t; NULL = the
  * null stream). Pointers and layouts as described above; k_scale / v_scale
- * must be NULL for bf16 pools and non-NULL for fp8 pools. `workspace` may be
- * NULL only when plan->workspace_bytes == 0. Writes `out` (and `lse`) for
- * every sequence with at most one split; writes workspace partials for the
- * others, which pdattn_reduce completes.
+ * must be NULL for bf16 pools and non-NULL for fp8 pools; `workspace` holds
+ * plan->workspace_bytes bytes (contents need no initialisation). Writes
+ * `out` (and `lse`) for every (b, kvh) pair that one worker covers, and for
+ * empty or invalid sequences; leaves partials and descriptors in the
+ * workspace for the cut pairs, which pdattn_reduce completes.
  */
 PDATTN_API pdattn_status pdattn_decode(const pdattn_plan_t* plan, const void* q, const void* k_pages,
                                        const void* v_pages, const float* k_scale, const float* v_scale,
@@ -137,15 +143,13 @@ PDATTN_API pdattn_status pdattn_decode(const pdattn_plan_t* plan, const void* q,
 
 /*
  * Enqueue the split reduce (FlashQuant wiki "CUDA Kernels", split_k_reduce.cu
- * Algorithm and Numerical Stability) on `stream`: for each sequence with
- * more than one split, out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
- * with M = max_s m_s, and lse = ln 2 * (M + log2 sum_s 2^(m_s - M) l_s).
- * Must follow pdattn_decode with the same plan, workspace and context_lens
- * on the same stream. Enqueues nothing when plan->max_splits == 1.
+ * Algorithm and Numerical Stability) on `stream`: for each pair cut into
+ * pieces s, out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s with
+ * M = max_s m_s, and lse = ln 2 * (M + log2 sum_s 2^(m_s - M) l_s). Must
+ * follow pdattn_decode with the same plan and workspace on the same stream.
  */
 PDATTN_API pdattn_status pdattn_reduce(const pdattn_plan_t* plan, const void* workspace,
-                                       uint64_t workspace_bytes, const int32_t* context_lens, float* out,
-                                       float* lse, void* stream);
+                                       uint64_t workspace_bytes, float* out, float* lse, void* stream);
 
 /* Static description of a status code. */
 PDATTN_API const char* pdattn_status_string(pdattn_status status);

@@ -12,7 +12,7 @@ import os
 
 import torch
 
-__all__ = ["Problem", "Plan", "PdattnError", "plan", "decode", "reduce", "paged_decode",
+__all__ = ["Problem", "Plan", "PdattnError", "plan", "decode", "reduce", "workspace", "paged_decode",
            "KV_BF16", "KV_FP8_E4M3", "library_path"]
 
 KV_BF16 = 0
@@ -46,14 +46,15 @@ class Plan(ctypes.Structure):
     """Mirror of ``pdattn_plan_t``."""
     _fields_ = [
         ("problem", Problem),
-        ("split_tokens", ctypes.c_int32),
-        ("max_splits", ctypes.c_int32),
         ("num_cus", ctypes.c_int32),
-        ("num_work_items", ctypes.c_int32),
+        ("num_workgroups", ctypes.c_int32),
+        ("num_workers", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
+        ("total_tiles", ctypes.c_int64),
         ("max_context_len", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_uint64),
         ("magic", ctypes.c_uint32),
-        ("reserved", ctypes.c_uint32),
+        ("reserved1", ctypes.c_uint32),
     ]
 
 
@@ -63,7 +64,7 @@ _lib.pdattn_plan.argtypes = [ctypes.POINTER(Problem), _P, ctypes.c_int32, ctypes
 _lib.pdattn_decode.restype = ctypes.c_int
 _lib.pdattn_decode.argtypes = [ctypes.POINTER(Plan), _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint64, _P, _P, _P]
 _lib.pdattn_reduce.restype = ctypes.c_int
-_lib.pdattn_reduce.argtypes = [ctypes.POINTER(Plan), _P, ctypes.c_uint64, _P, _P, _P, _P]
+_lib.pdattn_reduce.argtypes = [ctypes.POINTER(Plan), _P, ctypes.c_uint64, _P, _P, _P]
 _lib.pdattn_status_string.restype = ctypes.c_char_p
 _lib.pdattn_status_string.argtypes = [ctypes.c_int]
 _lib.pdattn_last_error.restype = ctypes.c_char_p
@@ -101,13 +102,13 @@ def _stream(stream):
 
 
 def plan(*, batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq, num_pages,
-         kv_dtype=KV_BF16, scale=0.0, context_lens_host, num_cus=0, force_split_tokens=0) -> Plan:
+         kv_dtype=KV_BF16, scale=0.0, context_lens_host, num_cus=0, force_workers=0) -> Plan:
     """``pdattn_plan``: context_lens_host is a CPU int32 tensor (or sequence)."""
     lens = torch.as_tensor(context_lens_host, dtype=torch.int32).cpu().contiguous()
     prob = Problem(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq, num_pages,
                    kv_dtype, float(scale))
     out = Plan()
-    _check(_lib.pdattn_plan(ctypes.byref(prob), _ptr(lens), int(num_cus), int(force_split_tokens),
+    _check(_lib.pdattn_plan(ctypes.byref(prob), _ptr(lens), int(num_cus), int(force_workers),
                             ctypes.byref(out)), "pdattn_plan")
     return out
 
@@ -121,15 +122,20 @@ def decode(pl: Plan, q, k_pages, v_pages, k_scale, v_scale, block_table, context
                               ws_bytes, _ptr(out), _ptr(lse), _stream(stream)), "pdattn_decode")
 
 
-def reduce(pl: Plan, workspace, context_lens, out, lse=None, stream=None):
+def reduce(pl: Plan, workspace, out, lse=None, stream=None):
     """``pdattn_reduce`` on device tensors."""
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(_lib.pdattn_reduce(ctypes.byref(pl), _ptr(workspace), ws_bytes, _ptr(context_lens), _ptr(out),
-                              _ptr(lse), _stream(stream)), "pdattn_reduce")
+    _check(_lib.pdattn_reduce(ctypes.byref(pl), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
+                              _stream(stream)), "pdattn_reduce")
+
+
+def workspace(pl: Plan, device):
+    """A torch-allocated workspace of the plan's size."""
+    return torch.empty(int(pl.workspace_bytes), dtype=torch.uint8, device=device)
 
 
 def paged_decode(q, k_pages, v_pages, block_table, context_lens, *, context_lens_host=None,
-                 k_scale=None, v_scale=None, scale=None, num_cus=0, force_split_tokens=0,
+                 k_scale=None, v_scale=None, scale=None, num_cus=0, force_workers=0,
                  return_lse=True):
     """Plan, allocate (torch) and run one decode step; returns (out, lse).
 
@@ -144,12 +150,11 @@ def paged_decode(q, k_pages, v_pages, block_table, context_lens, *, context_lens
     pl = plan(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=P,
               max_pages_per_seq=block_table.shape[1], num_pages=num_pages, kv_dtype=kv,
               scale=0.0 if scale is None else scale, context_lens_host=context_lens_host,
-              num_cus=num_cus, force_split_tokens=force_split_tokens)
+              num_cus=num_cus, force_workers=force_workers)
     dev = q.device
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if return_lse else None
-    ws = torch.empty(max(int(pl.workspace_bytes), 16), dtype=torch.uint8, device=dev) \
-        if pl.workspace_bytes else None
+    ws = workspace(pl, dev)
     decode(pl, q, k_pages, v_pages, k_scale, v_scale, block_table, context_lens, ws, out, lse)
-    reduce(pl, ws, context_lens, out, lse)
+    reduce(pl, ws, out, lse)
     return out, lse

@@ -7,16 +7,46 @@
 
 namespace pdattn {
 
-// Entries of one split's block-table slice staged in LDS. The planner keeps
-// ceil(split_tokens / page_size) + 1 within this bound.
-constexpr int kMaxPageList = 1024;
-// Waves per workgroup of the partial kernel; each wave owns every
-// kWaves-th 16-token tile of the workgroup's split.
+// Waves per workgroup of the decode kernel. Waves are independent workers;
+// the workgroup only shares the length scan that places them.
 constexpr int kWaves = 4;
 // Tokens per tile: the M extent of one 16x16x32 MFMA.
 constexpr int kTileTokens = 16;
 // Stages of each wave's direct-to-LDS load ring (tiles in flight).
-constexpr int kStages = 2;
+#ifndef PDATTN_STAGES
+#define PDATTN_STAGES 2
+#endif
+constexpr int kStages = PDATTN_STAGES;
+// Block-table entries a wave stages in LDS at a time.
+constexpr int kPagesPerWave = 256;
+// Fewest tiles the planner gives one worker wave.
+constexpr int kMinTilesPerWorker = 4;
+// Words of one worker's merge descriptor.
+constexpr int kDescWords = 8;
+
+constexpr int kv_row_bytes(int head_dim, bool fp8) { return head_dim * (fp8 ? 1 : 2); }
+
+// LDS bytes of one decode workgroup: per wave an S-stage ring (K tile, V
+// tile, fp8 scales) and a block-table buffer, plus the length-scan scratch.
+constexpr int decode_lds_bytes(int head_dim, bool fp8) {
+  return kWaves * (kStages * (2 * kTileTokens * kv_row_bytes(head_dim, fp8) + (fp8 ? 256 : 0)) +
+                   kPagesPerWave * 4) +
+         512;
+}
+
+// Resident decode workgroups per compute unit when no device can be asked
+// (160 KB LDS; 512 VGPRs per SIMD lane, 4 SIMDs; one wave per SIMD per
+// workgroup), from upper bounds of the builds' register counts.
+constexpr int decode_wgs_per_cu_estimate(int head_dim, int group, bool fp8) {
+  const int by_lds = (160 * 1024) / decode_lds_bytes(head_dim, fp8);
+  const int vgprs = group >= 8 ? 256 : 168;
+  const int by_vgpr = 512 / vgprs;
+  const int n = by_lds < by_vgpr ? by_lds : by_vgpr;
+  return n < 1 ? 1 : n;
+}
+
+// Floats of one worker's partial record: m[G], l[G], acc[G][D].
+constexpr int64_t record_floats(int head_dim, int group) { return (int64_t)group * (head_dim + 2); }
 
 struct DecodeParams {
   const uint16_t* q;          // bf16 bits [B][Hq][D]
@@ -28,35 +58,34 @@ struct DecodeParams {
   const int32_t* context_lens;
   float* out;                 // [B][Hq][D]
   float* lse;                 // [B][Hq] or null
-  float* part_acc;            // [B][Hq][max_splits][D]
-  float* part_ml;             // [B][Hq][max_splits][2] = (m, l), base-2 units
+  float* rec;                 // [num_workers][2][record_floats]
+  int32_t* desc;              // [num_workers][kDescWords]
+  int32_t batch;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t page_log2;
   int32_t max_pages_per_seq;
   int32_t num_pages;
-  int32_t split_tokens;
-  int32_t max_splits;
-  int32_t num_units;          // B * max_splits
+  int32_t num_workers;        // waves of the grid that own tile ranges
   float qk_scale_log2;        // softmax scale * log2(e)
 };
 
-struct ReduceParams {
-  const float* part_acc;
-  const float* part_ml;
-  const int32_t* context_lens;
+struct MergeParams {
+  const float* rec;
+  const int32_t* desc;
   float* out;
   float* lse;
   int32_t num_q_heads;
-  int32_t page_log2;
-  int32_t max_pages_per_seq;
-  int32_t split_tokens;
-  int32_t max_splits;
+  int32_t num_workers;
 };
 
+// Resident workgroups per compute unit of one decode instantiation, from the
+// runtime's occupancy query; 0 when it cannot be asked.
+int decode_wgs_per_cu(int head_dim, int group, bool fp8);
+
 // Returns hipErrorInvalidValue for an instantiation that is not built.
-hipError_t launch_partial(const DecodeParams& p, int head_dim, int group, bool fp8, uint32_t grid,
-                          hipStream_t stream);
-hipError_t launch_reduce(const ReduceParams& p, int head_dim, uint32_t grid, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, bool fp8, uint32_t grid,
+                         hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, int head_dim, int group, uint32_t grid, hipStream_t stream);
 
 }  // namespace pdattn

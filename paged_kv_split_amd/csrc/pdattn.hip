@@ -14,14 +14,7 @@
 
 namespace {
 
-constexpr uint32_t kPlanMagic = 0x70644131u;  // "pdA1"
-// Target number of resident workgroups per compute unit that the adaptive
-// planner sizes the split length for.
-constexpr int kWorkgroupsPerCu = 4;
-// Shortest adaptive split: one 16-token tile per wave of the workgroup.
-constexpr int kMinSplitTokens = pdattn::kTileTokens * pdattn::kWaves;
-// Upper bound on splits per sequence (workspace rows per (b, h)).
-constexpr int kMaxSplits = 1024;
+constexpr uint32_t kPlanMagic = 0x70644132u;  // "pdA2"
 
 thread_local char g_last_error[512] = "";
 
@@ -40,7 +33,6 @@ int ilog2(int64_t x) {
   return r;
 }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-int64_t round_up(int64_t a, int64_t m) { return ceil_div(a, m) * m; }
 bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
 
 pdattn_status check_problem(const pdattn_problem* p) {
@@ -61,10 +53,23 @@ pdattn_status check_problem(const pdattn_problem* p) {
     return fail(PDATTN_ERR_UNSUPPORTED, "page_size %d is not a power of two in [8, 128]", p->page_size);
   if (p->max_pages_per_seq < 0 || p->num_pages < 0)
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "negative block table or pool size");
+  if ((int64_t)p->max_pages_per_seq * p->page_size > INT32_MAX)
+    return fail(PDATTN_ERR_UNSUPPORTED, "max_pages_per_seq * page_size exceeds 2^31 - 1 tokens");
   if (p->kv_dtype != PDATTN_KV_BF16 && p->kv_dtype != PDATTN_KV_FP8_E4M3)
     return fail(PDATTN_ERR_UNSUPPORTED, "kv_dtype %d unknown", p->kv_dtype);
   if (!std::isfinite(p->scale)) return fail(PDATTN_ERR_INVALID_ARGUMENT, "scale is not finite");
   return PDATTN_OK;
+}
+
+int group_of(const pdattn_problem& p) { return p.num_q_heads / p.num_kv_heads; }
+
+// Workspace: 2 partial records per worker, then kDescWords descriptor words
+// per worker.
+uint64_t records_bytes(const pdattn_problem& p, int64_t workers) {
+  return (uint64_t)workers * 2 * pdattn::record_floats(p.head_dim, group_of(p)) * 4;
+}
+uint64_t workspace_for(const pdattn_problem& p, int64_t workers) {
+  return records_bytes(p, workers) + (uint64_t)workers * pdattn::kDescWords * 4;
 }
 
 pdattn_status check_plan(const pdattn_plan_t* plan) {
@@ -72,23 +77,11 @@ pdattn_status check_plan(const pdattn_plan_t* plan) {
   if (plan->magic != kPlanMagic) return fail(PDATTN_ERR_PLAN_MISMATCH, "plan was not produced by pdattn_plan");
   pdattn_status st = check_problem(&plan->problem);
   if (st != PDATTN_OK) return fail(PDATTN_ERR_PLAN_MISMATCH, "plan holds an invalid problem: %s", g_last_error);
-  const int64_t P = plan->problem.page_size;
-  if (plan->split_tokens <= 0 || plan->split_tokens % pdattn::kTileTokens != 0 || plan->max_splits < 1 ||
-      plan->max_splits > kMaxSplits || ceil_div(plan->split_tokens, P) + 1 > pdattn::kMaxPageList)
+  if (plan->num_workers < 1 || plan->num_workgroups < 1 ||
+      (int64_t)plan->num_workgroups * pdattn::kWaves < plan->num_workers ||
+      plan->workspace_bytes != workspace_for(plan->problem, plan->num_workers))
     return fail(PDATTN_ERR_PLAN_MISMATCH, "plan fields are inconsistent");
-  const int64_t ws = plan->max_splits > 1 ? (int64_t)plan->problem.batch * plan->problem.num_q_heads *
-                                                plan->max_splits * (plan->problem.head_dim + 2) * 4
-                                          : 0;
-  if ((int64_t)plan->workspace_bytes != ws) return fail(PDATTN_ERR_PLAN_MISMATCH, "plan workspace size is inconsistent");
   return PDATTN_OK;
-}
-
-int64_t num_units(const pdattn_plan_t* plan) { return (int64_t)plan->problem.batch * plan->max_splits; }
-
-// Workgroups of the partial kernel: Hkv per (sequence, split) unit, units
-// padded to a multiple of the 8 XCDs.
-int64_t partial_grid(const pdattn_plan_t* plan) {
-  return 8 * (int64_t)plan->problem.num_kv_heads * ceil_div(num_units(plan), 8);
 }
 
 }  // namespace
@@ -113,82 +106,74 @@ PDATTN_API uint64_t pdattn_problem_size(void) { return sizeof(pdattn_problem); }
 PDATTN_API uint64_t pdattn_plan_size(void) { return sizeof(pdattn_plan_t); }
 
 PDATTN_API pdattn_status pdattn_plan(const pdattn_problem* problem, const int32_t* context_lens_host,
-                                     int32_t num_cus, int32_t force_split_tokens, pdattn_plan_t* out) {
+                                     int32_t num_cus, int32_t force_workers, pdattn_plan_t* out) {
   g_last_error[0] = '\0';
   pdattn_status st = check_problem(problem);
   if (st != PDATTN_OK) return st;
   if (out == nullptr) return fail(PDATTN_ERR_INVALID_ARGUMENT, "out is NULL");
   if (problem->batch > 0 && context_lens_host == nullptr)
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "context_lens_host is NULL");
-  if (num_cus < 0 || force_split_tokens < 0)
-    return fail(PDATTN_ERR_INVALID_ARGUMENT, "num_cus and force_split_tokens must be >= 0");
+  if (num_cus < 0 || force_workers < 0)
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "num_cus and force_workers must be >= 0");
 
-  const int64_t P = problem->page_size;
-  const int64_t cap = (int64_t)problem->max_pages_per_seq * P;
-  int64_t total = 0, max_len = 0;
+  const int64_t cap = (int64_t)problem->max_pages_per_seq * problem->page_size;
+  int64_t tiles = 0, max_len = 0;
   for (int b = 0; b < problem->batch; ++b) {
     const int64_t L = context_lens_host[b];
     if (L < 0 || L > cap)
-      return fail(PDATTN_ERR_INVALID_ARGUMENT, "context_lens[%d] = %lld outside [0, max_pages_per_seq * page_size = %lld]",
-                  b, (long long)L, (long long)cap);
-    total += L;
+      return fail(PDATTN_ERR_INVALID_ARGUMENT,
+                  "context_lens[%d] = %lld outside [0, max_pages_per_seq * page_size = %lld]", b, (long long)L,
+                  (long long)cap);
+    tiles += ceil_div(L, pdattn::kTileTokens);
     if (L > max_len) max_len = L;
   }
+  tiles *= problem->num_kv_heads;
   if (max_len > 0 && problem->num_pages <= 0) return fail(PDATTN_ERR_INVALID_ARGUMENT, "empty page pool");
 
+  const bool fp8 = problem->kv_dtype == PDATTN_KV_FP8_E4M3;
+  // resident workgroups per CU: the runtime's occupancy figure for this
+  // instantiation when the device is asked, else a conservative estimate
+  int per_cu = 0;
   if (num_cus == 0) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess || num_cus <= 0)
       return fail(PDATTN_ERR_DEVICE, "cannot query the compute-unit count: %s", hipGetErrorString(e));
+    per_cu = pdattn::decode_wgs_per_cu(problem->head_dim, group_of(*problem), fp8);
   }
+  if (per_cu <= 0) per_cu = pdattn::decode_wgs_per_cu_estimate(problem->head_dim, group_of(*problem), fp8);
 
-  // Longest split whose block-table slice fits the LDS page list.
-  const int64_t page_cap = ((pdattn::kMaxPageList - 1) * P) / pdattn::kTileTokens * pdattn::kTileTokens;
-  int64_t split;
-  if (force_split_tokens > 0) {
-    split = round_up(force_split_tokens, pdattn::kTileTokens);
-  } else if (total == 0) {
-    split = pdattn::kTileTokens;
+  // Flash-decoding: as many worker waves as the device holds at once (the
+  // grid is persistent: no workgroup waits for a free slot), each with at
+  // least kMinTilesPerWorker tiles, so a small step is not spread thinner.
+  const int64_t capacity = (int64_t)num_cus * per_cu * pdattn::kWaves;
+  int64_t workers;
+  if (force_workers > 0) {
+    workers = force_workers;
   } else {
-    // Flash-decoding: cut the KV range only as far as needed to give every
-    // compute unit kWorkgroupsPerCu work items of equal length.
-    const int64_t slots = (int64_t)num_cus * kWorkgroupsPerCu;
-    split = round_up(ceil_div(total * problem->num_kv_heads, slots), pdattn::kTileTokens);
-    if (split < kMinSplitTokens) split = kMinSplitTokens;
-    const int64_t whole = round_up(max_len, pdattn::kTileTokens);
-    if (split > whole) split = whole;
+    workers = tiles / pdattn::kMinTilesPerWorker;
+    if (workers > capacity) workers = capacity;
+    if (workers < 1) workers = 1;
   }
-  if (split > page_cap) split = page_cap;
-  if (split < pdattn::kTileTokens) split = pdattn::kTileTokens;
-  if (max_len > 0 && ceil_div(max_len, split) > kMaxSplits) {
-    split = round_up(ceil_div(max_len, kMaxSplits), pdattn::kTileTokens);
-    if (split > page_cap)
-      return fail(PDATTN_ERR_UNSUPPORTED, "context length %lld needs more than %d splits", (long long)max_len,
-                  kMaxSplits);
-  }
-  const int64_t max_splits = max_len > 0 ? ceil_div(max_len, split) : 1;
-  int64_t items = 0;
-  for (int b = 0; b < problem->batch; ++b) {
-    const int64_t L = context_lens_host[b];
-    items += (L > 0 ? ceil_div(L, split) : 1) * problem->num_kv_heads;
-  }
+  if (workers > (int64_t)1 << 20) return fail(PDATTN_ERR_UNSUPPORTED, "more than 2^20 workers");
+  // the kernels form worker * total_tiles in 64-bit arithmetic, for any
+  // device lengths the block table admits
+  const double worst = (double)problem->batch * (double)ceil_div(cap, pdattn::kTileTokens) *
+                       (double)problem->num_kv_heads * (double)(workers + 1);
+  if (worst >= 4.0e18) return fail(PDATTN_ERR_UNSUPPORTED, "problem too large for 64-bit tile arithmetic");
 
   pdattn_plan_t plan;
   std::memset(&plan, 0, sizeof plan);
   plan.problem = *problem;
   if (!(plan.problem.scale > 0.0f)) plan.problem.scale = 1.0f / std::sqrt((float)problem->head_dim);
-  plan.split_tokens = (int32_t)split;
-  plan.max_splits = (int32_t)max_splits;
   plan.num_cus = num_cus;
-  plan.num_work_items = (int32_t)(items > INT32_MAX ? INT32_MAX : items);
+  plan.num_workers = (int32_t)workers;
+  plan.num_workgroups = (int32_t)ceil_div(workers, pdattn::kWaves);
+  plan.total_tiles = tiles;
   plan.max_context_len = max_len;
-  plan.workspace_bytes = max_splits > 1 ? (uint64_t)problem->batch * problem->num_q_heads * max_splits *
-                                              (problem->head_dim + 2) * 4
-                                        : 0;
+  plan.workspace_bytes = workspace_for(*problem, workers);
   plan.magic = kPlanMagic;
-  if (partial_grid(&plan) > INT32_MAX) return fail(PDATTN_ERR_UNSUPPORTED, "grid too large");
   *out = plan;
   return PDATTN_OK;
 }
@@ -214,12 +199,10 @@ PDATTN_API pdattn_status pdattn_decode(const pdattn_plan_t* plan, const void* q,
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "fp8 pools need 4-byte aligned k_scale and v_scale");
   if (!fp8 && (k_scale || v_scale))
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "k_scale / v_scale must be NULL for bf16 pools");
-  if (plan->workspace_bytes > 0) {
-    if (!workspace || workspace_bytes < plan->workspace_bytes)
-      return fail(PDATTN_ERR_WORKSPACE, "workspace needs %llu bytes, got %llu at %p",
-                  (unsigned long long)plan->workspace_bytes, (unsigned long long)workspace_bytes, workspace);
-    if (!aligned(workspace, 16)) return fail(PDATTN_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
-  }
+  if (!workspace || workspace_bytes < plan->workspace_bytes)
+    return fail(PDATTN_ERR_WORKSPACE, "workspace needs %llu bytes, got %llu at %p",
+                (unsigned long long)plan->workspace_bytes, (unsigned long long)workspace_bytes, workspace);
+  if (!aligned(workspace, 16)) return fail(PDATTN_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
 
   pdattn::DecodeParams p;
   std::memset(&p, 0, sizeof p);
@@ -232,55 +215,48 @@ PDATTN_API pdattn_status pdattn_decode(const pdattn_plan_t* plan, const void* q,
   p.context_lens = context_lens;
   p.out = out;
   p.lse = lse;
-  const int64_t rows = (int64_t)pr.batch * pr.num_q_heads * plan->max_splits;
-  p.part_acc = plan->workspace_bytes ? static_cast<float*>(workspace) : nullptr;
-  p.part_ml = plan->workspace_bytes ? static_cast<float*>(workspace) + rows * pr.head_dim : nullptr;
+  p.rec = static_cast<float*>(workspace);
+  p.desc = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(workspace) + records_bytes(pr, plan->num_workers));
+  p.batch = pr.batch;
   p.num_q_heads = pr.num_q_heads;
   p.num_kv_heads = pr.num_kv_heads;
   p.page_log2 = ilog2(pr.page_size);
   p.max_pages_per_seq = pr.max_pages_per_seq;
   p.num_pages = pr.num_pages;
-  p.split_tokens = plan->split_tokens;
-  p.max_splits = plan->max_splits;
-  p.num_units = (int32_t)num_units(plan);
+  p.num_workers = plan->num_workers;
   p.qk_scale_log2 = pr.scale * 1.44269504088896340736f;
 
-  hipError_t e = pdattn::launch_partial(p, pr.head_dim, pr.num_q_heads / pr.num_kv_heads, fp8,
-                                        (uint32_t)partial_grid(plan), static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "partial kernel launch: %s", hipGetErrorString(e));
+  hipError_t e = pdattn::launch_decode(p, pr.head_dim, group_of(pr), fp8, (uint32_t)plan->num_workgroups,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "decode kernel launch: %s", hipGetErrorString(e));
   return PDATTN_OK;
 }
 
 PDATTN_API pdattn_status pdattn_reduce(const pdattn_plan_t* plan, const void* workspace,
-                                       uint64_t workspace_bytes, const int32_t* context_lens, float* out,
-                                       float* lse, void* stream) {
+                                       uint64_t workspace_bytes, float* out, float* lse, void* stream) {
   g_last_error[0] = '\0';
   pdattn_status st = check_plan(plan);
   if (st != PDATTN_OK) return st;
   const pdattn_problem& pr = plan->problem;
-  if (pr.batch == 0 || plan->max_splits == 1) return PDATTN_OK;
-  if (!context_lens || !out) return fail(PDATTN_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
-  if (!aligned(context_lens, 4) || !aligned(out, 16) || (lse && !aligned(lse, 4)))
-    return fail(PDATTN_ERR_INVALID_ARGUMENT, "misaligned context_lens, out or lse");
+  if (pr.batch == 0) return PDATTN_OK;
+  if (!out) return fail(PDATTN_ERR_INVALID_ARGUMENT, "out is NULL");
+  if (!aligned(out, 16) || (lse && !aligned(lse, 4)))
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "misaligned out or lse");
   if (!workspace || workspace_bytes < plan->workspace_bytes)
     return fail(PDATTN_ERR_WORKSPACE, "workspace needs %llu bytes", (unsigned long long)plan->workspace_bytes);
   if (!aligned(workspace, 16)) return fail(PDATTN_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
 
-  pdattn::ReduceParams p;
+  pdattn::MergeParams p;
   std::memset(&p, 0, sizeof p);
-  const int64_t rows = (int64_t)pr.batch * pr.num_q_heads * plan->max_splits;
-  p.part_acc = static_cast<const float*>(workspace);
-  p.part_ml = static_cast<const float*>(workspace) + rows * pr.head_dim;
-  p.context_lens = context_lens;
+  p.rec = static_cast<const float*>(workspace);
+  p.desc = reinterpret_cast<const int32_t*>(static_cast<const unsigned char*>(workspace) +
+                                            records_bytes(pr, plan->num_workers));
   p.out = out;
   p.lse = lse;
   p.num_q_heads = pr.num_q_heads;
-  p.page_log2 = ilog2(pr.page_size);
-  p.max_pages_per_seq = pr.max_pages_per_seq;
-  p.split_tokens = plan->split_tokens;
-  p.max_splits = plan->max_splits;
-  hipError_t e = pdattn::launch_reduce(p, pr.head_dim, (uint32_t)((int64_t)pr.batch * pr.num_q_heads),
-                                       static_cast<hipStream_t>(stream));
+  p.num_workers = plan->num_workers;
+  hipError_t e = pdattn::launch_merge(p, pr.head_dim, group_of(pr), (uint32_t)plan->num_workers,
+                                      static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "reduce kernel launch: %s", hipGetErrorString(e));
   return PDATTN_OK;
 }

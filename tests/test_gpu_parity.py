@@ -87,9 +87,9 @@ def test_every_instantiation_matches_oracle(G, D, kv):
     w = small(B=5, Hq=2 * G, Hkv=2, D=D, P=16, lens=("uniform", 1, 700), kv=kv, seed=100 + G + D)
     inp = synth.make_inputs(w)
     ref = oracle_run(inp)
-    for force in (0, 64, 160):
-        out, lse = gpu_run(inp, force_split_tokens=force)
-        assert_parity(out, lse, *ref, fp8=kv != "bf16", tag=f"G{G} D{D} {kv} split={force}")
+    for force in (0, 1, 7, 64):
+        out, lse = gpu_run(inp, force_workers=force)
+        assert_parity(out, lse, *ref, fp8=kv != "bf16", tag=f"G{G} D{D} {kv} workers={force}")
 
 
 @pytest.mark.parametrize("P", [8, 16, 32, 64, 128])
@@ -97,6 +97,6 @@ def test_page_sizes(P):
     w = small(B=4, Hq=8, Hkv=2, D=128, P=P, lens=("uniform", 1, 1500), seed=200 + P)
     inp = synth.make_inputs(w)
     ref = oracle_run(inp)
-    for force in (0, 48, 1024):
-        out, lse = gpu_run(inp, force_split_tokens=force)
-        assert_parity(out, lse, *ref, tag=f"P{P} split={force}")
+    for force in (0, 3, 200):
+        out, lse = gpu_run(inp, force_workers=force)
+        assert_parity(out, lse, *ref, tag=f"P{P} workers={force}")

@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_split_amd", "csrc", "decode_kernels.hip")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "partial_kernel_llama3_8b_hbm_traffic.txt")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_kernel_llama3_8b_hbm_traffic.txt")
 METRIC = "decode-attn achieved HBM GB/s + µs/call, Llama-3-8B shape, 1×MI355X"
 
 
@@ -139,6 +139,25 @@ def main():
         torch.cuda.synchronize()
         warm.append(a.elapsed_time(b) * 1e3)
     ok = bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
+
+    # streaming-read reference over a buffer of the step's KV size
+    ceiling = None
+    num_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rbytes = (kv_bytes // 4096) * 4096
+    rbuf = torch.ones(rbytes, dtype=torch.uint8, device=dev)
+    sink = pk.stream_read_sink(num_cus, dev)
+    rt = []
+    for i in range(12):
+        flush.fill_(i & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        pk.stream_read(rbuf, sink, num_cus)
+        b.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            rt.append(a.elapsed_time(b) * 1e3)
+    ceiling = rbytes / (statistics.median(rt) * 1e-6) / 1e9
+    del rbuf
     if args.calibrate_copy:
         src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -197,6 +216,8 @@ def main():
         "reduce_kernel_us": round(statistics.fmean(red_us), 2),
         "warm_cache_us_per_call": round(statistics.median(warm), 2),
         "kv_bytes_per_call": kv_bytes,
+        "stream_read_ceiling_gbs": round(ceiling, 1),
+        "frac_of_stream_read_ceiling": round(kv_bytes / (mean_step * 1e-6) / 1e9 / ceiling, 4),
         "plan_host_us": round(plan_us, 1),
         "timed_wall_s": round(wall, 4),
         "cache_flush_between_steps": not args.no_flush,

@@ -157,6 +157,19 @@ PDATTN_API const char* pdattn_status_string(pdattn_status status);
 /* The last error message of the calling thread ("" if none). */
 PDATTN_API const char* pdattn_last_error(void);
 
+/*
+ * Measurement aid, not part of the decode path: enqueue a plain streaming
+ * read of `bytes` bytes at `buffer` (16-byte aligned, a multiple of 4096)
+ * with the same non-temporal 16-byte loads the decode kernel streams K/V
+ * with, on 2 * num_cus workgroups. `sink` (device, pdattn_stream_read_sink_
+ * words(num_cus) uint32 words, caller-owned) receives one folded word per
+ * thread. Timing it gives the read bandwidth the device sustains for this
+ * size, the ceiling the decode kernel is compared against.
+ */
+PDATTN_API pdattn_status pdattn_stream_read(const void* buffer, uint64_t bytes, uint32_t* sink, int32_t num_cus,
+                                            void* stream);
+PDATTN_API uint64_t pdattn_stream_read_sink_words(int32_t num_cus);
+
 /* sizeof(pdattn_problem) and sizeof(pdattn_plan_t), for binding checks. */
 PDATTN_API uint64_t pdattn_problem_size(void);
 PDATTN_API uint64_t pdattn_plan_size(void);

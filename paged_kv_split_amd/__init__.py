@@ -5,7 +5,7 @@ The functions below keep the C-ABI names (``plan``, ``decode``, ``reduce``)
 and only marshal arguments: torch tensors in, device pointers and the
 current HIP stream out. Every step of the computation runs in the library's
 kernels; there is no other code path. Importing this module fails loudly when
-the library has not been built (``python -m paged_kv_split_amd.build``).
+the library has not been built (``python paged_kv_split_amd/build.py``).
 """
 import ctypes
 import os
@@ -13,7 +13,7 @@ import os
 import torch
 
 __all__ = ["Problem", "Plan", "PdattnError", "plan", "decode", "reduce", "workspace", "paged_decode",
-           "KV_BF16", "KV_FP8_E4M3", "library_path"]
+           "KV_BF16", "KV_FP8_E4M3", "library_path", "stream_read", "stream_read_sink"]
 
 KV_BF16 = 0
 KV_FP8_E4M3 = 1
@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libpdattn.so")
 
 if not os.path.exists(library_path):
-    raise ImportError(f"{library_path} is missing: build it with `python -m paged_kv_split_amd.build`")
+    raise ImportError(f"{library_path} is missing: build it with `python paged_kv_split_amd/build.py`")
 
 _lib = ctypes.CDLL(library_path)
 
@@ -69,6 +69,10 @@ _lib.pdattn_status_string.restype = ctypes.c_char_p
 _lib.pdattn_status_string.argtypes = [ctypes.c_int]
 _lib.pdattn_last_error.restype = ctypes.c_char_p
 _lib.pdattn_last_error.argtypes = []
+_lib.pdattn_stream_read.restype = ctypes.c_int
+_lib.pdattn_stream_read.argtypes = [_P, ctypes.c_uint64, _P, ctypes.c_int32, _P]
+_lib.pdattn_stream_read_sink_words.restype = ctypes.c_uint64
+_lib.pdattn_stream_read_sink_words.argtypes = [ctypes.c_int32]
 _lib.pdattn_problem_size.restype = ctypes.c_uint64
 _lib.pdattn_plan_size.restype = ctypes.c_uint64
 
@@ -132,6 +136,16 @@ def reduce(pl: Plan, workspace, out, lse=None, stream=None):
 def workspace(pl: Plan, device):
     """A torch-allocated workspace of the plan's size."""
     return torch.empty(int(pl.workspace_bytes), dtype=torch.uint8, device=device)
+
+
+def stream_read(buffer, sink, num_cus, stream=None):
+    """``pdattn_stream_read``: the streaming-read bandwidth reference."""
+    _check(_lib.pdattn_stream_read(_ptr(buffer), buffer.numel() * buffer.element_size(), _ptr(sink),
+                                   int(num_cus), _stream(stream)), "pdattn_stream_read")
+
+
+def stream_read_sink(num_cus, device):
+    return torch.empty(int(_lib.pdattn_stream_read_sink_words(int(num_cus))), dtype=torch.int32, device=device)
 
 
 def paged_decode(q, k_pages, v_pages, block_table, context_lens, *, context_lens_host=None,

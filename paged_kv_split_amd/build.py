@@ -1,6 +1,6 @@
 """Compile the HIP library libpdattn.so for gfx950, in-tree.
 
-    python -m paged_kv_split_amd.build
+    python paged_kv_split_amd/build.py
 """
 import os
 import subprocess
@@ -10,7 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libpdattn.so")
-SOURCES = [os.path.join(CSRC, "pdattn.hip"), os.path.join(CSRC, "decode_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "pdattn.hip"), os.path.join(CSRC, "decode_kernels.hip"),
+           os.path.join(CSRC, "stream_read.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

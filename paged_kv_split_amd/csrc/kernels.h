@@ -87,5 +87,6 @@ int decode_wgs_per_cu(int head_dim, int group, bool fp8);
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, bool fp8, uint32_t grid,
                          hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int head_dim, int group, uint32_t grid, hipStream_t stream);
+hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, uint32_t grid, hipStream_t stream);
 
 }  // namespace pdattn

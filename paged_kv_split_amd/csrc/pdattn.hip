@@ -261,4 +261,19 @@ PDATTN_API pdattn_status pdattn_reduce(const pdattn_plan_t* plan, const void* wo
   return PDATTN_OK;
 }
 
+PDATTN_API uint64_t pdattn_stream_read_sink_words(int32_t num_cus) {
+  return (uint64_t)(num_cus > 0 ? num_cus : 0) * 2 * 256;
+}
+
+PDATTN_API pdattn_status pdattn_stream_read(const void* buffer, uint64_t bytes, uint32_t* sink, int32_t num_cus,
+                                            void* stream) {
+  g_last_error[0] = '\0';
+  if (!buffer || !sink || num_cus <= 0) return fail(PDATTN_ERR_INVALID_ARGUMENT, "buffer, sink and num_cus required");
+  if (!aligned(buffer, 16) || !aligned(sink, 4) || bytes % 4096 != 0)
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "buffer must be 16-byte aligned and a multiple of 4096 bytes");
+  hipError_t e = pdattn::launch_stream_read(buffer, bytes, sink, (uint32_t)num_cus * 2, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "stream-read kernel launch: %s", hipGetErrorString(e));
+  return PDATTN_OK;
+}
+
 }  // extern "C"

@@ -1,0 +1,174 @@
+"""The C ABI of libpdattn.so on the CPU: exports, struct layout, the planner
+and argument validation. Nothing here launches a kernel: every decode and
+reduce call below is rejected by validation before any HIP call."""
+import ctypes
+import math
+import os
+import random
+import re
+
+import pytest
+import torch
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pdattn.h")
+
+import paged_kv_split_amd as pk
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, MISMATCH, DEVICE = range(6)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"PDATTN_API\s+[\w\s\*]+?\b(pdattn_\w+)\s*\(", text)
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"pdattn_plan", "pdattn_decode", "pdattn_reduce", "pdattn_status_string",
+            "pdattn_last_error"} <= set(names)
+    lib = ctypes.CDLL(pk.library_path)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layout_matches_binding():
+    assert pk._lib.pdattn_problem_size() == ctypes.sizeof(pk.Problem) == 36
+    assert pk._lib.pdattn_plan_size() == ctypes.sizeof(pk.Plan)
+
+
+def test_status_strings():
+    for s in range(6):
+        assert pk._lib.pdattn_status_string(s).decode()
+    assert pk._lib.pdattn_status_string(99).decode() == "unknown status"
+
+
+def problem(**kw):
+    d = dict(batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, max_pages_per_seq=64,
+             num_pages=512, kv_dtype=0, scale=0.0)
+    d.update(kw)
+    return d
+
+
+def plan_raw(lens, num_cus=256, force=0, **kw):
+    p = problem(**kw)
+    prob = pk.Problem(*[p[f] for f, _ in pk.Problem._fields_])
+    lens_t = torch.as_tensor(lens, dtype=torch.int32).contiguous() if lens is not None else None
+    out = pk.Plan()
+    ptr = ctypes.c_void_p(lens_t.data_ptr()) if lens_t is not None else None
+    st = pk._lib.pdattn_plan(ctypes.byref(prob), ptr, num_cus, force, ctypes.byref(out))
+    return st, out
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_plan_for_each_workload(name):
+    w = synth.WORKLOADS[name]
+    g = torch.Generator().manual_seed(w.seed)
+    lens = synth._lens(w, g)
+    maxp = int((lens.max() + w.page_size - 1) // w.page_size)
+    st, pl = plan_raw(lens, batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                      head_dim=w.head_dim, page_size=w.page_size, max_pages_per_seq=maxp, num_pages=10 ** 6,
+                      kv_dtype=0 if w.kv_dtype == "bf16" else 1)
+    assert st == OK, pk._lib.pdattn_last_error()
+    tiles = w.num_kv_heads * sum((int(L) + 15) // 16 for L in lens.tolist())
+    assert pl.total_tiles == tiles
+    assert pl.max_context_len == int(lens.max())
+    G = w.num_q_heads // w.num_kv_heads
+    rec = G * (w.head_dim + 2) * 4
+    assert pl.workspace_bytes == pl.num_workers * (2 * rec + 8 * 4)
+    assert 1 <= pl.num_workers <= 4 * pl.num_workgroups
+    assert pl.num_workers <= max(1, tiles // 4)
+    assert abs(pl.problem.scale - 1.0 / math.sqrt(w.head_dim)) < 1e-7
+
+
+def test_plan_forced_workers_and_empty_batch():
+    st, pl = plan_raw([100, 0, 37, 1024], force=7)
+    assert st == OK and pl.num_workers == 7 and pl.num_workgroups == 2
+    st, pl = plan_raw([], batch=0)
+    assert st == OK and pl.num_workers == 1
+    st, pl = plan_raw([0, 0, 0, 0])
+    assert st == OK and pl.total_tiles == 0 and pl.num_workers == 1
+
+
+@pytest.mark.parametrize("kw,lens,expect", [
+    (dict(num_q_heads=12), [1, 1, 1, 1], INVALID),           # Hq not a multiple of Hkv
+    (dict(num_q_heads=24), [1, 1, 1, 1], UNSUPPORTED),       # G = 3
+    (dict(num_q_heads=256), [1, 1, 1, 1], UNSUPPORTED),      # G = 32
+    (dict(head_dim=96), [1, 1, 1, 1], UNSUPPORTED),
+    (dict(page_size=12), [1, 1, 1, 1], UNSUPPORTED),
+    (dict(page_size=4), [1, 1, 1, 1], UNSUPPORTED),
+    (dict(page_size=256), [1, 1, 1, 1], UNSUPPORTED),
+    (dict(kv_dtype=7), [1, 1, 1, 1], UNSUPPORTED),
+    (dict(scale=float("nan")), [1, 1, 1, 1], INVALID),
+    (dict(batch=70000), [1] * 4, INVALID),
+    (dict(num_kv_heads=0), [1, 1, 1, 1], INVALID),
+    (dict(), [1, 1, 1, 64 * 16 + 1], INVALID),               # length beyond the block table
+    (dict(), [1, -1, 1, 1], INVALID),
+    (dict(), None, INVALID),                                 # no host lengths
+    (dict(num_pages=0), [1, 1, 1, 1], INVALID),              # nothing to read from
+])
+def test_plan_rejects(kw, lens, expect):
+    st, _ = plan_raw(lens, **kw)
+    assert st == expect
+    assert pk._lib.pdattn_last_error().decode()
+
+
+def _decode_raw(pl, q=16, k=16, v=16, ks=None, vs=None, bt=16, lens=16, ws=16, ws_bytes=None, out=16, lse=None):
+    P = ctypes.c_void_p
+    ws_bytes = pl.workspace_bytes if ws_bytes is None else ws_bytes
+    return pk._lib.pdattn_decode(ctypes.byref(pl), P(q) if q else None, P(k) if k else None,
+                                 P(v) if v else None, P(ks) if ks else None, P(vs) if vs else None,
+                                 P(bt) if bt else None, P(lens) if lens else None, P(ws) if ws else None,
+                                 ws_bytes, P(out) if out else None, P(lse) if lse else None, None)
+
+
+def test_decode_validation_rejects_before_launch():
+    st, pl = plan_raw([5, 9, 100, 33])
+    assert st == OK
+    assert _decode_raw(pl, q=0) == INVALID
+    assert _decode_raw(pl, out=0) == INVALID
+    assert _decode_raw(pl, q=0x1008) == INVALID          # not 16-byte aligned
+    assert _decode_raw(pl, k=0x1004) == INVALID
+    assert _decode_raw(pl, bt=0x1002) == INVALID
+    assert _decode_raw(pl, ks=0x2000, vs=0x2000) == INVALID   # scales on a bf16 pool
+    assert _decode_raw(pl, ws=0) == WORKSPACE
+    assert _decode_raw(pl, ws_bytes=pl.workspace_bytes - 1) == WORKSPACE
+    assert _decode_raw(pl, ws=0x1008) == INVALID
+    st, pl8 = plan_raw([5, 9, 100, 33], kv_dtype=1)
+    assert _decode_raw(pl8) == INVALID                     # fp8 pool without scales
+    bad = pk.Plan.from_buffer_copy(bytes(pl))
+    bad.magic = 0
+    assert _decode_raw(bad) == MISMATCH
+    bad = pk.Plan.from_buffer_copy(bytes(pl))
+    bad.num_workers = 10 ** 7
+    assert _decode_raw(bad) == MISMATCH
+    assert "workspace" in pk._lib.pdattn_last_error().decode() or pk._lib.pdattn_last_error()
+    st, empty = plan_raw([], batch=0)
+    assert _decode_raw(empty, q=0, k=0, v=0, bt=0, lens=0, out=0, ws=0) == OK   # nothing to do
+
+
+def test_reduce_validation_rejects_before_launch():
+    st, pl = plan_raw([5, 9, 100, 33])
+    P = ctypes.c_void_p
+    assert pk._lib.pdattn_reduce(ctypes.byref(pl), None, pl.workspace_bytes, P(16), None, None) == WORKSPACE
+    assert pk._lib.pdattn_reduce(ctypes.byref(pl), P(16), pl.workspace_bytes - 4, P(16), None, None) == WORKSPACE
+    assert pk._lib.pdattn_reduce(ctypes.byref(pl), P(16), pl.workspace_bytes, None, None, None) == INVALID
+    assert pk._lib.pdattn_reduce(ctypes.byref(pl), P(16), pl.workspace_bytes, P(0x1004), None, None) == INVALID
+    assert pk._lib.pdattn_reduce(None, P(16), 0, P(16), None, None) == INVALID
+
+
+def test_worker_range_arithmetic():
+    """The kernels place worker w on tiles [w*T/NW, (w+1)*T/NW) and find the
+    first worker reaching tile C as ceil((C+1)*NW/T) - 1; check that formula
+    against a brute-force search."""
+    rng = random.Random(5)
+    for _ in range(3000):
+        T = rng.randint(1, 5000)
+        NW = rng.randint(1, 700)
+        C = rng.randrange(T)
+        wf = ((C + 1) * NW + T - 1) // T - 1
+        brute = max(w for w in range(NW) if w * T // NW <= C)
+        assert wf == brute
+        assert wf * T // NW <= C < (wf + 1) * T // NW

@@ -4,16 +4,19 @@
     python bench.py [--gpus 1] [--steps 50] [--warmup 20] [--workload llama3_8b]
 
 A step is one pass of the whole hot path, pdattn_decode + pdattn_reduce, over
-one batch of seeded synthetic input already resident in HBM. Before every
+one batch of seeded synthetic input already resident in HBM (in the
+balanced mode the merge runs inside pdattn_decode and pdattn_reduce enqueues
+nothing; --balanced times that kernel instead of the default static split +
+reduce kernel). Before every
 timed step (outside its events) a 512 MiB buffer is rewritten, which evicts
 the L2s and the 256 MB Infinity Cache, so the KV pages are read from HBM.
 
 Prints ONE JSON line. value = KV algorithmic bytes (every K and V element of
 every valid (token, kv head) once, plus the fp8 scales) / mean step time, in
-GB/s. roofline = the same bytes / the mean duration of the partial kernel
+GB/s. roofline = the same bytes / the mean duration of the decode kernel
 alone (events around that launch on its stream), against MI355X's 8 TB/s HBM
 peak. traffic = measured HBM bytes per launch of that kernel from the
-committed rocprofv3 counter summary, or null when the kernel source has
+committed rocprofv3 counter summary, or null when the kernel's sources have
 changed since the counters were taken. cpu_baseline = the CPU fp64 oracle
 timed on this host's cores on the same step's inputs.
 """
@@ -29,28 +32,41 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_split_amd", "csrc", "decode_kernels.hip")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_kernel_llama3_8b_hbm_traffic.txt")
+CSRC = os.path.join(ROOT, "paged_kv_split_amd", "csrc")
+# the sources each mode's decode kernel is built from
+KERNEL_SOURCES = {
+    "balanced": ["decode_dynamic.hip", "tile_ops.h", "kernels.h"],
+    "static": ["decode_kernels.hip", "tile_ops.h", "kernels.h"],
+}
+KERNEL_NAMES = {"balanced": "decode_dynamic_kernel", "static": "decode_kernel"}
 METRIC = "decode-attn achieved HBM GB/s + µs/call, Llama-3-8B shape, 1×MI355X"
 
 
-def source_digest():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_digest(mode):
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[mode]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def read_traffic(workload):
+def traffic_summary_path(mode, workload):
+    return os.path.join(ROOT, "profiles", f"{KERNEL_NAMES[mode]}_{workload}_hbm_traffic.txt")
+
+
+def read_traffic(mode, workload):
     """Bytes per launch from the committed counter summary, if it still
-    describes the current kernel source and this workload."""
-    if not os.path.exists(TRAFFIC_SUMMARY):
+    describes the current kernel sources and this workload."""
+    path = traffic_summary_path(mode, workload)
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(TRAFFIC_SUMMARY) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != source_digest() or vals.get("workload") != workload:
+    if vals.get("kernel_source_sha256_16") != source_digest(mode) or vals.get("workload") != workload:
         return None
     try:
         return int(float(vals["hbm_bytes_per_launch"]))
@@ -67,6 +83,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time budget of the oracle baseline (0 skips it)")
     ap.add_argument("--no-flush", action="store_true", help="time with warm caches")
+    ap.add_argument("--balanced", action="store_true",
+                    help="time the on-device balanced kernel instead of the static split + reduce")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run 3 device copies of 256 MiB (a plain copy kernel of known "
                          "size, for scaling the HBM byte counters)")
@@ -87,13 +105,22 @@ def main():
     d = {k: (inp[k].to(dev) if inp[k] is not None else None)
          for k in ("q", "k_pages", "v_pages", "k_scale", "v_scale", "block_table", "context_lens")}
     kv_bytes = synth.kv_bytes(w, inp["context_lens"])
+    mode = "balanced" if args.balanced else "static"
+
+    def make_plan():
+        return pk.plan(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                       head_dim=w.head_dim, page_size=w.page_size,
+                       max_pages_per_seq=inp["block_table"].shape[1], num_pages=inp["k_pages"].shape[0],
+                       kv_dtype=pk.KV_BF16 if w.kv_dtype == "bf16" else pk.KV_FP8_E4M3,
+                       context_lens_host=inp["context_lens"], balanced=args.balanced)
+
     t0 = time.perf_counter()
-    pl = pk.plan(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
-                 head_dim=w.head_dim, page_size=w.page_size,
-                 max_pages_per_seq=inp["block_table"].shape[1], num_pages=inp["k_pages"].shape[0],
-                 kv_dtype=pk.KV_BF16 if w.kv_dtype == "bf16" else pk.KV_FP8_E4M3,
-                 context_lens_host=inp["context_lens"])
-    plan_us = (time.perf_counter() - t0) * 1e6
+    pl = make_plan()  # the first plan on a device also queries its occupancy
+    plan_first_us = (time.perf_counter() - t0) * 1e6
+    t0 = time.perf_counter()
+    for _ in range(20):
+        pl = make_plan()
+    plan_us = (time.perf_counter() - t0) * 1e6 / 20
     out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
     lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=dev)
     ws = pk.workspace(pl, dev)
@@ -187,7 +214,7 @@ def main():
                "sample": f"the full {w.name} step ({w.batch} sequences) repeated {len(times)} times "
                          f"({sum(times):.1f} s); median {per_call * 1e6:.0f} us/call"}
 
-    traffic = read_traffic(w.name)
+    traffic = read_traffic(mode, w.name)
     achieved = kv_bytes / (mean_dec * 1e-6) / 1e9
     rec = {
         "metric": METRIC,
@@ -212,18 +239,20 @@ def main():
         "cpu_baseline": cpu,
         "us_per_call": round(mean_step, 2),
         "us_per_call_p10_p50_p90": [round(qs[0], 2), round(statistics.median(step_us), 2), round(qs[-1], 2)],
-        "partial_kernel_us": round(mean_dec, 2),
+        "mode": mode,
+        "decode_kernel_us": round(mean_dec, 2),
         "reduce_kernel_us": round(statistics.fmean(red_us), 2),
         "warm_cache_us_per_call": round(statistics.median(warm), 2),
         "kv_bytes_per_call": kv_bytes,
         "stream_read_ceiling_gbs": round(ceiling, 1),
         "frac_of_stream_read_ceiling": round(kv_bytes / (mean_step * 1e-6) / 1e9 / ceiling, 4),
         "plan_host_us": round(plan_us, 1),
+        "plan_host_first_call_us": round(plan_first_us, 1),
         "timed_wall_s": round(wall, 4),
         "cache_flush_between_steps": not args.no_flush,
         "outputs_finite": ok,
         "device": torch.cuda.get_device_name(0),
-        "kernel_source_sha256_16": source_digest(),
+        "kernel_source_sha256_16": source_digest(mode),
     }
     print(json.dumps(rec), flush=True)
 

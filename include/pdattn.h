@@ -17,12 +17,22 @@
  *
  * Work decomposition (flash-decoding): the (b, kvh) pairs are laid end to
  * end, each cut into 16-token tiles, and a persistent grid of
- * plan->num_workers waves takes equal contiguous ranges of that tile list.
- * A wave computes all G query heads of a kv head with an online softmax
- * (running max and sum in base 2, fp32 accumulators). A pair covered by one
- * wave is written to `out` by pdattn_decode; a pair cut by wave boundaries
- * leaves per-piece (m, l, acc) partials in the workspace, which
- * pdattn_reduce merges with the log-sum-exp rule.
+ * plan->num_workers waves streams that tile list. A wave computes all G
+ * query heads of a kv head with an online softmax (running max and sum in
+ * base 2, fp32 accumulators); pieces of a pair computed by different waves
+ * leave (m, l, acc) partials in the workspace and are merged with the
+ * log-sum-exp rule. Two modes (plan flags):
+ *   default   each wave takes an equal contiguous range of the tile list;
+ *             pdattn_decode writes the pairs one wave covers and
+ *             pdattn_reduce merges the others. Bitwise reproducible for a
+ *             fixed plan.
+ *   BALANCED  the split points are decided on the device while the kernel
+ *             runs (each wave streams a static share, then takes further
+ *             tiles from atomic counters as it gets ahead), and the merge
+ *             runs in the same kernel: pdattn_decode alone produces every
+ *             output; pdattn_reduce enqueues nothing. Results agree with the
+ *             default mode to fp32 rounding but may differ between calls in
+ *             the last bits; the workspace needs pdattn_workspace_init.
  *
  * Layouts (all contiguous, row-major):
  *   q            bf16 [B][Hq][d]
@@ -103,14 +113,17 @@ typedef struct pdattn_plan_t {
   pdattn_problem problem;   /* copy of the problem, scale resolved */
   int32_t num_cus;          /* compute units the plan was sized for */
   int32_t num_workgroups;   /* grid of the decode kernel (4 waves each) */
-  int32_t num_workers;      /* waves that own tile ranges, <= 4 * num_workgroups */
-  int32_t reserved0;
+  int32_t num_workers;      /* worker waves, <= 4 * num_workgroups */
+  int32_t flags;            /* PDATTN_PLAN_* flags the plan was made with */
   int64_t total_tiles;      /* Hkv * sum_b ceil(L_b / 16) over the host lengths */
   int64_t max_context_len;  /* largest host context length planned for */
-  uint64_t workspace_bytes; /* partial records and merge descriptors */
+  uint64_t workspace_bytes; /* partial records, merge descriptors or counters */
   uint32_t magic;           /* set by pdattn_plan; checked by decode / reduce */
   uint32_t reserved1;
 } pdattn_plan_t;
+
+/* Plan flags (0: static equal ranges + pdattn_reduce; bitwise reproducible). */
+#define PDATTN_PLAN_BALANCED 2 /* on-device balancing, merge inside pdattn_decode */
 
 /*
  * Plan one decode step.
@@ -120,20 +133,40 @@ typedef struct pdattn_plan_t {
  *   force_workers      0 = adaptive (fill the device's resident capacity, at
  *                      least 4 tiles per worker); > 0 forces this number of
  *                      worker waves (tests use it to move the split points)
+ *   flags              0 or PDATTN_PLAN_BALANCED
  *   out                receives the plan (caller-owned POD)
- * Pure host computation apart from the optional device query.
+ * Pure host computation apart from the optional device query (cached per
+ * device after the first call).
  */
 PDATTN_API pdattn_status pdattn_plan(const pdattn_problem* problem, const int32_t* context_lens_host,
-                                     int32_t num_cus, int32_t force_workers, pdattn_plan_t* out);
+                                     int32_t num_cus, int32_t force_workers, int32_t flags, pdattn_plan_t* out);
 
 /*
- * Enqueue the split-KV partial pass on `stream` (a hipStream_t; NULL = the
- * null stream). Pointers and layouts as described above; k_scale / v_scale
- * must be NULL for bf16 pools and non-NULL for fp8 pools; `workspace` holds
- * plan->workspace_bytes bytes (contents need no initialisation). Writes
- * `out` (and `lse`) for every (b, kvh) pair that one worker covers, and for
- * empty or invalid sequences; leaves partials and descriptors in the
- * workspace for the cut pairs, which pdattn_reduce completes.
+ * Prepare a workspace of plan->workspace_bytes bytes (or more) for balanced-
+ * mode decodes: zero its counters and stamp it with the counter layout, with
+ * one small kernel on `stream` (no memset, so it can be captured). Every
+ * decode leaves the counters zero again, so one preparation serves every
+ * later plan with the same counter layout (the same batch, num_kv_heads,
+ * page_size and max_pages_per_seq; any lengths and worker counts) whose
+ * workspace_bytes fits in the buffer; a plan with another layout needs the
+ * workspace prepared again. A decode that finds the workspace unprepared, or
+ * prepared for another layout, writes NaN to every output. Concurrent
+ * decodes on one workspace race; give each stream its own. No-op for
+ * default-mode plans.
+ */
+PDATTN_API pdattn_status pdattn_workspace_init(const pdattn_plan_t* plan, void* workspace, uint64_t workspace_bytes,
+                                               void* stream);
+
+/*
+ * Enqueue the decode step on `stream` (a hipStream_t; NULL = the null
+ * stream). Pointers and layouts as described above; k_scale / v_scale must
+ * be NULL for bf16 pools and non-NULL for fp8 pools; `workspace` holds
+ * plan->workspace_bytes bytes, prepared by pdattn_workspace_init for
+ * balanced plans (default-mode plans need no preparation). Default mode:
+ * writes `out` (and `lse`) for every (b, kvh) pair that one worker covers
+ * and for empty or invalid sequences, and leaves partials and descriptors
+ * in the workspace for the cut pairs, which pdattn_reduce completes.
+ * Balanced mode: writes every output.
  */
 PDATTN_API pdattn_status pdattn_decode(const pdattn_plan_t* plan, const void* q, const void* k_pages,
                                        const void* v_pages, const float* k_scale, const float* v_scale,
@@ -147,6 +180,8 @@ PDATTN_API pdattn_status pdattn_decode(const pdattn_plan_t* plan, const void* q,
  * pieces s, out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s with
  * M = max_s m_s, and lse = ln 2 * (M + log2 sum_s 2^(m_s - M) l_s). Must
  * follow pdattn_decode with the same plan and workspace on the same stream.
+ * Balanced plans merge inside pdattn_decode: this call then validates its
+ * arguments and enqueues nothing.
  */
 PDATTN_API pdattn_status pdattn_reduce(const pdattn_plan_t* plan, const void* workspace,
                                        uint64_t workspace_bytes, float* out, float* lse, void* stream);

@@ -12,11 +12,13 @@ import os
 
 import torch
 
-__all__ = ["Problem", "Plan", "PdattnError", "plan", "decode", "reduce", "workspace", "paged_decode",
-           "KV_BF16", "KV_FP8_E4M3", "library_path", "stream_read", "stream_read_sink"]
+__all__ = ["Problem", "Plan", "PdattnError", "plan", "decode", "reduce", "workspace", "workspace_init",
+           "paged_decode", "KV_BF16", "KV_FP8_E4M3", "PLAN_BALANCED", "library_path", "stream_read",
+           "stream_read_sink"]
 
 KV_BF16 = 0
 KV_FP8_E4M3 = 1
+PLAN_BALANCED = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libpdattn.so")
@@ -49,7 +51,7 @@ class Plan(ctypes.Structure):
         ("num_cus", ctypes.c_int32),
         ("num_workgroups", ctypes.c_int32),
         ("num_workers", ctypes.c_int32),
-        ("reserved0", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
         ("total_tiles", ctypes.c_int64),
         ("max_context_len", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_uint64),
@@ -60,7 +62,10 @@ class Plan(ctypes.Structure):
 
 _P = ctypes.c_void_p
 _lib.pdattn_plan.restype = ctypes.c_int
-_lib.pdattn_plan.argtypes = [ctypes.POINTER(Problem), _P, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(Plan)]
+_lib.pdattn_plan.argtypes = [ctypes.POINTER(Problem), _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                             ctypes.POINTER(Plan)]
+_lib.pdattn_workspace_init.restype = ctypes.c_int
+_lib.pdattn_workspace_init.argtypes = [ctypes.POINTER(Plan), _P, ctypes.c_uint64, _P]
 _lib.pdattn_decode.restype = ctypes.c_int
 _lib.pdattn_decode.argtypes = [ctypes.POINTER(Plan), _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint64, _P, _P, _P]
 _lib.pdattn_reduce.restype = ctypes.c_int
@@ -106,13 +111,15 @@ def _stream(stream):
 
 
 def plan(*, batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq, num_pages,
-         kv_dtype=KV_BF16, scale=0.0, context_lens_host, num_cus=0, force_workers=0) -> Plan:
+         kv_dtype=KV_BF16, scale=0.0, context_lens_host, num_cus=0, force_workers=0,
+         balanced=False) -> Plan:
     """``pdattn_plan``: context_lens_host is a CPU int32 tensor (or sequence)."""
     lens = torch.as_tensor(context_lens_host, dtype=torch.int32).cpu().contiguous()
     prob = Problem(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq, num_pages,
                    kv_dtype, float(scale))
     out = Plan()
-    _check(_lib.pdattn_plan(ctypes.byref(prob), _ptr(lens), int(num_cus), int(force_workers),
+    flags = PLAN_BALANCED if balanced else 0
+    _check(_lib.pdattn_plan(ctypes.byref(prob), _ptr(lens), int(num_cus), int(force_workers), flags,
                             ctypes.byref(out)), "pdattn_plan")
     return out
 
@@ -133,9 +140,18 @@ def reduce(pl: Plan, workspace, out, lse=None, stream=None):
                               _stream(stream)), "pdattn_reduce")
 
 
-def workspace(pl: Plan, device):
-    """A torch-allocated workspace of the plan's size."""
-    return torch.empty(int(pl.workspace_bytes), dtype=torch.uint8, device=device)
+def workspace_init(pl: Plan, workspace, stream=None):
+    """``pdattn_workspace_init``: prepare a workspace for balanced-mode decodes."""
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.pdattn_workspace_init(ctypes.byref(pl), _ptr(workspace), ws_bytes, _stream(stream)),
+           "pdattn_workspace_init")
+
+
+def workspace(pl: Plan, device, stream=None):
+    """A torch-allocated workspace of the plan's size, prepared for use."""
+    ws = torch.empty(int(pl.workspace_bytes), dtype=torch.uint8, device=device)
+    workspace_init(pl, ws, stream)
+    return ws
 
 
 def stream_read(buffer, sink, num_cus, stream=None):
@@ -150,7 +166,7 @@ def stream_read_sink(num_cus, device):
 
 def paged_decode(q, k_pages, v_pages, block_table, context_lens, *, context_lens_host=None,
                  k_scale=None, v_scale=None, scale=None, num_cus=0, force_workers=0,
-                 return_lse=True):
+                 balanced=False, return_lse=True):
     """Plan, allocate (torch) and run one decode step; returns (out, lse).
 
     q: bf16 [B,Hq,d]; k_pages/v_pages: bf16 or float8_e4m3fn [num_pages,P,Hkv,d];
@@ -164,7 +180,7 @@ def paged_decode(q, k_pages, v_pages, block_table, context_lens, *, context_lens
     pl = plan(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=P,
               max_pages_per_seq=block_table.shape[1], num_pages=num_pages, kv_dtype=kv,
               scale=0.0 if scale is None else scale, context_lens_host=context_lens_host,
-              num_cus=num_cus, force_workers=force_workers)
+              num_cus=num_cus, force_workers=force_workers, balanced=balanced)
     dev = q.device
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if return_lse else None

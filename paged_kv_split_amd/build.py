@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libpdattn.so")
 SOURCES = [os.path.join(CSRC, "pdattn.hip"), os.path.join(CSRC, "decode_kernels.hip"),
-           os.path.join(CSRC, "stream_read.hip")]
+           os.path.join(CSRC, "decode_dynamic.hip"), os.path.join(CSRC, "stream_read.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -29,9 +29,7 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    tmp = LIBRARY + ".tmp"
-    cmd = [HIPCC] + FLAGS + list(extra_flags) + SOURCES + ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -42,6 +40,21 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(lines))
     if verbose and lines:
         print("\n".join(lines))
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile each source to an object in parallel, then link the library."""
+    from concurrent.futures import ThreadPoolExecutor
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.basename(src) + ".o") for src in SOURCES]
+    cflags = [f for f in FLAGS if f != "-shared"] + list(extra_flags)
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        futs = [ex.submit(_run, [HIPCC] + cflags + ["-c", src, "-o", obj], verbose) for src, obj in zip(SOURCES, objs)]
+        for f in futs:
+            f.result()
+    tmp = LIBRARY + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
     os.replace(tmp, LIBRARY)
     return LIBRARY
 

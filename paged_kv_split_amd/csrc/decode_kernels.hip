@@ -51,213 +51,12 @@
 // (FlashQuant wiki, split_k_reduce.cu, Algorithm and Numerical Stability,
 // on un-normalised accumulators).
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
-#include <type_traits>
-#include <utility>
-
-#include "kernels.h"
+#include "tile_ops.h"
 
 namespace pdattn {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
-
-constexpr float kLn2 = 0.69314718055994530942f;
-
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
-// Value of lane SRC of the caller's 16-lane row (DPP row_newbcast).
-template <int SRC>
-__device__ __forceinline__ float row_bcast(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + SRC, 0xf, 0xf, false));
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
-
-// Eight e4m3fn bytes (w0 holds bytes 0..3, w1 bytes 4..7, memory order) as
-// eight bf16 values in the same order, by gfx950's fp8 -> bf16 pair convert
-// with unit scale. The widening is exact: an e4m3 value has 4 significant
-// bits and an exponent inside bf16's range.
-__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
-  u32x4 r;
-  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
-  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
-  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
-  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
-  return r;
-}
-
-template <int VB>
-struct VChunk;
-template <>
-struct VChunk<16> { using type = u32x4; };
-template <>
-struct VChunk<8> { using type = u32x2; };
-template <>
-struct VChunk<4> { using type = uint32_t; };
-
-// Dword w of a V chunk.
-template <typename T>
-__device__ __forceinline__ uint32_t dword(const T& x, int w) {
-  if constexpr (std::is_same_v<T, uint32_t>) {
-    return x;
-  } else {
-    return x[w];
-  }
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8), followed by a
-// compiler barrier so that no LDS access is moved across it.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-  asm volatile("" ::: "memory");
-}
-
-// Wait until at most `ahead` tiles of C loads each are still in flight.
-template <int C, int S>
-__device__ __forceinline__ void wait_tiles(int ahead) {
-  if constexpr (S >= 4) {
-    if (ahead >= 3) { wait_vmcnt<3 * C>(); return; }
-  }
-  if constexpr (S >= 3) {
-    if (ahead >= 2) { wait_vmcnt<2 * C>(); return; }
-  }
-  if (ahead >= 1) { wait_vmcnt<C>(); return; }
-  wait_vmcnt<0>();
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// Cache policy of the K/V stream: non-temporal. Each KV byte is read once
-// per call, so it is not kept in L2 or the Infinity Cache; on MI355X this
-// lifts a streaming read from about 4.7 to about 6.9 TB/s.
-constexpr int kStreamPolicy = 2;  // nt
-
-__device__ __forceinline__ void dma16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, kStreamPolicy);
-}
-__device__ __forceinline__ void dma4(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 4, 0, kStreamPolicy);
-}
-
-// LDS byte address of a generic pointer into __shared__ memory.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// Read one ring stage into registers: the lane's K fragments (kf), its four
-// V chunks (V rows row + 4 j; vp points at row `row`) and, for fp8, the k / v
-// scales of its four tokens. One inline-assembly block issues the reads and
-// waits for them (lgkmcnt(0)), so every destination is defined only once
-// its data has landed and no use or copy can be scheduled earlier; the
-// compiler also adds no wait of its own for the ring's direct-to-LDS loads
-// (the caller has waited for them with wait_tiles).
-template <int D, bool FP8, typename VVec, int K_LD>
-__device__ __forceinline__ void read_stage(const unsigned char* kp, const unsigned char* vp, const unsigned char* sp,
-                                           u32x4 (&kf)[K_LD], VVec (&vf)[4], float (&ks)[4], float (&vs)[4]) {
-  const uint32_t ka = lds_addr(kp), va = lds_addr(vp), sa = lds_addr(sp);
-  if constexpr (!FP8 && D == 128) {  // row 256 B: 4 K fragments, V rows 1024 B apart
-    asm volatile(
-        "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %8 offset:1024\n\t"
-        "ds_read_b128 %2, %8 offset:2048\n\t"
-        "ds_read_b128 %3, %8 offset:3072\n\t"
-        "ds_read_b128 %4, %9\n\t"
-        "ds_read_b128 %5, %9 offset:1024\n\t"
-        "ds_read_b128 %6, %9 offset:2048\n\t"
-        "ds_read_b128 %7, %9 offset:3072\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3]), "=&v"(vf[0]), "=&v"(vf[1]), "=&v"(vf[2]),
-          "=&v"(vf[3])
-        : "v"(ka), "v"(va)
-        : "memory");
-  } else if constexpr (!FP8 && D == 64) {  // row 128 B: 2 K fragments, 8-byte V chunks 512 B apart
-    asm volatile(
-        "ds_read_b128 %0, %6\n\t"
-        "ds_read_b128 %1, %6 offset:1024\n\t"
-        "ds_read_b64 %2, %7\n\t"
-        "ds_read_b64 %3, %7 offset:512\n\t"
-        "ds_read_b64 %4, %7 offset:1024\n\t"
-        "ds_read_b64 %5, %7 offset:1536\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(vf[0]), "=&v"(vf[1]), "=&v"(vf[2]), "=&v"(vf[3])
-        : "v"(ka), "v"(va)
-        : "memory");
-  } else if constexpr (FP8 && D == 128) {  // row 128 B, plus two scale quads
-    f32x4 a, c;
-    asm volatile(
-        "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %8 offset:1024\n\t"
-        "ds_read_b64 %2, %9\n\t"
-        "ds_read_b64 %3, %9 offset:512\n\t"
-        "ds_read_b64 %4, %9 offset:1024\n\t"
-        "ds_read_b64 %5, %9 offset:1536\n\t"
-        "ds_read_b128 %6, %10\n\t"
-        "ds_read_b128 %7, %10 offset:64\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(vf[0]), "=&v"(vf[1]), "=&v"(vf[2]), "=&v"(vf[3]), "=&v"(a), "=&v"(c)
-        : "v"(ka), "v"(va), "v"(sa)
-        : "memory");
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      ks[v] = a[v];
-      vs[v] = c[v];
-    }
-  } else {  // fp8, D == 64: row 64 B: 1 K fragment, 4-byte V chunks 256 B apart
-    static_assert(FP8 && D == 64, "layout");
-    f32x4 a, c;
-    asm volatile(
-        "ds_read_b128 %0, %7\n\t"
-        "ds_read_b32 %1, %8\n\t"
-        "ds_read_b32 %2, %8 offset:256\n\t"
-        "ds_read_b32 %3, %8 offset:512\n\t"
-        "ds_read_b32 %4, %8 offset:768\n\t"
-        "ds_read_b128 %5, %9\n\t"
-        "ds_read_b128 %6, %9 offset:64\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(kf[0]), "=&v"(vf[0]), "=&v"(vf[1]), "=&v"(vf[2]), "=&v"(vf[3]), "=&v"(a), "=&v"(c)
-        : "v"(ka), "v"(va), "v"(sa)
-        : "memory");
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      ks[v] = a[v];
-      vs[v] = c[v];
-    }
-  }
-}
-
-// Token order inside a 16-token tile. MFMA A-row m carries token
-// tile_token(m) = m / 4 + 4 (m mod 4), so the result row 4 r + v held by
-// 16-lane row r is token r + 4 v: every 16-lane row owns the tokens
-// congruent to r mod 4, for the scores as well as for the V rows it reads.
-__device__ __forceinline__ int tile_token(int m) { return (m >> 2) + 4 * (m & 3); }
-
-
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ long long wave_incl_scan(long long v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const long long t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
+using namespace dev;
 
 // Range [t0, t1) of the tile list owned by worker w of nw, T tiles in all.
 __device__ __forceinline__ void worker_range(long long w, long long nw, long long T, long long& t0, long long& t1) {
@@ -267,25 +66,12 @@ __device__ __forceinline__ void worker_range(long long w, long long nw, long lon
 
 template <int D, int G, bool FP8>
 __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p) {
-  constexpr int ESZ = FP8 ? 1 : 2;             // bytes per stored element
-  constexpr int ROW_BYTES = D * ESZ;           // one (token, kv head) row
-  constexpr int KSTEPS = D / 32;               // MFMA k-steps over head_dim
-  constexpr int K_LD = ROW_BYTES / 64;         // 16-byte loads per lane per tile, K
-  constexpr int V_LD = ROW_BYTES / 64;         // and V (a tile is 16 rows)
-  constexpr int C = K_LD + V_LD + (FP8 ? 1 : 0);  // direct-to-LDS loads per tile
-  constexpr int VE = D / 16;                   // V elements per lane per row
-  constexpr int VB = VE * ESZ;                 // V bytes per lane per row
+  using TL = Tile<D, G, FP8>;
+  constexpr int C = TL::C;
   constexpr int NT = kWaves * 64;
   constexpr int S = kStages;
-  // one ring stage: K tile in MFMA-operand lane order, V tile row-major,
-  // then (fp8) 64 scale slots: k scales 0..15, v scales 16..31
-  constexpr int K_TILE = kTileTokens * ROW_BYTES;
-  constexpr int V_TILE = kTileTokens * ROW_BYTES;
-  constexpr int STAGE = K_TILE + V_TILE + (FP8 ? 256 : 0);
-  constexpr int RF = (int)record_floats(D, G);
-  using VVec = typename VChunk<VB>::type;
-  static_assert(K_LD >= 1 && (D == 64 || D == 128), "head_dim");
-  static_assert(G >= 1 && G <= 16, "group size");
+  constexpr int STAGE = TL::STAGE;
+  constexpr int RF = TL::RF;
   static_assert(C * (S - 1) < 64, "vmcnt range");
 
   // LDS: per-wave load rings and block-table buffers; the length-scan scratch.
@@ -307,7 +93,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p) {
   const int P = 1 << lp;
   const long long cap = (long long)p.max_pages_per_seq << lp;
   const long long NW = p.num_workers;
-  auto tiles_of = [&](int L) -> long long { return (L > 0 && (long long)L <= cap) ? (L + kTileTokens - 1) / kTileTokens : 0; };
+  auto tiles_of = [&](int L) -> long long { return (L > 0 && (long long)L <= cap) ? (L - 1) / kTileTokens + 1 : 0; };
 
   // ---- 1. tile counts of the sequences, prefix-summed across the workgroup
   const int CH = (B + NT - 1) / NT;
@@ -388,7 +174,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p) {
     bool first = true;
     while (remaining > 0) {
       const int L = __builtin_amdgcn_readfirstlane(p.context_lens[b]);
-      const int nt = (L + kTileTokens - 1) / kTileTokens;
+      const int nt = (L - 1) / kTileTokens + 1;  // L >= 1 here
       const int seg = (int)min((long long)(nt - j), remaining);
       const bool cut_start = j > 0;
       const bool reaches_end = j + seg == nt;
@@ -396,31 +182,10 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p) {
       const int s0 = j * kTileTokens;
       const int s1 = min(L, (j + seg) * kTileTokens);
 
-      // Q as the MFMA B operand: lane (row, col) holds head col (zero for
-      // col >= G) at 8 head_dim positions per k-step; dpos() is the order
-      // shared with the K fragments.
-      auto dpos = [&](int kk) -> int {
-        if constexpr (FP8) return (kk >> 1) * 64 + row * 16 + (kk & 1) * 8;
-        else return kk * 32 + row * 8;
-      };
-      bf16x8 qop[KSTEPS];
-      {
-        const uint16_t* qrow = p.q + ((long long)b * Hq + h0 + min(col, G - 1)) * D;
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-          u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + dpos(kk));
-          if (col >= G) raw = u32x4{0u, 0u, 0u, 0u};
-          qop[kk] = __builtin_bit_cast(bf16x8, raw);
-        }
-      }
-
-      float m_run = -__builtin_inff();
-      float l_run = 0.0f;
-      float acc[G][VE];
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int e = 0; e < VE; ++e) acc[g][e] = 0.0f;
+      bf16x8 qop[TL::KSTEPS];
+      TL::load_q(qop, p.q + ((long long)b * Hq + h0) * D, row, col);
+      typename TL::State st;
+      TL::reset(st);
       int bad = 0;
 
       // sub-runs of at most kPagesPerWave pages (tile-aligned)
@@ -444,37 +209,9 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p) {
           return ((((long long)pages[(pos >> lp) - pg0]) << lp) + (pos & (P - 1))) * Hkv + kvh;
         };
         const int nk = (c1 - c0 + kTileTokens - 1) / kTileTokens;
-
-        // Issue the C direct-to-LDS loads of tile k of this sub-run into stage
-        // k % S. Rows past the pair's last token are clamped onto that token
-        // (finite data, masked in the softmax).
         auto issue = [&](int k) {
-          unsigned char* st = ring + (k % S) * STAGE;
-          const int tb = c0 + k * kTileTokens;
-          {
-            // K: lane (row, col) fetches bytes [j*64 + row*16, +16) of token
-            // tile_token(col); it lands at j*1024 + lane*16, the lane's own
-            // A-operand fragment for k-steps 2j, 2j+1 (fp8) or j (bf16).
-            const int pos = min(tb + tile_token(col), s1 - 1);
-            const unsigned char* src = p.k + row_of(pos) * ROW_BYTES + row * 16;
-#pragma unroll
-            for (int jj = 0; jj < K_LD; ++jj) dma16(src + jj * 64, st + jj * 1024 + lane * 16);
-          }
-#pragma unroll
-          for (int jj = 0; jj < V_LD; ++jj) {
-            // V: row-major tile, 64 lanes x 16 bytes per load
-            const int byte = jj * 1024 + lane * 16;
-            const int pos = min(tb + byte / ROW_BYTES, s1 - 1);
-            dma16(p.v + row_of(pos) * ROW_BYTES + (byte % ROW_BYTES), st + K_TILE + jj * 1024 + lane * 16);
-          }
-          if constexpr (FP8) {
-            // scale slot m < 16 holds k_scale of token tile_token(m); slot
-            // 16 + m holds its v_scale; lanes 32..63 repeat lanes 0..31
-            const int m = lane & 15;
-            const int pos = min(tb + tile_token(m), s1 - 1);
-            const float* src = ((lane & 16) ? p.v_scale : p.k_scale) + row_of(pos);
-            dma4(src, st + K_TILE + V_TILE + lane * 4);
-          }
+          TL::issue(ring + (k % S) * STAGE, p.k, p.v, p.k_scale, p.v_scale, row_of, c0 + k * kTileTokens, s1 - 1,
+                    lane, row, col);
         };
 
 #pragma unroll
@@ -484,139 +221,25 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p) {
         for (int k = 0; k < nk; ++k) {
           // tiles k+1 .. min(k+S-1, nk-1) may stay in flight
           wait_tiles<C, S>(min(S - 1, nk - 1 - k));
-          const unsigned char* st = ring + (k % S) * STAGE;
-          u32x4 kf[K_LD];
-          VVec vf_raw[4];
-          float ks[4], vs[4];
-          read_stage<D, FP8>(st + lane * 16, st + K_TILE + row * ROW_BYTES + col * VB,
-                             st + K_TILE + V_TILE + row * 16, kf, vf_raw, ks, vs);
+          typename TL::Frag f;
+          TL::read(f, ring + (k % S) * STAGE, lane, row, col);
           // the stage's reads have returned (read_stage waits for them): refill it
           if (k + S < nk) issue(k + S);
-
-          const int tb = c0 + k * kTileTokens;
-          // S[t][g]: lane (row, col) holds head col for tokens row + 4 v
-          f32x4 Sacc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int kk = 0; kk < KSTEPS; ++kk) {
-            u32x4 kw;
-            if constexpr (FP8) {
-              const u32x4& c = kf[kk >> 1];
-              kw = fp8x8_to_bf16x8(c[(kk & 1) * 2], c[(kk & 1) * 2 + 1]);
-            } else {
-              kw = kf[kk];
-            }
-            Sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw), qop[kk], Sacc, 0, 0, 0);
-          }
-          float s[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            float x = Sacc[v] * p.qk_scale_log2;
-            if constexpr (FP8) x *= ks[v];
-            s[v] = (tb + row + 4 * v < s1) ? x : -__builtin_inff();
-          }
-          float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-          mx = fmaxf(mx, __shfl_xor(mx, 16));
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
-          const float m_new = fmaxf(m_run, mx);
-          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-          float pr[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) pr[v] = __builtin_amdgcn_exp2f(s[v] - m_new);
-          l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-          const bool grew = m_new > m_run;
-          m_run = m_new;
-          if (__any(grew)) {
-            static_for<0, G>([&](auto gc) {
-              constexpr int g = decltype(gc)::value;
-              const float a = row_bcast<g>(alpha);
-#pragma unroll
-              for (int e = 0; e < VE; ++e) acc[g][e] *= a;
-            });
-          }
-          if constexpr (FP8) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) pr[v] *= vs[v];
-          }
-          // p . V: lane (row, col) takes V row (token) row + 4 j, d-chunk col
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            float vf[VE];
-            if constexpr (FP8) {
-#pragma unroll
-              for (int w = 0; w < VB / 4; ++w) {
-                const uint32_t x = dword(vf_raw[jj], w);
-                auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(x, false);
-                auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(x, true);
-                vf[4 * w + 0] = lo[0];
-                vf[4 * w + 1] = lo[1];
-                vf[4 * w + 2] = hi[0];
-                vf[4 * w + 3] = hi[1];
-              }
-            } else {
-#pragma unroll
-              for (int w = 0; w < VB / 4; ++w) {
-                const uint32_t x = dword(vf_raw[jj], w);
-                vf[2 * w + 0] = bf16_lo(x);
-                vf[2 * w + 1] = bf16_hi(x);
-              }
-            }
-            const float pj = pr[jj];
-            static_for<0, G>([&](auto gc) {
-              constexpr int g = decltype(gc)::value;
-              const float pg = row_bcast<g>(pj);
-#pragma unroll
-              for (int e = 0; e < VE; ++e) acc[g][e] = fmaf(pg, vf[e], acc[g][e]);
-            });
-          }
+          TL::compute(st, f, qop, c0 + k * kTileTokens, s1, p.qk_scale_log2, row);
         }
         c0 = c1;
       }
 
-      // ---- finish the piece: sum l and acc over the four rows (disjoint
-      // tokens); every row then holds the totals
-      l_run += __shfl_xor(l_run, 16);
-      l_run += __shfl_xor(l_run, 32);
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int e = 0; e < VE; ++e) {
-          float a = acc[g][e];
-          a += __shfl_xor(a, 16);
-          a += __shfl_xor(a, 32);
-          acc[g][e] = a;
-        }
+      // ---- finish the piece
+      TL::reduce_rows(st);
       const bool poisoned = __any(bad);
-      const float nan = __builtin_nanf("");
       if (!cut_start && reaches_end) {
-        // the whole pair: out = acc / l, lse = ln 2 (m + log2 l); row r
-        // writes the heads g with g mod 4 == r
-        static_for<0, G>([&](auto gc) {
-          constexpr int g = decltype(gc)::value;
-          const float lg = row_bcast<g>(l_run);
-          if (row == (g & 3)) {
-            float* o = p.out + ((long long)b * Hq + h0 + g) * D + col * VE;
-#pragma unroll
-            for (int e = 0; e < VE; ++e) o[e] = poisoned ? nan : acc[g][e] / lg;
-          }
-        });
-        if (p.lse != nullptr && row == 0 && col < G)
-          p.lse[(long long)b * Hq + h0 + col] = poisoned ? nan : (m_run + log2f(l_run)) * kLn2;
+        TL::store_out(st, p.out + ((long long)b * Hq + h0) * D, p.lse ? p.lse + (long long)b * Hq + h0 : nullptr,
+                      poisoned, row, col);
       } else {
         // a piece of a cut pair: record (m, l, acc); slot 0 for the wave's
         // first piece, 1 for its last
-        float* r = p.rec + (gw * 2 + (first ? 0 : 1)) * RF;
-        static_for<0, G>([&](auto gc) {
-          constexpr int g = decltype(gc)::value;
-          if (row == (g & 3)) {
-            float* o = r + 2 * G + g * D + col * VE;
-#pragma unroll
-            for (int e = 0; e < VE; ++e) o[e] = poisoned ? nan : acc[g][e];
-          }
-        });
-        if (row == 0 && col < G) {
-          r[col] = poisoned ? 0.0f : m_run;
-          r[G + col] = poisoned ? nan : l_run;
-        }
+        TL::store_record(st, p.rec + (gw * 2 + (first ? 0 : 1)) * RF, poisoned, row, col);
         if (cut_start && reaches_end) {
           // this wave holds the pair's last tile (only possible for its first
           // piece): describe the pieces for the merge

@@ -23,6 +23,11 @@ constexpr int kPagesPerWave = 256;
 constexpr int kMinTilesPerWorker = 4;
 // Words of one worker's merge descriptor.
 constexpr int kDescWords = 8;
+// Tiles of one balancing unit of the dynamic kernel (a pair longer than this
+// is cut into several units, merged once more at the end).
+constexpr int kUnitTiles = 512;
+// Stamped into a dynamic-mode workspace by its initialisation.
+constexpr uint32_t kWorkspaceMagic = 0x70645731u;
 
 constexpr int kv_row_bytes(int head_dim, bool fp8) { return head_dim * (fp8 ? 1 : 2); }
 
@@ -34,11 +39,19 @@ constexpr int decode_lds_bytes(int head_dim, bool fp8) {
          512;
 }
 
+// LDS bytes of one dynamic-kernel workgroup: per wave the ring, a block-
+// table buffer and the producer state; the scan and placement scratch.
+constexpr int dynamic_lds_bytes(int head_dim, int group, bool fp8) {
+  return kWaves * (kStages * (2 * kTileTokens * kv_row_bytes(head_dim, fp8) + (fp8 ? 256 : 0)) +
+                   kPagesPerWave * 4 + 96 + 72) +
+         64 + 0 * group;
+}
+
 // Resident decode workgroups per compute unit when no device can be asked
 // (160 KB LDS; 512 VGPRs per SIMD lane, 4 SIMDs; one wave per SIMD per
 // workgroup), from upper bounds of the builds' register counts.
-constexpr int decode_wgs_per_cu_estimate(int head_dim, int group, bool fp8) {
-  const int by_lds = (160 * 1024) / decode_lds_bytes(head_dim, fp8);
+constexpr int decode_wgs_per_cu_estimate(int head_dim, int group, bool fp8, bool dynamic) {
+  const int by_lds = (160 * 1024) / (dynamic ? dynamic_lds_bytes(head_dim, group, fp8) : decode_lds_bytes(head_dim, fp8));
   const int vgprs = group >= 8 ? 256 : 168;
   const int by_vgpr = 512 / vgprs;
   const int n = by_lds < by_vgpr ? by_lds : by_vgpr;
@@ -70,6 +83,33 @@ struct DecodeParams {
   float qk_scale_log2;        // softmax scale * log2(e)
 };
 
+// The dynamic kernel: the same inputs, plus its workspace regions.
+struct DynParams {
+  const uint16_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  float* out;
+  float* lse;
+  float* rec;                 // unit records [units_max + 3 * num_workers][record_floats]
+  float* rec2;                // pair-level records [units_max][record_floats] (seg_max > 1)
+  uint32_t* ctl;              // counters: claims, records, done tiles [units_max] each; done units [B * Hkv]
+  const uint32_t* ws_magic;   // header: kWorkspaceMagic, units_max, batch * num_kv_heads once initialised
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t page_log2;
+  int32_t max_pages_per_seq;
+  int32_t num_pages;
+  int32_t num_workers;
+  int32_t seg_max;            // units per pair at most
+  int32_t units_max;          // batch * num_kv_heads * seg_max
+  float qk_scale_log2;
+};
+
 struct MergeParams {
   const float* rec;
   const int32_t* desc;
@@ -87,6 +127,10 @@ int decode_wgs_per_cu(int head_dim, int group, bool fp8);
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, bool fp8, uint32_t grid,
                          hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int head_dim, int group, uint32_t grid, hipStream_t stream);
+int dynamic_wgs_per_cu(int head_dim, int group, bool fp8);
+hipError_t launch_dynamic(const DynParams& p, int head_dim, int group, bool fp8, uint32_t grid, hipStream_t stream);
+hipError_t launch_workspace_init(uint32_t* ctl, uint64_t words, uint32_t* header, uint32_t units_max,
+                                 uint32_t pairs, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, uint32_t grid, hipStream_t stream);
 
 }  // namespace pdattn

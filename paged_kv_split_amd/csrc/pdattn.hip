@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -63,13 +64,56 @@ pdattn_status check_problem(const pdattn_problem* p) {
 
 int group_of(const pdattn_problem& p) { return p.num_q_heads / p.num_kv_heads; }
 
-// Workspace: 2 partial records per worker, then kDescWords descriptor words
-// per worker.
+bool balanced(int32_t flags) { return (flags & PDATTN_PLAN_BALANCED) != 0; }
+uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+// Default-mode workspace: 2 partial records per worker, then
+// kDescWords descriptor words per worker.
 uint64_t records_bytes(const pdattn_problem& p, int64_t workers) {
   return (uint64_t)workers * 2 * pdattn::record_floats(p.head_dim, group_of(p)) * 4;
 }
-uint64_t workspace_for(const pdattn_problem& p, int64_t workers) {
-  return records_bytes(p, workers) + (uint64_t)workers * pdattn::kDescWords * 4;
+
+// Balanced-mode workspace: a 256-byte header (words 0..2: the initialisation
+// stamp), the counters, the unit records, then (pairs longer than one unit)
+// the pair-level records.
+struct DynLayout {
+  int64_t seg_max;     // units per pair at most
+  int64_t units_max;   // batch * Hkv * seg_max
+  uint64_t ctl_off, ctl_words;
+  uint64_t rec_off, rec2_off, total;
+};
+DynLayout dyn_layout(const pdattn_problem& p, int64_t workers) {
+  DynLayout d;
+  const int64_t max_tiles = ceil_div((int64_t)p.max_pages_per_seq * p.page_size, pdattn::kTileTokens);
+  d.seg_max = max_tiles > 0 ? ceil_div(max_tiles, pdattn::kUnitTiles) : 1;
+  d.units_max = (int64_t)p.batch * p.num_kv_heads * d.seg_max;
+  const uint64_t rec = (uint64_t)pdattn::record_floats(p.head_dim, group_of(p)) * 4;
+  d.ctl_off = 256;
+  d.ctl_words = 3 * (uint64_t)d.units_max + (uint64_t)p.batch * p.num_kv_heads;
+  d.rec_off = d.ctl_off + round_up(d.ctl_words * 4, 256);
+  d.rec2_off = d.rec_off + round_up(((uint64_t)d.units_max + 3 * (uint64_t)workers) * rec, 256);
+  d.total = d.rec2_off + (d.seg_max > 1 ? (uint64_t)d.units_max * rec : 0);
+  return d;
+}
+
+uint64_t workspace_for(const pdattn_problem& p, int64_t workers, int32_t flags) {
+  if (!balanced(flags)) return records_bytes(p, workers) + (uint64_t)workers * pdattn::kDescWords * 4;
+  return dyn_layout(p, workers).total;
+}
+
+// Resident workgroups per CU of one kernel instantiation on the current
+// device, from the runtime's occupancy query (cached: the query costs
+// milliseconds), 0 if it cannot be asked.
+int wgs_per_cu_cached(int device, int head_dim, int group, bool fp8, bool dyn) {
+  static std::atomic<int> cache[64][2][5][2][2];
+  if (device < 0 || device >= 64) return 0;
+  const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : group == 8 ? 3 : 4;
+  std::atomic<int>& slot = cache[device][head_dim == 128][gi][fp8][dyn];
+  int v = slot.load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  v = dyn ? pdattn::dynamic_wgs_per_cu(head_dim, group, fp8) : pdattn::decode_wgs_per_cu(head_dim, group, fp8);
+  if (v > 0) slot.store(v, std::memory_order_relaxed);
+  return v;
 }
 
 pdattn_status check_plan(const pdattn_plan_t* plan) {
@@ -79,7 +123,8 @@ pdattn_status check_plan(const pdattn_plan_t* plan) {
   if (st != PDATTN_OK) return fail(PDATTN_ERR_PLAN_MISMATCH, "plan holds an invalid problem: %s", g_last_error);
   if (plan->num_workers < 1 || plan->num_workgroups < 1 ||
       (int64_t)plan->num_workgroups * pdattn::kWaves < plan->num_workers ||
-      plan->workspace_bytes != workspace_for(plan->problem, plan->num_workers))
+      (plan->flags & ~PDATTN_PLAN_BALANCED) != 0 ||
+      plan->workspace_bytes != workspace_for(plan->problem, plan->num_workers, plan->flags))
     return fail(PDATTN_ERR_PLAN_MISMATCH, "plan fields are inconsistent");
   return PDATTN_OK;
 }
@@ -106,7 +151,7 @@ PDATTN_API uint64_t pdattn_problem_size(void) { return sizeof(pdattn_problem); }
 PDATTN_API uint64_t pdattn_plan_size(void) { return sizeof(pdattn_plan_t); }
 
 PDATTN_API pdattn_status pdattn_plan(const pdattn_problem* problem, const int32_t* context_lens_host,
-                                     int32_t num_cus, int32_t force_workers, pdattn_plan_t* out) {
+                                     int32_t num_cus, int32_t force_workers, int32_t flags, pdattn_plan_t* out) {
   g_last_error[0] = '\0';
   pdattn_status st = check_problem(problem);
   if (st != PDATTN_OK) return st;
@@ -115,6 +160,8 @@ PDATTN_API pdattn_status pdattn_plan(const pdattn_problem* problem, const int32_
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "context_lens_host is NULL");
   if (num_cus < 0 || force_workers < 0)
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "num_cus and force_workers must be >= 0");
+  if ((flags & ~PDATTN_PLAN_BALANCED) != 0) return fail(PDATTN_ERR_INVALID_ARGUMENT, "unknown plan flags %d", flags);
+  const bool dyn = balanced(flags);
 
   const int64_t cap = (int64_t)problem->max_pages_per_seq * problem->page_size;
   int64_t tiles = 0, max_len = 0;
@@ -140,9 +187,9 @@ PDATTN_API pdattn_status pdattn_plan(const pdattn_problem* problem, const int32_
     if (e == hipSuccess) e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess || num_cus <= 0)
       return fail(PDATTN_ERR_DEVICE, "cannot query the compute-unit count: %s", hipGetErrorString(e));
-    per_cu = pdattn::decode_wgs_per_cu(problem->head_dim, group_of(*problem), fp8);
+    per_cu = wgs_per_cu_cached(dev, problem->head_dim, group_of(*problem), fp8, dyn);
   }
-  if (per_cu <= 0) per_cu = pdattn::decode_wgs_per_cu_estimate(problem->head_dim, group_of(*problem), fp8);
+  if (per_cu <= 0) per_cu = pdattn::decode_wgs_per_cu_estimate(problem->head_dim, group_of(*problem), fp8, dyn);
 
   // Flash-decoding: as many worker waves as the device holds at once (the
   // grid is persistent: no workgroup waits for a free slot), each with at
@@ -162,6 +209,12 @@ PDATTN_API pdattn_status pdattn_plan(const pdattn_problem* problem, const int32_
   const double worst = (double)problem->batch * (double)ceil_div(cap, pdattn::kTileTokens) *
                        (double)problem->num_kv_heads * (double)(workers + 1);
   if (worst >= 4.0e18) return fail(PDATTN_ERR_UNSUPPORTED, "problem too large for 64-bit tile arithmetic");
+  if (dyn && dyn_layout(*problem, workers).units_max > ((int64_t)1 << 24))
+    return fail(PDATTN_ERR_UNSUPPORTED, "batch * num_kv_heads * units per pair exceeds 2^24");
+  // the balanced kernel keeps tile positions in 31 bits, for any device
+  // lengths the block table admits
+  if (dyn && (double)problem->batch * problem->num_kv_heads * (double)ceil_div(cap, pdattn::kTileTokens) >= 2147483648.0)
+    return fail(PDATTN_ERR_UNSUPPORTED, "batch * num_kv_heads * tiles per block-table row reaches 2^31");
 
   pdattn_plan_t plan;
   std::memset(&plan, 0, sizeof plan);
@@ -172,7 +225,8 @@ PDATTN_API pdattn_status pdattn_plan(const pdattn_problem* problem, const int32_
   plan.num_workgroups = (int32_t)ceil_div(workers, pdattn::kWaves);
   plan.total_tiles = tiles;
   plan.max_context_len = max_len;
-  plan.workspace_bytes = workspace_for(*problem, workers);
+  plan.flags = flags;
+  plan.workspace_bytes = workspace_for(*problem, workers, flags);
   plan.magic = kPlanMagic;
   *out = plan;
   return PDATTN_OK;
@@ -203,6 +257,40 @@ PDATTN_API pdattn_status pdattn_decode(const pdattn_plan_t* plan, const void* q,
     return fail(PDATTN_ERR_WORKSPACE, "workspace needs %llu bytes, got %llu at %p",
                 (unsigned long long)plan->workspace_bytes, (unsigned long long)workspace_bytes, workspace);
   if (!aligned(workspace, 16)) return fail(PDATTN_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+
+  if (balanced(plan->flags)) {
+    const DynLayout d = dyn_layout(pr, plan->num_workers);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    pdattn::DynParams p;
+    std::memset(&p, 0, sizeof p);
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint8_t*>(k_pages);
+    p.v = static_cast<const uint8_t*>(v_pages);
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    p.block_table = block_table;
+    p.context_lens = context_lens;
+    p.out = out;
+    p.lse = lse;
+    p.rec = reinterpret_cast<float*>(ws + d.rec_off);
+    p.rec2 = d.seg_max > 1 ? reinterpret_cast<float*>(ws + d.rec2_off) : nullptr;
+    p.ctl = reinterpret_cast<uint32_t*>(ws + d.ctl_off);
+    p.ws_magic = reinterpret_cast<const uint32_t*>(ws);
+    p.batch = pr.batch;
+    p.num_q_heads = pr.num_q_heads;
+    p.num_kv_heads = pr.num_kv_heads;
+    p.page_log2 = ilog2(pr.page_size);
+    p.max_pages_per_seq = pr.max_pages_per_seq;
+    p.num_pages = pr.num_pages;
+    p.num_workers = plan->num_workers;
+    p.seg_max = (int32_t)d.seg_max;
+    p.units_max = (int32_t)d.units_max;
+    p.qk_scale_log2 = pr.scale * 1.44269504088896340736f;
+    hipError_t e = pdattn::launch_dynamic(p, pr.head_dim, group_of(pr), fp8, (uint32_t)plan->num_workgroups,
+                                          static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "decode kernel launch: %s", hipGetErrorString(e));
+    return PDATTN_OK;
+  }
 
   pdattn::DecodeParams p;
   std::memset(&p, 0, sizeof p);
@@ -245,6 +333,7 @@ PDATTN_API pdattn_status pdattn_reduce(const pdattn_plan_t* plan, const void* wo
   if (!workspace || workspace_bytes < plan->workspace_bytes)
     return fail(PDATTN_ERR_WORKSPACE, "workspace needs %llu bytes", (unsigned long long)plan->workspace_bytes);
   if (!aligned(workspace, 16)) return fail(PDATTN_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  if (balanced(plan->flags)) return PDATTN_OK;  // merged inside pdattn_decode
 
   pdattn::MergeParams p;
   std::memset(&p, 0, sizeof p);
@@ -258,6 +347,27 @@ PDATTN_API pdattn_status pdattn_reduce(const pdattn_plan_t* plan, const void* wo
   hipError_t e = pdattn::launch_merge(p, pr.head_dim, group_of(pr), (uint32_t)plan->num_workers,
                                       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "reduce kernel launch: %s", hipGetErrorString(e));
+  return PDATTN_OK;
+}
+
+PDATTN_API pdattn_status pdattn_workspace_init(const pdattn_plan_t* plan, void* workspace, uint64_t workspace_bytes,
+                                               void* stream) {
+  g_last_error[0] = '\0';
+  pdattn_status st = check_plan(plan);
+  if (st != PDATTN_OK) return st;
+  if (!balanced(plan->flags)) return PDATTN_OK;
+  if (!workspace || workspace_bytes < plan->workspace_bytes)
+    return fail(PDATTN_ERR_WORKSPACE, "workspace needs %llu bytes, got %llu at %p",
+                (unsigned long long)plan->workspace_bytes, (unsigned long long)workspace_bytes, workspace);
+  if (!aligned(workspace, 16)) return fail(PDATTN_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  const DynLayout d = dyn_layout(plan->problem, plan->num_workers);
+  // words 3 .. end of the counters are zeroed; words 0..2 receive the stamp
+  uint32_t* w = static_cast<uint32_t*>(workspace);
+  const uint64_t words = d.ctl_off / 4 + d.ctl_words - 3;
+  hipError_t e = pdattn::launch_workspace_init(
+      w + 3, words, w, (uint32_t)d.units_max, (uint32_t)((int64_t)plan->problem.batch * plan->problem.num_kv_heads),
+      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "workspace init launch: %s", hipGetErrorString(e));
   return PDATTN_OK;
 }
 

@@ -1,0 +1,502 @@
+// Device building blocks shared by the gfx950 decode kernels: the direct-to-
+// LDS tile loads, the per-tile q.K / online-softmax / p.V step on one wave,
+// and the partial-record layout. Internal; included by the kernel sources.
+//
+// One tile is 16 consecutive tokens of one (sequence, kv head) pair. A wave
+// computes all G query heads of the kv head at once (AstrAI "CUDA Kernels",
+// GQA head packing; FlashQuant wiki "CUDA Kernels", GQA Support):
+//   * S = K_tile (16 tokens x d) . Q^T (d x 16, the G heads zero-padded) on
+//     v_mfma_f32_16x16x32_bf16. The K tile lands in LDS already in A-operand
+//     lane order; the head_dim order inside a fragment is the same for Q and
+//     K, so the contraction is exact.
+//   * online softmax (FlashQuant wiki, flash_attention.cu, Online Softmax) in
+//     base 2 with the scale pre-multiplied by log2(e) (same page, utils.cuh):
+//     lane (row r, column g) holds head g for tokens r, r+4, r+8, r+12; the
+//     tile max comes from a local max and two cross-row exchanges.
+//   * p . V on the VALU with fp32 accumulators: lane (row r, chunk c) owns
+//     d-chunk c of tokens r + 4j; their probabilities for head g sit in lane
+//     g of the same 16-lane row and arrive by DPP row broadcast.
+// fp8 pools: e4m3fn bytes widen exactly in registers (to bf16 for the MFMA
+// operand, to fp32 for V) and the per-(token, kv head) scales multiply the
+// score (k) and the probability (v) (OASR "Kernel Layer", FP8 KV variants).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+#include <utility>
+
+#include "kernels.h"
+
+namespace pdattn {
+namespace dev {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Value of lane SRC of the caller's 16-lane row (DPP row_newbcast).
+template <int SRC>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + SRC, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// Eight e4m3fn bytes (w0 holds bytes 0..3, w1 bytes 4..7, memory order) as
+// eight bf16 values in the same order, by gfx950's fp8 -> bf16 pair convert
+// with unit scale. The widening is exact: an e4m3 value has 4 significant
+// bits and an exponent inside bf16's range.
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+  return r;
+}
+
+template <int VB>
+struct VChunk;
+template <>
+struct VChunk<16> { using type = u32x4; };
+template <>
+struct VChunk<8> { using type = u32x2; };
+template <>
+struct VChunk<4> { using type = uint32_t; };
+
+// Dword w of a V chunk.
+template <typename T>
+__device__ __forceinline__ uint32_t dword(const T& x, int w) {
+  if constexpr (std::is_same_v<T, uint32_t>) {
+    return x;
+  } else {
+    return x[w];
+  }
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8), followed by a
+// compiler barrier so that no LDS access is moved across it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most `ahead` tiles of C loads each are still in flight (the
+// loads of a wave return in issue order).
+template <int C, int S>
+__device__ __forceinline__ void wait_tiles(int ahead) {
+  if constexpr (S >= 4) {
+    if (ahead >= 3) { wait_vmcnt<3 * C>(); return; }
+  }
+  if constexpr (S >= 3) {
+    if (ahead >= 2) { wait_vmcnt<2 * C>(); return; }
+  }
+  if (ahead >= 1) { wait_vmcnt<C>(); return; }
+  wait_vmcnt<0>();
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Cache policy of the K/V stream: non-temporal. Each KV byte is read once
+// per call, so it is not kept in L2 or the Infinity Cache; on MI355X this
+// lifts a streaming read from about 4.7 to about 6.9 TB/s.
+constexpr int kStreamPolicy = 2;  // nt
+
+// Direct-to-LDS loads: lane i's `bytes` bytes from g land at lds + i * bytes
+// (lds is the wave-uniform base).
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, kStreamPolicy);
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 4, 0, kStreamPolicy);
+}
+// Same, cached (small metadata reused by many waves: block-table windows).
+__device__ __forceinline__ void dma4_cached(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 4, 0, 0);
+}
+
+// LDS byte address of a generic pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Read one ring stage into registers: the lane's K fragments (kf), its four
+// V chunks (V rows row + 4 j; vp points at row `row`) and, for fp8, the k / v
+// scales of its four tokens. One inline-assembly block issues the reads and
+// waits for them (lgkmcnt(0)), so every destination is defined only once
+// its data has landed and no use or copy can be scheduled earlier; the
+// compiler also adds no wait of its own for the ring's direct-to-LDS loads
+// (the caller has waited for them).
+template <int D, bool FP8, typename VVec, int K_LD>
+__device__ __forceinline__ void read_stage(const unsigned char* kp, const unsigned char* vp, const unsigned char* sp,
+                                           u32x4 (&kf)[K_LD], VVec (&vf)[4], float (&ks)[4], float (&vs)[4]) {
+  const uint32_t ka = lds_addr(kp), va = lds_addr(vp), sa = lds_addr(sp);
+  if constexpr (!FP8 && D == 128) {  // row 256 B: 4 K fragments, V rows 1024 B apart
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b128 %2, %8 offset:2048\n\t"
+        "ds_read_b128 %3, %8 offset:3072\n\t"
+        "ds_read_b128 %4, %9\n\t"
+        "ds_read_b128 %5, %9 offset:1024\n\t"
+        "ds_read_b128 %6, %9 offset:2048\n\t"
+        "ds_read_b128 %7, %9 offset:3072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3]), "=&v"(vf[0]), "=&v"(vf[1]), "=&v"(vf[2]),
+          "=&v"(vf[3])
+        : "v"(ka), "v"(va)
+        : "memory");
+  } else if constexpr (!FP8 && D == 64) {  // row 128 B: 2 K fragments, 8-byte V chunks 512 B apart
+    asm volatile(
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %6 offset:1024\n\t"
+        "ds_read_b64 %2, %7\n\t"
+        "ds_read_b64 %3, %7 offset:512\n\t"
+        "ds_read_b64 %4, %7 offset:1024\n\t"
+        "ds_read_b64 %5, %7 offset:1536\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(vf[0]), "=&v"(vf[1]), "=&v"(vf[2]), "=&v"(vf[3])
+        : "v"(ka), "v"(va)
+        : "memory");
+  } else if constexpr (FP8 && D == 128) {  // row 128 B, plus two scale quads
+    f32x4 a, c;
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b64 %2, %9\n\t"
+        "ds_read_b64 %3, %9 offset:512\n\t"
+        "ds_read_b64 %4, %9 offset:1024\n\t"
+        "ds_read_b64 %5, %9 offset:1536\n\t"
+        "ds_read_b128 %6, %10\n\t"
+        "ds_read_b128 %7, %10 offset:64\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(vf[0]), "=&v"(vf[1]), "=&v"(vf[2]), "=&v"(vf[3]), "=&v"(a), "=&v"(c)
+        : "v"(ka), "v"(va), "v"(sa)
+        : "memory");
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      ks[v] = a[v];
+      vs[v] = c[v];
+    }
+  } else {  // fp8, D == 64: row 64 B: 1 K fragment, 4-byte V chunks 256 B apart
+    static_assert(FP8 && D == 64, "layout");
+    f32x4 a, c;
+    asm volatile(
+        "ds_read_b128 %0, %7\n\t"
+        "ds_read_b32 %1, %8\n\t"
+        "ds_read_b32 %2, %8 offset:256\n\t"
+        "ds_read_b32 %3, %8 offset:512\n\t"
+        "ds_read_b32 %4, %8 offset:768\n\t"
+        "ds_read_b128 %5, %9\n\t"
+        "ds_read_b128 %6, %9 offset:64\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kf[0]), "=&v"(vf[0]), "=&v"(vf[1]), "=&v"(vf[2]), "=&v"(vf[3]), "=&v"(a), "=&v"(c)
+        : "v"(ka), "v"(va), "v"(sa)
+        : "memory");
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      ks[v] = a[v];
+      vs[v] = c[v];
+    }
+  }
+}
+
+// Token order inside a 16-token tile. MFMA A-row m carries token
+// tile_token(m) = m / 4 + 4 (m mod 4), so the result row 4 r + v held by
+// 16-lane row r is token r + 4 v: every 16-lane row owns the tokens
+// congruent to r mod 4, for the scores as well as for the V rows it reads.
+__device__ __forceinline__ int tile_token(int m) { return (m >> 2) + 4 * (m & 3); }
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ long long wave_incl_scan(long long v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const long long t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ long long uniform64(long long x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(x & 0xffffffffll));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((unsigned long long)x >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+// The per-wave tile machinery for head_dim D, group size G and pool type.
+template <int D, int G, bool FP8>
+struct Tile {
+  static constexpr int ESZ = FP8 ? 1 : 2;             // bytes per stored element
+  static constexpr int ROW_BYTES = D * ESZ;           // one (token, kv head) row
+  static constexpr int KSTEPS = D / 32;               // MFMA k-steps over head_dim
+  static constexpr int K_LD = ROW_BYTES / 64;         // 16-byte loads per lane per tile, K
+  static constexpr int V_LD = ROW_BYTES / 64;         // and V (a tile is 16 rows)
+  static constexpr int C = K_LD + V_LD + (FP8 ? 1 : 0);  // direct-to-LDS loads per tile
+  static constexpr int VE = D / 16;                   // V elements per lane per row
+  static constexpr int VB = VE * ESZ;                 // V bytes per lane per row
+  // one ring stage: K tile in MFMA-operand lane order, V tile row-major,
+  // then (fp8) 64 scale slots: k scales 0..15, v scales 16..31
+  static constexpr int K_TILE = kTileTokens * ROW_BYTES;
+  static constexpr int V_TILE = kTileTokens * ROW_BYTES;
+  static constexpr int STAGE = K_TILE + V_TILE + (FP8 ? 256 : 0);
+  static constexpr int RF = (int)record_floats(D, G);
+  static constexpr int EPL = G * D / 64;  // accumulator elements per lane in the merge layout
+  using VVec = typename VChunk<VB>::type;
+  static_assert(K_LD >= 1 && (D == 64 || D == 128), "head_dim");
+  static_assert(G >= 1 && G <= 16, "group size");
+  static_assert(EPL >= 1 && D % EPL == 0, "merge lane slice");
+
+  // Online-softmax state of one piece: running max m (base 2) and sum l of
+  // head `col` (every row holds the same after reduce_rows), and acc[g][e]:
+  // head g, d = col * VE + e, summed over this row's tokens.
+  struct State {
+    float m, l;
+    float acc[G][VE];
+  };
+  // One stage read back into registers.
+  struct Frag {
+    u32x4 kf[K_LD];
+    VVec vf[4];
+    float ks[4], vs[4];
+  };
+
+  __device__ static void reset(State& s) {
+    s.m = -__builtin_inff();
+    s.l = 0.0f;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < VE; ++e) s.acc[g][e] = 0.0f;
+  }
+
+  // head_dim position of element 0 of lane (row, ·)'s fragment at k-step kk;
+  // the K fragments follow the same order
+  __device__ static int dpos(int kk, int row) {
+    if constexpr (FP8) return (kk >> 1) * 64 + row * 16 + (kk & 1) * 8;
+    else return kk * 32 + row * 8;
+  }
+
+  // Q as the MFMA B operand: lane (row, col) holds head col (zero for col >=
+  // G) at 8 head_dim positions per k-step. qpair points at q[b][kvh * G][0].
+  __device__ static void load_q(bf16x8 (&qop)[KSTEPS], const uint16_t* qpair, int row, int col) {
+    const uint16_t* qrow = qpair + (long long)min(col, G - 1) * D;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + dpos(kk, row));
+      if (col >= G) raw = u32x4{0u, 0u, 0u, 0u};
+      qop[kk] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+
+  // Issue the C direct-to-LDS loads of the tile starting at token tb of one
+  // pair into stage st. row_of(pos) gives the (token, kv head) row index of
+  // sequence position pos; rows past `last` (the pair's last token) are
+  // clamped onto it (finite data, masked in the softmax).
+  template <typename RowOf>
+  __device__ static void issue(unsigned char* st, const uint8_t* k, const uint8_t* v, const float* k_scale,
+                               const float* v_scale, RowOf&& row_of, int tb, int last, int lane, int row,
+                               int col) {
+    {
+      // K: lane (row, col) fetches bytes [j*64 + row*16, +16) of token
+      // tile_token(col); it lands at j*1024 + lane*16, the lane's own
+      // A-operand fragment for k-steps 2j, 2j+1 (fp8) or j (bf16).
+      const int pos = min(tb + tile_token(col), last);
+      const unsigned char* src = k + row_of(pos) * ROW_BYTES + row * 16;
+#pragma unroll
+      for (int jj = 0; jj < K_LD; ++jj) dma16(src + jj * 64, st + jj * 1024);
+    }
+#pragma unroll
+    for (int jj = 0; jj < V_LD; ++jj) {
+      // V: row-major tile, 64 lanes x 16 bytes per load
+      const int byte = jj * 1024 + lane * 16;
+      const int pos = min(tb + byte / ROW_BYTES, last);
+      dma16(v + row_of(pos) * ROW_BYTES + (byte % ROW_BYTES), st + K_TILE + jj * 1024);
+    }
+    if constexpr (FP8) {
+      // scale slot m < 16 holds k_scale of token tile_token(m); slot 16 + m
+      // holds its v_scale; lanes 32..63 repeat lanes 0..31
+      const int m = lane & 15;
+      const int pos = min(tb + tile_token(m), last);
+      const float* src = ((lane & 16) ? v_scale : k_scale) + row_of(pos);
+      dma4(src, st + K_TILE + V_TILE);
+    }
+  }
+
+  __device__ static void read(Frag& f, const unsigned char* st, int lane, int row, int col) {
+    read_stage<D, FP8>(st + lane * 16, st + K_TILE + row * ROW_BYTES + col * VB, st + K_TILE + V_TILE + row * 16,
+                       f.kf, f.vf, f.ks, f.vs);
+  }
+
+  // One tile of the online softmax: tokens tb .. tb+15 of the pair, those
+  // at or past L masked.
+  __device__ static void compute(State& s, const Frag& f, const bf16x8 (&qop)[KSTEPS], int tb, int L,
+                                 float qk_scale_log2, int row) {
+    // S[t][g]: lane (row, col) holds head col for tokens row + 4 v
+    f32x4 Sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      u32x4 kw;
+      if constexpr (FP8) {
+        const u32x4& c = f.kf[kk >> 1];
+        kw = fp8x8_to_bf16x8(c[(kk & 1) * 2], c[(kk & 1) * 2 + 1]);
+      } else {
+        kw = f.kf[kk];
+      }
+      Sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw), qop[kk], Sacc, 0, 0, 0);
+    }
+    float sc[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float x = Sacc[v] * qk_scale_log2;
+      if constexpr (FP8) x *= f.ks[v];
+      sc[v] = (tb + row + 4 * v < L) ? x : -__builtin_inff();
+    }
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(s.m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(s.m - m_new);
+    float pr[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) pr[v] = __builtin_amdgcn_exp2f(sc[v] - m_new);
+    s.l = s.l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    const bool grew = m_new > s.m;
+    s.m = m_new;
+    if (__any(grew)) {
+      static_for<0, G>([&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        const float a = row_bcast<g>(alpha);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) s.acc[g][e] *= a;
+      });
+    }
+    if constexpr (FP8) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) pr[v] *= f.vs[v];
+    }
+    // p . V: lane (row, col) takes V row (token) row + 4 j, d-chunk col
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      float vf[VE];
+      if constexpr (FP8) {
+#pragma unroll
+        for (int w = 0; w < VB / 4; ++w) {
+          const uint32_t x = dword(f.vf[jj], w);
+          auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(x, false);
+          auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(x, true);
+          vf[4 * w + 0] = lo[0];
+          vf[4 * w + 1] = lo[1];
+          vf[4 * w + 2] = hi[0];
+          vf[4 * w + 3] = hi[1];
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < VB / 4; ++w) {
+          const uint32_t x = dword(f.vf[jj], w);
+          vf[2 * w + 0] = bf16_lo(x);
+          vf[2 * w + 1] = bf16_hi(x);
+        }
+      }
+      const float pj = pr[jj];
+      static_for<0, G>([&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        const float pg = row_bcast<g>(pj);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) s.acc[g][e] = fmaf(pg, vf[e], s.acc[g][e]);
+      });
+    }
+  }
+
+  // Sum l and acc over the four rows (disjoint tokens); every row then holds
+  // the totals.
+  __device__ static void reduce_rows(State& s) {
+    s.l += __shfl_xor(s.l, 16);
+    s.l += __shfl_xor(s.l, 32);
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        float a = s.acc[g][e];
+        a += __shfl_xor(a, 16);
+        a += __shfl_xor(a, 32);
+        s.acc[g][e] = a;
+      }
+  }
+
+  // A whole pair after reduce_rows: out = acc / l, lse = ln 2 (m + log2 l).
+  // o points at out[b][kvh * G][0], lo at lse[b][kvh * G] (or null); row r
+  // writes the heads g with g mod 4 == r.
+  __device__ static void store_out(const State& s, float* o, float* lo, bool poisoned, int row, int col) {
+    const float nan = __builtin_nanf("");
+    static_for<0, G>([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      const float lg = row_bcast<g>(s.l);
+      if (row == (g & 3)) {
+        float* d = o + g * D + col * VE;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) d[e] = poisoned ? nan : s.acc[g][e] / lg;
+      }
+    });
+    if (lo != nullptr && row == 0 && col < G) lo[col] = poisoned ? nan : (s.m + log2f(s.l)) * kLn2;
+  }
+
+  // A partial record after reduce_rows: m[G], l[G], acc[G][D] (un-normalised).
+  // A poisoned piece records m = 0, l = acc = NaN, so every merge it enters
+  // gives NaN. COHERENT: device-scope atomic stores (visible to waves on
+  // other XCDs once complete) instead of plain ones.
+  template <bool COHERENT = false>
+  __device__ static void store_record(const State& s, float* r, bool poisoned, int row, int col) {
+    const float nan = __builtin_nanf("");
+    if constexpr (COHERENT) {
+      // every row holds the totals: row 0 writes all heads (lane-dependent
+      // head choices would move the accumulators to scratch memory here)
+      if (row == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int e = 0; e < VE; ++e) put<true>(r + 2 * G + g * D + col * VE + e, poisoned ? nan : s.acc[g][e]);
+      }
+    } else {
+      // row r writes the heads g with g mod 4 == r
+      static_for<0, G>([&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        if (row == (g & 3)) {
+          float* d = r + 2 * G + g * D + col * VE;
+#pragma unroll
+          for (int e = 0; e < VE; ++e) d[e] = poisoned ? nan : s.acc[g][e];
+        }
+      });
+    }
+    if (row == 0 && col < G) {
+      put<COHERENT>(r + col, poisoned ? 0.0f : s.m);
+      put<COHERENT>(r + G + col, poisoned ? nan : s.l);
+    }
+  }
+  template <bool COHERENT>
+  __device__ static void put(float* a, float v) {
+    if constexpr (COHERENT) __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *a = v;
+  }
+};
+
+}  // namespace dev
+}  // namespace pdattn

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert {"pdattn_plan", "pdattn_decode", "pdattn_reduce", "pdattn_status_string",
+    assert {"pdattn_plan", "pdattn_decode", "pdattn_reduce", "pdattn_workspace_init", "pdattn_status_string",
             "pdattn_last_error"} <= set(names)
     lib = ctypes.CDLL(pk.library_path)
     for n in names:
@@ -52,32 +52,55 @@ def problem(**kw):
     return d
 
 
-def plan_raw(lens, num_cus=256, force=0, **kw):
+def plan_raw(lens, num_cus=256, force=0, flags=0, **kw):
     p = problem(**kw)
     prob = pk.Problem(*[p[f] for f, _ in pk.Problem._fields_])
     lens_t = torch.as_tensor(lens, dtype=torch.int32).contiguous() if lens is not None else None
     out = pk.Plan()
     ptr = ctypes.c_void_p(lens_t.data_ptr()) if lens_t is not None else None
-    st = pk._lib.pdattn_plan(ctypes.byref(prob), ptr, num_cus, force, ctypes.byref(out))
+    st = pk._lib.pdattn_plan(ctypes.byref(prob), ptr, num_cus, force, flags, ctypes.byref(out))
     return st, out
 
 
+def dyn_workspace_bytes(pl):
+    """Balanced-mode workspace: 256-byte header, counters (claims, records,
+    done tiles per unit; done units per pair), unit records (units_max + 3
+    per worker), pair-level records when a pair can span several units."""
+    pr = pl.problem
+    G = pr.num_q_heads // pr.num_kv_heads
+    rec = G * (pr.head_dim + 2) * 4
+    max_tiles = -(-pr.max_pages_per_seq * pr.page_size // 16)
+    seg_max = max(1, -(-max_tiles // 512))
+    units = pr.batch * pr.num_kv_heads * seg_max
+    up = lambda x: -(-x // 256) * 256
+    ctl = 4 * (3 * units + pr.batch * pr.num_kv_heads)
+    total = 256 + up(ctl) + up((units + 3 * pl.num_workers) * rec)
+    if seg_max > 1:
+        total += units * rec
+    return total
+
+
+@pytest.mark.parametrize("flags", [0, 2], ids=["static", "balanced"])
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
-def test_plan_for_each_workload(name):
+def test_plan_for_each_workload(name, flags):
     w = synth.WORKLOADS[name]
     g = torch.Generator().manual_seed(w.seed)
     lens = synth._lens(w, g)
     maxp = int((lens.max() + w.page_size - 1) // w.page_size)
-    st, pl = plan_raw(lens, batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+    st, pl = plan_raw(lens, flags=flags, batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
                       head_dim=w.head_dim, page_size=w.page_size, max_pages_per_seq=maxp, num_pages=10 ** 6,
                       kv_dtype=0 if w.kv_dtype == "bf16" else 1)
     assert st == OK, pk._lib.pdattn_last_error()
+    assert pl.flags == flags
     tiles = w.num_kv_heads * sum((int(L) + 15) // 16 for L in lens.tolist())
     assert pl.total_tiles == tiles
     assert pl.max_context_len == int(lens.max())
     G = w.num_q_heads // w.num_kv_heads
     rec = G * (w.head_dim + 2) * 4
-    assert pl.workspace_bytes == pl.num_workers * (2 * rec + 8 * 4)
+    if flags:
+        assert pl.workspace_bytes == dyn_workspace_bytes(pl)
+    else:
+        assert pl.workspace_bytes == pl.num_workers * (2 * rec + 8 * 4)
     assert 1 <= pl.num_workers <= 4 * pl.num_workgroups
     assert pl.num_workers <= max(1, tiles // 4)
     assert abs(pl.problem.scale - 1.0 / math.sqrt(w.head_dim)) < 1e-7
@@ -108,6 +131,9 @@ def test_plan_forced_workers_and_empty_batch():
     (dict(), [1, -1, 1, 1], INVALID),
     (dict(), None, INVALID),                                 # no host lengths
     (dict(num_pages=0), [1, 1, 1, 1], INVALID),              # nothing to read from
+    (dict(flags=1), [1, 1, 1, 1], INVALID),                  # unknown flag
+    (dict(flags=2, batch=65535, num_q_heads=128, num_kv_heads=128, max_pages_per_seq=4096), [1] * 65535,
+     UNSUPPORTED),                                           # 2^31 tiles per row set (balanced mode)
 ])
 def test_plan_rejects(kw, lens, expect):
     st, _ = plan_raw(lens, **kw)
@@ -144,6 +170,9 @@ def test_decode_validation_rejects_before_launch():
     bad = pk.Plan.from_buffer_copy(bytes(pl))
     bad.num_workers = 10 ** 7
     assert _decode_raw(bad) == MISMATCH
+    bad = pk.Plan.from_buffer_copy(bytes(pl))
+    bad.flags = 6
+    assert _decode_raw(bad) == MISMATCH
     assert "workspace" in pk._lib.pdattn_last_error().decode() or pk._lib.pdattn_last_error()
     st, empty = plan_raw([], batch=0)
     assert _decode_raw(empty, q=0, k=0, v=0, bt=0, lens=0, out=0, ws=0) == OK   # nothing to do
@@ -172,3 +201,22 @@ def test_worker_range_arithmetic():
         brute = max(w for w in range(NW) if w * T // NW <= C)
         assert wf == brute
         assert wf * T // NW <= C < (wf + 1) * T // NW
+
+
+def test_workspace_init_validation():
+    st, pl = plan_raw([5, 9, 100, 33], flags=2)
+    P = ctypes.c_void_p
+    assert pk._lib.pdattn_workspace_init(ctypes.byref(pl), None, pl.workspace_bytes, None) == WORKSPACE
+    assert pk._lib.pdattn_workspace_init(ctypes.byref(pl), P(16), pl.workspace_bytes - 1, None) == WORKSPACE
+    assert pk._lib.pdattn_workspace_init(ctypes.byref(pl), P(0x1008), pl.workspace_bytes, None) == INVALID
+    assert pk._lib.pdattn_workspace_init(None, P(16), 0, None) == INVALID
+    st, static = plan_raw([5, 9, 100, 33])
+    assert pk._lib.pdattn_workspace_init(ctypes.byref(static), None, 0, None) == OK   # nothing to prepare
+
+
+def test_balanced_reduce_is_a_validated_no_op():
+    st, pl = plan_raw([5, 9, 100, 33], flags=2)
+    P = ctypes.c_void_p
+    # valid-looking arguments: nothing is launched for a default-mode plan
+    assert pk._lib.pdattn_reduce(ctypes.byref(pl), P(16), pl.workspace_bytes, P(16), None, None) == OK
+    assert pk._lib.pdattn_reduce(ctypes.byref(pl), P(16), pl.workspace_bytes - 1, P(16), None, None) == WORKSPACE

@@ -65,12 +65,18 @@ def assert_parity(out, lse, ref_out, ref_lse, fp8=False, tag=""):
     assert ldiff <= LSE_MAX, (tag, ldiff)
 
 
+MODES = [False, True]
+MODE_IDS = ["static", "balanced"]
+
+
+@pytest.mark.parametrize("balanced", MODES, ids=MODE_IDS)
 @pytest.mark.parametrize("name", ["tiny", "llama3_8b", "many_short", "fp8_kv", "long_ctx"])
-def test_workload_matches_oracle(name):
+def test_workload_matches_oracle(name, balanced):
     inp = synth.make_inputs(name)
-    out, lse = gpu_run(inp)
+    out, lse = gpu_run(inp, balanced=balanced)
     ref_out, ref_lse = oracle_run(inp)
-    assert_parity(out, lse, ref_out, ref_lse, fp8=inp["k_pages"].dtype == torch.float8_e4m3fn, tag=name)
+    assert_parity(out, lse, ref_out, ref_lse, fp8=inp["k_pages"].dtype == torch.float8_e4m3fn,
+                  tag=f"{name} balanced={balanced}")
 
 
 def small(B, Hq, Hkv, D, P, lens, kv="bf16", seed=0):
@@ -87,9 +93,10 @@ def test_every_instantiation_matches_oracle(G, D, kv):
     w = small(B=5, Hq=2 * G, Hkv=2, D=D, P=16, lens=("uniform", 1, 700), kv=kv, seed=100 + G + D)
     inp = synth.make_inputs(w)
     ref = oracle_run(inp)
-    for force in (0, 1, 7, 64):
-        out, lse = gpu_run(inp, force_workers=force)
-        assert_parity(out, lse, *ref, fp8=kv != "bf16", tag=f"G{G} D{D} {kv} workers={force}")
+    for bal in MODES:
+        for force in (0, 1, 7, 64):
+            out, lse = gpu_run(inp, force_workers=force, balanced=bal)
+            assert_parity(out, lse, *ref, fp8=kv != "bf16", tag=f"G{G} D{D} {kv} workers={force} balanced={bal}")
 
 
 @pytest.mark.parametrize("P", [8, 16, 32, 64, 128])
@@ -97,6 +104,7 @@ def test_page_sizes(P):
     w = small(B=4, Hq=8, Hkv=2, D=128, P=P, lens=("uniform", 1, 1500), seed=200 + P)
     inp = synth.make_inputs(w)
     ref = oracle_run(inp)
-    for force in (0, 3, 200):
-        out, lse = gpu_run(inp, force_workers=force)
-        assert_parity(out, lse, *ref, tag=f"P{P} workers={force}")
+    for bal in MODES:
+        for force in (0, 3, 200):
+            out, lse = gpu_run(inp, force_workers=force, balanced=bal)
+            assert_parity(out, lse, *ref, tag=f"P{P} workers={force} balanced={bal}")

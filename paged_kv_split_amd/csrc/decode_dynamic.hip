@@ -389,17 +389,12 @@ void decode_dynamic_kernel(DynParams p) {
   // and is read back when that segment has been streamed (the wave has no
   // loads in flight then), so its round trip overlaps the segment.
   const int t0 = (int)((long long)w * gl.T / gl.NW);
-  bool claim_pending = false;
   uint32_t claim_reg = 0;  // lane 0: result of the pending claim
   auto issue_claim = [&](int uid) {
     if (lane == 0)
       claim_reg = __hip_atomic_fetch_add(ctr + uid, (uint32_t)kClaimTiles, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    claim_pending = true;
   };
-  auto take_claim = [&]() -> uint32_t {
-    claim_pending = false;
-    return __builtin_amdgcn_readfirstlane(claim_reg);
-  };
+  auto take_claim = [&]() -> uint32_t { return __builtin_amdgcn_readfirstlane(claim_reg); };
   // longest run the staged block-table entries cover from any starting token
   const int max_seg = ((W - 1) << lp) / kTileTokens;
 

@@ -274,24 +274,29 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p) {
   if (lane < kDescWords) p.desc[gw * kDescWords + lane] = dsc[lane];
 }
 
+// Waves of a merge workgroup, and the pieces one merge wave loads per step.
+constexpr int kMergeWaves = kWaves;
+constexpr int kMergeUnroll = 4;
+
 // One workgroup per worker descriptor; only the descriptors of cut pairs
 // are valid. Every worker wf .. w holds a record for the pair (a worker
 // with an empty tile range holds the empty record m = -inf, l = acc = 0).
-// Pass 1 takes M[g] = max m over the pieces; in pass 2 the four waves take
-// every fourth piece and each lane accumulates its own slice of one head's
-// accumulator with vector loads, so the piece loop keeps many loads in
-// flight; the waves' sums meet in LDS.
+// One pass: each of the kMergeWaves waves merges every kMergeWaves-th piece
+// with the online rule (a
+// running maximum M, l and acc rescaled by 2^(M_old - M_new)), loading
+// kMergeUnroll pieces per step so their loads overlap; each lane keeps its
+// own slice of one head's accumulator. The four waves' (M, l, acc) meet in LDS and are
+// merged by the same rule.
 template <int D, int G>
-__global__ __launch_bounds__(kWaves * 64) void merge_kernel(MergeParams p) {
+__global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(MergeParams p) {
   constexpr int RF = (int)record_floats(D, G);
-  constexpr int NT = kWaves * 64;
+  constexpr int NT = kMergeWaves * 64;
   constexpr int EPL = G * D / 64;      // accumulator elements per lane
   constexpr int LPH = D / EPL;         // lanes per head
   static_assert(EPL >= 1 && D % EPL == 0, "lane slice");
-  __shared__ float s_red[kWaves][G];
-  __shared__ float s_M[G];
-  __shared__ __attribute__((aligned(16))) float s_acc[kWaves][G * D];
-  __shared__ float s_l[kWaves][G];
+  __shared__ float s_m[kMergeWaves][G];
+  __shared__ float s_l[kMergeWaves][G];
+  __shared__ __attribute__((aligned(16))) float s_acc[kMergeWaves][G * D];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -308,63 +313,63 @@ __global__ __launch_bounds__(kWaves * 64) void merge_kernel(MergeParams p) {
     return p.rec + ((wf + i) * 2 + (i == 0 ? slot_first : 0)) * RF;
   };
 
-  // pass 1
-  float mloc[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) mloc[g] = -__builtin_inff();
-  for (long long i = tid; i < n; i += NT) {
-    const float* r = piece(i);
-#pragma unroll
-    for (int g = 0; g < G; ++g) mloc[g] = fmaxf(mloc[g], r[g]);
-  }
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float x = mloc[g];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-    if (lane == 0) s_red[wave][g] = x;
-  }
-  __syncthreads();
-  if (tid < G) {
-    float x = s_red[0][tid];
-#pragma unroll
-    for (int k = 1; k < kWaves; ++k) x = fmaxf(x, s_red[k][tid]);
-    s_M[tid] = x;
-  }
-  __syncthreads();
-
-  // pass 2
-  const int g = lane / LPH;             // this lane's head
-  const int e0 = lane * EPL;            // first element of its slice (g * D + ...)
-  const float Mg = s_M[g];
-  float A[EPL];
+  const int g = lane / LPH;   // this lane's head
+  const int e0 = lane * EPL;  // first element of its slice (g * D + ...)
+  float M = -__builtin_inff(), L = 0.0f, A[EPL];
 #pragma unroll
   for (int k = 0; k < EPL; ++k) A[k] = 0.0f;
-  float lsum = 0.0f;
-#pragma unroll 4
-  for (long long i = wave; i < n; i += kWaves) {
-    const float* r = piece(i);
-    const float wgt = __builtin_amdgcn_exp2f(r[g] - Mg);
-    lsum = fmaf(wgt, r[G + g], lsum);
-    const float* a = r + 2 * G + e0;
+  // fold one piece (m, l, acc slice) into the running state
+  auto fold = [&](float mi, float li, const float (&ai)[EPL]) {
+    const float Mn = fmaxf(M, mi);
+    // equal maxima (including both -inf: an empty record) scale by 1
+    const float so = M == Mn ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
+    const float si = mi == Mn ? 1.0f : __builtin_amdgcn_exp2f(mi - Mn);
+    L = L * so + li * si;
 #pragma unroll
-    for (int k = 0; k < EPL; ++k) A[k] = fmaf(wgt, a[k], A[k]);
+    for (int k = 0; k < EPL; ++k) A[k] = A[k] * so + ai[k] * si;
+    M = Mn;
+  };
+  constexpr int U = kMergeUnroll;
+  for (long long i = wave; i < n; i += U * kMergeWaves) {
+    // U pieces per step (every fourth piece from i), all loads issued first
+    float mu[U], lu[U], au[U][EPL];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const long long iu = i + (long long)u * kMergeWaves;
+      const float* r = piece(iu < n ? iu : i);
+      mu[u] = r[g];
+      lu[u] = r[G + g];
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) au[u][k] = r[2 * G + e0 + k];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i + (long long)u * kMergeWaves < n) fold(mu[u], lu[u], au[u]);
   }
 #pragma unroll
   for (int k = 0; k < EPL; ++k) s_acc[wave][e0 + k] = A[k];
-  if (lane % LPH == 0) s_l[wave][g] = lsum;
+  if (lane % LPH == 0) {
+    s_m[wave][g] = M;
+    s_l[wave][g] = L;
+  }
   __syncthreads();
   for (int e = tid; e < G * D; e += NT) {
     const int gg = e / D;
+    float Mx = s_m[0][gg];
+#pragma unroll
+    for (int q = 1; q < kMergeWaves; ++q) Mx = fmaxf(Mx, s_m[q][gg]);
     float Av = 0.0f, Ls = 0.0f;
 #pragma unroll
-    for (int q = 0; q < kWaves; ++q) {
-      Av += s_acc[q][e];
-      Ls += s_l[q][gg];
+    for (int q = 0; q < kMergeWaves; ++q) {
+      const float mq = s_m[q][gg];
+      // a wave without pieces holds M = -inf, l = acc = 0: weight 0
+      const float wq = mq == Mx ? 1.0f : __builtin_amdgcn_exp2f(mq - Mx);
+      Av += wq * s_acc[q][e];
+      Ls += wq * s_l[q][gg];
     }
     const long long bh = (long long)b * p.num_q_heads + kvh * G + gg;
     p.out[bh * D + (e % D)] = Av / Ls;
-    if (e % D == 0 && p.lse != nullptr) p.lse[bh] = (s_M[gg] + log2f(Ls)) * kLn2;
+    if (e % D == 0 && p.lse != nullptr) p.lse[bh] = (Mx + log2f(Ls)) * kLn2;
   }
 }
 
@@ -410,11 +415,11 @@ template <int D>
 hipError_t launch_merge_d(const MergeParams& p, int group, uint32_t grid, hipStream_t stream) {
   // one workgroup per worker descriptor
   switch (group) {
-    case 1: hipLaunchKernelGGL((merge_kernel<D, 1>), dim3(grid), dim3(kWaves * 64), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((merge_kernel<D, 2>), dim3(grid), dim3(kWaves * 64), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((merge_kernel<D, 4>), dim3(grid), dim3(kWaves * 64), 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((merge_kernel<D, 8>), dim3(grid), dim3(kWaves * 64), 0, stream, p); break;
-    case 16: hipLaunchKernelGGL((merge_kernel<D, 16>), dim3(grid), dim3(kWaves * 64), 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((merge_kernel<D, 1>), dim3(grid), dim3(kMergeWaves * 64), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((merge_kernel<D, 2>), dim3(grid), dim3(kMergeWaves * 64), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((merge_kernel<D, 4>), dim3(grid), dim3(kMergeWaves * 64), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((merge_kernel<D, 8>), dim3(grid), dim3(kMergeWaves * 64), 0, stream, p); break;
+    case 16: hipLaunchKernelGGL((merge_kernel<D, 16>), dim3(grid), dim3(kMergeWaves * 64), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -186,6 +186,50 @@ PDATTN_API pdattn_status pdattn_decode(const pdattn_plan_t* plan, const void* q,
 PDATTN_API pdattn_status pdattn_reduce(const pdattn_plan_t* plan, const void* workspace,
                                        uint64_t workspace_bytes, float* out, float* lse, void* stream);
 
+/* Append flags. */
+#define PDATTN_APPEND_POW2_SCALES 1 /* fp8 pools: power-of-two scales */
+
+/*
+ * Enqueue the KV append on `stream`: write the K and V rows of num_tokens
+ * new tokens into the paged pools (FlashQuant wiki "CUDA Kernels",
+ * paged_decode.cu Page Table Addressing: the slot of position t of sequence
+ * b is page block_table[b][t / P], row t mod P; Atlas "CUDA Kernel
+ * Engineering", kernel inventory: per-token K/V write into the paged cache;
+ * OASR "Kernel Layer", FP8 KV variants: the quantise-and-scatter that fills
+ * an FP8 cache, with power-of-two scales).
+ *   problem      the pools' shape: batch, num_kv_heads, head_dim,
+ *                page_size, max_pages_per_seq, num_pages and kv_dtype are
+ *                used (num_q_heads and scale are validated, not used)
+ *   k_new, v_new bf16 [num_tokens][Hkv][d], device, 16-byte aligned
+ *   token_seq    int32 [num_tokens], device: the sequence b of each token
+ *   token_pos    int32 [num_tokens], device: its position t in that sequence
+ *   block_table  int32 [B][max_pages_per_seq], device
+ *   k_pages,     the pools, layouts as for pdattn_decode; written in place
+ *   v_pages
+ *   k_scale,     fp32 [num_pages][P][Hkv] for fp8 pools (written in place),
+ *   v_scale      NULL for bf16 pools
+ *   flags        0 or PDATTN_APPEND_POW2_SCALES (fp8 pools only)
+ * A bf16 pool receives the rows bit for bit. An fp8 pool receives, for each
+ * (token, kv head) and separately for K and V, a scale s and the codes
+ * code_i = e4m3fn(clamp(x_i / s, -448, 448)), rounded to the nearest code,
+ * ties to even, every division a correctly rounded fp32 division: s =
+ * absmax / 448 by default, or with PDATTN_APPEND_POW2_SCALES the smallest
+ * power of two s with 448 * s >= absmax (then x_i / s is exact and so is the
+ * decode's product code * s); an all-zero row gets s = 1. Non-finite inputs
+ * give unspecified codes.
+ * A token whose sequence is outside [0, B), whose position is outside
+ * [0, max_pages_per_seq * P), or whose block_table entry is outside
+ * [0, num_pages) is skipped: nothing is written for it. Tokens must name
+ * distinct slots (two tokens writing one slot race). Nothing else in the
+ * pools changes. The library allocates nothing and never synchronises; the
+ * call is safe to capture in a graph. Errors: validated before launch as
+ * for pdattn_decode; an invalid call enqueues nothing.
+ */
+PDATTN_API pdattn_status pdattn_kv_append(const pdattn_problem* problem, int32_t num_tokens, const void* k_new,
+                                          const void* v_new, const int32_t* token_seq, const int32_t* token_pos,
+                                          const int32_t* block_table, void* k_pages, void* v_pages, float* k_scale,
+                                          float* v_scale, int32_t flags, void* stream);
+
 /* Static description of a status code. */
 PDATTN_API const char* pdattn_status_string(pdattn_status status);
 

@@ -14,11 +14,12 @@ import torch
 
 __all__ = ["Problem", "Plan", "PdattnError", "plan", "decode", "reduce", "workspace", "workspace_init",
            "paged_decode", "KV_BF16", "KV_FP8_E4M3", "PLAN_BALANCED", "library_path", "stream_read",
-           "stream_read_sink"]
+           "stream_read_sink", "kv_append", "APPEND_POW2_SCALES"]
 
 KV_BF16 = 0
 KV_FP8_E4M3 = 1
 PLAN_BALANCED = 2
+APPEND_POW2_SCALES = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libpdattn.so")
@@ -78,6 +79,9 @@ _lib.pdattn_stream_read.restype = ctypes.c_int
 _lib.pdattn_stream_read.argtypes = [_P, ctypes.c_uint64, _P, ctypes.c_int32, _P]
 _lib.pdattn_stream_read_sink_words.restype = ctypes.c_uint64
 _lib.pdattn_stream_read_sink_words.argtypes = [ctypes.c_int32]
+_lib.pdattn_kv_append.restype = ctypes.c_int
+_lib.pdattn_kv_append.argtypes = [ctypes.POINTER(Problem), ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                  ctypes.c_int32, _P]
 _lib.pdattn_problem_size.restype = ctypes.c_uint64
 _lib.pdattn_plan_size.restype = ctypes.c_uint64
 
@@ -162,6 +166,26 @@ def stream_read(buffer, sink, num_cus, stream=None):
 
 def stream_read_sink(num_cus, device):
     return torch.empty(int(_lib.pdattn_stream_read_sink_words(int(num_cus))), dtype=torch.int32, device=device)
+
+
+def kv_append(k_new, v_new, token_seq, token_pos, block_table, k_pages, v_pages, k_scale=None, v_scale=None,
+              *, batch=None, pow2_scales=False, stream=None):
+    """``pdattn_kv_append``: write new K/V rows into the pools in place.
+
+    k_new/v_new: bf16 [N,Hkv,d]; token_seq/token_pos: int32 [N]; block_table
+    int32 [B,max_pages]; k_pages/v_pages: bf16 or float8_e4m3fn [num_pages,P,Hkv,d];
+    k_scale/v_scale: fp32 [num_pages,P,Hkv] for fp8 pools. ``batch`` defaults
+    to the block table's row count.
+    """
+    N = k_new.shape[0]
+    num_pages, P, Hkv, D = k_pages.shape
+    kv = KV_FP8_E4M3 if k_pages.dtype == torch.float8_e4m3fn else KV_BF16
+    B = block_table.shape[0] if batch is None else batch
+    prob = Problem(B, Hkv, Hkv, D, P, block_table.shape[1], num_pages, kv, 0.0)
+    flags = APPEND_POW2_SCALES if pow2_scales else 0
+    _check(_lib.pdattn_kv_append(ctypes.byref(prob), int(N), _ptr(k_new), _ptr(v_new), _ptr(token_seq),
+                                 _ptr(token_pos), _ptr(block_table), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
+                                 _ptr(v_scale), flags, _stream(stream)), "pdattn_kv_append")
 
 
 def paged_decode(q, k_pages, v_pages, block_table, context_lens, *, context_lens_host=None,

@@ -11,7 +11,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libpdattn.so")
 SOURCES = [os.path.join(CSRC, "pdattn.hip"), os.path.join(CSRC, "decode_kernels.hip"),
-           os.path.join(CSRC, "decode_dynamic.hip"), os.path.join(CSRC, "stream_read.hip")]
+           os.path.join(CSRC, "decode_dynamic.hip"), os.path.join(CSRC, "stream_read.hip"),
+           os.path.join(CSRC, "kv_append.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

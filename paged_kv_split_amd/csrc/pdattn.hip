@@ -371,6 +371,58 @@ PDATTN_API pdattn_status pdattn_workspace_init(const pdattn_plan_t* plan, void* 
   return PDATTN_OK;
 }
 
+PDATTN_API pdattn_status pdattn_kv_append(const pdattn_problem* problem, int32_t num_tokens, const void* k_new,
+                                          const void* v_new, const int32_t* token_seq, const int32_t* token_pos,
+                                          const int32_t* block_table, void* k_pages, void* v_pages, float* k_scale,
+                                          float* v_scale, int32_t flags, void* stream) {
+  g_last_error[0] = '\0';
+  pdattn_status st = check_problem(problem);
+  if (st != PDATTN_OK) return st;
+  if (num_tokens < 0) return fail(PDATTN_ERR_INVALID_ARGUMENT, "num_tokens %d is negative", num_tokens);
+  if ((flags & ~PDATTN_APPEND_POW2_SCALES) != 0)
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "unknown append flags %d", flags);
+  const bool fp8 = problem->kv_dtype == PDATTN_KV_FP8_E4M3;
+  if (!fp8 && (flags & PDATTN_APPEND_POW2_SCALES))
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "PDATTN_APPEND_POW2_SCALES applies to fp8 pools only");
+  if (num_tokens == 0 || problem->batch == 0) return PDATTN_OK;
+  if (!k_new || !v_new || !token_seq || !token_pos || !block_table || !k_pages || !v_pages)
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16))
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "k_new, v_new, k_pages and v_pages must be 16-byte aligned");
+  if (!aligned(token_seq, 4) || !aligned(token_pos, 4) || !aligned(block_table, 4))
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "token_seq, token_pos and block_table must be 4-byte aligned");
+  if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "fp8 pools need 4-byte aligned k_scale and v_scale");
+  if (!fp8 && (k_scale || v_scale))
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "k_scale / v_scale must be NULL for bf16 pools");
+
+  pdattn::AppendParams p;
+  std::memset(&p, 0, sizeof p);
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.token_seq = token_seq;
+  p.token_pos = token_pos;
+  p.block_table = block_table;
+  p.k_pages = k_pages;
+  p.v_pages = v_pages;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.num_tokens = num_tokens;
+  p.batch = problem->batch;
+  p.num_kv_heads = problem->num_kv_heads;
+  p.page_log2 = ilog2(problem->page_size);
+  p.max_pages_per_seq = problem->max_pages_per_seq;
+  p.num_pages = problem->num_pages;
+  p.pow2_scales = (flags & PDATTN_APPEND_POW2_SCALES) ? 1 : 0;
+  // one wave per (token, kv head) row, four rows per workgroup; a larger
+  // append is covered by a grid-stride loop
+  const int64_t wgs = ceil_div((int64_t)num_tokens * problem->num_kv_heads, pdattn::kWaves);
+  const uint32_t grid = (uint32_t)(wgs < ((int64_t)1 << 20) ? wgs : ((int64_t)1 << 20));
+  hipError_t e = pdattn::launch_kv_append(p, problem->head_dim, fp8, grid, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "append kernel launch: %s", hipGetErrorString(e));
+  return PDATTN_OK;
+}
+
 PDATTN_API uint64_t pdattn_stream_read_sink_words(int32_t num_cus) {
   return (uint64_t)(num_cus > 0 ? num_cus : 0) * 2 * 256;
 }

@@ -6,7 +6,8 @@ score, softmax, merge or dequantisation. The fp8 workload's quantiser lives
 here because its codes and scales are inputs that both the GPU path and the
 oracle consume unchanged.
 
-Recipe (every workload):
+Recipe (every decode workload; the append inputs have their own recipe in
+``make_append_inputs``):
   * ``g = torch.Generator().manual_seed(seed)`` on the CPU.
   * context lengths: fixed, or ``torch.randint(lo, hi + 1)`` (inclusive).
   * pages needed by sequence b: ceil(L_b / P); pool = 2 x total needed pages
@@ -26,7 +27,7 @@ import math
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "kv_bytes"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "kv_bytes", "make_append_inputs", "append_bytes"]
 
 E4M3_MAX = 448.0
 
@@ -162,3 +163,108 @@ def kv_bytes(w, context_lens) -> int:
     esize = 2 if w.kv_dtype == "bf16" else 1
     per = 2 * w.head_dim * esize + (8 if w.kv_dtype == "fp8_e4m3" else 0)
     return tokens * w.num_kv_heads * per
+
+
+def make_append_inputs(*, batch, num_kv_heads, head_dim, page_size, new_tokens, context, kv_dtype="bf16",
+                       num_q_heads=None, invalid=True, special_rows=True, spread=24, seed=2000):
+    """Draw the inputs of one KV append on the CPU.
+
+    Recipe: ``g = torch.Generator().manual_seed(seed)``; existing context
+    lengths L_b ~ U[context] (inclusive); new tokens n_b = new_tokens (an int)
+    or ~ U[new_tokens] (inclusive); sequence b needs ceil((L_b + n_b) / P)
+    pages, the pool holds 2x the total, block_table rows take consecutive
+    entries of a random permutation of the pool and keep one extra column of
+    -1. Every pool row holds randn data rounded to bf16 (fp8 pools: quantised
+    per row like the fp8 decode workload), so a stray write shows. The new
+    rows are randn * 2^u, u ~ U{-spread..spread} per (token, kv head, K or
+    V) (spread 0: plain N(0,1) rows, as in the decode workloads);
+    with ``special_rows`` about 1/16 of them are all zero, 1/16 a single
+    spike, 1/16 scaled by 2^-128 (bf16 subnormals) and 1/16 hold values that
+    sit exactly on e4m3 rounding ties. New token i of sequence b sits at
+    position L_b + i. With ``invalid`` five tokens that do not resolve are
+    added (sequence -1 and B, position -1 and max_pages * P, a position on a
+    -1 block-table entry); the token order is a random permutation.
+
+    Returns a dict: k_new, v_new bf16 [N,Hkv,d]; token_seq, token_pos int32
+    [N]; block_table int32 [B,max_pages]; k_pages, v_pages (bf16 or
+    float8_e4m3fn) [num_pages,P,Hkv,d]; k_scale, v_scale fp32 or None;
+    context_lens (before) and new_lens (after) int32 [B]; q bf16 [B,Hq,d]
+    when num_q_heads is given.
+    """
+    g = torch.Generator().manual_seed(int(seed))
+    B, Hkv, D, P = batch, num_kv_heads, head_dim, page_size
+    lo, hi = context
+    lens = torch.randint(int(lo), int(hi) + 1, (B,), generator=g, dtype=torch.int64)
+    if isinstance(new_tokens, int):
+        n_new = torch.full((B,), new_tokens, dtype=torch.int64)
+    else:
+        n_new = torch.randint(int(new_tokens[0]), int(new_tokens[1]) + 1, (B,), generator=g, dtype=torch.int64)
+    total = lens + n_new
+    needed = [(int(t) + P - 1) // P for t in total.tolist()]
+    pool = max(2 * sum(needed), 1)
+    max_pages = max(needed) + 1
+    perm = torch.randperm(pool, generator=g).to(torch.int32)
+    block_table = torch.full((B, max_pages), -1, dtype=torch.int32)
+    off = 0
+    for b, n in enumerate(needed):
+        block_table[b, :n] = perm[off:off + n]
+        off += n
+    rows = torch.randn((pool, P, Hkv, D), generator=g, dtype=torch.float32)
+    vrows = torch.randn((pool, P, Hkv, D), generator=g, dtype=torch.float32)
+    k_scale = v_scale = None
+    if kv_dtype == "bf16":
+        k_pages, v_pages = rows.to(torch.bfloat16), vrows.to(torch.bfloat16)
+    elif kv_dtype == "fp8_e4m3":
+        k_pages, k_scale = quantize_rows_e4m3(rows)
+        v_pages, v_scale = quantize_rows_e4m3(vrows)
+    else:
+        raise ValueError(f"unknown kv dtype {kv_dtype!r}")
+
+    N = int(n_new.sum())
+    seq = torch.repeat_interleave(torch.arange(B, dtype=torch.int64), n_new)
+    starts = torch.cumsum(n_new, 0) - n_new
+    pos = lens[seq] + (torch.arange(N, dtype=torch.int64) - starts[seq])
+
+    def new_rows():
+        x = torch.randn((N, Hkv, D), generator=g, dtype=torch.float32)
+        x = x * torch.exp2(torch.randint(-spread, spread + 1, (N, Hkv, 1), generator=g).to(torch.float32))
+        if special_rows and N > 0:
+            kind = torch.randint(0, 16, (N, Hkv), generator=g)
+            x[kind == 0] = 0.0
+            spike = torch.zeros((N, Hkv, D))
+            spike[..., 0] = 3.0
+            x = torch.where((kind == 1)[..., None], spike, x)
+            x = torch.where((kind == 2)[..., None], x * 2.0 ** -128, x)
+            # multiples of 2^-4 in a row whose absmax is 14 = 448 * 2^-5: the
+            # scale is 2^-5 (plain or power of two), x / scale an even
+            # integer, many of them halfway between two e4m3 values
+            ties = torch.randint(-224, 225, (N, Hkv, D), generator=g).to(torch.float32) * 2.0 ** -4
+            ties[..., 0] = 14.0
+            x = torch.where((kind == 3)[..., None], ties, x)
+        return x.to(torch.bfloat16)
+
+    k_new, v_new = new_rows(), new_rows()
+    if invalid:
+        bad_seq = torch.tensor([-1, B, 0, 0, B - 1], dtype=torch.int64)
+        bad_pos = torch.tensor([0, 0, -1, max_pages * P, (max_pages - 1) * P], dtype=torch.int64)
+        seq = torch.cat([seq, bad_seq])
+        pos = torch.cat([pos, bad_pos])
+        extra = torch.randn((5, Hkv, D), generator=g).to(torch.bfloat16)
+        k_new = torch.cat([k_new, extra])
+        v_new = torch.cat([v_new, extra])
+    order = torch.randperm(seq.numel(), generator=g)
+    out = dict(k_new=k_new[order].contiguous(), v_new=v_new[order].contiguous(),
+               token_seq=seq[order].to(torch.int32), token_pos=pos[order].to(torch.int32),
+               block_table=block_table, k_pages=k_pages, v_pages=v_pages, k_scale=k_scale, v_scale=v_scale,
+               context_lens=lens.to(torch.int32), new_lens=total.to(torch.int32))
+    if num_q_heads is not None:
+        out["q"] = torch.randn((B, num_q_heads, D), generator=g).to(torch.bfloat16)
+    return out
+
+
+def append_bytes(num_rows, head_dim, kv_dtype) -> int:
+    """Algorithmic bytes of an append of num_rows (token, kv head) rows: the
+    bf16 K and V rows read once, the K and V rows written once in the pool's
+    element size, plus two fp32 scales per row for an fp8 pool."""
+    write = 2 * head_dim * (2 if kv_dtype == "bf16" else 1) + (8 if kv_dtype == "fp8_e4m3" else 0)
+    return num_rows * (4 * head_dim + write)

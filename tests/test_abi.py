@@ -220,3 +220,33 @@ def test_balanced_reduce_is_a_validated_no_op():
     # valid-looking arguments: nothing is launched for a default-mode plan
     assert pk._lib.pdattn_reduce(ctypes.byref(pl), P(16), pl.workspace_bytes, P(16), None, None) == OK
     assert pk._lib.pdattn_reduce(ctypes.byref(pl), P(16), pl.workspace_bytes - 1, P(16), None, None) == WORKSPACE
+
+
+def _append_raw(prob=None, n=4, kn=0x1000, vn=0x2000, seq=0x3000, pos=0x4000, bt=0x5000, kp=0x6000, vp=0x7000,
+                ks=None, vs=None, flags=0, **kw):
+    p = problem(**kw) if prob is None else prob
+    pr = pk.Problem(*[p[f] for f, _ in pk.Problem._fields_])
+    P = lambda a: ctypes.c_void_p(a) if a else None
+    return pk._lib.pdattn_kv_append(ctypes.byref(pr), n, P(kn), P(vn), P(seq), P(pos), P(bt), P(kp), P(vp),
+                                    P(ks), P(vs), flags, None)
+
+
+def test_kv_append_validation_rejects_before_launch():
+    assert _append_raw(n=-1) == INVALID
+    assert _append_raw(kn=0) == INVALID
+    assert _append_raw(bt=0) == INVALID
+    assert _append_raw(kn=0x1008) == INVALID                 # not 16-byte aligned
+    assert _append_raw(vp=0x7004) == INVALID
+    assert _append_raw(pos=0x4002) == INVALID
+    assert _append_raw(ks=0x8000, vs=0x9000) == INVALID      # scales on a bf16 pool
+    assert _append_raw(flags=pk.APPEND_POW2_SCALES) == INVALID   # pow2 scales on a bf16 pool
+    assert _append_raw(flags=4) == INVALID
+    assert _append_raw(kv_dtype=1) == INVALID                # fp8 pool without scales
+    assert _append_raw(kv_dtype=1, ks=0x8000, vs=0x9002) == INVALID
+    assert _append_raw(head_dim=96) == UNSUPPORTED
+    assert _append_raw(page_size=24) == UNSUPPORTED
+    assert _append_raw(num_kv_heads=3) == INVALID            # 32 q heads not a multiple of 3
+    assert "aligned" in (_append_raw(kn=0x1008), pk._lib.pdattn_last_error().decode())[1]
+    # nothing to do: no pointer is read
+    assert _append_raw(n=0, kn=0, vn=0, seq=0, pos=0, bt=0, kp=0, vp=0) == OK
+    assert _append_raw(batch=0, kn=0, vn=0, seq=0, pos=0, bt=0, kp=0, vp=0) == OK

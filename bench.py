@@ -74,6 +74,53 @@ def read_traffic(mode, workload):
         return None
 
 
+def time_append(pk, w, flush, dev, reps=20):
+    """pdattn_kv_append timings (secondary figures, not the step): the
+    decode step's append (one new token per sequence of the workload) and a
+    prefill-sized append (16 sequences x 512 new tokens, in position
+    order), into a bf16 pool
+    and into an fp8 pool with power-of-two scales. Caches are flushed before
+    every timed call; bytes are the algorithmic append bytes (bf16 rows read
+    once, pool rows and scales written once)."""
+    import torch
+    import synth
+    res = {}
+    shapes = {"decode_step": dict(batch=w.batch, new_tokens=1, context=(512, 4096)),
+              "prefill_16x512": dict(batch=16, new_tokens=512, context=(0, 0))}
+    for sname, sh in shapes.items():
+        for kv in ("bf16", "fp8_e4m3"):
+            inp = synth.make_append_inputs(num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, page_size=w.page_size,
+                                           kv_dtype=kv, invalid=False, special_rows=False, spread=0, shuffle=False,
+                                           seed=4000,
+                                           **sh)
+            d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+            pow2 = kv == "fp8_e4m3"
+
+            def call():
+                pk.kv_append(d["k_new"], d["v_new"], d["token_seq"], d["token_pos"], d["block_table"],
+                             d["k_pages"], d["v_pages"], d["k_scale"], d["v_scale"], pow2_scales=pow2)
+            for _ in range(3):
+                call()
+            ts = []
+            for i in range(reps):
+                flush.fill_(i & 0xFF)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                call()
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b) * 1e3)
+            rows = int(inp["token_seq"].numel()) * w.num_kv_heads
+            nbytes = synth.append_bytes(rows, w.head_dim, kv)
+            us = statistics.fmean(ts)
+            res[f"{sname}_{'bf16' if kv == 'bf16' else 'fp8_pow2'}"] = {
+                "tokens": int(inp["token_seq"].numel()), "rows": rows, "bytes": nbytes,
+                "us_per_call": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            del d, inp
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -85,6 +132,7 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="time with warm caches")
     ap.add_argument("--balanced", action="store_true",
                     help="time the on-device balanced kernel instead of the static split + reduce")
+    ap.add_argument("--no-append", action="store_true", help="skip the KV-append timings")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run 3 device copies of 256 MiB (a plain copy kernel of known "
                          "size, for scaling the HBM byte counters)")
@@ -194,6 +242,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    append = None if args.no_append else time_append(pk, w, flush, dev)
+
     cpu = None
     if args.cpu_seconds > 0:
         import oracle
@@ -253,6 +303,7 @@ def main():
         "outputs_finite": ok,
         "device": torch.cuda.get_device_name(0),
         "kernel_source_sha256_16": source_digest(mode),
+        "kv_append": append,
     }
     print(json.dumps(rec), flush=True)
 

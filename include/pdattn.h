@@ -230,6 +230,17 @@ PDATTN_API pdattn_status pdattn_kv_append(const pdattn_problem* problem, int32_t
                                           const int32_t* block_table, void* k_pages, void* v_pages, float* k_scale,
                                           float* v_scale, int32_t flags, void* stream);
 
+/*
+ * Diagnostic, not part of the path: enqueue a comparison of the hardware
+ * float -> e4m3fn conversion the fp8 append uses with the format's
+ * definition (nearest code, ties to even, sign kept, subnormals m * 2^-9),
+ * over every fp32 value y with |y| <= 448, both signs (about 2.3e9 values;
+ * milliseconds on the device). `mismatches` (device, one uint64, zeroed by
+ * the caller) receives the number of values where the two differ; 0 means
+ * the conversion is exact on everything the append can feed it.
+ */
+PDATTN_API pdattn_status pdattn_fp8_conversion_check(uint64_t* mismatches, void* stream);
+
 /* Static description of a status code. */
 PDATTN_API const char* pdattn_status_string(pdattn_status status);
 

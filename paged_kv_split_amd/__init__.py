@@ -14,7 +14,7 @@ import torch
 
 __all__ = ["Problem", "Plan", "PdattnError", "plan", "decode", "reduce", "workspace", "workspace_init",
            "paged_decode", "KV_BF16", "KV_FP8_E4M3", "PLAN_BALANCED", "library_path", "stream_read",
-           "stream_read_sink", "kv_append", "APPEND_POW2_SCALES"]
+           "stream_read_sink", "kv_append", "APPEND_POW2_SCALES", "fp8_conversion_check"]
 
 KV_BF16 = 0
 KV_FP8_E4M3 = 1
@@ -82,6 +82,8 @@ _lib.pdattn_stream_read_sink_words.argtypes = [ctypes.c_int32]
 _lib.pdattn_kv_append.restype = ctypes.c_int
 _lib.pdattn_kv_append.argtypes = [ctypes.POINTER(Problem), ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                   ctypes.c_int32, _P]
+_lib.pdattn_fp8_conversion_check.restype = ctypes.c_int
+_lib.pdattn_fp8_conversion_check.argtypes = [_P, _P]
 _lib.pdattn_problem_size.restype = ctypes.c_uint64
 _lib.pdattn_plan_size.restype = ctypes.c_uint64
 
@@ -186,6 +188,14 @@ def kv_append(k_new, v_new, token_seq, token_pos, block_table, k_pages, v_pages,
     _check(_lib.pdattn_kv_append(ctypes.byref(prob), int(N), _ptr(k_new), _ptr(v_new), _ptr(token_seq),
                                  _ptr(token_pos), _ptr(block_table), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
                                  _ptr(v_scale), flags, _stream(stream)), "pdattn_kv_append")
+
+
+def fp8_conversion_check(device, stream=None) -> int:
+    """``pdattn_fp8_conversion_check``: mismatches of the hardware e4m3fn
+    conversion against the format definition over every |y| <= 448."""
+    out = torch.zeros(1, dtype=torch.int64, device=device)
+    _check(_lib.pdattn_fp8_conversion_check(_ptr(out), _stream(stream)), "pdattn_fp8_conversion_check")
+    return int(out.item())
 
 
 def paged_decode(q, k_pages, v_pages, block_table, context_lens, *, context_lens_host=None,

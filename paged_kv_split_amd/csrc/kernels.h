@@ -152,6 +152,7 @@ hipError_t launch_dynamic(const DynParams& p, int head_dim, int group, bool fp8,
 hipError_t launch_workspace_init(uint32_t* ctl, uint64_t words, uint32_t* header, uint32_t units_max,
                                  uint32_t pairs, hipStream_t stream);
 hipError_t launch_kv_append(const AppendParams& p, int head_dim, bool fp8, uint32_t grid, hipStream_t stream);
+hipError_t launch_fp8_conversion_check(unsigned long long* mismatches, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, uint32_t grid, hipStream_t stream);
 
 }  // namespace pdattn

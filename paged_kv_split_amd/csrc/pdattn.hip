@@ -384,7 +384,11 @@ PDATTN_API pdattn_status pdattn_kv_append(const pdattn_problem* problem, int32_t
   const bool fp8 = problem->kv_dtype == PDATTN_KV_FP8_E4M3;
   if (!fp8 && (flags & PDATTN_APPEND_POW2_SCALES))
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "PDATTN_APPEND_POW2_SCALES applies to fp8 pools only");
-  if (num_tokens == 0 || problem->batch == 0) return PDATTN_OK;
+  if ((int64_t)problem->num_kv_heads * problem->head_dim > (1 << 19))
+    return fail(PDATTN_ERR_UNSUPPORTED, "num_kv_heads * head_dim above 2^19");
+  // nothing can resolve without a block-table column and a page
+  if (num_tokens == 0 || problem->batch == 0 || problem->max_pages_per_seq == 0 || problem->num_pages == 0)
+    return PDATTN_OK;
   if (!k_new || !v_new || !token_seq || !token_pos || !block_table || !k_pages || !v_pages)
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16))
@@ -414,12 +418,22 @@ PDATTN_API pdattn_status pdattn_kv_append(const pdattn_problem* problem, int32_t
   p.max_pages_per_seq = problem->max_pages_per_seq;
   p.num_pages = problem->num_pages;
   p.pow2_scales = (flags & PDATTN_APPEND_POW2_SCALES) ? 1 : 0;
-  // one wave per (token, kv head) row, four rows per workgroup; a larger
-  // append is covered by a grid-stride loop
-  const int64_t wgs = ceil_div((int64_t)num_tokens * problem->num_kv_heads, pdattn::kWaves);
+  // one wave per token, four tokens per workgroup; a larger append is
+  // covered by a grid-stride loop
+  const int64_t wgs = ceil_div((int64_t)num_tokens, pdattn::kWaves);
   const uint32_t grid = (uint32_t)(wgs < ((int64_t)1 << 20) ? wgs : ((int64_t)1 << 20));
   hipError_t e = pdattn::launch_kv_append(p, problem->head_dim, fp8, grid, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "append kernel launch: %s", hipGetErrorString(e));
+  return PDATTN_OK;
+}
+
+PDATTN_API pdattn_status pdattn_fp8_conversion_check(uint64_t* mismatches, void* stream) {
+  g_last_error[0] = '\0';
+  if (!mismatches || !aligned(mismatches, 8))
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "mismatches must be an 8-byte aligned device pointer");
+  hipError_t e = pdattn::launch_fp8_conversion_check(reinterpret_cast<unsigned long long*>(mismatches),
+                                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "conversion check launch: %s", hipGetErrorString(e));
   return PDATTN_OK;
 }
 

@@ -166,7 +166,7 @@ def kv_bytes(w, context_lens) -> int:
 
 
 def make_append_inputs(*, batch, num_kv_heads, head_dim, page_size, new_tokens, context, kv_dtype="bf16",
-                       num_q_heads=None, invalid=True, special_rows=True, spread=24, seed=2000):
+                       num_q_heads=None, invalid=True, special_rows=True, spread=24, shuffle=True, seed=2000):
     """Draw the inputs of one KV append on the CPU.
 
     Recipe: ``g = torch.Generator().manual_seed(seed)``; existing context
@@ -183,7 +183,9 @@ def make_append_inputs(*, batch, num_kv_heads, head_dim, page_size, new_tokens, 
     sit exactly on e4m3 rounding ties. New token i of sequence b sits at
     position L_b + i. With ``invalid`` five tokens that do not resolve are
     added (sequence -1 and B, position -1 and max_pages * P, a position on a
-    -1 block-table entry); the token order is a random permutation.
+    -1 block-table entry); with ``shuffle`` the token order is a random
+    permutation, else sequence by sequence in position order (a prefill
+    chunk as a serving engine hands it over).
 
     Returns a dict: k_new, v_new bf16 [N,Hkv,d]; token_seq, token_pos int32
     [N]; block_table int32 [B,max_pages]; k_pages, v_pages (bf16 or
@@ -252,7 +254,7 @@ def make_append_inputs(*, batch, num_kv_heads, head_dim, page_size, new_tokens, 
         extra = torch.randn((5, Hkv, D), generator=g).to(torch.bfloat16)
         k_new = torch.cat([k_new, extra])
         v_new = torch.cat([v_new, extra])
-    order = torch.randperm(seq.numel(), generator=g)
+    order = torch.randperm(seq.numel(), generator=g) if shuffle else torch.arange(seq.numel())
     out = dict(k_new=k_new[order].contiguous(), v_new=v_new[order].contiguous(),
                token_seq=seq[order].to(torch.int32), token_pos=pos[order].to(torch.int32),
                block_table=block_table, k_pages=k_pages, v_pages=v_pages, k_scale=k_scale, v_scale=v_scale,

@@ -231,6 +231,11 @@ def _append_raw(prob=None, n=4, kn=0x1000, vn=0x2000, seq=0x3000, pos=0x4000, bt
                                     P(ks), P(vs), flags, None)
 
 
+def test_fp8_conversion_check_validation():
+    assert pk._lib.pdattn_fp8_conversion_check(None, None) == INVALID
+    assert pk._lib.pdattn_fp8_conversion_check(ctypes.c_void_p(0x1004), None) == INVALID
+
+
 def test_kv_append_validation_rejects_before_launch():
     assert _append_raw(n=-1) == INVALID
     assert _append_raw(kn=0) == INVALID

@@ -68,15 +68,26 @@ def assert_pools_equal(d, ref, tag):
             assert bad.size == 0, f"{tag} {name}: {len(bad)} scales differ, first at {bad[:4].tolist()}"
 
 
+def test_hardware_fp8_conversion_matches_the_format_definition():
+    """The append's float -> e4m3fn conversion instruction against the
+    format's definition over every fp32 value with |y| <= 448 (both signs)."""
+    assert _pk().fp8_conversion_check(DEV) == 0
+
+
 CASES = [
     # (head_dim, page_size, Hkv, batch, new_tokens, context)
     (128, 16, 8, 6, (1, 70), (0, 100)),
     (64, 8, 2, 5, (1, 40), (0, 30)),
     (128, 128, 4, 3, (100, 300), (0, 200)),
+    # a token's rows span several 1 KB steps, a partial last step, less than one step
+    (128, 16, 16, 4, (1, 50), (0, 60)),
+    (128, 32, 5, 4, (1, 50), (0, 60)),
+    (64, 16, 1, 4, (1, 50), (0, 60)),
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=["d128_p16", "d64_p8", "d128_p128"])
+@pytest.mark.parametrize("case", CASES, ids=["d128_p16", "d64_p8", "d128_p128", "d128_hkv16", "d128_hkv5",
+                                             "d64_hkv1"])
 @pytest.mark.parametrize("mode", ["bf16", "fp8", "fp8_pow2"])
 def test_append_matches_oracle_bit_exact(case, mode):
     D, P, Hkv, B, new, ctx = case
@@ -109,8 +120,8 @@ def test_append_of_nothing_and_of_unresolved_tokens_changes_nothing(mode):
 
 def test_fp8_extremes_bit_exact():
     """Rows at the edges of the fp32 and e4m3 ranges: bf16's largest finite
-    magnitude, bf16 subnormals, a lone nonzero, and values that round onto
-    ties at every e4m3 exponent."""
+    magnitude, bf16 subnormals, a lone nonzero, values that round onto ties
+    at every e4m3 exponent, and rows around absmax 2^-82."""
     pk = _pk()
     Hkv, D, P = 1, 128, 16
     vals = []
@@ -129,6 +140,14 @@ def test_fp8_extremes_bit_exact():
     row[1:1 + min(len(mids), D - 1)] = mids[:D - 1]
     vals.append(row)
     vals.append(-row)
+    # rows on both sides of absmax 2^-82, where plain scales switch from the
+    # refined reciprocal to a division per element
+    g = torch.Generator().manual_seed(2)
+    for top in (2.0 ** -82, 1.5 * 2.0 ** -83, 2.0 ** -81):
+        r = torch.randn(D, generator=g) * 2.0 ** -84
+        r = r.to(torch.bfloat16).float().clamp(-top, top)
+        r[5] = top
+        vals.append(r)
     rows = torch.stack(vals)[:, None, :].to(torch.bfloat16)           # [N, 1, D]
     N = rows.shape[0]
     for pow2 in (False, True):

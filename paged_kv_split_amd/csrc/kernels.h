@@ -119,26 +119,6 @@ struct MergeParams {
   int32_t num_workers;
 };
 
-// The KV append (one wave per (token, kv head) row).
-struct AppendParams {
-  const uint16_t* k_new;      // bf16 bits [num_tokens][Hkv][D]
-  const uint16_t* v_new;
-  const int32_t* token_seq;   // [num_tokens]
-  const int32_t* token_pos;   // [num_tokens]
-  const int32_t* block_table; // [B][max_pages_per_seq]
-  void* k_pages;              // pool [num_pages][P][Hkv][D * esize]
-  void* v_pages;
-  float* k_scale;             // fp8 pools: [num_pages][P][Hkv]
-  float* v_scale;
-  int32_t num_tokens;
-  int32_t batch;
-  int32_t num_kv_heads;
-  int32_t page_log2;
-  int32_t max_pages_per_seq;
-  int32_t num_pages;
-  int32_t pow2_scales;        // fp8: power-of-two scales instead of absmax / 448
-};
-
 // Resident workgroups per compute unit of one decode instantiation, from the
 // runtime's occupancy query; 0 when it cannot be asked.
 int decode_wgs_per_cu(int head_dim, int group, bool fp8);
@@ -151,8 +131,6 @@ int dynamic_wgs_per_cu(int head_dim, int group, bool fp8);
 hipError_t launch_dynamic(const DynParams& p, int head_dim, int group, bool fp8, uint32_t grid, hipStream_t stream);
 hipError_t launch_workspace_init(uint32_t* ctl, uint64_t words, uint32_t* header, uint32_t units_max,
                                  uint32_t pairs, hipStream_t stream);
-hipError_t launch_kv_append(const AppendParams& p, int head_dim, bool fp8, uint32_t grid, hipStream_t stream);
-hipError_t launch_fp8_conversion_check(unsigned long long* mismatches, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, uint64_t bytes, uint32_t* sink, uint32_t grid, hipStream_t stream);
 
 }  // namespace pdattn

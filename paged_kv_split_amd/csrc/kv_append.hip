@@ -13,7 +13,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "kernels.h"
+#include "append.h"
 
 namespace pdattn {
 namespace {

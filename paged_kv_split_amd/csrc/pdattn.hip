@@ -12,6 +12,7 @@
 #include <cstring>
 
 #include "kernels.h"
+#include "append.h"
 
 namespace {
 

@@ -121,6 +121,38 @@ def time_append(pk, w, flush, dev, reps=20):
     return res
 
 
+def time_merge(pk, flush, dev, reps=20):
+    """pdattn_merge timings (secondary figures): a two-piece cascade (shared
+    prefix + suffix) over the Llama-3-8B decode rows (32 x 32 rows, d128)
+    and an eight-piece merge over the long-context rows (4 x 64 rows, d128,
+    one piece per context shard). Caches flushed before every call; bytes =
+    the pieces' outputs and lse read once, the merged ones written once."""
+    import torch
+    res = {}
+    for name, S, R, D in (("cascade_2x1024_d128", 2, 1024, 128), ("shards_8x256_d128", 8, 256, 128)):
+        g = torch.Generator().manual_seed(4100 + S)
+        po = torch.randn((S, R, D), generator=g).to(dev)
+        pl = (torch.randn((S, R), generator=g) * 4).to(dev)
+        out = torch.empty((R, D), device=dev)
+        lse = torch.empty((R,), device=dev)
+        for _ in range(3):
+            pk.merge(po, pl, out, lse)
+        ts = []
+        for i in range(reps):
+            flush.fill_(i & 0xFF)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            pk.merge(po, pl, out, lse)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        nbytes = (S + 1) * R * (D + 1) * 4
+        us = statistics.fmean(ts)
+        res[name] = {"pieces": S, "rows": R, "bytes": nbytes, "us_per_call": round(us, 2),
+                     "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,6 +165,7 @@ def main():
     ap.add_argument("--balanced", action="store_true",
                     help="time the on-device balanced kernel instead of the static split + reduce")
     ap.add_argument("--no-append", action="store_true", help="skip the KV-append timings")
+    ap.add_argument("--no-merge", action="store_true", help="skip the partial-state merge timings")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run 3 device copies of 256 MiB (a plain copy kernel of known "
                          "size, for scaling the HBM byte counters)")
@@ -243,6 +276,7 @@ def main():
         del src, dst
 
     append = None if args.no_append else time_append(pk, w, flush, dev)
+    merge = None if args.no_merge else time_merge(pk, flush, dev)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -304,6 +338,7 @@ def main():
         "device": torch.cuda.get_device_name(0),
         "kernel_source_sha256_16": source_digest(mode),
         "kv_append": append,
+        "merge": merge,
     }
     print(json.dumps(rec), flush=True)
 

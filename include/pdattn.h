@@ -231,6 +231,36 @@ PDATTN_API pdattn_status pdattn_kv_append(const pdattn_problem* problem, int32_t
                                           float* v_scale, int32_t flags, void* stream);
 
 /*
+ * Enqueue the merge of exported partial attention states on `stream`: for
+ * each row r (a (sequence, query head) pair) and pieces s over disjoint key
+ * sets, each a normalised output o_s and a natural-log lse_s as
+ * pdattn_decode exports them (FlashQuant wiki "CUDA Kernels",
+ * split_k_reduce.cu Algorithm and Numerical Stability):
+ *   M = max_s lse_s,  w_s = exp(lse_s - M),
+ *   out = sum_s w_s o_s / sum_s w_s,  lse = M + ln sum_s w_s
+ * i.e. attention over the union of the pieces' keys (a shared prefix and a
+ * per-request suffix decoded separately; or the pages of one sequence split
+ * across devices, each decoding its share).
+ *   num_partials  S >= 1
+ *   num_rows      R, e.g. batch * num_q_heads (0: nothing to do)
+ *   head_dim      d in {64, 128, 256}
+ *   partial_out   fp32 [S][R][d], device, 16-byte aligned
+ *   partial_lse   fp32 [S][R], device (natural log)
+ *   out           fp32 [R][d], device, 16-byte aligned; may be the same
+ *                 buffer as piece 0 of partial_out (no other overlap)
+ *   lse           fp32 [R], device, optional (NULL to skip); may be piece 0
+ *                 of partial_lse
+ * A piece with lse = -inf is empty and weighs nothing; a row whose pieces
+ * are all empty gets out = 0, lse = -inf; a NaN or +inf lse in any piece
+ * makes the row's out and lse NaN. fp32 arithmetic, one pass over the
+ * pieces. Allocates nothing, never synchronises, graph-capturable;
+ * validated before launch.
+ */
+PDATTN_API pdattn_status pdattn_merge(int32_t num_partials, int64_t num_rows, int32_t head_dim,
+                                      const float* partial_out, const float* partial_lse, float* out, float* lse,
+                                      void* stream);
+
+/*
  * Diagnostic, not part of the path: enqueue a comparison of the hardware
  * float -> e4m3fn conversion the fp8 append uses with the format's
  * definition (nearest code, ties to even, sign kept, subnormals m * 2^-9),

@@ -14,7 +14,7 @@ import torch
 
 __all__ = ["Problem", "Plan", "PdattnError", "plan", "decode", "reduce", "workspace", "workspace_init",
            "paged_decode", "KV_BF16", "KV_FP8_E4M3", "PLAN_BALANCED", "library_path", "stream_read",
-           "stream_read_sink", "kv_append", "APPEND_POW2_SCALES", "fp8_conversion_check"]
+           "stream_read_sink", "kv_append", "APPEND_POW2_SCALES", "fp8_conversion_check", "merge"]
 
 KV_BF16 = 0
 KV_FP8_E4M3 = 1
@@ -82,6 +82,8 @@ _lib.pdattn_stream_read_sink_words.argtypes = [ctypes.c_int32]
 _lib.pdattn_kv_append.restype = ctypes.c_int
 _lib.pdattn_kv_append.argtypes = [ctypes.POINTER(Problem), ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                   ctypes.c_int32, _P]
+_lib.pdattn_merge.restype = ctypes.c_int
+_lib.pdattn_merge.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P, _P]
 _lib.pdattn_fp8_conversion_check.restype = ctypes.c_int
 _lib.pdattn_fp8_conversion_check.argtypes = [_P, _P]
 _lib.pdattn_problem_size.restype = ctypes.c_uint64
@@ -188,6 +190,20 @@ def kv_append(k_new, v_new, token_seq, token_pos, block_table, k_pages, v_pages,
     _check(_lib.pdattn_kv_append(ctypes.byref(prob), int(N), _ptr(k_new), _ptr(v_new), _ptr(token_seq),
                                  _ptr(token_pos), _ptr(block_table), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
                                  _ptr(v_scale), flags, _stream(stream)), "pdattn_kv_append")
+
+
+def merge(partial_out, partial_lse, out=None, lse=None, stream=None):
+    """``pdattn_merge``: partial_out fp32 [S, ..., d], partial_lse fp32 [S, ...]
+    (the same leading shape); returns (out [..., d], lse [...])."""
+    S, d = partial_out.shape[0], partial_out.shape[-1]
+    rows = partial_lse[0].numel() if S > 0 else 0
+    if out is None:
+        out = torch.empty(partial_out.shape[1:], dtype=torch.float32, device=partial_out.device)
+    if lse is None:
+        lse = torch.empty(partial_lse.shape[1:], dtype=torch.float32, device=partial_lse.device)
+    _check(_lib.pdattn_merge(int(S), int(rows), int(d), _ptr(partial_out), _ptr(partial_lse), _ptr(out), _ptr(lse),
+                             _stream(stream)), "pdattn_merge")
+    return out, lse
 
 
 def fp8_conversion_check(device, stream=None) -> int:

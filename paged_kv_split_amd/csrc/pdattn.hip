@@ -13,6 +13,7 @@
 
 #include "kernels.h"
 #include "append.h"
+#include "merge.h"
 
 namespace {
 
@@ -425,6 +426,31 @@ PDATTN_API pdattn_status pdattn_kv_append(const pdattn_problem* problem, int32_t
   const uint32_t grid = (uint32_t)(wgs < ((int64_t)1 << 20) ? wgs : ((int64_t)1 << 20));
   hipError_t e = pdattn::launch_kv_append(p, problem->head_dim, fp8, grid, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "append kernel launch: %s", hipGetErrorString(e));
+  return PDATTN_OK;
+}
+
+PDATTN_API pdattn_status pdattn_merge(int32_t num_partials, int64_t num_rows, int32_t head_dim,
+                                      const float* partial_out, const float* partial_lse, float* out, float* lse,
+                                      void* stream) {
+  g_last_error[0] = '\0';
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(PDATTN_ERR_UNSUPPORTED, "head_dim %d not in {64, 128, 256}", head_dim);
+  if (num_partials < 1) return fail(PDATTN_ERR_INVALID_ARGUMENT, "num_partials %d < 1", num_partials);
+  if (num_rows < 0 || num_rows > ((int64_t)1 << 31))
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "num_rows %lld outside [0, 2^31]", (long long)num_rows);
+  if (num_rows == 0) return PDATTN_OK;
+  if (!partial_out || !partial_lse || !out) return fail(PDATTN_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if (!aligned(partial_out, 16) || !aligned(out, 16) || !aligned(partial_lse, 4) || (lse && !aligned(lse, 4)))
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "partial_out and out must be 16-byte aligned, the lse arrays 4-byte");
+  pdattn::MergeStatesParams p;
+  p.partial_out = partial_out;
+  p.partial_lse = partial_lse;
+  p.out = out;
+  p.lse = lse;
+  p.num_rows = num_rows;
+  p.num_partials = num_partials;
+  hipError_t e = pdattn::launch_merge_states(p, head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "merge kernel launch: %s", hipGetErrorString(e));
   return PDATTN_OK;
 }
 

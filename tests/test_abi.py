@@ -231,6 +231,20 @@ def _append_raw(prob=None, n=4, kn=0x1000, vn=0x2000, seq=0x3000, pos=0x4000, bt
                                     P(ks), P(vs), flags, None)
 
 
+def test_merge_validation_rejects_before_launch():
+    P = ctypes.c_void_p
+    m = pk._lib.pdattn_merge
+    assert m(2, 10, 96, P(0x1000), P(0x2000), P(0x3000), None, None) == UNSUPPORTED
+    assert m(0, 10, 128, P(0x1000), P(0x2000), P(0x3000), None, None) == INVALID
+    assert m(2, -1, 128, P(0x1000), P(0x2000), P(0x3000), None, None) == INVALID
+    assert m(2, 10, 128, None, P(0x2000), P(0x3000), None, None) == INVALID
+    assert m(2, 10, 128, P(0x1000), P(0x2000), None, None, None) == INVALID
+    assert m(2, 10, 128, P(0x1008), P(0x2000), P(0x3000), None, None) == INVALID
+    assert m(2, 10, 128, P(0x1000), P(0x2002), P(0x3000), None, None) == INVALID
+    assert m(2, 10, 128, P(0x1000), P(0x2000), P(0x3000), P(0x4001), None) == INVALID
+    assert m(2, 0, 128, None, None, None, None, None) == OK        # nothing to do
+
+
 def test_fp8_conversion_check_validation():
     assert pk._lib.pdattn_fp8_conversion_check(None, None) == INVALID
     assert pk._lib.pdattn_fp8_conversion_check(ctypes.c_void_p(0x1004), None) == INVALID

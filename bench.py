@@ -7,9 +7,12 @@ A step is one pass of the whole hot path, pdattn_decode + pdattn_reduce, over
 one batch of seeded synthetic input already resident in HBM (in the
 balanced mode the merge runs inside pdattn_decode and pdattn_reduce enqueues
 nothing; --balanced times that kernel instead of the default static split +
-reduce kernel). Before every
-timed step (outside its events) a 512 MiB buffer is rewritten, which evicts
-the L2s and the 256 MB Infinity Cache, so the KV pages are read from HBM.
+reduce kernel). The KV pools are laid out head-major, rows
+[page][kv head][slot] (--layout nhd: [page][slot][kv head]); the same step
+in the other layout is timed too and reported under other_layout. Before
+every timed step (outside its events) a 512 MiB buffer is rewritten, which
+evicts the L2s and the 256 MB Infinity Cache, so the KV pages are read from
+HBM.
 
 Prints ONE JSON line. value = KV algorithmic bytes (every K and V element of
 every valid (token, kv head) once, plus the fp8 scales) / mean step time, in
@@ -50,14 +53,14 @@ def source_digest(mode):
     return h.hexdigest()[:16]
 
 
-def traffic_summary_path(mode, workload):
-    return os.path.join(ROOT, "profiles", f"{KERNEL_NAMES[mode]}_{workload}_hbm_traffic.txt")
+def traffic_summary_path(mode, workload, layout):
+    return os.path.join(ROOT, "profiles", f"{KERNEL_NAMES[mode]}_{workload}_{layout}_hbm_traffic.txt")
 
 
-def read_traffic(mode, workload):
+def read_traffic(mode, workload, layout):
     """Bytes per launch from the committed counter summary, if it still
     describes the current kernel sources and this workload."""
-    path = traffic_summary_path(mode, workload)
+    path = traffic_summary_path(mode, workload, layout)
     if not os.path.exists(path):
         return None
     vals = {}
@@ -74,7 +77,47 @@ def read_traffic(mode, workload):
         return None
 
 
-def time_append(pk, w, flush, dev, reps=20):
+def time_other_layout(pk, w, inp, args, flush, dev, reps=30):
+    """The same step with the pools in the other row order (same values, same
+    bytes): mean step time and rate, for comparison."""
+    import torch
+    import synth
+    hnd = args.layout != "hnd"
+    laid = synth.to_hnd(inp) if hnd else inp
+    d = {k: (laid[k].to(dev) if laid[k] is not None else None)
+         for k in ("q", "k_pages", "v_pages", "k_scale", "v_scale", "block_table", "context_lens")}
+    pl = pk.plan(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                 page_size=w.page_size, max_pages_per_seq=inp["block_table"].shape[1],
+                 num_pages=inp["k_pages"].shape[0], kv_dtype=pk.KV_BF16 if w.kv_dtype == "bf16" else pk.KV_FP8_E4M3,
+                 context_lens_host=inp["context_lens"], balanced=args.balanced,
+                 kv_layout=pk.LAYOUT_HND if hnd else pk.LAYOUT_NHD)
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=dev)
+    ws = pk.workspace(pl, dev)
+
+    def step():
+        pk.decode(pl, d["q"], d["k_pages"], d["v_pages"], d["k_scale"], d["v_scale"], d["block_table"],
+                  d["context_lens"], ws, out, lse)
+        pk.reduce(pl, ws, out, lse)
+    for _ in range(5):
+        step()
+    ts = []
+    for i in range(reps):
+        flush.fill_(i & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3)
+    kvb = synth.kv_bytes(w, inp["context_lens"])
+    us = statistics.fmean(ts)
+    del d, ws
+    return {"kv_layout": "HND" if hnd else "NHD", "us_per_call": round(us, 2),
+            "gbs": round(kvb / (us * 1e-6) / 1e9, 1)}
+
+
+def time_append(pk, w, flush, dev, layout, reps=20):
     """pdattn_kv_append timings (secondary figures, not the step): the
     decode step's append (one new token per sequence of the workload) and a
     prefill-sized append (16 sequences x 512 new tokens, in position
@@ -93,12 +136,14 @@ def time_append(pk, w, flush, dev, reps=20):
                                            kv_dtype=kv, invalid=False, special_rows=False, spread=0, shuffle=False,
                                            seed=4000,
                                            **sh)
-            d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+            laid = synth.to_hnd(inp) if layout == pk.LAYOUT_HND else inp
+            d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in laid.items()}
             pow2 = kv == "fp8_e4m3"
 
             def call():
                 pk.kv_append(d["k_new"], d["v_new"], d["token_seq"], d["token_pos"], d["block_table"],
-                             d["k_pages"], d["v_pages"], d["k_scale"], d["v_scale"], pow2_scales=pow2)
+                             d["k_pages"], d["v_pages"], d["k_scale"], d["v_scale"], pow2_scales=pow2,
+                             layout=layout)
             for _ in range(3):
                 call()
             ts = []
@@ -117,7 +162,7 @@ def time_append(pk, w, flush, dev, reps=20):
                 "tokens": int(inp["token_seq"].numel()), "rows": rows, "bytes": nbytes,
                 "us_per_call": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
                 "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-            del d, inp
+            del d, inp, laid
     return res
 
 
@@ -164,6 +209,8 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="time with warm caches")
     ap.add_argument("--balanced", action="store_true",
                     help="time the on-device balanced kernel instead of the static split + reduce")
+    ap.add_argument("--layout", choices=("hnd", "nhd"), default="hnd",
+                    help="KV pool rows [page][kv head][slot] (hnd, the default) or [page][slot][kv head] (nhd)")
     ap.add_argument("--no-append", action="store_true", help="skip the KV-append timings")
     ap.add_argument("--no-merge", action="store_true", help="skip the partial-state merge timings")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -183,7 +230,9 @@ def main():
     w = synth.WORKLOADS[args.workload]
     inp = synth.make_inputs(w)
     dev = torch.device("cuda:0")
-    d = {k: (inp[k].to(dev) if inp[k] is not None else None)
+    layout = pk.LAYOUT_HND if args.layout == "hnd" else pk.LAYOUT_NHD
+    laid = synth.to_hnd(inp) if args.layout == "hnd" else inp
+    d = {k: (laid[k].to(dev) if laid[k] is not None else None)
          for k in ("q", "k_pages", "v_pages", "k_scale", "v_scale", "block_table", "context_lens")}
     kv_bytes = synth.kv_bytes(w, inp["context_lens"])
     mode = "balanced" if args.balanced else "static"
@@ -193,7 +242,7 @@ def main():
                        head_dim=w.head_dim, page_size=w.page_size,
                        max_pages_per_seq=inp["block_table"].shape[1], num_pages=inp["k_pages"].shape[0],
                        kv_dtype=pk.KV_BF16 if w.kv_dtype == "bf16" else pk.KV_FP8_E4M3,
-                       context_lens_host=inp["context_lens"], balanced=args.balanced)
+                       context_lens_host=inp["context_lens"], balanced=args.balanced, kv_layout=layout)
 
     t0 = time.perf_counter()
     pl = make_plan()  # the first plan on a device also queries its occupancy
@@ -275,7 +324,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    append = None if args.no_append else time_append(pk, w, flush, dev)
+    other = time_other_layout(pk, w, inp, args, flush, dev)
+    append = None if args.no_append else time_append(pk, w, flush, dev, layout)
     merge = None if args.no_merge else time_merge(pk, flush, dev)
 
     cpu = None
@@ -298,7 +348,7 @@ def main():
                "sample": f"the full {w.name} step ({w.batch} sequences) repeated {len(times)} times "
                          f"({sum(times):.1f} s); median {per_call * 1e6:.0f} us/call"}
 
-    traffic = read_traffic(mode, w.name)
+    traffic = read_traffic(mode, w.name, args.layout)
     achieved = kv_bytes / (mean_dec * 1e-6) / 1e9
     rec = {
         "metric": METRIC,
@@ -316,8 +366,8 @@ def main():
         "config": {"workload": w.description, "batch": w.batch, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
                    "context_lens": list(w.lens[1:]) if w.lens[0] == "uniform" else list(w.lens[1]),
-                   "seed": w.seed, "workers": pl.num_workers, "workgroups": pl.num_workgroups,
-                   "parallelism": "single GPU"},
+                   "seed": w.seed, "kv_layout": args.layout.upper(), "workers": pl.num_workers,
+                   "workgroups": pl.num_workgroups, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "cpu_baseline": cpu,
@@ -337,6 +387,7 @@ def main():
         "outputs_finite": ok,
         "device": torch.cuda.get_device_name(0),
         "kernel_source_sha256_16": source_digest(mode),
+        "other_layout": other,
         "kv_append": append,
         "merge": merge,
     }

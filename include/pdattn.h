@@ -36,10 +36,11 @@
  *
  * Layouts (all contiguous, row-major):
  *   q            bf16 [B][Hq][d]
- *   k_pages,     bf16 or OCP e4m3fn bytes [num_pages][P][Hkv][d]
- *   v_pages
- *   k_scale,     fp32 [num_pages][P][Hkv], fp8 pools only (NULL for bf16):
- *   v_scale      the stored value of element d is e4m3fn(code) * scale
+ *   k_pages,     bf16 or OCP e4m3fn bytes, [num_pages][P][Hkv][d] (NHD) or
+ *   v_pages      [num_pages][Hkv][P][d] (HND), per problem->kv_layout
+ *   k_scale,     fp32 [num_pages][P][Hkv] (NHD) or [num_pages][Hkv][P] (HND),
+ *   v_scale      fp8 pools only (NULL for bf16): the stored value of
+ *                element d is e4m3fn(code) * scale
  *   block_table  int32 [B][max_pages_per_seq]; only entries < ceil(L_b / P)
  *                are read; a page may appear in several rows
  *   context_lens int32 [B], device copy, read by the kernels
@@ -88,6 +89,19 @@ typedef enum pdattn_kv_dtype {
   PDATTN_KV_FP8_E4M3 = 1 /* OCP e4m3fn codes with one fp32 scale per (token, kv head) */
 } pdattn_kv_dtype;
 
+/* The order of the (slot, kv head) rows inside one page of the K and V
+ * pools (and of the fp8 scales). The paged addressing (FlashQuant wiki "CUDA
+ * Kernels", paged_decode.cu Page Table Addressing) fixes the page and the
+ * slot of a position, not this order; both are served:
+ *   NHD  rows [page][slot][kv head]: a token's kv heads are adjacent
+ *   HND  rows [page][kv head][slot]: one kv head's P rows of a page are one
+ *        contiguous block (for P = 16, d = 128, bf16: 4 KB), which the decode
+ *        streams measurably faster on MI355X. */
+typedef enum pdattn_kv_layout {
+  PDATTN_LAYOUT_NHD = 0,
+  PDATTN_LAYOUT_HND = 1
+} pdattn_kv_layout;
+
 /* The problem shape (AstrAI "CUDA Kernels", Python Wrappers: blhd layout,
  * scale 1/sqrt(head_dim); OASR "Kernel Layer", Fused attention: paged mode
  * takes block_table and per-sequence lengths). */
@@ -101,6 +115,7 @@ typedef struct pdattn_problem {
   int32_t num_pages;         /* pool size, in pages */
   int32_t kv_dtype;          /* pdattn_kv_dtype */
   float scale;               /* softmax scale; <= 0 selects 1/sqrt(head_dim) */
+  int32_t kv_layout;         /* pdattn_kv_layout: the order of rows inside a page */
 } pdattn_problem;
 
 /* A launch plan: a pure function of the problem, the host copy of the
@@ -204,10 +219,10 @@ PDATTN_API pdattn_status pdattn_reduce(const pdattn_plan_t* plan, const void* wo
  *   token_seq    int32 [num_tokens], device: the sequence b of each token
  *   token_pos    int32 [num_tokens], device: its position t in that sequence
  *   block_table  int32 [B][max_pages_per_seq], device
- *   k_pages,     the pools, layouts as for pdattn_decode; written in place
- *   v_pages
- *   k_scale,     fp32 [num_pages][P][Hkv] for fp8 pools (written in place),
- *   v_scale      NULL for bf16 pools
+ *   k_pages,     the pools, layouts as for pdattn_decode (problem->kv_layout);
+ *   v_pages      written in place
+ *   k_scale,     fp32, one per row as for pdattn_decode, for fp8 pools
+ *   v_scale      (written in place); NULL for bf16 pools
  *   flags        0 or PDATTN_APPEND_POW2_SCALES (fp8 pools only)
  * A bf16 pool receives the rows bit for bit. An fp8 pool receives, for each
  * (token, kv head) and separately for K and V, a scale s and the codes

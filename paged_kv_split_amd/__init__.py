@@ -14,11 +14,14 @@ import torch
 
 __all__ = ["Problem", "Plan", "PdattnError", "plan", "decode", "reduce", "workspace", "workspace_init",
            "paged_decode", "KV_BF16", "KV_FP8_E4M3", "PLAN_BALANCED", "library_path", "stream_read",
-           "stream_read_sink", "kv_append", "APPEND_POW2_SCALES", "fp8_conversion_check", "merge"]
+           "stream_read_sink", "kv_append", "APPEND_POW2_SCALES", "fp8_conversion_check", "merge", "LAYOUT_NHD", "LAYOUT_HND",
+           "pool_dims"]
 
 KV_BF16 = 0
 KV_FP8_E4M3 = 1
 PLAN_BALANCED = 2
+LAYOUT_NHD = 0   # pool rows [page][slot][kv head]
+LAYOUT_HND = 1   # pool rows [page][kv head][slot]
 APPEND_POW2_SCALES = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -42,6 +45,7 @@ class Problem(ctypes.Structure):
         ("num_pages", ctypes.c_int32),
         ("kv_dtype", ctypes.c_int32),
         ("scale", ctypes.c_float),
+        ("kv_layout", ctypes.c_int32),
     ]
 
 
@@ -118,13 +122,19 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def pool_dims(pages, layout=LAYOUT_NHD):
+    """(num_pages, P, Hkv, d) of a pool tensor in the given layout."""
+    n, a, b, d = pages.shape
+    return (n, a, b, d) if layout == LAYOUT_NHD else (n, b, a, d)
+
+
 def plan(*, batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq, num_pages,
          kv_dtype=KV_BF16, scale=0.0, context_lens_host, num_cus=0, force_workers=0,
-         balanced=False) -> Plan:
+         balanced=False, kv_layout=LAYOUT_NHD) -> Plan:
     """``pdattn_plan``: context_lens_host is a CPU int32 tensor (or sequence)."""
     lens = torch.as_tensor(context_lens_host, dtype=torch.int32).cpu().contiguous()
     prob = Problem(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq, num_pages,
-                   kv_dtype, float(scale))
+                   kv_dtype, float(scale), kv_layout)
     out = Plan()
     flags = PLAN_BALANCED if balanced else 0
     _check(_lib.pdattn_plan(ctypes.byref(prob), _ptr(lens), int(num_cus), int(force_workers), flags,
@@ -173,19 +183,19 @@ def stream_read_sink(num_cus, device):
 
 
 def kv_append(k_new, v_new, token_seq, token_pos, block_table, k_pages, v_pages, k_scale=None, v_scale=None,
-              *, batch=None, pow2_scales=False, stream=None):
+              *, batch=None, pow2_scales=False, layout=LAYOUT_NHD, stream=None):
     """``pdattn_kv_append``: write new K/V rows into the pools in place.
 
     k_new/v_new: bf16 [N,Hkv,d]; token_seq/token_pos: int32 [N]; block_table
-    int32 [B,max_pages]; k_pages/v_pages: bf16 or float8_e4m3fn [num_pages,P,Hkv,d];
-    k_scale/v_scale: fp32 [num_pages,P,Hkv] for fp8 pools. ``batch`` defaults
-    to the block table's row count.
+    int32 [B,max_pages]; k_pages/v_pages: bf16 or float8_e4m3fn, [num_pages,P,Hkv,d]
+    (NHD) or [num_pages,Hkv,P,d] (HND); k_scale/v_scale: fp32, one per row, for
+    fp8 pools. ``batch`` defaults to the block table's row count.
     """
     N = k_new.shape[0]
-    num_pages, P, Hkv, D = k_pages.shape
+    num_pages, P, Hkv, D = pool_dims(k_pages, layout)
     kv = KV_FP8_E4M3 if k_pages.dtype == torch.float8_e4m3fn else KV_BF16
     B = block_table.shape[0] if batch is None else batch
-    prob = Problem(B, Hkv, Hkv, D, P, block_table.shape[1], num_pages, kv, 0.0)
+    prob = Problem(B, Hkv, Hkv, D, P, block_table.shape[1], num_pages, kv, 0.0, layout)
     flags = APPEND_POW2_SCALES if pow2_scales else 0
     _check(_lib.pdattn_kv_append(ctypes.byref(prob), int(N), _ptr(k_new), _ptr(v_new), _ptr(token_seq),
                                  _ptr(token_pos), _ptr(block_table), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
@@ -216,21 +226,22 @@ def fp8_conversion_check(device, stream=None) -> int:
 
 def paged_decode(q, k_pages, v_pages, block_table, context_lens, *, context_lens_host=None,
                  k_scale=None, v_scale=None, scale=None, num_cus=0, force_workers=0,
-                 balanced=False, return_lse=True):
+                 balanced=False, return_lse=True, layout=LAYOUT_NHD):
     """Plan, allocate (torch) and run one decode step; returns (out, lse).
 
-    q: bf16 [B,Hq,d]; k_pages/v_pages: bf16 or float8_e4m3fn [num_pages,P,Hkv,d];
-    block_table int32 [B,max_pages]; context_lens int32 [B] on the device.
+    q: bf16 [B,Hq,d]; k_pages/v_pages: bf16 or float8_e4m3fn, [num_pages,P,Hkv,d]
+    (NHD) or [num_pages,Hkv,P,d] (HND); block_table int32 [B,max_pages];
+    context_lens int32 [B] on the device.
     """
     B, Hq, D = q.shape
-    num_pages, P, Hkv, _ = k_pages.shape
+    num_pages, P, Hkv, _ = pool_dims(k_pages, layout)
     if context_lens_host is None:
         context_lens_host = context_lens.cpu()
     kv = KV_FP8_E4M3 if k_pages.dtype == torch.float8_e4m3fn else KV_BF16
     pl = plan(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=P,
               max_pages_per_seq=block_table.shape[1], num_pages=num_pages, kv_dtype=kv,
               scale=0.0 if scale is None else scale, context_lens_host=context_lens_host,
-              num_cus=num_cus, force_workers=force_workers, balanced=balanced)
+              num_cus=num_cus, force_workers=force_workers, balanced=balanced, kv_layout=layout)
     dev = q.device
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if return_lse else None

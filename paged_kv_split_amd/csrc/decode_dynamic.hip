@@ -628,8 +628,10 @@ void decode_dynamic_kernel(DynParams p) {
     // an out-of-range entry among the staged pages (all of them belong to
     // this sequence, whose every pair reads every page) poisons the piece
     bad_piece |= winbad;
+    const long long page_rows = (long long)P * Hkv;
+    const int kvh_off = cu.kvh * p.head_stride;
     auto row_of = [&](int pos) -> long long {
-      return ((((long long)pages[(pos >> lp) - winpg]) << lp) + (pos & (P - 1))) * Hkv + cu.kvh;
+      return (long long)pages[(pos >> lp) - winpg] * page_rows + (pos & (P - 1)) * p.slot_stride + kvh_off;
     };
     const int nk = hi - lo;
     auto issue = [&](int k) {

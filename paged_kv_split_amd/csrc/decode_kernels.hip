@@ -205,8 +205,10 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p) {
           }
         }
         // (token, kv head) row index of sequence position pos
+        const long long page_rows = (long long)P * Hkv;
+        const int kvh_off = kvh * p.head_stride;
         auto row_of = [&](int pos) -> long long {
-          return ((((long long)pages[(pos >> lp) - pg0]) << lp) + (pos & (P - 1))) * Hkv + kvh;
+          return (long long)pages[(pos >> lp) - pg0] * page_rows + (pos & (P - 1)) * p.slot_stride + kvh_off;
         };
         const int nk = (c1 - c0 + kTileTokens - 1) / kTileTokens;
         auto issue = [&](int k) {

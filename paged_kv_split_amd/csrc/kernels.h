@@ -80,6 +80,8 @@ struct DecodeParams {
   int32_t max_pages_per_seq;
   int32_t num_pages;
   int32_t num_workers;        // waves of the grid that own tile ranges
+  int32_t slot_stride;        // row index = page * P * Hkv + slot * slot_stride + kvh * head_stride
+  int32_t head_stride;        // (Hkv, 1): rows [page][slot][kvh]; (1, P): rows [page][kvh][slot]
   float qk_scale_log2;        // softmax scale * log2(e)
 };
 
@@ -107,6 +109,8 @@ struct DynParams {
   int32_t num_workers;
   int32_t seg_max;            // units per pair at most
   int32_t units_max;          // batch * num_kv_heads * seg_max
+  int32_t slot_stride;        // row strides as in DecodeParams
+  int32_t head_stride;
   float qk_scale_log2;
 };
 

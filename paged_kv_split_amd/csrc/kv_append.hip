@@ -115,9 +115,9 @@ __device__ inline u32x2 quantise_chunk(u32x4 w, bool pow2, float* scale_out) {
 }
 
 // One wave per new token. The token's K rows for all kv heads are one
-// contiguous chunk of Hkv * D bf16 values in k_new and one contiguous
-// chunk in the pool (rows [page][slot][0..Hkv)), and so are its V rows: a
-// step moves 1 KB of each with 16-byte lanes, and the first loads are
+// contiguous chunk of Hkv * D bf16 values in k_new, and so are its V rows: a
+// step moves 1 KB of each with 16-byte lanes into the token's rows (adjacent
+// in an NHD pool, P rows apart in an HND pool), and the first loads are
 // issued before the token's slot is resolved, so the block-table round
 // trip overlaps them.
 template <int D, bool FP8>
@@ -153,9 +153,11 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
       for (int u = 0; u < kBatch; ++u) asm volatile("" ::"v"(kx[u]), "v"(vx[u]));
       continue;
     }
-    const int64_t row0 = (((int64_t)page << p.page_log2) | (t & ((1 << p.page_log2) - 1))) * p.num_kv_heads;
-    unsigned char* kdst = static_cast<unsigned char*>(p.k_pages) + row0 * D * (FP8 ? 1 : 2);
-    unsigned char* vdst = static_cast<unsigned char*>(p.v_pages) + row0 * D * (FP8 ? 1 : 2);
+    // the token's row for kv head h: base + h * head_stride
+    const int64_t base = ((int64_t)page << p.page_log2) * p.num_kv_heads +
+                         (int64_t)(t & ((1 << p.page_log2) - 1)) * p.slot_stride;
+    unsigned char* kpool = static_cast<unsigned char*>(p.k_pages);
+    unsigned char* vpool = static_cast<unsigned char*>(p.v_pages);
     for (int j0 = 0; j0 < steps; j0 += kBatch) {
       if (j0 > 0) {
 #pragma unroll
@@ -168,10 +170,13 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int o = (j0 + u) * 1024 + lane * 16;
+        // a 16-byte lane chunk lies inside one row: kv head o / (2 D)
+        const int64_t r = base + (int64_t)(o / (2 * D)) * p.head_stride;
+        const int within = o & (2 * D - 1);
         if constexpr (!FP8) {
           if (o < chunk) {
-            *reinterpret_cast<u32x4*>(kdst + o) = kx[u];
-            *reinterpret_cast<u32x4*>(vdst + o) = vx[u];
+            *reinterpret_cast<u32x4*>(kpool + r * (2 * D) + within) = kx[u];
+            *reinterpret_cast<u32x4*>(vpool + r * (2 * D) + within) = vx[u];
           }
         } else {
           // whole rows are in or out of range together, so every lane of a
@@ -182,10 +187,9 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
           const u32x2 kc = quantise_chunk<D>(in ? kx[u] : u32x4{0, 0, 0, 0}, p.pow2_scales, &ks);
           const u32x2 vc = quantise_chunk<D>(in ? vx[u] : u32x4{0, 0, 0, 0}, p.pow2_scales, &vs);
           if (in) {
-            *reinterpret_cast<u32x2*>(kdst + o / 2) = kc;
-            *reinterpret_cast<u32x2*>(vdst + o / 2) = vc;
+            *reinterpret_cast<u32x2*>(kpool + r * D + within / 2) = kc;
+            *reinterpret_cast<u32x2*>(vpool + r * D + within / 2) = vc;
             if ((lane & (D / 8 - 1)) == 0) {
-              const int64_t r = row0 + o / (2 * D);
               p.k_scale[r] = ks;
               p.v_scale[r] = vs;
             }

@@ -61,10 +61,17 @@ pdattn_status check_problem(const pdattn_problem* p) {
   if (p->kv_dtype != PDATTN_KV_BF16 && p->kv_dtype != PDATTN_KV_FP8_E4M3)
     return fail(PDATTN_ERR_UNSUPPORTED, "kv_dtype %d unknown", p->kv_dtype);
   if (!std::isfinite(p->scale)) return fail(PDATTN_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (p->kv_layout != PDATTN_LAYOUT_NHD && p->kv_layout != PDATTN_LAYOUT_HND)
+    return fail(PDATTN_ERR_UNSUPPORTED, "kv_layout %d unknown", p->kv_layout);
   return PDATTN_OK;
 }
 
 int group_of(const pdattn_problem& p) { return p.num_q_heads / p.num_kv_heads; }
+
+// Row strides of the pools: row index = page * P * Hkv + slot * slot_stride
+// + kvh * head_stride.
+int slot_stride_of(const pdattn_problem& p) { return p.kv_layout == PDATTN_LAYOUT_HND ? 1 : p.num_kv_heads; }
+int head_stride_of(const pdattn_problem& p) { return p.kv_layout == PDATTN_LAYOUT_HND ? p.page_size : 1; }
 
 bool balanced(int32_t flags) { return (flags & PDATTN_PLAN_BALANCED) != 0; }
 uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
@@ -287,6 +294,8 @@ PDATTN_API pdattn_status pdattn_decode(const pdattn_plan_t* plan, const void* q,
     p.num_workers = plan->num_workers;
     p.seg_max = (int32_t)d.seg_max;
     p.units_max = (int32_t)d.units_max;
+    p.slot_stride = slot_stride_of(pr);
+    p.head_stride = head_stride_of(pr);
     p.qk_scale_log2 = pr.scale * 1.44269504088896340736f;
     hipError_t e = pdattn::launch_dynamic(p, pr.head_dim, group_of(pr), fp8, (uint32_t)plan->num_workgroups,
                                           static_cast<hipStream_t>(stream));
@@ -314,6 +323,8 @@ PDATTN_API pdattn_status pdattn_decode(const pdattn_plan_t* plan, const void* q,
   p.max_pages_per_seq = pr.max_pages_per_seq;
   p.num_pages = pr.num_pages;
   p.num_workers = plan->num_workers;
+  p.slot_stride = slot_stride_of(pr);
+  p.head_stride = head_stride_of(pr);
   p.qk_scale_log2 = pr.scale * 1.44269504088896340736f;
 
   hipError_t e = pdattn::launch_decode(p, pr.head_dim, group_of(pr), fp8, (uint32_t)plan->num_workgroups,
@@ -420,6 +431,8 @@ PDATTN_API pdattn_status pdattn_kv_append(const pdattn_problem* problem, int32_t
   p.max_pages_per_seq = problem->max_pages_per_seq;
   p.num_pages = problem->num_pages;
   p.pow2_scales = (flags & PDATTN_APPEND_POW2_SCALES) ? 1 : 0;
+  p.slot_stride = slot_stride_of(*problem);
+  p.head_stride = head_stride_of(*problem);
   // one wave per token, four tokens per workgroup; a larger append is
   // covered by a grid-stride loop
   const int64_t wgs = ceil_div((int64_t)num_tokens, pdattn::kWaves);

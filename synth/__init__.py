@@ -27,7 +27,8 @@ import math
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "kv_bytes", "make_append_inputs", "append_bytes"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "kv_bytes", "make_append_inputs", "append_bytes", "to_hnd",
+           "from_hnd"]
 
 E4M3_MAX = 448.0
 
@@ -270,3 +271,22 @@ def append_bytes(num_rows, head_dim, kv_dtype) -> int:
     element size, plus two fp32 scales per row for an fp8 pool."""
     write = 2 * head_dim * (2 if kv_dtype == "bf16" else 1) + (8 if kv_dtype == "fp8_e4m3" else 0)
     return num_rows * (4 * head_dim + write)
+
+
+def to_hnd(inp):
+    """A copy of an input dict whose pools (and fp8 scales) are re-laid from
+    rows [page][slot][kv head] to rows [page][kv head][slot]: the same
+    values, another order in memory."""
+    out = dict(inp)
+    for k in ("k_pages", "v_pages"):
+        out[k] = inp[k].permute(0, 2, 1, 3).contiguous()
+    for k in ("k_scale", "v_scale"):
+        if inp.get(k) is not None:
+            out[k] = inp[k].permute(0, 2, 1).contiguous()
+    return out
+
+
+def from_hnd(t):
+    """A pool [page][kv head][slot][d] (or scales [page][kv head][slot]) back
+    in rows [page][slot][kv head]."""
+    return t.permute(0, 2, 1, 3) if t.dim() == 4 else t.permute(0, 2, 1)

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_struct_layout_matches_binding():
-    assert pk._lib.pdattn_problem_size() == ctypes.sizeof(pk.Problem) == 36
+    assert pk._lib.pdattn_problem_size() == ctypes.sizeof(pk.Problem) == 40
     assert pk._lib.pdattn_plan_size() == ctypes.sizeof(pk.Plan)
 
 
@@ -47,7 +47,7 @@ def test_status_strings():
 
 def problem(**kw):
     d = dict(batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, max_pages_per_seq=64,
-             num_pages=512, kv_dtype=0, scale=0.0)
+             num_pages=512, kv_dtype=0, scale=0.0, kv_layout=0)
     d.update(kw)
     return d
 
@@ -124,6 +124,8 @@ def test_plan_forced_workers_and_empty_batch():
     (dict(page_size=4), [1, 1, 1, 1], UNSUPPORTED),
     (dict(page_size=256), [1, 1, 1, 1], UNSUPPORTED),
     (dict(kv_dtype=7), [1, 1, 1, 1], UNSUPPORTED),
+    (dict(kv_layout=2), [1, 1, 1, 1], UNSUPPORTED),
+    (dict(kv_layout=-1), [1, 1, 1, 1], UNSUPPORTED),
     (dict(scale=float("nan")), [1, 1, 1, 1], INVALID),
     (dict(batch=70000), [1] * 4, INVALID),
     (dict(num_kv_heads=0), [1, 1, 1, 1], INVALID),
@@ -265,6 +267,7 @@ def test_kv_append_validation_rejects_before_launch():
     assert _append_raw(head_dim=96) == UNSUPPORTED
     assert _append_raw(page_size=24) == UNSUPPORTED
     assert _append_raw(num_kv_heads=3) == INVALID            # 32 q heads not a multiple of 3
+    assert _append_raw(kv_layout=5) == UNSUPPORTED
     assert "aligned" in (_append_raw(kn=0x1008), pk._lib.pdattn_last_error().decode())[1]
     # nothing to do: no pointer is read
     assert _append_raw(n=0, kn=0, vn=0, seq=0, pos=0, bt=0, kp=0, vp=0) == OK

@@ -34,12 +34,20 @@ def _np_pool(t):
     return t.to(torch.float32).numpy().copy()
 
 
-def run_gpu(inp, pow2=False):
+def run_gpu(inp, pow2=False, hnd=False):
+    """Append on the device; with hnd the pools are laid out [page][kv head]
+    [slot] for the call and returned in the token-major order."""
     pk = _pk()
-    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    src = synth.to_hnd(inp) if hnd else inp
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in src.items()}
     pk.kv_append(d["k_new"], d["v_new"], d["token_seq"], d["token_pos"], d["block_table"], d["k_pages"],
-                 d["v_pages"], d["k_scale"], d["v_scale"], pow2_scales=pow2)
+                 d["v_pages"], d["k_scale"], d["v_scale"], pow2_scales=pow2,
+                 layout=pk.LAYOUT_HND if hnd else pk.LAYOUT_NHD)
     torch.cuda.synchronize()
+    if hnd:
+        for k in ("k_pages", "v_pages", "k_scale", "v_scale"):
+            if d[k] is not None:
+                d[k] = synth.from_hnd(d[k]).contiguous()
     return d
 
 
@@ -86,18 +94,19 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("layout", ["nhd", "hnd"])
 @pytest.mark.parametrize("case", CASES, ids=["d128_p16", "d64_p8", "d128_p128", "d128_hkv16", "d128_hkv5",
                                              "d64_hkv1"])
 @pytest.mark.parametrize("mode", ["bf16", "fp8", "fp8_pow2"])
-def test_append_matches_oracle_bit_exact(case, mode):
+def test_append_matches_oracle_bit_exact(case, mode, layout):
     D, P, Hkv, B, new, ctx = case
     kv = "bf16" if mode == "bf16" else "fp8_e4m3"
     pow2 = mode == "fp8_pow2"
     inp = synth.make_append_inputs(batch=B, num_kv_heads=Hkv, head_dim=D, page_size=P, new_tokens=new,
                                    context=ctx, kv_dtype=kv, seed=3000 + D + P)
-    tag = f"append {mode} d{D} P{P} Hkv{Hkv} N{inp['token_seq'].numel()}"
+    tag = f"append {mode} {layout} d{D} P{P} Hkv{Hkv} N{inp['token_seq'].numel()}"
     print(tag, flush=True)
-    d = run_gpu(inp, pow2)
+    d = run_gpu(inp, pow2, hnd=layout == "hnd")
     assert_pools_equal(d, run_oracle(inp, pow2), tag)
 
 

@@ -108,3 +108,20 @@ def test_page_sizes(P):
         for force in (0, 3, 200):
             out, lse = gpu_run(inp, force_workers=force, balanced=bal)
             assert_parity(out, lse, *ref, tag=f"P{P} workers={force} balanced={bal}")
+
+
+@pytest.mark.parametrize("balanced", MODES, ids=MODE_IDS)
+@pytest.mark.parametrize("name", ["tiny", "llama3_8b", "many_short", "fp8_kv", "long_ctx"])
+def test_head_major_pages_match_oracle_and_token_major(name, balanced):
+    """The same pools laid out [page][kv head][slot]: the oracle's values, and
+    (same tiles in the same order) bitwise the token-major result."""
+    pk = _lib()
+    inp = synth.make_inputs(name)
+    hnd = synth.to_hnd(inp)
+    out_n, lse_n = gpu_run(inp, balanced=balanced)
+    out, lse = gpu_run(hnd, layout=pk.LAYOUT_HND, balanced=balanced)
+    ref_out, ref_lse = oracle_run(inp)
+    assert_parity(out, lse, ref_out, ref_lse, fp8=inp["k_pages"].dtype == torch.float8_e4m3fn,
+                  tag=f"{name} HND balanced={balanced}")
+    if not balanced:
+        assert torch.equal(out, out_n) and torch.equal(lse, lse_n), name

@@ -16,9 +16,10 @@ HBM.
 
 Prints ONE JSON line. value = KV algorithmic bytes (every K and V element of
 every valid (token, kv head) once, plus the fp8 scales) / mean step time, in
-GB/s. roofline = the same bytes / the mean duration of the decode kernel
-alone (events around that launch on its stream), against MI355X's 8 TB/s HBM
-peak. traffic = measured HBM bytes per launch of that kernel from the
+GB/s, the step timed by one event pair around decode + reduce. roofline =
+the same bytes / the mean duration of the decode kernel alone (an event pair
+around that launch on its stream, in a second flushed loop), against
+MI355X's 8 TB/s HBM peak. traffic = measured HBM bytes per launch of that kernel from the
 committed rocprofv3 counter summary, or null when the kernel's sources have
 changed since the counters were taken. cpu_baseline = the CPU fp64 oracle
 timed on this host's cores on the same step's inputs.
@@ -211,6 +212,7 @@ def main():
                     help="time the on-device balanced kernel instead of the static split + reduce")
     ap.add_argument("--layout", choices=("hnd", "nhd"), default="hnd",
                     help="KV pool rows [page][kv head][slot] (hnd, the default) or [page][slot][kv head] (nhd)")
+    ap.add_argument("--no-other-layout", action="store_true", help="skip the other-layout step timing")
     ap.add_argument("--no-append", action="store_true", help="skip the KV-append timings")
     ap.add_argument("--no-merge", action="store_true", help="skip the partial-state merge timings")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -265,26 +267,43 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # the timed steps: one event pair around decode + reduce (an event between
+    # the two launches would itself add a few microseconds to the step)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(args.steps):
         if not args.no_flush:
             flush.fill_(i & 0xFF)
         ev[i][0].record()
-        pk.decode(pl, d["q"], d["k_pages"], d["v_pages"], d["k_scale"], d["v_scale"], d["block_table"],
-                  d["context_lens"], ws, out, lse)
+        step()
         ev[i][1].record()
-        pk.reduce(pl, ws, out, lse)
-        ev[i][2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    step_us = [e[0].elapsed_time(e[2]) * 1e3 for e in ev]
-    dec_us = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
-    red_us = [e[1].elapsed_time(e[2]) * 1e3 for e in ev]
+    step_us = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
     mean_step = statistics.fmean(step_us)
-    mean_dec = statistics.fmean(dec_us)
     qs = statistics.quantiles(step_us, n=10)
+
+    # each kernel alone between events, on the stream it runs on, after the
+    # same flush: the decode kernel's duration for the roofline, and the
+    # reduce's
+    dec_us, red_us = [], []
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush.fill_(i & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        pk.decode(pl, d["q"], d["k_pages"], d["v_pages"], d["k_scale"], d["v_scale"], d["block_table"],
+                  d["context_lens"], ws, out, lse)
+        b.record()
+        c, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c.record()
+        pk.reduce(pl, ws, out, lse)
+        e.record()
+        torch.cuda.synchronize()
+        dec_us.append(a.elapsed_time(b) * 1e3)
+        red_us.append(c.elapsed_time(e) * 1e3)
+    mean_dec = statistics.fmean(dec_us)
 
     # warm-cache figure (secondary): same steps without the flush
     warm = []
@@ -324,7 +343,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    other = time_other_layout(pk, w, inp, args, flush, dev)
+    other = None if args.no_other_layout else time_other_layout(pk, w, inp, args, flush, dev)
     append = None if args.no_append else time_append(pk, w, flush, dev, layout)
     merge = None if args.no_merge else time_merge(pk, flush, dev)
 

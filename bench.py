@@ -167,6 +167,52 @@ def time_append(pk, w, flush, dev, layout, reps=20):
     return res
 
 
+def time_multi_query(pk, w, inp, args, flush, dev, n=4, reps=30):
+    """The same step with n query rows per sequence (speculative decoding's
+    next_n; row i attends causally to the positions before L - (n - 1 - i)):
+    the same pools and the same KV bytes, n times the queries. Mean step
+    time (decode + reduce, one event pair), KV GB/s and query rows per
+    second."""
+    import torch
+    import synth
+    if w.num_q_heads // w.num_kv_heads * n > 16:
+        return None
+    laid = synth.to_hnd(inp) if args.layout == "hnd" else inp
+    d = {k: (laid[k].to(dev) if laid[k] is not None else None)
+         for k in ("k_pages", "v_pages", "k_scale", "v_scale", "block_table", "context_lens")}
+    g = torch.Generator().manual_seed(4300)
+    q4 = torch.randn((w.batch, n, w.num_q_heads, w.head_dim), generator=g).to(torch.bfloat16).to(dev)
+    pl = pk.plan(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                 page_size=w.page_size, max_pages_per_seq=inp["block_table"].shape[1],
+                 num_pages=inp["k_pages"].shape[0], kv_dtype=pk.KV_BF16 if w.kv_dtype == "bf16" else pk.KV_FP8_E4M3,
+                 context_lens_host=inp["context_lens"], q_len=n,
+                 kv_layout=pk.LAYOUT_HND if args.layout == "hnd" else pk.LAYOUT_NHD)
+    out = torch.empty((w.batch, n, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, n, w.num_q_heads), dtype=torch.float32, device=dev)
+    ws = pk.workspace(pl, dev)
+
+    def step():
+        pk.decode(pl, q4, d["k_pages"], d["v_pages"], d["k_scale"], d["v_scale"], d["block_table"],
+                  d["context_lens"], ws, out, lse)
+        pk.reduce(pl, ws, out, lse)
+    for _ in range(5):
+        step()
+    ts = []
+    for i in range(reps):
+        flush.fill_(i & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3)
+    kvb = synth.kv_bytes(w, inp["context_lens"])
+    us = statistics.fmean(ts)
+    return {"next_n": n, "columns_per_kv_head": w.num_q_heads // w.num_kv_heads * n, "us_per_call": round(us, 2),
+            "gbs": round(kvb / (us * 1e-6) / 1e9, 1),
+            "query_rows_per_s": round(w.batch * n * w.num_q_heads / (us * 1e-6), 0)}
+
+
 def time_merge(pk, flush, dev, reps=20):
     """pdattn_merge timings (secondary figures): a two-piece cascade (shared
     prefix + suffix) over the Llama-3-8B decode rows (32 x 32 rows, d128)
@@ -215,6 +261,7 @@ def main():
     ap.add_argument("--no-other-layout", action="store_true", help="skip the other-layout step timing")
     ap.add_argument("--no-append", action="store_true", help="skip the KV-append timings")
     ap.add_argument("--no-merge", action="store_true", help="skip the partial-state merge timings")
+    ap.add_argument("--no-multi-query", action="store_true", help="skip the multi-query decode timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run 3 device copies of 256 MiB (a plain copy kernel of known "
                          "size, for scaling the HBM byte counters)")
@@ -346,6 +393,7 @@ def main():
     other = None if args.no_other_layout else time_other_layout(pk, w, inp, args, flush, dev)
     append = None if args.no_append else time_append(pk, w, flush, dev, layout)
     merge = None if args.no_merge else time_merge(pk, flush, dev)
+    multi = None if args.no_multi_query else time_multi_query(pk, w, inp, args, flush, dev)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -409,6 +457,7 @@ def main():
         "other_layout": other,
         "kv_append": append,
         "merge": merge,
+        "multi_query": multi,
     }
     print(json.dumps(rec), flush=True)
 

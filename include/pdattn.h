@@ -15,6 +15,17 @@
  *     lse[b][h]    = ln sum_t exp(s_t)            (natural log)
  *   L == 0 gives out = 0 and lse = -inf.
  *
+ * Multi-query decode (problem->q_len = n > 1; speculative decoding's next_n
+ * tokens, DeepGEMM documentation section 6.1: paged q of shape
+ * [batch, next_n, heads, d]): each sequence has n query rows, the last n
+ * positions of its context, already in the cache. Query row i (0 <= i < n)
+ * attends causally, to the positions t < L - (n - 1 - i); a row that sees
+ * no position gets out = 0 and lse = -inf. q, out and lse then carry a row
+ * axis: q [B][n][Hq][d], out [B][n][Hq][d], lse [B][n][Hq]. The kernel
+ * treats the n * G (row, head) pairs of a kv head as the columns of one
+ * MFMA operand, so n * G must be one of 1, 2, 4, 8, 16; the K/V bytes read
+ * are those of one decode step. Static plans only (not PDATTN_PLAN_BALANCED).
+ *
  * Work decomposition (flash-decoding): the (b, kvh) pairs are laid end to
  * end, each cut into 16-token tiles, and a persistent grid of
  * plan->num_workers waves streams that tile list. A wave computes all G
@@ -47,8 +58,9 @@
  *   out          fp32 [B][Hq][d]
  *   lse          fp32 [B][Hq], optional (NULL to skip)
  *
- * Supported: d in {64, 128}; G in {1, 2, 4, 8, 16}; P a power of two in
- * [8, 128]; q / k / v / out bases 16-byte aligned; B <= 65535.
+ * Supported: d in {64, 128}; G in {1, 2, 4, 8, 16} (and n * G in that set);
+ * P a power of two in [8, 128]; q / k / v / out bases 16-byte aligned;
+ * B <= 65535.
  *
  * Ownership and execution: the caller allocates and owns every buffer,
  * including the workspace (size from the plan). The library allocates
@@ -116,6 +128,7 @@ typedef struct pdattn_problem {
   int32_t kv_dtype;          /* pdattn_kv_dtype */
   float scale;               /* softmax scale; <= 0 selects 1/sqrt(head_dim) */
   int32_t kv_layout;         /* pdattn_kv_layout: the order of rows inside a page */
+  int32_t q_len;             /* query rows per sequence n (0 or 1: one-token decode) */
 } pdattn_problem;
 
 /* A launch plan: a pure function of the problem, the host copy of the

@@ -46,6 +46,7 @@ class Problem(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("kv_layout", ctypes.c_int32),
+        ("q_len", ctypes.c_int32),
     ]
 
 
@@ -130,11 +131,11 @@ def pool_dims(pages, layout=LAYOUT_NHD):
 
 def plan(*, batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq, num_pages,
          kv_dtype=KV_BF16, scale=0.0, context_lens_host, num_cus=0, force_workers=0,
-         balanced=False, kv_layout=LAYOUT_NHD) -> Plan:
+         balanced=False, kv_layout=LAYOUT_NHD, q_len=1) -> Plan:
     """``pdattn_plan``: context_lens_host is a CPU int32 tensor (or sequence)."""
     lens = torch.as_tensor(context_lens_host, dtype=torch.int32).cpu().contiguous()
     prob = Problem(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq, num_pages,
-                   kv_dtype, float(scale), kv_layout)
+                   kv_dtype, float(scale), kv_layout, q_len)
     out = Plan()
     flags = PLAN_BALANCED if balanced else 0
     _check(_lib.pdattn_plan(ctypes.byref(prob), _ptr(lens), int(num_cus), int(force_workers), flags,
@@ -195,7 +196,7 @@ def kv_append(k_new, v_new, token_seq, token_pos, block_table, k_pages, v_pages,
     num_pages, P, Hkv, D = pool_dims(k_pages, layout)
     kv = KV_FP8_E4M3 if k_pages.dtype == torch.float8_e4m3fn else KV_BF16
     B = block_table.shape[0] if batch is None else batch
-    prob = Problem(B, Hkv, Hkv, D, P, block_table.shape[1], num_pages, kv, 0.0, layout)
+    prob = Problem(B, Hkv, Hkv, D, P, block_table.shape[1], num_pages, kv, 0.0, layout, 1)
     flags = APPEND_POW2_SCALES if pow2_scales else 0
     _check(_lib.pdattn_kv_append(ctypes.byref(prob), int(N), _ptr(k_new), _ptr(v_new), _ptr(token_seq),
                                  _ptr(token_pos), _ptr(block_table), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
@@ -229,11 +230,14 @@ def paged_decode(q, k_pages, v_pages, block_table, context_lens, *, context_lens
                  balanced=False, return_lse=True, layout=LAYOUT_NHD):
     """Plan, allocate (torch) and run one decode step; returns (out, lse).
 
-    q: bf16 [B,Hq,d]; k_pages/v_pages: bf16 or float8_e4m3fn, [num_pages,P,Hkv,d]
+    q: bf16 [B,Hq,d], or [B,n,Hq,d] for multi-query decode (n query rows per
+    sequence, the last n positions of its context; outputs then [B,n,Hq,d]
+    and [B,n,Hq]); k_pages/v_pages: bf16 or float8_e4m3fn, [num_pages,P,Hkv,d]
     (NHD) or [num_pages,Hkv,P,d] (HND); block_table int32 [B,max_pages];
     context_lens int32 [B] on the device.
     """
-    B, Hq, D = q.shape
+    n = q.shape[1] if q.dim() == 4 else 1
+    B, Hq, D = q.shape[0], q.shape[-2], q.shape[-1]
     num_pages, P, Hkv, _ = pool_dims(k_pages, layout)
     if context_lens_host is None:
         context_lens_host = context_lens.cpu()
@@ -241,10 +245,11 @@ def paged_decode(q, k_pages, v_pages, block_table, context_lens, *, context_lens
     pl = plan(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=P,
               max_pages_per_seq=block_table.shape[1], num_pages=num_pages, kv_dtype=kv,
               scale=0.0 if scale is None else scale, context_lens_host=context_lens_host,
-              num_cus=num_cus, force_workers=force_workers, balanced=balanced, kv_layout=layout)
+              num_cus=num_cus, force_workers=force_workers, balanced=balanced, kv_layout=layout, q_len=n)
     dev = q.device
-    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if return_lse else None
+    lead = (B, n) if q.dim() == 4 else (B,)
+    out = torch.empty(lead + (Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty(lead + (Hq,), dtype=torch.float32, device=dev) if return_lse else None
     ws = workspace(pl, dev)
     decode(pl, q, k_pages, v_pages, k_scale, v_scale, block_table, context_lens, ws, out, lse)
     reduce(pl, ws, out, lse)

@@ -64,8 +64,11 @@ __device__ __forceinline__ void worker_range(long long w, long long nw, long lon
   t1 = (w + 1) * T / nw;
 }
 
+// fp8 d128 with up to 4 columns: the LDS holds four workgroups per CU; the
+// register budget is held to the 128 VGPRs that let four waves share a SIMD
 template <int D, int G, bool FP8>
-__global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FP8 && D == 128 && G <= 4 ? 4 : 1)))
+void decode_kernel(DecodeParams p) {
   using TL = Tile<D, G, FP8>;
   constexpr int C = TL::C;
   constexpr int NT = kWaves * 64;
@@ -138,14 +141,16 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p) {
     }
   }
   if (blockIdx.x == 0) {
+    // every query row of such a sequence (q_len rows of Hq heads)
+    const int rows = p.q_len * Hq;
     for (int b = b_lo; b < b_hi; ++b) {
       const int L = p.context_lens[b];
       if (tiles_of(L) > 0) continue;
       const bool bad = L != 0;
       const float fo = bad ? __builtin_nanf("") : 0.0f;
-      for (int i = 0; i < Hq * D; ++i) p.out[(long long)b * Hq * D + i] = fo;
+      for (int i = 0; i < rows * D; ++i) p.out[(long long)b * rows * D + i] = fo;
       if (p.lse != nullptr)
-        for (int h = 0; h < Hq; ++h) p.lse[(long long)b * Hq + h] = bad ? __builtin_nanf("") : -__builtin_inff();
+        for (int h = 0; h < rows; ++h) p.lse[(long long)b * rows + h] = bad ? __builtin_nanf("") : -__builtin_inff();
     }
   }
   __syncthreads();
@@ -178,12 +183,20 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p) {
       const int seg = (int)min((long long)(nt - j), remaining);
       const bool cut_start = j > 0;
       const bool reaches_end = j + seg == nt;
-      const int h0 = kvh * G;
       const int s0 = j * kTileTokens;
       const int s1 = min(L, (j + seg) * kTileTokens);
+      // Column c of the G = q_len * 2^group_log2 columns is query row
+      // c >> group_log2 of head (kvh << group_log2) + (c & mask); its rows of
+      // q, out and lse sit (c >> group_log2) * Hq + (c & mask) rows past
+      // base_row. Query row i sees the positions before L - (q_len - 1 - i).
+      const int qmask = (1 << p.group_log2) - 1;
+      auto col_row = [&](int c) { return (c >> p.group_log2) * Hq + (c & qmask); };
+      const long long base_row = (long long)b * p.q_len * Hq + ((long long)kvh << p.group_log2);
+      const int cl = min(col, G - 1);
+      const int lim = min(s1, L - (p.q_len - 1 - (cl >> p.group_log2)));
 
       bf16x8 qop[TL::KSTEPS];
-      TL::load_q(qop, p.q + ((long long)b * Hq + h0) * D, row, col);
+      TL::load_q(qop, p.q + (base_row + col_row(cl)) * D, row, col);
       typename TL::State st;
       TL::reset(st);
       int bad = 0;
@@ -227,7 +240,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p) {
           TL::read(f, ring + (k % S) * STAGE, lane, row, col);
           // the stage's reads have returned (read_stage waits for them): refill it
           if (k + S < nk) issue(k + S);
-          TL::compute(st, f, qop, c0 + k * kTileTokens, s1, p.qk_scale_log2, row);
+          TL::compute(st, f, qop, c0 + k * kTileTokens, lim, p.qk_scale_log2, row);
         }
         c0 = c1;
       }
@@ -236,7 +249,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p) {
       TL::reduce_rows(st);
       const bool poisoned = __any(bad);
       if (!cut_start && reaches_end) {
-        TL::store_out(st, p.out + ((long long)b * Hq + h0) * D, p.lse ? p.lse + (long long)b * Hq + h0 : nullptr,
+        TL::store_out(st, p.out + base_row * D, p.lse ? p.lse + base_row : nullptr, col_row,
                       poisoned, row, col);
       } else {
         // a piece of a cut pair: record (m, l, acc); slot 0 for the wave's
@@ -273,7 +286,12 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p) {
       }
     }
   }
-  if (lane < kDescWords) p.desc[gw * kDescWords + lane] = dsc[lane];
+  // lane i writes word i (selected, not indexed: an indexed register array
+  // would live in scratch memory)
+  int dword_i = 0;
+#pragma unroll
+  for (int i = 0; i < kDescWords; ++i) dword_i = lane == i ? dsc[i] : dword_i;
+  if (lane < kDescWords) p.desc[gw * kDescWords + lane] = dword_i;
 }
 
 // Waves of a merge workgroup, and the pieces one merge wave loads per step.
@@ -369,9 +387,13 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(MergeParams p) 
       Av += wq * s_acc[q][e];
       Ls += wq * s_l[q][gg];
     }
-    const long long bh = (long long)b * p.num_q_heads + kvh * G + gg;
-    p.out[bh * D + (e % D)] = Av / Ls;
-    if (e % D == 0 && p.lse != nullptr) p.lse[bh] = (Mx + log2f(Ls)) * kLn2;
+    // column gg: query row gg >> group_log2 of head (kvh << group_log2) +
+    // (gg & mask); a column that saw no token (Ls = 0) gets 0 and -inf
+    const long long bh = (long long)b * p.q_len * p.num_q_heads + ((long long)kvh << p.group_log2) +
+                         (gg >> p.group_log2) * p.num_q_heads + (gg & ((1 << p.group_log2) - 1));
+    // (a NaN sum, from a poisoned piece, stays NaN)
+    p.out[bh * D + (e % D)] = Ls != 0.0f ? Av / Ls : 0.0f;
+    if (e % D == 0 && p.lse != nullptr) p.lse[bh] = Ls != 0.0f ? (Mx + log2f(Ls)) * kLn2 : -__builtin_inff();
   }
 }
 

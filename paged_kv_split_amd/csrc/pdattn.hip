@@ -50,6 +50,10 @@ pdattn_status check_problem(const pdattn_problem* p) {
   const int g = p->num_q_heads / p->num_kv_heads;
   if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16)
     return fail(PDATTN_ERR_UNSUPPORTED, "group size %d not in {1, 2, 4, 8, 16}", g);
+  if (p->q_len < 0 || p->q_len > 16) return fail(PDATTN_ERR_INVALID_ARGUMENT, "q_len %d outside [0, 16]", p->q_len);
+  const int cols = g * (p->q_len > 1 ? p->q_len : 1);
+  if (cols != 1 && cols != 2 && cols != 4 && cols != 8 && cols != 16)
+    return fail(PDATTN_ERR_UNSUPPORTED, "q_len * group size = %d not in {1, 2, 4, 8, 16}", cols);
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(PDATTN_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", p->head_dim);
   if (!is_pow2(p->page_size) || p->page_size < 8 || p->page_size > 128)
@@ -66,7 +70,10 @@ pdattn_status check_problem(const pdattn_problem* p) {
   return PDATTN_OK;
 }
 
-int group_of(const pdattn_problem& p) { return p.num_q_heads / p.num_kv_heads; }
+int qlen_of(const pdattn_problem& p) { return p.q_len > 1 ? p.q_len : 1; }
+int heads_per_kv(const pdattn_problem& p) { return p.num_q_heads / p.num_kv_heads; }
+// Columns of a kernel instantiation: the (query row, head) pairs of one kv head.
+int group_of(const pdattn_problem& p) { return heads_per_kv(p) * qlen_of(p); }
 
 // Row strides of the pools: row index = page * P * Hkv + slot * slot_stride
 // + kvh * head_stride.
@@ -132,7 +139,7 @@ pdattn_status check_plan(const pdattn_plan_t* plan) {
   if (st != PDATTN_OK) return fail(PDATTN_ERR_PLAN_MISMATCH, "plan holds an invalid problem: %s", g_last_error);
   if (plan->num_workers < 1 || plan->num_workgroups < 1 ||
       (int64_t)plan->num_workgroups * pdattn::kWaves < plan->num_workers ||
-      (plan->flags & ~PDATTN_PLAN_BALANCED) != 0 ||
+      (plan->flags & ~PDATTN_PLAN_BALANCED) != 0 || (balanced(plan->flags) && qlen_of(plan->problem) > 1) ||
       plan->workspace_bytes != workspace_for(plan->problem, plan->num_workers, plan->flags))
     return fail(PDATTN_ERR_PLAN_MISMATCH, "plan fields are inconsistent");
   return PDATTN_OK;
@@ -171,6 +178,8 @@ PDATTN_API pdattn_status pdattn_plan(const pdattn_problem* problem, const int32_
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "num_cus and force_workers must be >= 0");
   if ((flags & ~PDATTN_PLAN_BALANCED) != 0) return fail(PDATTN_ERR_INVALID_ARGUMENT, "unknown plan flags %d", flags);
   const bool dyn = balanced(flags);
+  if (dyn && qlen_of(*problem) > 1)
+    return fail(PDATTN_ERR_UNSUPPORTED, "multi-query decode (q_len > 1) needs a static plan");
 
   const int64_t cap = (int64_t)problem->max_pages_per_seq * problem->page_size;
   int64_t tiles = 0, max_len = 0;
@@ -323,6 +332,8 @@ PDATTN_API pdattn_status pdattn_decode(const pdattn_plan_t* plan, const void* q,
   p.max_pages_per_seq = pr.max_pages_per_seq;
   p.num_pages = pr.num_pages;
   p.num_workers = plan->num_workers;
+  p.q_len = qlen_of(pr);
+  p.group_log2 = ilog2(heads_per_kv(pr));
   p.slot_stride = slot_stride_of(pr);
   p.head_stride = head_stride_of(pr);
   p.qk_scale_log2 = pr.scale * 1.44269504088896340736f;
@@ -357,6 +368,8 @@ PDATTN_API pdattn_status pdattn_reduce(const pdattn_plan_t* plan, const void* wo
   p.lse = lse;
   p.num_q_heads = pr.num_q_heads;
   p.num_workers = plan->num_workers;
+  p.q_len = qlen_of(pr);
+  p.group_log2 = ilog2(heads_per_kv(pr));
   hipError_t e = pdattn::launch_merge(p, pr.head_dim, group_of(pr), (uint32_t)plan->num_workers,
                                       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "reduce kernel launch: %s", hipGetErrorString(e));

@@ -295,10 +295,10 @@ struct Tile {
     else return kk * 32 + row * 8;
   }
 
-  // Q as the MFMA B operand: lane (row, col) holds head col (zero for col >=
-  // G) at 8 head_dim positions per k-step. qpair points at q[b][kvh * G][0].
-  __device__ static void load_q(bf16x8 (&qop)[KSTEPS], const uint16_t* qpair, int row, int col) {
-    const uint16_t* qrow = qpair + (long long)min(col, G - 1) * D;
+  // Q as the MFMA B operand: lane (row, col) holds column col's query row
+  // (zero for col >= G) at 8 head_dim positions per k-step. qrow points at
+  // that column's query row (any valid row for col >= G).
+  __device__ static void load_q(bf16x8 (&qop)[KSTEPS], const uint16_t* qrow, int row, int col) {
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + dpos(kk, row));
@@ -347,7 +347,8 @@ struct Tile {
   }
 
   // One tile of the online softmax: tokens tb .. tb+15 of the pair, those
-  // at or past L masked.
+  // at or past L masked (L may differ between columns: lane (row, col)
+  // passes its column's limit).
   __device__ static void compute(State& s, const Frag& f, const bf16x8 (&qop)[KSTEPS], int tb, int L,
                                  float qk_scale_log2, int row) {
     // S[t][g]: lane (row, col) holds head col for tokens row + 4 v
@@ -374,10 +375,13 @@ struct Tile {
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(s.m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(s.m - m_new);
+    // a column with no visible token yet keeps m = -inf; exponents are then
+    // taken against 0, so every weight is exactly 0 (never -inf - -inf)
+    const float m_ref = m_new == -__builtin_inff() ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(s.m - m_ref);
     float pr[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) pr[v] = __builtin_amdgcn_exp2f(sc[v] - m_new);
+    for (int v = 0; v < 4; ++v) pr[v] = __builtin_amdgcn_exp2f(sc[v] - m_ref);
     s.l = s.l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
     const bool grew = m_new > s.m;
     s.m = m_new;
@@ -442,21 +446,26 @@ struct Tile {
       }
   }
 
-  // A whole pair after reduce_rows: out = acc / l, lse = ln 2 (m + log2 l).
-  // o points at out[b][kvh * G][0], lo at lse[b][kvh * G] (or null); row r
-  // writes the heads g with g mod 4 == r.
-  __device__ static void store_out(const State& s, float* o, float* lo, bool poisoned, int row, int col) {
+  // A whole pair after reduce_rows: out = acc / l, lse = ln 2 (m + log2 l);
+  // a column that saw no token (l = 0) gets out = 0, lse = -inf (a NaN l
+  // stays NaN). Column c's
+  // output row is o + row_of(c) * D and its lse lo[row_of(c)] (lo may be
+  // null); row r writes the columns c with c mod 4 == r.
+  template <typename RowOfCol>
+  __device__ static void store_out(const State& s, float* o, float* lo, RowOfCol&& row_of, bool poisoned, int row,
+                                   int col) {
     const float nan = __builtin_nanf("");
     static_for<0, G>([&](auto gc) {
       constexpr int g = decltype(gc)::value;
       const float lg = row_bcast<g>(s.l);
       if (row == (g & 3)) {
-        float* d = o + g * D + col * VE;
+        float* d = o + (long long)row_of(g) * D + col * VE;
 #pragma unroll
-        for (int e = 0; e < VE; ++e) d[e] = poisoned ? nan : s.acc[g][e] / lg;
+        for (int e = 0; e < VE; ++e) d[e] = poisoned ? nan : (lg != 0.0f ? s.acc[g][e] / lg : 0.0f);
       }
     });
-    if (lo != nullptr && row == 0 && col < G) lo[col] = poisoned ? nan : (s.m + log2f(s.l)) * kLn2;
+    if (lo != nullptr && row == 0 && col < G)
+      lo[row_of(col)] = poisoned ? nan : (s.l != 0.0f ? (s.m + log2f(s.l)) * kLn2 : -__builtin_inff());
   }
 
   // A partial record after reduce_rows: m[G], l[G], acc[G][D] (un-normalised).

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_struct_layout_matches_binding():
-    assert pk._lib.pdattn_problem_size() == ctypes.sizeof(pk.Problem) == 40
+    assert pk._lib.pdattn_problem_size() == ctypes.sizeof(pk.Problem) == 44
     assert pk._lib.pdattn_plan_size() == ctypes.sizeof(pk.Plan)
 
 
@@ -47,7 +47,7 @@ def test_status_strings():
 
 def problem(**kw):
     d = dict(batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, max_pages_per_seq=64,
-             num_pages=512, kv_dtype=0, scale=0.0, kv_layout=0)
+             num_pages=512, kv_dtype=0, scale=0.0, kv_layout=0, q_len=0)
     d.update(kw)
     return d
 
@@ -125,6 +125,10 @@ def test_plan_forced_workers_and_empty_batch():
     (dict(page_size=256), [1, 1, 1, 1], UNSUPPORTED),
     (dict(kv_dtype=7), [1, 1, 1, 1], UNSUPPORTED),
     (dict(kv_layout=2), [1, 1, 1, 1], UNSUPPORTED),
+    (dict(q_len=8), [1, 1, 1, 1], UNSUPPORTED),              # 8 rows x 4 heads = 32 columns
+    (dict(q_len=3), [1, 1, 1, 1], UNSUPPORTED),              # 12 columns
+    (dict(q_len=-1), [1, 1, 1, 1], INVALID),
+    (dict(q_len=2, flags=2), [1, 1, 1, 1], UNSUPPORTED),     # multi-query needs a static plan
     (dict(kv_layout=-1), [1, 1, 1, 1], UNSUPPORTED),
     (dict(scale=float("nan")), [1, 1, 1, 1], INVALID),
     (dict(batch=70000), [1] * 4, INVALID),

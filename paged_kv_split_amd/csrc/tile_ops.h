@@ -13,9 +13,19 @@
 //     base 2 with the scale pre-multiplied by log2(e) (same page, utils.cuh):
 //     lane (row r, column g) holds head g for tokens r, r+4, r+8, r+12; the
 //     tile max comes from a local max and two cross-row exchanges.
-//   * p . V on the VALU with fp32 accumulators: lane (row r, chunk c) owns
-//     d-chunk c of tokens r + 4j; their probabilities for head g sit in lane
-//     g of the same 16-lane row and arrive by DPP row broadcast.
+//   * p . V, G <= 8: on the VALU with fp32 accumulators and fp32
+//     probabilities: lane (row r, chunk c) owns d-chunk c of tokens r + 4j;
+//     their probabilities for head g sit in lane g of the same 16-lane row
+//     and arrive by DPP row broadcast.
+//   * p . V, G = 16 (a 16-head group, or query rows x heads = 16): the
+//     probabilities of a tile form a full 16-column x 16-token operand, so
+//     the product runs on v_mfma_f32_16x16x16_bf16 (fp32 accumulation, the
+//     probabilities rounded to bf16: each weight within 2^-9 relative; the
+//     normaliser l and lse stay fp32). The operands need no data movement:
+//     the k index of the product is chosen as k = 4 r + j <-> token r + 4 j,
+//     which is where lane (r, c) already holds column c's probabilities
+//     (A operand) and its V chunk rows (B operand: MFMA number e takes
+//     element e of the lane's chunk, so its n = c stands for d = c VE + e).
 // fp8 pools: e4m3fn bytes widen exactly in registers (to bf16 for the MFMA
 // operand, to fp32 for V) and the per-(token, kv head) scales multiply the
 // score (k) and the probability (v) (OASR "Kernel Layer", FP8 KV variants).
@@ -36,6 +46,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -261,6 +272,10 @@ struct Tile {
   static constexpr int RF = (int)record_floats(D, G);
   static constexpr int EPL = G * D / 64;  // accumulator elements per lane in the merge layout
   using VVec = typename VChunk<VB>::type;
+  // p . V on the matrix cores at 16 columns (see the header): there the
+  // VALU form (G x d/16 x 4 FMAs per lane per tile) makes the step
+  // compute-bound; up to 8 columns it stays memory-bound and exact in fp32
+  static constexpr bool PV_MFMA = G == 16;
   static_assert(K_LD >= 1 && (D == 64 || D == 128), "head_dim");
   static_assert(G >= 1 && G <= 16, "group size");
   static_assert(EPL >= 1 && D % EPL == 0, "merge lane slice");
@@ -268,9 +283,12 @@ struct Tile {
   // Online-softmax state of one piece: running max m (base 2) and sum l of
   // head `col` (every row holds the same after reduce_rows), and acc[g][e]:
   // head g, d = col * VE + e, summed over this row's tokens.
+  // MFMA p . V: cacc[e][v] is column 4 row + v at d = col * VE + e, summed
+  // over all tokens of the piece (acc is then unused, and the reverse).
   struct State {
     float m, l;
-    float acc[G][VE];
+    float acc[PV_MFMA ? 1 : G][VE];
+    f32x4 cacc[PV_MFMA ? VE : 1];
   };
   // One stage read back into registers.
   struct Frag {
@@ -282,10 +300,44 @@ struct Tile {
   __device__ static void reset(State& s) {
     s.m = -__builtin_inff();
     s.l = 0.0f;
+    if constexpr (PV_MFMA) {
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+      for (int e = 0; e < VE; ++e) s.cacc[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    } else {
 #pragma unroll
-      for (int e = 0; e < VE; ++e) s.acc[g][e] = 0.0f;
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < VE; ++e) s.acc[g][e] = 0.0f;
+    }
+  }
+
+  // Value of x in lane (row, 4 row + v): column 4 row + v's copy of a
+  // per-column quantity (m, l, alpha: every row holds the same).
+  __device__ static float col_of_row(float x, int row, int v) { return __shfl(x, 20 * row + v); }
+
+  // Element e of each of the lane's four V chunk rows as the MFMA B operand
+  // (bf16; fp8 codes widen exactly).
+  __device__ static bf16x4 v_operand(const Frag& f, int e) {
+    uint32_t lo, hi;
+    if constexpr (FP8) {
+      const int sh = 8 * (e & 3);
+      const uint32_t b0 = (dword(f.vf[0], e >> 2) >> sh) & 0xffu;
+      const uint32_t b1 = (dword(f.vf[1], e >> 2) >> sh) & 0xffu;
+      const uint32_t b2 = (dword(f.vf[2], e >> 2) >> sh) & 0xffu;
+      const uint32_t b3 = (dword(f.vf[3], e >> 2) >> sh) & 0xffu;
+      const uint32_t w = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+      lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+      hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+    } else {
+      const int sh = 16 * (e & 1);
+      const uint32_t h0 = (dword(f.vf[0], e >> 1) >> sh) & 0xffffu;
+      const uint32_t h1 = (dword(f.vf[1], e >> 1) >> sh) & 0xffffu;
+      const uint32_t h2 = (dword(f.vf[2], e >> 1) >> sh) & 0xffffu;
+      const uint32_t h3 = (dword(f.vf[3], e >> 1) >> sh) & 0xffffu;
+      lo = h0 | (h1 << 16);
+      hi = h2 | (h3 << 16);
+    }
+    return __builtin_bit_cast(bf16x4, u32x2{lo, hi});
   }
 
   // head_dim position of element 0 of lane (row, ·)'s fragment at k-step kk;
@@ -386,16 +438,33 @@ struct Tile {
     const bool grew = m_new > s.m;
     s.m = m_new;
     if (__any(grew)) {
-      static_for<0, G>([&](auto gc) {
-        constexpr int g = decltype(gc)::value;
-        const float a = row_bcast<g>(alpha);
+      if constexpr (PV_MFMA) {
 #pragma unroll
-        for (int e = 0; e < VE; ++e) s.acc[g][e] *= a;
-      });
+        for (int v = 0; v < 4; ++v) {
+          const float a = col_of_row(alpha, row, v);
+#pragma unroll
+          for (int e = 0; e < VE; ++e) s.cacc[e][v] *= a;
+        }
+      } else {
+        static_for<0, G>([&](auto gc) {
+          constexpr int g = decltype(gc)::value;
+          const float a = row_bcast<g>(alpha);
+#pragma unroll
+          for (int e = 0; e < VE; ++e) s.acc[g][e] *= a;
+        });
+      }
     }
     if constexpr (FP8) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) pr[v] *= f.vs[v];
+    }
+    if constexpr (PV_MFMA) {
+      // A: column col's probabilities for tokens row + 4 j, k = 4 row + j
+      const bf16x4 pa = {(__bf16)pr[0], (__bf16)pr[1], (__bf16)pr[2], (__bf16)pr[3]};
+#pragma unroll
+      for (int e = 0; e < VE; ++e)
+        s.cacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, v_operand(f, e), s.cacc[e], 0, 0, 0);
+      return;
     }
     // p . V: lane (row, col) takes V row (token) row + 4 j, d-chunk col
 #pragma unroll
@@ -435,6 +504,7 @@ struct Tile {
   __device__ static void reduce_rows(State& s) {
     s.l += __shfl_xor(s.l, 16);
     s.l += __shfl_xor(s.l, 32);
+    if constexpr (PV_MFMA) return;  // the MFMA already summed over the tile's tokens
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -455,15 +525,29 @@ struct Tile {
   __device__ static void store_out(const State& s, float* o, float* lo, RowOfCol&& row_of, bool poisoned, int row,
                                    int col) {
     const float nan = __builtin_nanf("");
-    static_for<0, G>([&](auto gc) {
-      constexpr int g = decltype(gc)::value;
-      const float lg = row_bcast<g>(s.l);
-      if (row == (g & 3)) {
-        float* d = o + (long long)row_of(g) * D + col * VE;
+    if constexpr (PV_MFMA) {
+      // lane (row, col) holds columns 4 row + v at d = col * VE + e
 #pragma unroll
-        for (int e = 0; e < VE; ++e) d[e] = poisoned ? nan : (lg != 0.0f ? s.acc[g][e] / lg : 0.0f);
+      for (int v = 0; v < 4; ++v) {
+        const float lg = col_of_row(s.l, row, v);
+        const int c = 4 * row + v;
+        if (c < G) {
+          float* d = o + (long long)row_of(c) * D + col * VE;
+#pragma unroll
+          for (int e = 0; e < VE; ++e) d[e] = poisoned ? nan : (lg != 0.0f ? s.cacc[e][v] / lg : 0.0f);
+        }
       }
-    });
+    } else {
+      static_for<0, G>([&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        const float lg = row_bcast<g>(s.l);
+        if (row == (g & 3)) {
+          float* d = o + (long long)row_of(g) * D + col * VE;
+#pragma unroll
+          for (int e = 0; e < VE; ++e) d[e] = poisoned ? nan : (lg != 0.0f ? s.acc[g][e] / lg : 0.0f);
+        }
+      });
+    }
     if (lo != nullptr && row == 0 && col < G)
       lo[row_of(col)] = poisoned ? nan : (s.l != 0.0f ? (s.m + log2f(s.l)) * kLn2 : -__builtin_inff());
   }
@@ -475,7 +559,17 @@ struct Tile {
   template <bool COHERENT = false>
   __device__ static void store_record(const State& s, float* r, bool poisoned, int row, int col) {
     const float nan = __builtin_nanf("");
-    if constexpr (COHERENT) {
+    if constexpr (PV_MFMA) {
+      // every lane holds distinct values: columns 4 row + v, d = col * VE + e
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int c = 4 * row + v;
+        if (c < G) {
+#pragma unroll
+          for (int e = 0; e < VE; ++e) put<COHERENT>(r + 2 * G + c * D + col * VE + e, poisoned ? nan : s.cacc[e][v]);
+        }
+      }
+    } else if constexpr (COHERENT) {
       // every row holds the totals: row 0 writes all heads (lane-dependent
       // head choices would move the accumulators to scratch memory here)
       if (row == 0) {

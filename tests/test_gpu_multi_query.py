@@ -94,6 +94,11 @@ def test_multi_query_cut_pairs_match_oracle(force):
 
 
 def test_rows_equal_one_token_decodes_with_shifted_lengths():
+    """With 16 columns (4 rows x 4 heads) the kernel forms p . V on the
+    matrix cores from bf16-rounded probabilities (each within 2^-9 of its
+    fp32 value); the one-token decodes (4 columns) keep fp32 probabilities.
+    So |difference| <= 2^-9 * sum_t p_t |V_t| / l <= 2^-9 * max |V| (plus
+    fp32 summation order); lse is formed from fp32 probabilities in both."""
     pk = _pk()
     n = 4
     inp = _inputs("llama3_8b", LENS, n, seed=13)
@@ -105,7 +110,9 @@ def test_rows_equal_one_token_decodes_with_shifted_lengths():
         o1, l1 = pk.paged_decode(inp["q4"][:, i].contiguous().to(DEV), d["k_pages"], d["v_pages"], d["block_table"],
                                  lens_i.to(DEV), context_lens_host=lens_i)
         torch.cuda.synchronize()
-        assert float((out[:, i] - o1.cpu()).abs().max()) <= 1e-5, i
+        vv = inp["v_pages"].float()
+        vmax = float(vv[torch.isfinite(vv)].abs().max())   # unreferenced pages hold NaN
+        assert float((out[:, i] - o1.cpu()).abs().max()) <= 2.0 ** -9 * vmax + 1e-5, i
         assert torch.equal(torch.isneginf(lse[:, i]), torch.isneginf(l1.cpu())), i
         fin = torch.isfinite(l1.cpu())
         assert float((lse[:, i][fin] - l1.cpu()[fin]).abs().max()) <= 1e-5, i

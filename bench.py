@@ -213,6 +213,47 @@ def time_multi_query(pk, w, inp, args, flush, dev, n=4, reps=30):
             "query_rows_per_s": round(w.batch * n * w.num_q_heads / (us * 1e-6), 0)}
 
 
+def time_d256(pk, w, args, flush, dev, reps=30):
+    """The same workload with head_dim 256 (twice the KV bytes): mean step
+    time (decode + reduce, one event pair) and KV GB/s."""
+    import torch
+    import synth
+    w2 = w.with_(head_dim=256)
+    inp = synth.make_inputs(w2)
+    laid = synth.to_hnd(inp) if args.layout == "hnd" else inp
+    d = {k: (laid[k].to(dev) if laid[k] is not None else None)
+         for k in ("q", "k_pages", "v_pages", "k_scale", "v_scale", "block_table", "context_lens")}
+    pl = pk.plan(batch=w2.batch, num_q_heads=w2.num_q_heads, num_kv_heads=w2.num_kv_heads, head_dim=256,
+                 page_size=w2.page_size, max_pages_per_seq=inp["block_table"].shape[1],
+                 num_pages=inp["k_pages"].shape[0], kv_dtype=pk.KV_BF16 if w2.kv_dtype == "bf16" else pk.KV_FP8_E4M3,
+                 context_lens_host=inp["context_lens"],
+                 kv_layout=pk.LAYOUT_HND if args.layout == "hnd" else pk.LAYOUT_NHD)
+    out = torch.empty((w2.batch, w2.num_q_heads, 256), dtype=torch.float32, device=dev)
+    lse = torch.empty((w2.batch, w2.num_q_heads), dtype=torch.float32, device=dev)
+    ws = pk.workspace(pl, dev)
+
+    def step():
+        pk.decode(pl, d["q"], d["k_pages"], d["v_pages"], d["k_scale"], d["v_scale"], d["block_table"],
+                  d["context_lens"], ws, out, lse)
+        pk.reduce(pl, ws, out, lse)
+    for _ in range(5):
+        step()
+    ts = []
+    for i in range(reps):
+        flush.fill_(i & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3)
+    kvb = synth.kv_bytes(w2, inp["context_lens"])
+    us = statistics.fmean(ts)
+    del d, ws, inp, laid
+    return {"kv_bytes": kvb, "us_per_call": round(us, 2), "gbs": round(kvb / (us * 1e-6) / 1e9, 1),
+            "workers": pl.num_workers}
+
+
 def time_merge(pk, flush, dev, reps=20):
     """pdattn_merge timings (secondary figures): a two-piece cascade (shared
     prefix + suffix) over the Llama-3-8B decode rows (32 x 32 rows, d128)
@@ -262,6 +303,7 @@ def main():
     ap.add_argument("--no-append", action="store_true", help="skip the KV-append timings")
     ap.add_argument("--no-merge", action="store_true", help="skip the partial-state merge timings")
     ap.add_argument("--no-multi-query", action="store_true", help="skip the multi-query decode timing")
+    ap.add_argument("--no-d256", action="store_true", help="skip the head_dim 256 timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run 3 device copies of 256 MiB (a plain copy kernel of known "
                          "size, for scaling the HBM byte counters)")
@@ -394,6 +436,7 @@ def main():
     append = None if args.no_append else time_append(pk, w, flush, dev, layout)
     merge = None if args.no_merge else time_merge(pk, flush, dev)
     multi = None if args.no_multi_query else time_multi_query(pk, w, inp, args, flush, dev)
+    d256 = None if args.no_d256 else time_d256(pk, w, args, flush, dev)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -458,6 +501,7 @@ def main():
         "kv_append": append,
         "merge": merge,
         "multi_query": multi,
+        "head_dim_256": d256,
     }
     print(json.dumps(rec), flush=True)
 

@@ -58,7 +58,8 @@
  *   out          fp32 [B][Hq][d]
  *   lse          fp32 [B][Hq], optional (NULL to skip)
  *
- * Supported: d in {64, 128}; G in {1, 2, 4, 8, 16} (and n * G in that set);
+ * Supported: d in {64, 128, 256} (256: static plans); G in {1, 2, 4, 8, 16}
+ * (and n * G in that set);
  * P a power of two in [8, 128]; q / k / v / out bases 16-byte aligned;
  * B <= 65535.
  *

@@ -349,7 +349,8 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(MergeParams p) 
     for (int k = 0; k < EPL; ++k) A[k] = A[k] * so + ai[k] * si;
     M = Mn;
   };
-  constexpr int U = kMergeUnroll;
+  // pieces in flight per step: fewer when a lane's slice is long
+  constexpr int U = EPL >= 32 ? 1 : (EPL >= 16 ? 2 : kMergeUnroll);
   for (long long i = wave; i < n; i += U * kMergeWaves) {
     // U pieces per step (every fourth piece from i), all loads issued first
     float mu[U], lu[U], au[U][EPL];
@@ -454,6 +455,7 @@ hipError_t launch_merge_d(const MergeParams& p, int group, uint32_t grid, hipStr
 int decode_wgs_per_cu(int head_dim, int group, bool fp8) {
   if (head_dim == 64) return fp8 ? occupancy_group<64, true>(group) : occupancy_group<64, false>(group);
   if (head_dim == 128) return fp8 ? occupancy_group<128, true>(group) : occupancy_group<128, false>(group);
+  if (head_dim == 256) return fp8 ? occupancy_group<256, true>(group) : occupancy_group<256, false>(group);
   return 0;
 }
 
@@ -463,12 +465,15 @@ hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, bool fp
                                  : launch_group<64, false>(p, group, grid, stream);
   if (head_dim == 128) return fp8 ? launch_group<128, true>(p, group, grid, stream)
                                   : launch_group<128, false>(p, group, grid, stream);
+  if (head_dim == 256) return fp8 ? launch_group<256, true>(p, group, grid, stream)
+                                  : launch_group<256, false>(p, group, grid, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_merge(const MergeParams& p, int head_dim, int group, uint32_t grid, hipStream_t stream) {
   if (head_dim == 64) return launch_merge_d<64>(p, group, grid, stream);
   if (head_dim == 128) return launch_merge_d<128>(p, group, grid, stream);
+  if (head_dim == 256) return launch_merge_d<256>(p, group, grid, stream);
   return hipErrorInvalidValue;
 }
 

@@ -52,7 +52,7 @@ constexpr int dynamic_lds_bytes(int head_dim, int group, bool fp8) {
 // workgroup), from upper bounds of the builds' register counts.
 constexpr int decode_wgs_per_cu_estimate(int head_dim, int group, bool fp8, bool dynamic) {
   const int by_lds = (160 * 1024) / (dynamic ? dynamic_lds_bytes(head_dim, group, fp8) : decode_lds_bytes(head_dim, fp8));
-  const int vgprs = group >= 8 ? 256 : 168;
+  const int vgprs = head_dim == 256 ? (group >= 16 ? 512 : 256) : (group >= 8 ? 256 : 168);
   const int by_vgpr = 512 / vgprs;
   const int n = by_lds < by_vgpr ? by_lds : by_vgpr;
   return n < 1 ? 1 : n;

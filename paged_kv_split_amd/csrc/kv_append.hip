@@ -27,9 +27,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // lane; each lane keeps kBatch chunks of K and of V in flight.
 constexpr int kBatch = 2;
 
-// Max over aligned groups of L lanes (L = 8 or 16) with DPP lane moves:
+// Max over aligned groups of L lanes (L = 8, 16 or 32) with DPP lane moves:
 // swap neighbours, swap pairs, mirror each 8-lane half, mirror each 16-lane
-// row.
+// row; then (L = 32) the neighbouring 16-lane row.
 template <int Ctrl>
 __device__ inline float dpp_move(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), Ctrl, 0xF, 0xF, false));
@@ -40,7 +40,8 @@ __device__ inline float group_max(float v) {
   v = fmaxf(v, dpp_move<0xB1>(v));   // quad_perm [1, 0, 3, 2]
   v = fmaxf(v, dpp_move<0x4E>(v));   // quad_perm [2, 3, 0, 1]
   v = fmaxf(v, dpp_move<0x141>(v));  // row_half_mirror
-  if constexpr (L == 16) v = fmaxf(v, dpp_move<0x140>(v));  // row_mirror
+  if constexpr (L >= 16) v = fmaxf(v, dpp_move<0x140>(v));  // row_mirror
+  if constexpr (L == 32) v = fmaxf(v, __shfl_xor(v, 16));     // the neighbouring row
   return v;
 }
 
@@ -256,6 +257,7 @@ hipError_t launch_kv_append(const AppendParams& p, int head_dim, bool fp8, uint3
   switch (head_dim) {
     case 64: return launch_d<64>(p, fp8, grid, stream);
     case 128: return launch_d<128>(p, fp8, grid, stream);
+    case 256: return launch_d<256>(p, fp8, grid, stream);
   }
   return hipErrorInvalidValue;
 }

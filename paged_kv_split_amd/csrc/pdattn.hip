@@ -54,8 +54,8 @@ pdattn_status check_problem(const pdattn_problem* p) {
   const int cols = g * (p->q_len > 1 ? p->q_len : 1);
   if (cols != 1 && cols != 2 && cols != 4 && cols != 8 && cols != 16)
     return fail(PDATTN_ERR_UNSUPPORTED, "q_len * group size = %d not in {1, 2, 4, 8, 16}", cols);
-  if (p->head_dim != 64 && p->head_dim != 128)
-    return fail(PDATTN_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", p->head_dim);
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
+    return fail(PDATTN_ERR_UNSUPPORTED, "head_dim %d not in {64, 128, 256}", p->head_dim);
   if (!is_pow2(p->page_size) || p->page_size < 8 || p->page_size > 128)
     return fail(PDATTN_ERR_UNSUPPORTED, "page_size %d is not a power of two in [8, 128]", p->page_size);
   if (p->max_pages_per_seq < 0 || p->num_pages < 0)
@@ -121,10 +121,10 @@ uint64_t workspace_for(const pdattn_problem& p, int64_t workers, int32_t flags) 
 // device, from the runtime's occupancy query (cached: the query costs
 // milliseconds), 0 if it cannot be asked.
 int wgs_per_cu_cached(int device, int head_dim, int group, bool fp8, bool dyn) {
-  static std::atomic<int> cache[64][2][5][2][2];
+  static std::atomic<int> cache[64][3][5][2][2];
   if (device < 0 || device >= 64) return 0;
   const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : group == 8 ? 3 : 4;
-  std::atomic<int>& slot = cache[device][head_dim == 128][gi][fp8][dyn];
+  std::atomic<int>& slot = cache[device][head_dim == 256 ? 2 : head_dim == 128 ? 1 : 0][gi][fp8][dyn];
   int v = slot.load(std::memory_order_relaxed);
   if (v > 0) return v;
   v = dyn ? pdattn::dynamic_wgs_per_cu(head_dim, group, fp8) : pdattn::decode_wgs_per_cu(head_dim, group, fp8);
@@ -139,7 +139,8 @@ pdattn_status check_plan(const pdattn_plan_t* plan) {
   if (st != PDATTN_OK) return fail(PDATTN_ERR_PLAN_MISMATCH, "plan holds an invalid problem: %s", g_last_error);
   if (plan->num_workers < 1 || plan->num_workgroups < 1 ||
       (int64_t)plan->num_workgroups * pdattn::kWaves < plan->num_workers ||
-      (plan->flags & ~PDATTN_PLAN_BALANCED) != 0 || (balanced(plan->flags) && qlen_of(plan->problem) > 1) ||
+      (plan->flags & ~PDATTN_PLAN_BALANCED) != 0 ||
+      (balanced(plan->flags) && (qlen_of(plan->problem) > 1 || plan->problem.head_dim == 256)) ||
       plan->workspace_bytes != workspace_for(plan->problem, plan->num_workers, plan->flags))
     return fail(PDATTN_ERR_PLAN_MISMATCH, "plan fields are inconsistent");
   return PDATTN_OK;
@@ -180,6 +181,7 @@ PDATTN_API pdattn_status pdattn_plan(const pdattn_problem* problem, const int32_
   const bool dyn = balanced(flags);
   if (dyn && qlen_of(*problem) > 1)
     return fail(PDATTN_ERR_UNSUPPORTED, "multi-query decode (q_len > 1) needs a static plan");
+  if (dyn && problem->head_dim == 256) return fail(PDATTN_ERR_UNSUPPORTED, "head_dim 256 needs a static plan");
 
   const int64_t cap = (int64_t)problem->max_pages_per_seq * problem->page_size;
   int64_t tiles = 0, max_len = 0;

@@ -44,6 +44,7 @@ namespace dev {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -83,6 +84,8 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
 
 template <int VB>
 struct VChunk;
+template <>
+struct VChunk<32> { using type = u32x8; };
 template <>
 struct VChunk<16> { using type = u32x4; };
 template <>
@@ -175,6 +178,56 @@ __device__ __forceinline__ void read_stage(const unsigned char* kp, const unsign
           "=&v"(vf[3])
         : "v"(ka), "v"(va)
         : "memory");
+  } else if constexpr (!FP8 && D == 256) {  // row 512 B: 8 K fragments, 32-byte V chunks 2048 B apart
+    u32x4 h[8];
+    asm volatile(
+        "ds_read_b128 %0, %16\n\t"
+        "ds_read_b128 %1, %16 offset:1024\n\t"
+        "ds_read_b128 %2, %16 offset:2048\n\t"
+        "ds_read_b128 %3, %16 offset:3072\n\t"
+        "ds_read_b128 %4, %16 offset:4096\n\t"
+        "ds_read_b128 %5, %16 offset:5120\n\t"
+        "ds_read_b128 %6, %16 offset:6144\n\t"
+        "ds_read_b128 %7, %16 offset:7168\n\t"
+        "ds_read_b128 %8, %17\n\t"
+        "ds_read_b128 %9, %17 offset:16\n\t"
+        "ds_read_b128 %10, %17 offset:2048\n\t"
+        "ds_read_b128 %11, %17 offset:2064\n\t"
+        "ds_read_b128 %12, %17 offset:4096\n\t"
+        "ds_read_b128 %13, %17 offset:4112\n\t"
+        "ds_read_b128 %14, %17 offset:6144\n\t"
+        "ds_read_b128 %15, %17 offset:6160\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3]), "=&v"(kf[4]), "=&v"(kf[5]), "=&v"(kf[6]),
+          "=&v"(kf[7]), "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3]), "=&v"(h[4]), "=&v"(h[5]), "=&v"(h[6]),
+          "=&v"(h[7])
+        : "v"(ka), "v"(va)
+        : "memory");
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vf[j] = __builtin_shufflevector(h[2 * j], h[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+  } else if constexpr (FP8 && D == 256) {  // row 256 B: 4 K fragments, 16-byte V chunks 1024 B apart, scales
+    f32x4 a, c;
+    asm volatile(
+        "ds_read_b128 %0, %10\n\t"
+        "ds_read_b128 %1, %10 offset:1024\n\t"
+        "ds_read_b128 %2, %10 offset:2048\n\t"
+        "ds_read_b128 %3, %10 offset:3072\n\t"
+        "ds_read_b128 %4, %11\n\t"
+        "ds_read_b128 %5, %11 offset:1024\n\t"
+        "ds_read_b128 %6, %11 offset:2048\n\t"
+        "ds_read_b128 %7, %11 offset:3072\n\t"
+        "ds_read_b128 %8, %12\n\t"
+        "ds_read_b128 %9, %12 offset:64\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3]), "=&v"(vf[0]), "=&v"(vf[1]), "=&v"(vf[2]),
+          "=&v"(vf[3]), "=&v"(a), "=&v"(c)
+        : "v"(ka), "v"(va), "v"(sa)
+        : "memory");
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      ks[v] = a[v];
+      vs[v] = c[v];
+    }
   } else if constexpr (!FP8 && D == 64) {  // row 128 B: 2 K fragments, 8-byte V chunks 512 B apart
     asm volatile(
         "ds_read_b128 %0, %6\n\t"
@@ -276,7 +329,7 @@ struct Tile {
   // VALU form (G x d/16 x 4 FMAs per lane per tile) makes the step
   // compute-bound; up to 8 columns it stays memory-bound and exact in fp32
   static constexpr bool PV_MFMA = G == 16;
-  static_assert(K_LD >= 1 && (D == 64 || D == 128), "head_dim");
+  static_assert(K_LD >= 1 && (D == 64 || D == 128 || D == 256), "head_dim");
   static_assert(G >= 1 && G <= 16, "group size");
   static_assert(EPL >= 1 && D % EPL == 0, "merge lane slice");
 

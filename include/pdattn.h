@@ -23,8 +23,8 @@
  * no position gets out = 0 and lse = -inf. q, out and lse then carry a row
  * axis: q [B][n][Hq][d], out [B][n][Hq][d], lse [B][n][Hq]. The kernel
  * treats the n * G (row, head) pairs of a kv head as the columns of one
- * MFMA operand, so n * G must be one of 1, 2, 4, 8, 16; the K/V bytes read
- * are those of one decode step. Static plans only (not PDATTN_PLAN_BALANCED).
+ * MFMA operand, so n * G must be at most 16; the K/V bytes read are those
+ * of one decode step. Static plans only (not PDATTN_PLAN_BALANCED).
  *
  * Work decomposition (flash-decoding): the (b, kvh) pairs are laid end to
  * end, each cut into 16-token tiles, and a persistent grid of
@@ -58,8 +58,9 @@
  *   out          fp32 [B][Hq][d]
  *   lse          fp32 [B][Hq], optional (NULL to skip)
  *
- * Supported: d in {64, 128, 256} (256: static plans); G in {1, 2, 4, 8, 16}
- * (and n * G in that set);
+ * Supported: d in {64, 128, 256} (256: static plans); any G <= 16 (and
+ * n * G <= 16; a G that is not a power of two: static plans): the kernel
+ * instance has the next power of two of columns, the rest padding;
  * P a power of two in [8, 128]; q / k / v / out bases 16-byte aligned;
  * B <= 65535.
  *
@@ -91,7 +92,7 @@ extern "C" {
 typedef enum pdattn_status {
   PDATTN_OK = 0,
   PDATTN_ERR_INVALID_ARGUMENT = 1, /* null or misaligned pointer, bad shape or length */
-  PDATTN_ERR_UNSUPPORTED = 2,      /* head_dim, group size, page size or dtype not built */
+  PDATTN_ERR_UNSUPPORTED = 2,      /* head_dim, group size, page size, dtype or mode not built */
   PDATTN_ERR_WORKSPACE = 3,        /* workspace missing or smaller than plan->workspace_bytes */
   PDATTN_ERR_PLAN_MISMATCH = 4,    /* plan not produced by pdattn_plan */
   PDATTN_ERR_DEVICE = 5            /* HIP runtime error; detail in pdattn_last_error() */

@@ -536,7 +536,7 @@ void decode_dynamic_kernel(DynParams p) {
     const UnitRef r = cu;
     auto rec_from_state = [&](float* dst) { TL::template store_record<true>(st, dst, poisoned, row, col); };
     auto out_from_state = [&](float* o, float* lo) {
-      TL::store_out(st, o, lo, [](int c) { return c; }, poisoned, row, col);
+      TL::store_out(st, o, lo, [](int c) { return c; }, G, poisoned, row, col);
     };
     if (my_tiles == r.n) {  // this wave did the whole unit
       emit_unit(r, rec_from_state, out_from_state);
@@ -597,7 +597,7 @@ void decode_dynamic_kernel(DynParams p) {
     if (piece != piece_c) {
       if (piece_c >= 0) finish_piece();
       cu = r;
-      TL::load_q(qop, p.q + ((long long)cu.b * Hq + cu.kvh * G + min(col, G - 1)) * D, row, col);
+      TL::load_q(qop, p.q + ((long long)cu.b * Hq + cu.kvh * G + min(col, G - 1)) * D, row, col, G);
 #pragma unroll
       for (int kk = 0; kk < TL::KSTEPS; ++kk) asm volatile("" : "+v"(qop[kk]));  // q in registers before the run
       TL::reset(st);

@@ -185,18 +185,18 @@ void decode_kernel(DecodeParams p) {
       const bool reaches_end = j + seg == nt;
       const int s0 = j * kTileTokens;
       const int s1 = min(L, (j + seg) * kTileTokens);
-      // Column c of the G = q_len * 2^group_log2 columns is query row
-      // c >> group_log2 of head (kvh << group_log2) + (c & mask); its rows of
-      // q, out and lse sit (c >> group_log2) * Hq + (c & mask) rows past
-      // base_row. Query row i sees the positions before L - (q_len - 1 - i).
-      const int qmask = (1 << p.group_log2) - 1;
-      auto col_row = [&](int c) { return (c >> p.group_log2) * Hq + (c & qmask); };
-      const long long base_row = (long long)b * p.q_len * Hq + ((long long)kvh << p.group_log2);
-      const int cl = min(col, G - 1);
-      const int lim = min(s1, L - (p.q_len - 1 - (cl >> p.group_log2)));
+      // Column c < num_cols = q_len * Gh (the rest of the G columns pad) is
+      // query row c / Gh of head kvh * Gh + c % Gh; its rows of q, out and
+      // lse sit (c / Gh) * Hq + c % Gh rows past base_row. Query row i sees
+      // the positions before L - (q_len - 1 - i).
+      const int Gh = p.heads_per_kv;
+      auto col_row = [&](int c) { return (c / Gh) * Hq + c % Gh; };
+      const long long base_row = (long long)b * p.q_len * Hq + (long long)kvh * Gh;
+      const int cl = min(col, p.num_cols - 1);
+      const int lim = min(s1, L - (p.q_len - 1 - cl / Gh));
 
       bf16x8 qop[TL::KSTEPS];
-      TL::load_q(qop, p.q + (base_row + col_row(cl)) * D, row, col);
+      TL::load_q(qop, p.q + (base_row + col_row(cl)) * D, row, col, p.num_cols);
       typename TL::State st;
       TL::reset(st);
       int bad = 0;
@@ -249,7 +249,7 @@ void decode_kernel(DecodeParams p) {
       TL::reduce_rows(st);
       const bool poisoned = __any(bad);
       if (!cut_start && reaches_end) {
-        TL::store_out(st, p.out + base_row * D, p.lse ? p.lse + base_row : nullptr, col_row,
+        TL::store_out(st, p.out + base_row * D, p.lse ? p.lse + base_row : nullptr, col_row, p.num_cols,
                       poisoned, row, col);
       } else {
         // a piece of a cut pair: record (m, l, acc); slot 0 for the wave's
@@ -388,10 +388,13 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(MergeParams p) 
       Av += wq * s_acc[q][e];
       Ls += wq * s_l[q][gg];
     }
-    // column gg: query row gg >> group_log2 of head (kvh << group_log2) +
-    // (gg & mask); a column that saw no token (Ls = 0) gets 0 and -inf
-    const long long bh = (long long)b * p.q_len * p.num_q_heads + ((long long)kvh << p.group_log2) +
-                         (gg >> p.group_log2) * p.num_q_heads + (gg & ((1 << p.group_log2) - 1));
+    // column gg < num_cols: query row gg / Gh of head kvh * Gh + gg % Gh
+    // (padding columns are not written); a column that saw no token
+    // (Ls = 0) gets 0 and -inf
+    if (gg >= p.num_cols) continue;
+    const int Gh = p.heads_per_kv;
+    const long long bh = (long long)b * p.q_len * p.num_q_heads + (long long)kvh * Gh +
+                         (long long)(gg / Gh) * p.num_q_heads + gg % Gh;
     // (a NaN sum, from a poisoned piece, stays NaN)
     p.out[bh * D + (e % D)] = Ls != 0.0f ? Av / Ls : 0.0f;
     if (e % D == 0 && p.lse != nullptr) p.lse[bh] = Ls != 0.0f ? (Mx + log2f(Ls)) * kLn2 : -__builtin_inff();

@@ -80,8 +80,9 @@ struct DecodeParams {
   int32_t max_pages_per_seq;
   int32_t num_pages;
   int32_t num_workers;        // waves of the grid that own tile ranges
-  int32_t q_len;              // query rows per sequence (n); the kernel's G columns are n * 2^group_log2
-  int32_t group_log2;         // log2 of the query heads per kv head
+  int32_t q_len;              // query rows per sequence (n)
+  int32_t heads_per_kv;       // query heads per kv head (Gh)
+  int32_t num_cols;           // valid columns n * Gh (<= the kernel's G; the rest is padding)
   int32_t slot_stride;        // row index = page * P * Hkv + slot * slot_stride + kvh * head_stride
   int32_t head_stride;        // (Hkv, 1): rows [page][slot][kvh]; (1, P): rows [page][kvh][slot]
   float qk_scale_log2;        // softmax scale * log2(e)
@@ -124,7 +125,8 @@ struct MergeParams {
   int32_t num_q_heads;
   int32_t num_workers;
   int32_t q_len;              // as in DecodeParams
-  int32_t group_log2;
+  int32_t heads_per_kv;
+  int32_t num_cols;
 };
 
 // Resident workgroups per compute unit of one decode instantiation, from the

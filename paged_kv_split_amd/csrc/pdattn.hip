@@ -48,12 +48,10 @@ pdattn_status check_problem(const pdattn_problem* p) {
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "num_q_heads %d is not a multiple of num_kv_heads %d",
                 p->num_q_heads, p->num_kv_heads);
   const int g = p->num_q_heads / p->num_kv_heads;
-  if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16)
-    return fail(PDATTN_ERR_UNSUPPORTED, "group size %d not in {1, 2, 4, 8, 16}", g);
+  if (g > 16) return fail(PDATTN_ERR_UNSUPPORTED, "group size %d above 16", g);
   if (p->q_len < 0 || p->q_len > 16) return fail(PDATTN_ERR_INVALID_ARGUMENT, "q_len %d outside [0, 16]", p->q_len);
   const int cols = g * (p->q_len > 1 ? p->q_len : 1);
-  if (cols != 1 && cols != 2 && cols != 4 && cols != 8 && cols != 16)
-    return fail(PDATTN_ERR_UNSUPPORTED, "q_len * group size = %d not in {1, 2, 4, 8, 16}", cols);
+  if (cols > 16) return fail(PDATTN_ERR_UNSUPPORTED, "q_len * group size = %d above 16", cols);
   if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
     return fail(PDATTN_ERR_UNSUPPORTED, "head_dim %d not in {64, 128, 256}", p->head_dim);
   if (!is_pow2(p->page_size) || p->page_size < 8 || p->page_size > 128)
@@ -72,8 +70,15 @@ pdattn_status check_problem(const pdattn_problem* p) {
 
 int qlen_of(const pdattn_problem& p) { return p.q_len > 1 ? p.q_len : 1; }
 int heads_per_kv(const pdattn_problem& p) { return p.num_q_heads / p.num_kv_heads; }
-// Columns of a kernel instantiation: the (query row, head) pairs of one kv head.
-int group_of(const pdattn_problem& p) { return heads_per_kv(p) * qlen_of(p); }
+// Valid columns: the (query row, head) pairs of one kv head; a kernel
+// instantiation has the next power of two (the rest are padding).
+int cols_of(const pdattn_problem& p) { return heads_per_kv(p) * qlen_of(p); }
+int group_of(const pdattn_problem& p) {
+  int c = 1;
+  while (c < cols_of(p)) c <<= 1;
+  return c;
+}
+bool pow2_heads(const pdattn_problem& p) { return is_pow2(heads_per_kv(p)); }
 
 // Row strides of the pools: row index = page * P * Hkv + slot * slot_stride
 // + kvh * head_stride.
@@ -140,7 +145,8 @@ pdattn_status check_plan(const pdattn_plan_t* plan) {
   if (plan->num_workers < 1 || plan->num_workgroups < 1 ||
       (int64_t)plan->num_workgroups * pdattn::kWaves < plan->num_workers ||
       (plan->flags & ~PDATTN_PLAN_BALANCED) != 0 ||
-      (balanced(plan->flags) && (qlen_of(plan->problem) > 1 || plan->problem.head_dim == 256)) ||
+      (balanced(plan->flags) &&
+       (qlen_of(plan->problem) > 1 || plan->problem.head_dim == 256 || !pow2_heads(plan->problem))) ||
       plan->workspace_bytes != workspace_for(plan->problem, plan->num_workers, plan->flags))
     return fail(PDATTN_ERR_PLAN_MISMATCH, "plan fields are inconsistent");
   return PDATTN_OK;
@@ -182,6 +188,8 @@ PDATTN_API pdattn_status pdattn_plan(const pdattn_problem* problem, const int32_
   if (dyn && qlen_of(*problem) > 1)
     return fail(PDATTN_ERR_UNSUPPORTED, "multi-query decode (q_len > 1) needs a static plan");
   if (dyn && problem->head_dim == 256) return fail(PDATTN_ERR_UNSUPPORTED, "head_dim 256 needs a static plan");
+  if (dyn && !pow2_heads(*problem))
+    return fail(PDATTN_ERR_UNSUPPORTED, "a group size that is not a power of two needs a static plan");
 
   const int64_t cap = (int64_t)problem->max_pages_per_seq * problem->page_size;
   int64_t tiles = 0, max_len = 0;
@@ -335,7 +343,8 @@ PDATTN_API pdattn_status pdattn_decode(const pdattn_plan_t* plan, const void* q,
   p.num_pages = pr.num_pages;
   p.num_workers = plan->num_workers;
   p.q_len = qlen_of(pr);
-  p.group_log2 = ilog2(heads_per_kv(pr));
+  p.heads_per_kv = heads_per_kv(pr);
+  p.num_cols = cols_of(pr);
   p.slot_stride = slot_stride_of(pr);
   p.head_stride = head_stride_of(pr);
   p.qk_scale_log2 = pr.scale * 1.44269504088896340736f;
@@ -371,7 +380,8 @@ PDATTN_API pdattn_status pdattn_reduce(const pdattn_plan_t* plan, const void* wo
   p.num_q_heads = pr.num_q_heads;
   p.num_workers = plan->num_workers;
   p.q_len = qlen_of(pr);
-  p.group_log2 = ilog2(heads_per_kv(pr));
+  p.heads_per_kv = heads_per_kv(pr);
+  p.num_cols = cols_of(pr);
   hipError_t e = pdattn::launch_merge(p, pr.head_dim, group_of(pr), (uint32_t)plan->num_workers,
                                       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "reduce kernel launch: %s", hipGetErrorString(e));

@@ -401,13 +401,14 @@ struct Tile {
   }
 
   // Q as the MFMA B operand: lane (row, col) holds column col's query row
-  // (zero for col >= G) at 8 head_dim positions per k-step. qrow points at
-  // that column's query row (any valid row for col >= G).
-  __device__ static void load_q(bf16x8 (&qop)[KSTEPS], const uint16_t* qrow, int row, int col) {
+  // (zero for col >= ncols: padding columns) at 8 head_dim positions per
+  // k-step. qrow points at that column's query row (any valid row for a
+  // padding column).
+  __device__ static void load_q(bf16x8 (&qop)[KSTEPS], const uint16_t* qrow, int row, int col, int ncols) {
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + dpos(kk, row));
-      if (col >= G) raw = u32x4{0u, 0u, 0u, 0u};
+      if (col >= ncols) raw = u32x4{0u, 0u, 0u, 0u};
       qop[kk] = __builtin_bit_cast(bf16x8, raw);
     }
   }
@@ -571,12 +572,12 @@ struct Tile {
 
   // A whole pair after reduce_rows: out = acc / l, lse = ln 2 (m + log2 l);
   // a column that saw no token (l = 0) gets out = 0, lse = -inf (a NaN l
-  // stays NaN). Column c's
-  // output row is o + row_of(c) * D and its lse lo[row_of(c)] (lo may be
-  // null); row r writes the columns c with c mod 4 == r.
+  // stays NaN). Column c < ncols has its output row at o + row_of(c) * D and
+  // its lse at lo[row_of(c)] (lo may be null); padding columns are not
+  // written; row r writes the columns c with c mod 4 == r.
   template <typename RowOfCol>
-  __device__ static void store_out(const State& s, float* o, float* lo, RowOfCol&& row_of, bool poisoned, int row,
-                                   int col) {
+  __device__ static void store_out(const State& s, float* o, float* lo, RowOfCol&& row_of, int ncols, bool poisoned,
+                                   int row, int col) {
     const float nan = __builtin_nanf("");
     if constexpr (PV_MFMA) {
       // lane (row, col) holds columns 4 row + v at d = col * VE + e
@@ -584,7 +585,7 @@ struct Tile {
       for (int v = 0; v < 4; ++v) {
         const float lg = col_of_row(s.l, row, v);
         const int c = 4 * row + v;
-        if (c < G) {
+        if (c < ncols) {
           float* d = o + (long long)row_of(c) * D + col * VE;
 #pragma unroll
           for (int e = 0; e < VE; ++e) d[e] = poisoned ? nan : (lg != 0.0f ? s.cacc[e][v] / lg : 0.0f);
@@ -594,14 +595,14 @@ struct Tile {
       static_for<0, G>([&](auto gc) {
         constexpr int g = decltype(gc)::value;
         const float lg = row_bcast<g>(s.l);
-        if (row == (g & 3)) {
+        if (row == (g & 3) && g < ncols) {
           float* d = o + (long long)row_of(g) * D + col * VE;
 #pragma unroll
           for (int e = 0; e < VE; ++e) d[e] = poisoned ? nan : (lg != 0.0f ? s.acc[g][e] / lg : 0.0f);
         }
       });
     }
-    if (lo != nullptr && row == 0 && col < G)
+    if (lo != nullptr && row == 0 && col < ncols)
       lo[row_of(col)] = poisoned ? nan : (s.l != 0.0f ? (s.m + log2f(s.l)) * kLn2 : -__builtin_inff());
   }
 

@@ -117,7 +117,7 @@ def test_plan_forced_workers_and_empty_batch():
 
 @pytest.mark.parametrize("kw,lens,expect", [
     (dict(num_q_heads=12), [1, 1, 1, 1], INVALID),           # Hq not a multiple of Hkv
-    (dict(num_q_heads=24), [1, 1, 1, 1], UNSUPPORTED),       # G = 3
+    (dict(num_q_heads=24, flags=2), [1, 1, 1, 1], UNSUPPORTED),   # G = 3 needs a static plan
     (dict(num_q_heads=256), [1, 1, 1, 1], UNSUPPORTED),      # G = 32
     (dict(head_dim=96), [1, 1, 1, 1], UNSUPPORTED),
     (dict(page_size=12), [1, 1, 1, 1], UNSUPPORTED),
@@ -126,7 +126,7 @@ def test_plan_forced_workers_and_empty_batch():
     (dict(kv_dtype=7), [1, 1, 1, 1], UNSUPPORTED),
     (dict(kv_layout=2), [1, 1, 1, 1], UNSUPPORTED),
     (dict(q_len=8), [1, 1, 1, 1], UNSUPPORTED),              # 8 rows x 4 heads = 32 columns
-    (dict(q_len=3), [1, 1, 1, 1], UNSUPPORTED),              # 12 columns
+    (dict(q_len=5), [1, 1, 1, 1], UNSUPPORTED),              # 20 columns
     (dict(q_len=-1), [1, 1, 1, 1], INVALID),
     (dict(q_len=2, flags=2), [1, 1, 1, 1], UNSUPPORTED),     # multi-query needs a static plan
     (dict(kv_layout=-1), [1, 1, 1, 1], UNSUPPORTED),
@@ -276,3 +276,9 @@ def test_kv_append_validation_rejects_before_launch():
     # nothing to do: no pointer is read
     assert _append_raw(n=0, kn=0, vn=0, seq=0, pos=0, bt=0, kp=0, vp=0) == OK
     assert _append_raw(batch=0, kn=0, vn=0, seq=0, pos=0, bt=0, kp=0, vp=0) == OK
+
+
+def test_plan_accepts_any_group_up_to_16():
+    for hq, hkv, qlen in ((24, 8, 0), (28, 4, 0), (12, 4, 5), (40, 8, 3), (15, 1, 1), (32, 8, 3)):
+        st, pl = plan_raw([5, 9, 100, 33], num_q_heads=hq, num_kv_heads=hkv, q_len=qlen)
+        assert st == OK, (hq, hkv, qlen, pk._lib.pdattn_last_error())

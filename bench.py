@@ -457,8 +457,27 @@ def main():
                "kind": "oracle",
                "sample": f"the full {w.name} step ({w.batch} sequences) repeated {len(times)} times "
                          f"({sum(times):.1f} s); median {per_call * 1e6:.0f} us/call"}
+        # the same oracle on one thread, over a bounded prefix of the batch
+        nb = max(1, min(w.batch, 4))
+        sub = {k: inp[k] for k in ("q", "k_pages", "v_pages", "k_scale", "v_scale", "block_table", "context_lens")}
+        sub["q"], sub["block_table"], sub["context_lens"] = inp["q"][:nb], inp["block_table"][:nb], inp["context_lens"][:nb]
+        t1 = []
+        start = time.perf_counter()
+        while True:
+            t = time.perf_counter()
+            oracle.decode(sub["q"], sub["k_pages"], sub["v_pages"], sub["block_table"], sub["context_lens"],
+                          k_scale=sub["k_scale"], v_scale=sub["v_scale"], threads=1)
+            t1.append(time.perf_counter() - t)
+            if time.perf_counter() - start >= min(3.0, args.cpu_seconds):
+                break
+        sub_bytes = synth.kv_bytes(w, inp["context_lens"][:nb])
+        cpu["single_thread"] = {"value": round(sub_bytes / statistics.median(t1) / 1e9, 4), "unit": "GB/s",
+                                "cores": 1, "sample": f"the first {nb} sequences of the step, {len(t1)} calls"}
 
     traffic = read_traffic(mode, w.name, args.layout)
+    # fp8 pools: the two fp32 scales per (token, kv head) inside kv_bytes
+    scale_bytes = (int(inp["context_lens"].to(torch.int64).sum()) * w.num_kv_heads * 8
+                   if w.kv_dtype == "fp8_e4m3" else 0)
     achieved = kv_bytes / (mean_dec * 1e-6) / 1e9
     rec = {
         "metric": METRIC,
@@ -488,6 +507,8 @@ def main():
         "reduce_kernel_us": round(statistics.fmean(red_us), 2),
         "warm_cache_us_per_call": round(statistics.median(warm), 2),
         "kv_bytes_per_call": kv_bytes,
+        "kv_payload_bytes_per_call": kv_bytes - scale_bytes,
+        "value_payload_only_gbs": round((kv_bytes - scale_bytes) / (mean_step * 1e-6) / 1e9, 1),
         "stream_read_ceiling_gbs": round(ceiling, 1),
         "frac_of_stream_read_ceiling": round(kv_bytes / (mean_step * 1e-6) / 1e9 / ceiling, 4),
         "plan_host_us": round(plan_us, 1),

@@ -350,7 +350,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(MergeParams p) 
     M = Mn;
   };
   // pieces in flight per step: fewer when a lane's slice is long
-  constexpr int U = EPL >= 32 ? 1 : (EPL >= 16 ? 2 : kMergeUnroll);
+  constexpr int U = EPL >= 64 ? 1 : (EPL >= 16 ? 2 : kMergeUnroll);
   for (long long i = wave; i < n; i += U * kMergeWaves) {
     // U pieces per step (every fourth piece from i), all loads issued first
     float mu[U], lu[U], au[U][EPL];

@@ -28,6 +28,7 @@ import math
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "kv_bytes", "make_append_inputs", "append_bytes", "to_hnd",
+           "make_prefill_inputs", "prefill_flops",
            "from_hnd"]
 
 E4M3_MAX = 448.0
@@ -290,3 +291,52 @@ def from_hnd(t):
     """A pool [page][kv head][slot][d] (or scales [page][kv head][slot]) back
     in rows [page][slot][kv head]."""
     return t.permute(0, 2, 1, 3) if t.dim() == 4 else t.permute(0, 2, 1)
+
+
+def make_prefill_inputs(*, num_q_heads, num_kv_heads, head_dim, page_size, q_lens, prefix_lens=None,
+                        kv_dtype="bf16", pool="2x", unused="nan", seed=3000):
+    """Draw the inputs of one ragged paged prefill on the CPU.
+
+    Recipe: request b has q_lens[b] new query rows and prefix_lens[b]
+    (default 0) cached positions before them; its context is L_b = prefix_b
+    + n_b positions, the new rows' keys and values already in the cache. The
+    pools, block_table and K/V values follow ``make_inputs`` with those
+    fixed lengths and the same seed (unused pages NaN); q is then drawn from
+    ``torch.Generator().manual_seed(seed + 1)`` as randn rounded to bf16,
+    packed [total_q, Hq, d] request by request, and qo_indptr is the prefix
+    sum of q_lens (AstrAI "CUDA Kernels", Q Scheduling and KV Addressing).
+
+    Returns the ``make_inputs`` dict with q replaced by the packed rows and
+    qo_indptr int32 [B + 1], q_lens int32 [B] added.
+    """
+    q_lens = [int(x) for x in q_lens]
+    B = len(q_lens)
+    prefix_lens = [0] * B if prefix_lens is None else [int(x) for x in prefix_lens]
+    if len(prefix_lens) != B or min(q_lens + prefix_lens, default=0) < 0:
+        raise ValueError("one non-negative q length and prefix length per request")
+    lens = tuple(p + n for p, n in zip(prefix_lens, q_lens))
+    w = Workload("prefill", "ragged paged prefill", B, num_q_heads, num_kv_heads, head_dim, page_size,
+                 ("fixed", lens), kv_dtype=kv_dtype, pool=pool, seed=seed)
+    inp = make_inputs(w, unused=unused)
+    g = torch.Generator().manual_seed(int(seed) + 1)
+    total = sum(q_lens)
+    inp["q"] = torch.randn((total, num_q_heads, head_dim), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    ptr = [0]
+    for n in q_lens:
+        ptr.append(ptr[-1] + n)
+    inp["qo_indptr"] = torch.tensor(ptr, dtype=torch.int32)
+    inp["q_lens"] = torch.tensor(q_lens, dtype=torch.int32)
+    return inp
+
+
+def prefill_flops(q_lens, context_lens, num_q_heads, head_dim, causal=True) -> int:
+    """Algorithmic flops of a prefill: 4 d per (query row, head, visible
+    position) (2 d for q.k, 2 d for p.v), with row i of a request of n rows
+    and context L seeing L - n + i + 1 positions when causal (clamped to
+    [0, L]), L otherwise."""
+    pairs = 0
+    for n, L in zip([int(x) for x in q_lens], [int(x) for x in context_lens]):
+        for i in range(n):
+            lim = L - n + i + 1 if causal else L
+            pairs += min(max(lim, 0), L)
+    return 4 * head_dim * num_q_heads * pairs

@@ -301,6 +301,82 @@ PDATTN_API pdattn_status pdattn_merge(int32_t num_partials, int64_t num_rows, in
  */
 PDATTN_API pdattn_status pdattn_fp8_conversion_check(uint64_t* mismatches, void* stream);
 
+/*
+ * Ragged paged prefill (AstrAI "CUDA Kernels": the paged prefill entry over a
+ * ragged batch, qo_indptr plus the cache's own lengths; section "Q
+ * Scheduling and KV Addressing" for the tile map). Request b owns the packed
+ * query rows qo_indptr[b] .. qo_indptr[b+1] - 1 (n_b of them), the last n_b
+ * positions of its context of L_b = context_lens[b] positions, whose keys
+ * and values are already in the pools (pdattn_kv_append writes them). The
+ * pages leave that placement open; it is the reading under which a prompt
+ * prefilled in chunks gives the rows a whole-prompt prefill gives. Query
+ * row i of request b and head h (kv head h / G):
+ *   causal:      positions t < L_b - n_b + i + 1 (clamped to [0, L_b])
+ *   non-causal:  positions t < L_b
+ *   out[qo_indptr[b] + i][h][:] = softmax over those t of
+ *                scale * q . K[page(t)][slot(t)][kvh], times V, as for decode
+ *   lse[qo_indptr[b] + i][h]    = ln sum_t exp(s_t)
+ * A row that sees no position gets out = 0 and lse = -inf.
+ *
+ * The work is cut into query tiles of rows_per_tile rows of one request
+ * (pdattn_prefill_rows_per_tile: the (row, head) columns one workgroup of
+ * the kernel holds, divided by G), each paired with every kv head. The
+ * host builds the tile map once per batch (pdattn_prefill_tiles) and copies
+ * it to the device; the kernel finds a tile's request and rows in O(1).
+ */
+
+/* rows_per_tile for `problem` (head_dim and group size; q_len is not used):
+ * 128 / G for d in {64, 128}, 64 / G for d = 256. */
+PDATTN_API pdattn_status pdattn_prefill_rows_per_tile(const pdattn_problem* problem, int32_t* rows_per_tile);
+
+/* Tile-map flags. */
+#define PDATTN_TILES_LONGEST_FIRST 1 /* order tiles by positions read, most first */
+
+/*
+ * Build the tile map on the host. qo_indptr: host int32 [batch + 1],
+ * non-decreasing from a value >= 0. Without flags the tiles are listed
+ * request by request, tile by tile: tile_batch[t] = b, tile_index[t] = j
+ * covers rows qo_indptr[b] + j * rows_per_tile .. (the pages' worked
+ * example: Q lengths 70, 10, 130 at 64 rows give batch 0 0 1 2 2 2 and
+ * index 0 1 0 0 1 2). PDATTN_TILES_LONGEST_FIRST reorders them by the
+ * number of context positions their rows reach (causal: L_b - n_b + last
+ * row + 1; else L_b), most first, ties kept in order, so that the longest
+ * tiles start first; it needs context_lens (host int32 [batch]; otherwise
+ * ignored, may be NULL). *num_tiles receives the tile count; with
+ * tile_batch or tile_index NULL nothing else is written (a count query);
+ * else both must hold `capacity` >= *num_tiles entries. Host memory only.
+ */
+PDATTN_API pdattn_status pdattn_prefill_tiles(const int32_t* qo_indptr, const int32_t* context_lens, int32_t batch,
+                                              int32_t rows_per_tile, int32_t causal, int32_t flags,
+                                              int32_t* tile_batch, int32_t* tile_index, int32_t capacity,
+                                              int32_t* num_tiles);
+
+/*
+ * Enqueue the prefill on `stream`.
+ *   problem      pools and heads as for decode (q_len is not used; any G
+ *                up to 16, d in {64, 128, 256}, both layouts, bf16 or fp8)
+ *   causal       1: causal mask as above; 0: every row sees all L_b positions
+ *   q            bf16 [total_q][Hq][d], device, 16-byte aligned
+ *   qo_indptr    int32 [batch + 1], device: the same values the tile map
+ *                was built from
+ *   tile_batch,  int32 [num_tiles], device: from pdattn_prefill_tiles with
+ *   tile_index   this problem's rows_per_tile
+ *   k_pages ...  pools, scales, block_table and context_lens as for decode
+ *   out          fp32 [total_q][Hq][d], device, 16-byte aligned
+ *   lse          fp32 [total_q][Hq], device, optional (NULL to skip)
+ * Rows that no tile covers are not written. On the device, a context length
+ * outside [0, max_pages_per_seq * P] makes its request's rows NaN, and a
+ * block_table entry outside [0, num_pages) makes NaN the rows of every tile
+ * that reads it. Allocates nothing, never synchronises, graph-capturable;
+ * validated before launch (an invalid call enqueues nothing).
+ */
+PDATTN_API pdattn_status pdattn_prefill(const pdattn_problem* problem, int32_t causal, const void* q,
+                                        const int32_t* qo_indptr, const int32_t* tile_batch,
+                                        const int32_t* tile_index, int32_t num_tiles, const void* k_pages,
+                                        const void* v_pages, const float* k_scale, const float* v_scale,
+                                        const int32_t* block_table, const int32_t* context_lens, float* out,
+                                        float* lse, void* stream);
+
 /* Static description of a status code. */
 PDATTN_API const char* pdattn_status_string(pdattn_status status);
 

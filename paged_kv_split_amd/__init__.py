@@ -15,7 +15,7 @@ import torch
 __all__ = ["Problem", "Plan", "PdattnError", "plan", "decode", "reduce", "workspace", "workspace_init",
            "paged_decode", "KV_BF16", "KV_FP8_E4M3", "PLAN_BALANCED", "library_path", "stream_read",
            "stream_read_sink", "kv_append", "APPEND_POW2_SCALES", "fp8_conversion_check", "merge", "LAYOUT_NHD", "LAYOUT_HND",
-           "pool_dims"]
+           "pool_dims", "prefill_rows_per_tile", "prefill_tiles", "prefill", "paged_prefill", "TILES_LONGEST_FIRST"]
 
 KV_BF16 = 0
 KV_FP8_E4M3 = 1
@@ -23,6 +23,7 @@ PLAN_BALANCED = 2
 LAYOUT_NHD = 0   # pool rows [page][slot][kv head]
 LAYOUT_HND = 1   # pool rows [page][kv head][slot]
 APPEND_POW2_SCALES = 1
+TILES_LONGEST_FIRST = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libpdattn.so")
@@ -91,6 +92,14 @@ _lib.pdattn_merge.restype = ctypes.c_int
 _lib.pdattn_merge.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P, _P]
 _lib.pdattn_fp8_conversion_check.restype = ctypes.c_int
 _lib.pdattn_fp8_conversion_check.argtypes = [_P, _P]
+_lib.pdattn_prefill_rows_per_tile.restype = ctypes.c_int
+_lib.pdattn_prefill_rows_per_tile.argtypes = [ctypes.POINTER(Problem), _P]
+_lib.pdattn_prefill_tiles.restype = ctypes.c_int
+_lib.pdattn_prefill_tiles.argtypes = [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
+                                      ctypes.c_int32, _P]
+_lib.pdattn_prefill.restype = ctypes.c_int
+_lib.pdattn_prefill.argtypes = [ctypes.POINTER(Problem), ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P,
+                                _P, _P, _P, _P, _P, _P]
 _lib.pdattn_problem_size.restype = ctypes.c_uint64
 _lib.pdattn_plan_size.restype = ctypes.c_uint64
 
@@ -253,4 +262,68 @@ def paged_decode(q, k_pages, v_pages, block_table, context_lens, *, context_lens
     ws = workspace(pl, dev)
     decode(pl, q, k_pages, v_pages, k_scale, v_scale, block_table, context_lens, ws, out, lse)
     reduce(pl, ws, out, lse)
+    return out, lse
+
+
+def _prefill_problem(q, k_pages, block_table, layout, scale):
+    Hq, D = q.shape[1], q.shape[2]
+    num_pages, P, Hkv, _ = pool_dims(k_pages, layout)
+    kv = KV_FP8_E4M3 if k_pages.dtype == torch.float8_e4m3fn else KV_BF16
+    return Problem(block_table.shape[0], Hq, Hkv, D, P, block_table.shape[1], num_pages, kv,
+                   0.0 if scale is None else float(scale), layout, 1)
+
+
+def prefill_rows_per_tile(problem: Problem) -> int:
+    """``pdattn_prefill_rows_per_tile``."""
+    rows = ctypes.c_int32(0)
+    _check(_lib.pdattn_prefill_rows_per_tile(ctypes.byref(problem), ctypes.byref(rows)),
+           "pdattn_prefill_rows_per_tile")
+    return int(rows.value)
+
+
+def prefill_tiles(qo_indptr_host, rows_per_tile, *, context_lens_host=None, causal=True, longest_first=True):
+    """``pdattn_prefill_tiles`` on host int32 arrays; returns (tile_batch,
+    tile_index) as CPU int32 tensors."""
+    ptr = torch.as_tensor(qo_indptr_host, dtype=torch.int32).contiguous().cpu()
+    B = ptr.numel() - 1
+    lens = None if context_lens_host is None else torch.as_tensor(context_lens_host, dtype=torch.int32).contiguous().cpu()
+    flags = TILES_LONGEST_FIRST if longest_first else 0
+    count = ctypes.c_int32(0)
+    _check(_lib.pdattn_prefill_tiles(_ptr(ptr), _ptr(lens), B, int(rows_per_tile), int(bool(causal)), flags, None,
+                                     None, 0, ctypes.byref(count)), "pdattn_prefill_tiles")
+    tb = torch.empty(max(count.value, 1), dtype=torch.int32)
+    ti = torch.empty(max(count.value, 1), dtype=torch.int32)
+    _check(_lib.pdattn_prefill_tiles(_ptr(ptr), _ptr(lens), B, int(rows_per_tile), int(bool(causal)), flags,
+                                     _ptr(tb), _ptr(ti), tb.numel(), ctypes.byref(count)), "pdattn_prefill_tiles")
+    return tb[:count.value], ti[:count.value]
+
+
+def prefill(problem: Problem, q, qo_indptr, tile_batch, tile_index, k_pages, v_pages, k_scale, v_scale, block_table,
+            context_lens, out, lse=None, *, causal=True, stream=None):
+    """``pdattn_prefill``: every tensor on the device, the tile map from
+    ``prefill_tiles`` with ``prefill_rows_per_tile(problem)`` rows."""
+    _check(_lib.pdattn_prefill(ctypes.byref(problem), int(bool(causal)), _ptr(q), _ptr(qo_indptr), _ptr(tile_batch),
+                               _ptr(tile_index), int(tile_batch.numel()), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
+                               _ptr(v_scale), _ptr(block_table), _ptr(context_lens), _ptr(out), _ptr(lse),
+                               _stream(stream)), "pdattn_prefill")
+
+
+def paged_prefill(q, qo_indptr, k_pages, v_pages, block_table, context_lens, *, qo_indptr_host=None,
+                  context_lens_host=None, k_scale=None, v_scale=None, scale=None, causal=True, layout=LAYOUT_NHD,
+                  longest_first=True, return_lse=True):
+    """Build the tile map, allocate (torch) and run one prefill; returns
+    (out fp32 [total_q, Hq, d], lse fp32 [total_q, Hq]).
+
+    q: bf16 [total_q, Hq, d] packed by qo_indptr (int32 [B + 1], device);
+    pools, block_table and context_lens as for ``paged_decode`` (device)."""
+    prob = _prefill_problem(q, k_pages, block_table, layout, scale)
+    ptr_h = qo_indptr.cpu() if qo_indptr_host is None else qo_indptr_host
+    lens_h = context_lens.cpu() if context_lens_host is None else context_lens_host
+    tb, ti = prefill_tiles(ptr_h, prefill_rows_per_tile(prob), context_lens_host=lens_h, causal=causal,
+                           longest_first=longest_first)
+    dev = q.device
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev) if return_lse else None
+    prefill(prob, q, qo_indptr, tb.to(dev), ti.to(dev), k_pages, v_pages, k_scale, v_scale, block_table,
+            context_lens, out, lse, causal=causal)
     return out, lse

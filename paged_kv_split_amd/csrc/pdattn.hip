@@ -10,10 +10,13 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
+#include <vector>
 
 #include "kernels.h"
 #include "append.h"
 #include "merge.h"
+#include "prefill.h"
 
 namespace {
 
@@ -499,6 +502,138 @@ PDATTN_API pdattn_status pdattn_fp8_conversion_check(uint64_t* mismatches, void*
   hipError_t e = pdattn::launch_fp8_conversion_check(reinterpret_cast<unsigned long long*>(mismatches),
                                                      static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "conversion check launch: %s", hipGetErrorString(e));
+  return PDATTN_OK;
+}
+
+PDATTN_API pdattn_status pdattn_prefill_rows_per_tile(const pdattn_problem* problem, int32_t* rows_per_tile) {
+  g_last_error[0] = '\0';
+  pdattn_status st = check_problem(problem);
+  if (st != PDATTN_OK) return st;
+  if (!rows_per_tile) return fail(PDATTN_ERR_INVALID_ARGUMENT, "rows_per_tile is NULL");
+  *rows_per_tile = pdattn::prefill_columns(problem->head_dim) / heads_per_kv(*problem);
+  return PDATTN_OK;
+}
+
+PDATTN_API pdattn_status pdattn_prefill_tiles(const int32_t* qo_indptr, const int32_t* context_lens, int32_t batch,
+                                              int32_t rows_per_tile, int32_t causal, int32_t flags,
+                                              int32_t* tile_batch, int32_t* tile_index, int32_t capacity,
+                                              int32_t* num_tiles) {
+  g_last_error[0] = '\0';
+  if (!num_tiles) return fail(PDATTN_ERR_INVALID_ARGUMENT, "num_tiles is NULL");
+  *num_tiles = 0;
+  if (batch < 0 || batch > 65535) return fail(PDATTN_ERR_INVALID_ARGUMENT, "batch %d outside [0, 65535]", batch);
+  if (rows_per_tile <= 0) return fail(PDATTN_ERR_INVALID_ARGUMENT, "rows_per_tile %d must be positive", rows_per_tile);
+  if ((flags & ~PDATTN_TILES_LONGEST_FIRST) != 0) return fail(PDATTN_ERR_INVALID_ARGUMENT, "unknown tile flags %d", flags);
+  if (causal != 0 && causal != 1) return fail(PDATTN_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  if (batch > 0 && !qo_indptr) return fail(PDATTN_ERR_INVALID_ARGUMENT, "qo_indptr is NULL");
+  const bool longest = (flags & PDATTN_TILES_LONGEST_FIRST) != 0;
+  if (longest && batch > 0 && !context_lens)
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "PDATTN_TILES_LONGEST_FIRST needs the host context lengths");
+  int64_t count = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t n = (int64_t)qo_indptr[b + 1] - qo_indptr[b];
+    if (qo_indptr[b] < 0 || n < 0) return fail(PDATTN_ERR_INVALID_ARGUMENT, "qo_indptr must start at >= 0 and not decrease (request %d)", b);
+    count += ceil_div(n, rows_per_tile);
+  }
+  if (count > INT32_MAX) return fail(PDATTN_ERR_UNSUPPORTED, "more than 2^31 - 1 query tiles");
+  *num_tiles = (int32_t)count;
+  if (!tile_batch || !tile_index) return PDATTN_OK;  // count only
+  if (capacity < count)
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "%lld tiles do not fit in capacity %d", (long long)count, capacity);
+  // request by request, tile by tile (the order of the pages' example)
+  int64_t t = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t n = (int64_t)qo_indptr[b + 1] - qo_indptr[b];
+    for (int64_t j = 0; j < ceil_div(n, rows_per_tile); ++j, ++t) {
+      tile_batch[t] = b;
+      tile_index[t] = (int32_t)j;
+    }
+  }
+  if (longest && count > 1) {
+    // most positions read first (the rows' reach into the context); equal
+    // reaches keep their order
+    struct Item { int64_t reach; int32_t b, j; };
+    std::vector<Item> items;
+    try {
+      items.resize((size_t)count);
+    } catch (...) {
+      return fail(PDATTN_ERR_INVALID_ARGUMENT, "out of host memory for %lld tiles", (long long)count);
+    }
+    for (int64_t i = 0; i < count; ++i) {
+      const int b = tile_batch[i];
+      const int64_t n = (int64_t)qo_indptr[b + 1] - qo_indptr[b];
+      const int64_t L = context_lens[b];
+      const int64_t last = std::min<int64_t>((int64_t)(tile_index[i] + 1) * rows_per_tile, n) - 1;
+      int64_t reach = causal ? L - n + last + 1 : L;
+      reach = reach < 0 ? 0 : (reach > L ? L : reach);
+      items[i] = Item{reach, tile_batch[i], tile_index[i]};
+    }
+    std::stable_sort(items.begin(), items.end(), [](const Item& x, const Item& y) { return x.reach > y.reach; });
+    for (int64_t i = 0; i < count; ++i) {
+      tile_batch[i] = items[i].b;
+      tile_index[i] = items[i].j;
+    }
+  }
+  return PDATTN_OK;
+}
+
+PDATTN_API pdattn_status pdattn_prefill(const pdattn_problem* problem, int32_t causal, const void* q,
+                                        const int32_t* qo_indptr, const int32_t* tile_batch,
+                                        const int32_t* tile_index, int32_t num_tiles, const void* k_pages,
+                                        const void* v_pages, const float* k_scale, const float* v_scale,
+                                        const int32_t* block_table, const int32_t* context_lens, float* out,
+                                        float* lse, void* stream) {
+  g_last_error[0] = '\0';
+  pdattn_status st = check_problem(problem);
+  if (st != PDATTN_OK) return st;
+  if (causal != 0 && causal != 1) return fail(PDATTN_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  if (num_tiles < 0) return fail(PDATTN_ERR_INVALID_ARGUMENT, "num_tiles %d is negative", num_tiles);
+  if ((int64_t)num_tiles * problem->num_kv_heads > INT32_MAX)
+    return fail(PDATTN_ERR_UNSUPPORTED, "num_tiles * num_kv_heads exceeds 2^31 - 1");
+  if (num_tiles == 0 || problem->batch == 0) return PDATTN_OK;
+  if (!q || !qo_indptr || !tile_batch || !tile_index || !k_pages || !v_pages || !block_table || !context_lens || !out)
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(out, 16))
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "q, k_pages, v_pages and out must be 16-byte aligned");
+  if (!aligned(qo_indptr, 4) || !aligned(tile_batch, 4) || !aligned(tile_index, 4) || !aligned(block_table, 4) ||
+      !aligned(context_lens, 4) || (lse && !aligned(lse, 4)))
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "index arrays and lse must be 4-byte aligned");
+  const bool fp8 = problem->kv_dtype == PDATTN_KV_FP8_E4M3;
+  if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "fp8 pools need 4-byte aligned k_scale and v_scale");
+  if (!fp8 && (k_scale || v_scale))
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "k_scale / v_scale must be NULL for bf16 pools");
+
+  pdattn::PrefillParams p;
+  std::memset(&p, 0, sizeof p);
+  p.q = static_cast<const uint16_t*>(q);
+  p.qo_indptr = qo_indptr;
+  p.tile_batch = tile_batch;
+  p.tile_index = tile_index;
+  p.k = static_cast<const uint8_t*>(k_pages);
+  p.v = static_cast<const uint8_t*>(v_pages);
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.block_table = block_table;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.lse = lse;
+  p.batch = problem->batch;
+  p.num_q_heads = problem->num_q_heads;
+  p.num_kv_heads = problem->num_kv_heads;
+  p.heads_per_kv = heads_per_kv(*problem);
+  p.rows_per_tile = pdattn::prefill_columns(problem->head_dim) / p.heads_per_kv;
+  p.page_log2 = ilog2(problem->page_size);
+  p.max_pages_per_seq = problem->max_pages_per_seq;
+  p.num_pages = problem->num_pages;
+  p.slot_stride = slot_stride_of(*problem);
+  p.head_stride = head_stride_of(*problem);
+  p.causal = causal;
+  const float scale = problem->scale > 0.0f ? problem->scale : 1.0f / std::sqrt((float)problem->head_dim);
+  p.qk_scale_log2 = scale * 1.44269504088896340736f;
+  const uint32_t grid = (uint32_t)((int64_t)num_tiles * problem->num_kv_heads);
+  hipError_t e = pdattn::launch_prefill(p, problem->head_dim, fp8, grid, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "prefill kernel launch: %s", hipGetErrorString(e));
   return PDATTN_OK;
 }
 

@@ -1,0 +1,44 @@
+// Internal interface between the C-ABI host layer (pdattn.hip) and the
+// ragged paged prefill kernel (prefill.hip). Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pdattn {
+
+// (query row, head) columns one prefill workgroup computes: 4 waves of two
+// 16-column blocks (one block for head_dim 256).
+constexpr int prefill_columns(int head_dim) { return head_dim == 256 ? 64 : 128; }
+
+struct PrefillParams {
+  const uint16_t* q;          // bf16 bits [total_q][Hq][D]
+  const int32_t* qo_indptr;   // [B + 1]
+  const int32_t* tile_batch;  // [num_tiles]: request of each query tile
+  const int32_t* tile_index;  // [num_tiles]: its tile index inside that request
+  const uint8_t* k;           // pool bytes, rows as in the decode kernels
+  const uint8_t* v;
+  const float* k_scale;       // fp8 pools: one per row
+  const float* v_scale;
+  const int32_t* block_table; // [B][max_pages_per_seq]
+  const int32_t* context_lens;
+  float* out;                 // [total_q][Hq][D]
+  float* lse;                 // [total_q][Hq] or null
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t heads_per_kv;       // G (any value 1..16)
+  int32_t rows_per_tile;      // prefill_columns(D) / G
+  int32_t page_log2;
+  int32_t max_pages_per_seq;
+  int32_t num_pages;
+  int32_t slot_stride;        // row index = page * P * Hkv + slot * slot_stride + kvh * head_stride
+  int32_t head_stride;
+  int32_t causal;
+  float qk_scale_log2;        // softmax scale * log2(e)
+};
+
+// grid: num_tiles * num_kv_heads workgroups of 256 threads.
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, bool fp8, uint32_t grid, hipStream_t stream);
+
+}  // namespace pdattn

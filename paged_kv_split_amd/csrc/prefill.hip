@@ -1,0 +1,557 @@
+// Ragged paged prefill attention on gfx950.
+//
+// The operation (AstrAI "CUDA Kernels": the paged prefill entry over a
+// ragged batch, section "Q Scheduling and KV Addressing"; attention itself as
+// in the decode kernels): request b owns the packed query rows
+// qo_indptr[b] .. qo_indptr[b+1] - 1 (n of them), the last n positions of its
+// context of L positions; with the causal mask query row i sees the positions
+// t < L - n + i + 1, without it all t < L.
+//
+// Work decomposition. A host-built map gives every query tile its request
+// and its index inside the request in O(1) (same section). One workgroup
+// computes one (query tile, kv head): its 4 waves hold 16 NB (query row,
+// head) columns each (the G query heads of the kv head packed with the rows,
+// GQA head packing as on the same page), and share every K/V tile through a
+// two-stage LDS ring, so each K/V byte fetched serves 64 NB columns.
+//
+// Per KV tile of NT tokens, on each wave:
+//   * S^T = K_tile . Q^T on v_mfma_f32_16x16x32_bf16 (A: 16 tokens x 32 d,
+//     staged in LDS in operand order by the direct-to-LDS loads; B: the
+//     wave's columns, held in registers for the whole call);
+//   * online softmax per column in base 2 (FlashQuant wiki "CUDA Kernels",
+//     flash_attention.cu, Online Softmax): a lane holds 4 M-blocks x 4 rows of
+//     its column, the tile max needs two cross-row exchanges;
+//   * O^T += V^T . P on the same MFMA: the probabilities sit, after the
+//     softmax, exactly where the B operand wants them (k = 8 r + j is
+//     M-block 2 p + j / 4, row 4 r + j mod 4), and the V^T operand is
+//     gathered from LDS with the same k -> token order; O^T's columns are
+//     the lane's own, so the rescale by exp2(m_old - m_new) is per lane.
+// Tiles entirely below every column's causal limit skip the mask; tiles past
+// the last row's limit are not read (causal tile skipping, same page,
+// Causal Masking with Tile-Skipping).
+//
+// fp8 pools: codes widen exactly to bf16 for the operand; the k scale
+// multiplies the score, the v scale the probability (OASR "Kernel Layer",
+// FP8 KV variants), as in the decode kernels.
+
+#include "prefill.h"
+#include "tile_ops.h"
+
+namespace pdattn {
+namespace {
+
+using dev::bf16x8;
+using dev::f32x4;
+using dev::u32x2;
+using dev::u32x4;
+using dev::u32x8;
+
+template <int D, bool FP8>
+struct Cfg {
+  static constexpr int ESZ = FP8 ? 1 : 2;
+  static constexpr int NB = D == 256 ? 1 : 2;       // 16-column blocks per wave
+  static constexpr int NT = D == 256 ? 32 : 64;     // tokens per K/V tile
+  static constexpr int MB = NT / 16;                // 16-token M-blocks per tile
+  static constexpr int KS = D / 32;                 // k-steps of q.K
+  static constexpr int DB = D / 16;                 // 16-row d-blocks of O^T
+  static constexpr int PS = NT / 32;                // k-steps of p.V
+  static constexpr int ROW = D * ESZ;               // bytes of one (token, kv head) row
+  static constexpr int QK = ROW / 64;               // 16-byte K chunks per lane per M-block
+  static constexpr int K_T = NT * ROW;
+  static constexpr int V_T = NT * ROW;
+  static constexpr int SC_T = FP8 ? MB * 128 : 0;   // per M-block: 16 k scales, 16 v scales
+  static constexpr int STAGE = K_T + V_T + SC_T;
+  static constexpr int KI = K_T / (kWaves * 64 * 16);  // K loads per lane per tile
+  static constexpr int VI = V_T / (kWaves * 64 * 16);
+  static constexpr int VR = DB * ESZ;               // bytes of a lane's V piece of one token
+  static constexpr int COLS = kWaves * 16 * NB;
+  static_assert(COLS == prefill_columns(D), "columns");
+  static_assert(KI >= 1 && QK % KI == 0 && VI >= 1, "load split");
+  static_assert(MB * QK == kWaves * KI, "K image");
+};
+
+// LDS reads at immediate offsets from one address, and the wait for all of
+// them, in one asm block: no destination is copied or used before its data
+// has landed, and the compiler inserts no wait of its own for the direct-to-
+// LDS loads of the next tile that are in flight meanwhile.
+template <int... O>
+__device__ __forceinline__ void lds_b128(u32x4 (&r)[sizeof...(O)], uint32_t a) {
+  constexpr int o[] = {O...};
+  constexpr int N = sizeof...(O);
+  if constexpr (N == 1) {
+    asm volatile("ds_read_b128 %0, %1 offset:%2\n\ts_waitcnt lgkmcnt(0)" : "=&v"(r[0]) : "v"(a), "i"(o[0]) : "memory");
+  } else if constexpr (N == 2) {
+    asm volatile(
+        "ds_read_b128 %0, %2 offset:%3\n\t"
+        "ds_read_b128 %1, %2 offset:%4\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1])
+        : "v"(a), "i"(o[0]), "i"(o[1])
+        : "memory");
+  } else if constexpr (N == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:%5\n\t"
+        "ds_read_b128 %1, %4 offset:%6\n\t"
+        "ds_read_b128 %2, %4 offset:%7\n\t"
+        "ds_read_b128 %3, %4 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(a), "i"(o[0]), "i"(o[1]), "i"(o[2]), "i"(o[3])
+        : "memory");
+  } else {
+    static_assert(N == 8, "read count");
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:%9\n\t"
+        "ds_read_b128 %1, %8 offset:%10\n\t"
+        "ds_read_b128 %2, %8 offset:%11\n\t"
+        "ds_read_b128 %3, %8 offset:%12\n\t"
+        "ds_read_b128 %4, %8 offset:%13\n\t"
+        "ds_read_b128 %5, %8 offset:%14\n\t"
+        "ds_read_b128 %6, %8 offset:%15\n\t"
+        "ds_read_b128 %7, %8 offset:%16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(a), "i"(o[0]), "i"(o[1]), "i"(o[2]), "i"(o[3]), "i"(o[4]), "i"(o[5]), "i"(o[6]), "i"(o[7])
+        : "memory");
+  }
+}
+
+template <int... O>
+__device__ __forceinline__ void lds_b64x8(u32x2 (&r)[8], uint32_t a) {
+  constexpr int o[] = {O...};
+  static_assert(sizeof...(O) == 8, "read count");
+  asm volatile(
+      "ds_read_b64 %0, %8 offset:%9\n\t"
+      "ds_read_b64 %1, %8 offset:%10\n\t"
+      "ds_read_b64 %2, %8 offset:%11\n\t"
+      "ds_read_b64 %3, %8 offset:%12\n\t"
+      "ds_read_b64 %4, %8 offset:%13\n\t"
+      "ds_read_b64 %5, %8 offset:%14\n\t"
+      "ds_read_b64 %6, %8 offset:%15\n\t"
+      "ds_read_b64 %7, %8 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a), "i"(o[0]), "i"(o[1]), "i"(o[2]), "i"(o[3]), "i"(o[4]), "i"(o[5]), "i"(o[6]), "i"(o[7])
+      : "memory");
+}
+
+template <int... O>
+__device__ __forceinline__ void lds_b32x8(uint32_t (&r)[8], uint32_t a) {
+  constexpr int o[] = {O...};
+  static_assert(sizeof...(O) == 8, "read count");
+  asm volatile(
+      "ds_read_b32 %0, %8 offset:%9\n\t"
+      "ds_read_b32 %1, %8 offset:%10\n\t"
+      "ds_read_b32 %2, %8 offset:%11\n\t"
+      "ds_read_b32 %3, %8 offset:%12\n\t"
+      "ds_read_b32 %4, %8 offset:%13\n\t"
+      "ds_read_b32 %5, %8 offset:%14\n\t"
+      "ds_read_b32 %6, %8 offset:%15\n\t"
+      "ds_read_b32 %7, %8 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a), "i"(o[0]), "i"(o[1]), "i"(o[2]), "i"(o[3]), "i"(o[4]), "i"(o[5]), "i"(o[6]), "i"(o[7])
+      : "memory");
+}
+
+// The K chunks of M-block MB_ (QK 16-byte reads from the lane's slot).
+template <typename C, int MB_, size_t... I>
+__device__ __forceinline__ void read_k(u32x4 (&r)[C::QK], uint32_t ak, std::index_sequence<I...>) {
+  lds_b128<(int)((MB_ * C::QK + I) * 1024)...>(r, ak);
+}
+
+// Byte offset (from the lane's V base, which already holds its 4 r rows and
+// its d piece) of the token in k slot j of p.V k-step P_.
+template <typename C, int P_, int J>
+constexpr int v_off() { return (32 * P_ + 16 * (J >> 2) + (J & 3)) * C::ROW; }
+
+// The lane's V pieces of p.V k-step P_: for k slot j (j = 0..7), the DB
+// elements of its d range, as dwords.
+template <typename C, int P_>
+struct VPieces {
+  static constexpr int WORDS = C::VR / 4 > 0 ? C::VR / 4 : 1;
+  uint32_t w[8][WORDS];
+};
+
+template <typename C, int P_>
+__device__ __forceinline__ void read_v(VPieces<C, P_>& v, uint32_t av) {
+  if constexpr (C::VR == 32) {
+    u32x4 a[8], b[8];
+    lds_b128<v_off<C, P_, 0>(), v_off<C, P_, 1>(), v_off<C, P_, 2>(), v_off<C, P_, 3>(), v_off<C, P_, 4>(),
+             v_off<C, P_, 5>(), v_off<C, P_, 6>(), v_off<C, P_, 7>()>(a, av);
+    lds_b128<v_off<C, P_, 0>() + 16, v_off<C, P_, 1>() + 16, v_off<C, P_, 2>() + 16, v_off<C, P_, 3>() + 16,
+             v_off<C, P_, 4>() + 16, v_off<C, P_, 5>() + 16, v_off<C, P_, 6>() + 16, v_off<C, P_, 7>() + 16>(b, av);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        v.w[j][x] = a[j][x];
+        v.w[j][4 + x] = b[j][x];
+      }
+  } else if constexpr (C::VR == 16) {
+    u32x4 a[8];
+    lds_b128<v_off<C, P_, 0>(), v_off<C, P_, 1>(), v_off<C, P_, 2>(), v_off<C, P_, 3>(), v_off<C, P_, 4>(),
+             v_off<C, P_, 5>(), v_off<C, P_, 6>(), v_off<C, P_, 7>()>(a, av);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) v.w[j][x] = a[j][x];
+  } else if constexpr (C::VR == 8) {
+    u32x2 a[8];
+    lds_b64x8<v_off<C, P_, 0>(), v_off<C, P_, 1>(), v_off<C, P_, 2>(), v_off<C, P_, 3>(), v_off<C, P_, 4>(),
+              v_off<C, P_, 5>(), v_off<C, P_, 6>(), v_off<C, P_, 7>()>(a, av);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v.w[j][0] = a[j][0];
+      v.w[j][1] = a[j][1];
+    }
+  } else {
+    static_assert(C::VR == 4, "V piece");
+    uint32_t a[8];
+    lds_b32x8<v_off<C, P_, 0>(), v_off<C, P_, 1>(), v_off<C, P_, 2>(), v_off<C, P_, 3>(), v_off<C, P_, 4>(),
+              v_off<C, P_, 5>(), v_off<C, P_, 6>(), v_off<C, P_, 7>()>(a, av);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v.w[j][0] = a[j];
+  }
+}
+
+// The V^T operand of d-block e: element e of the eight k slots' pieces.
+template <bool FP8, typename VP>
+__device__ __forceinline__ bf16x8 v_operand(const VP& v, int e) {
+  if constexpr (FP8) {
+    const int wd = e >> 2, sh = 8 * (e & 3);
+    uint32_t x[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      x[h] = ((v.w[4 * h + 0][wd] >> sh) & 0xffu) | (((v.w[4 * h + 1][wd] >> sh) & 0xffu) << 8) |
+             (((v.w[4 * h + 2][wd] >> sh) & 0xffu) << 16) | (((v.w[4 * h + 3][wd] >> sh) & 0xffu) << 24);
+    }
+    return __builtin_bit_cast(bf16x8, dev::fp8x8_to_bf16x8(x[0], x[1]));
+  } else {
+    const int wd = e >> 1, sh = 16 * (e & 1);
+    u32x4 r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      r[q] = ((v.w[2 * q][wd] >> sh) & 0xffffu) | (((v.w[2 * q + 1][wd] >> sh) & 0xffffu) << 16);
+    return __builtin_bit_cast(bf16x8, r);
+  }
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const __bf16 x = (__bf16)a, y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(const PrefillParams p) {
+  using C = Cfg<D, FP8>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::STAGE];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, n = lane & 15;
+  const int kvh = blockIdx.x % p.num_kv_heads;
+  const int tile = blockIdx.x / p.num_kv_heads;
+  const int b = p.tile_batch[tile];
+  if (b < 0 || b >= p.batch) return;
+  const int row_base = p.tile_index[tile] * p.rows_per_tile;
+  const int q0 = p.qo_indptr[b];
+  const int nreq = p.qo_indptr[b + 1] - q0;
+  if (row_base < 0 || row_base >= nreq) return;
+  const int L = p.context_lens[b];
+  const bool bad_len = L < 0 || L > (p.max_pages_per_seq << p.page_log2);
+  const int G = p.heads_per_kv;
+  const int last_row = min(row_base + p.rows_per_tile, nreq) - 1;
+
+  // the lane's columns: block bb holds column c = 16 (NB w + bb) + n, the
+  // (tile row c / G, head c mod G) pair; lim = positions it may see
+  int lim[C::NB];
+  long long orow[C::NB];  // output row (packed query row * Hq + head), -1 if none
+#pragma unroll
+  for (int bb = 0; bb < C::NB; ++bb) {
+    const int c = 16 * (C::NB * w + bb) + n;
+    const int rr = c / G;
+    const int i = row_base + rr;
+    const bool valid = rr < p.rows_per_tile && i < nreq;
+    int li = p.causal ? L - nreq + i + 1 : L;
+    li = li < 0 ? 0 : (li > L ? L : li);
+    lim[bb] = valid && !bad_len ? li : 0;
+    orow[bb] = valid ? (long long)(q0 + i) * p.num_q_heads + (long long)kvh * G + (c - rr * G) : -1;
+  }
+  const float nan = __builtin_nanf("");
+  if (bad_len) {
+#pragma unroll
+    for (int bb = 0; bb < C::NB; ++bb) {
+      if (orow[bb] < 0) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < C::DB; ++e) p.out[orow[bb] * D + (4 * g + j) * C::DB + e] = nan;
+      if (p.lse != nullptr && g == 0) p.lse[orow[bb]] = nan;
+    }
+    return;
+  }
+  int kv_end = p.causal ? L - nreq + last_row + 1 : L;
+  kv_end = kv_end < 0 ? 0 : (kv_end > L ? L : kv_end);
+  int mask_from = p.causal ? L - nreq + row_base + 1 : L;
+  mask_from = mask_from < 0 ? 0 : (mask_from > L ? L : mask_from);
+  const int T = (kv_end + C::NT - 1) / C::NT;
+
+  // Q as the B operand of q.K, zero for columns without a row; the head_dim
+  // order inside a k-step matches the K chunks (bf16: 32 ks + 8 r + j; fp8:
+  // 16-byte chunks hold two k-steps, 64 (ks / 2) + 16 r + 8 (ks mod 2) + j)
+  bf16x8 qop[C::NB][C::KS];
+#pragma unroll
+  for (int bb = 0; bb < C::NB; ++bb) {
+    const uint16_t* qrow = p.q + (orow[bb] >= 0 ? orow[bb] * D : 0);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const int d0 = FP8 ? 64 * (ks >> 1) + 16 * g + 8 * (ks & 1) : 32 * ks + 8 * g;
+      u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + d0);
+      if (orow[bb] < 0) raw = u32x4{0u, 0u, 0u, 0u};
+      qop[bb][ks] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+
+  // page entries of the wave's 16-token group of the tile at tb: every
+  // position the wave loads lies in [first, first + 15] (clamped to L - 1),
+  // i.e. on at most two pages (P >= 8, groups 16-aligned)
+  // read-only for the whole call: through the constant address space the
+  // wave-uniform entries load with scalar loads, which the tile's vector-
+  // memory waits do not count
+  typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+  const const_i32_ptr bt = (const_i32_ptr)(p.block_table + (long long)b * p.max_pages_per_seq);
+  const int mbK = w * C::KI / C::QK;
+  bool bad_page = false;
+  auto group_first = [&](int tb) { return min(tb + 16 * mbK, L - 1); };
+  // loaded one tile ahead and checked only when used, so that the load's
+  // latency hides behind a tile of compute
+  auto load_pages = [&](int tb, int& e0, int& e1) {
+    const int first = group_first(tb);
+    const int lastp = min(first + 15, L - 1);
+    e0 = bt[first >> p.page_log2];
+    e1 = bt[lastp >> p.page_log2];
+  };
+  auto check_page = [&](int e) {
+    const bool ok = e >= 0 && e < p.num_pages;
+    bad_page |= !ok;
+    return ok ? e : 0;
+  };
+  const int P = 1 << p.page_log2;
+  auto row_of = [&](int pos, int first, int e0, int e1) -> long long {
+    const int page = (pos >> p.page_log2) == (first >> p.page_log2) ? e0 : e1;
+    return ((long long)page * P * p.num_kv_heads) + (long long)(pos & (P - 1)) * p.slot_stride +
+           (long long)kvh * p.head_stride;
+  };
+  auto issue = [&](int tb, int stage, int raw0, int raw1) {
+    const int e0 = check_page(raw0), e1 = check_page(raw1);
+    unsigned char* st = smem + stage * C::STAGE;
+    const int first = group_first(tb);
+    {
+      const int pos = min(tb + 16 * mbK + n, L - 1);
+      const uint8_t* src = p.k + row_of(pos, first, e0, e1) * C::ROW + 16 * g;
+#pragma unroll
+      for (int i = 0; i < C::KI; ++i) {
+        const int q = w * C::KI + i;
+        dev::dma16(src + 64 * (q % C::QK), st + q * 1024);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::VI; ++i) {
+      const int cv = (w * C::VI + i) * 64 + lane;
+      const int pos = min(tb + cv * 16 / C::ROW, L - 1);
+      dev::dma16(p.v + row_of(pos, first, e0, e1) * C::ROW + (cv * 16) % C::ROW,
+                 st + C::K_T + (w * C::VI + i) * 1024);
+    }
+    if constexpr (FP8) {
+      // the first wave of each M-block group stages its 16 k and 16 v scales
+      if ((w * C::KI) % C::QK == 0 && lane < 32) {
+        const int pos = min(tb + 16 * mbK + (lane & 15), L - 1);
+        const float* src = (lane < 16 ? p.k_scale : p.v_scale) + row_of(pos, first, e0, e1);
+        dev::dma4(src, st + C::K_T + C::V_T + mbK * 128);
+      }
+    }
+  };
+
+  float m[C::NB], l[C::NB];
+  f32x4 acc[C::NB][C::DB];
+#pragma unroll
+  for (int bb = 0; bb < C::NB; ++bb) {
+    m[bb] = -__builtin_inff();
+    l[bb] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < C::DB; ++e) acc[bb][e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  const uint32_t lds0 = dev::lds_addr(smem);
+  int e0 = 0, e1 = 0;
+  if (T > 0) {
+    load_pages(0, e0, e1);
+    issue(0, 0, e0, e1);
+    if (T > 1) load_pages(C::NT, e0, e1);
+  }
+  for (int it = 0; it < T; ++it) {
+    dev::wait_vmcnt<0>();
+    __syncthreads();  // every wave's loads of tile it landed; stage (it + 1) & 1 is free
+    const int tb = it * C::NT;
+    if (it + 1 < T) {
+      issue(tb + C::NT, (it + 1) & 1, e0, e1);
+      if (it + 2 < T) load_pages(tb + 2 * C::NT, e0, e1);
+    }
+    const uint32_t sb = lds0 + (it & 1) * C::STAGE;
+
+    // S^T = K . Q^T
+    f32x4 S[C::MB][C::NB];
+    dev::static_for<0, C::MB>([&](auto mbc) {
+      constexpr int mb = decltype(mbc)::value;
+      u32x4 kc[C::QK];
+      read_k<C, mb>(kc, sb + lane * 16, std::make_index_sequence<C::QK>{});
+#pragma unroll
+      for (int bb = 0; bb < C::NB; ++bb) S[mb][bb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kq = 0; kq < C::QK; ++kq) {
+        if constexpr (FP8) {
+          const bf16x8 k0 = __builtin_bit_cast(bf16x8, dev::fp8x8_to_bf16x8(kc[kq][0], kc[kq][1]));
+          const bf16x8 k1 = __builtin_bit_cast(bf16x8, dev::fp8x8_to_bf16x8(kc[kq][2], kc[kq][3]));
+#pragma unroll
+          for (int bb = 0; bb < C::NB; ++bb) {
+            S[mb][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[bb][2 * kq], S[mb][bb], 0, 0, 0);
+            S[mb][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qop[bb][2 * kq + 1], S[mb][bb], 0, 0, 0);
+          }
+        } else {
+          const bf16x8 k0 = __builtin_bit_cast(bf16x8, kc[kq]);
+#pragma unroll
+          for (int bb = 0; bb < C::NB; ++bb)
+            S[mb][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[bb][kq], S[mb][bb], 0, 0, 0);
+        }
+      }
+    });
+
+    float ksc[C::MB][4], vsc[C::MB][4];
+    if constexpr (FP8) {
+      dev::static_for<0, C::MB>([&](auto mbc) {
+        constexpr int mb = decltype(mbc)::value;
+        u32x4 s2[2];
+        lds_b128<mb * 128, mb * 128 + 64>(s2, sb + C::K_T + C::V_T + 16 * g);
+        // __uint_as_float: hipcc mistranslates __builtin_bit_cast applied
+        // to one element of a vector (every element reads as element 0)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          ksc[mb][j] = __uint_as_float(s2[0][j]);
+          vsc[mb][j] = __uint_as_float(s2[1][j]);
+        }
+      });
+    }
+
+    // online softmax per column block; P as the B operand of p.V
+    const bool need_mask = tb + C::NT > mask_from;
+    bf16x8 pop[C::NB][C::PS];
+#pragma unroll
+    for (int bb = 0; bb < C::NB; ++bb) {
+      float x[C::MB][4];
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float s = S[mb][bb][j] * p.qk_scale_log2;
+          if constexpr (FP8) s *= ksc[mb][j];
+          if (need_mask && tb + 16 * mb + 4 * g + j >= lim[bb]) s = -__builtin_inff();
+          x[mb][j] = s;
+          mx = fmaxf(mx, s);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m[bb], mx);
+      // a column with nothing visible yet keeps m = -inf; its weights are
+      // then taken against 0 and are exactly 0
+      const float m_ref = m_new == -__builtin_inff() ? 0.0f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m[bb] - m_ref);
+      float sum = 0.0f;
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[mb][j] = __builtin_amdgcn_exp2f(x[mb][j] - m_ref);
+          sum += x[mb][j];
+        }
+      l[bb] = l[bb] * alpha + sum;
+      const bool grew = m_new > m[bb];
+      m[bb] = m_new;
+      if (__any(grew)) {
+#pragma unroll
+        for (int e = 0; e < C::DB; ++e) acc[bb][e] *= alpha;
+      }
+#pragma unroll
+      for (int pp = 0; pp < C::PS; ++pp) {
+        float y[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          y[j] = x[2 * pp][j];
+          y[4 + j] = x[2 * pp + 1][j];
+          if constexpr (FP8) {
+            y[j] *= vsc[2 * pp][j];
+            y[4 + j] *= vsc[2 * pp + 1][j];
+          }
+        }
+        const u32x4 pw = {pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]),
+                          pack_bf16(y[6], y[7])};
+        pop[bb][pp] = __builtin_bit_cast(bf16x8, pw);
+      }
+    }
+
+    // O^T += V^T . P
+    const uint32_t av = sb + C::K_T + 4 * g * C::ROW + n * C::VR;
+    dev::static_for<0, C::PS>([&](auto ppc) {
+      constexpr int pp = decltype(ppc)::value;
+      VPieces<C, pp> vp;
+      read_v<C, pp>(vp, av);
+#pragma unroll
+      for (int e = 0; e < C::DB; ++e) {
+        const bf16x8 va = v_operand<FP8>(vp, e);
+#pragma unroll
+        for (int bb = 0; bb < C::NB; ++bb)
+          acc[bb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop[bb][pp], acc[bb][e], 0, 0, 0);
+      }
+    });
+  }
+
+  // totals over the four lane rows (disjoint tokens), then the outputs:
+  // lane (r, c) holds d = (4 r + j) DB + e of its column
+  const bool poisoned = __syncthreads_or(bad_page) != 0;
+#pragma unroll
+  for (int bb = 0; bb < C::NB; ++bb) {
+    float lt = l[bb];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    if (orow[bb] < 0) continue;
+    float* o = p.out + orow[bb] * D;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float r[C::DB];
+#pragma unroll
+      for (int e = 0; e < C::DB; ++e) r[e] = poisoned ? nan : (lt != 0.0f ? acc[bb][e][j] / lt : 0.0f);
+#pragma unroll
+      for (int e = 0; e < C::DB; e += 4)
+        *reinterpret_cast<f32x4*>(o + (4 * g + j) * C::DB + e) = f32x4{r[e], r[e + 1], r[e + 2], r[e + 3]};
+    }
+    if (p.lse != nullptr && g == 0)
+      p.lse[orow[bb]] = poisoned ? nan : (lt != 0.0f ? (m[bb] + log2f(lt)) * dev::kLn2 : -__builtin_inff());
+  }
+}
+
+template <int D, bool FP8>
+hipError_t launch_one(const PrefillParams& p, uint32_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL((prefill_kernel<D, FP8>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, bool fp8, uint32_t grid, hipStream_t stream) {
+  if (head_dim == 64) return fp8 ? launch_one<64, true>(p, grid, stream) : launch_one<64, false>(p, grid, stream);
+  if (head_dim == 128) return fp8 ? launch_one<128, true>(p, grid, stream) : launch_one<128, false>(p, grid, stream);
+  if (head_dim == 256) return fp8 ? launch_one<256, true>(p, grid, stream) : launch_one<256, false>(p, grid, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pdattn

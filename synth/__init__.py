@@ -28,7 +28,7 @@ import math
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "kv_bytes", "make_append_inputs", "append_bytes", "to_hnd",
-           "make_prefill_inputs", "prefill_flops",
+           "make_prefill_inputs", "prefill_flops", "PREFILL_WORKLOADS", "prefill_workload",
            "from_hnd"]
 
 E4M3_MAX = 448.0
@@ -340,3 +340,34 @@ def prefill_flops(q_lens, context_lens, num_q_heads, head_dim, causal=True) -> i
             lim = L - n + i + 1 if causal else L
             pairs += min(max(lim, 0), L)
     return 4 * head_dim * num_q_heads * pairs
+
+
+# Prefill workloads: name -> (description, heads/dims, q length recipe,
+# prefix recipe, seed). Lengths are drawn with torch.randint (inclusive) from
+# torch.Generator().manual_seed(seed + 2).
+PREFILL_WORKLOADS = {
+    "llama3_8b_prefill": ("Llama-3-8B-shaped ragged paged prefill: 8 prompts, q lengths ~U[512, 2048], no cached "
+                          "prefix, 32 q / 8 kv heads, d128, P16, bf16, causal",
+                          dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16), 8, (512, 2048), (0, 0),
+                          3900),
+    "llama3_8b_prefill_2048": ("one Llama-3-8B-shaped prompt, q = kv = 2048, 32 q / 8 kv heads, d128, P16, bf16, "
+                               "causal", dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16), 1,
+                               (2048, 2048), (0, 0), 3901),
+    "llama3_8b_chunked_prefill": ("Llama-3-8B-shaped chunked prefill: 16 requests, 512-row chunks after cached "
+                                  "prefixes ~U[0, 4096], 32 q / 8 kv heads, d128, P16, bf16, causal",
+                                  dict(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16), 16, (512, 512),
+                                  (0, 4096), 3902),
+}
+
+
+def prefill_workload(name, **overrides):
+    """Draw the named prefill workload's inputs (``make_prefill_inputs``)."""
+    desc, dims, batch, qr, pr, seed = PREFILL_WORKLOADS[name]
+    g = torch.Generator().manual_seed(seed + 2)
+    q_lens = torch.randint(qr[0], qr[1] + 1, (batch,), generator=g).tolist()
+    prefix = torch.randint(pr[0], pr[1] + 1, (batch,), generator=g).tolist()
+    kw = dict(dims, q_lens=q_lens, prefix_lens=prefix, seed=seed)
+    kw.update(overrides)
+    inp = make_prefill_inputs(**kw)
+    inp["description"] = desc
+    return inp

@@ -286,6 +286,61 @@ def time_merge(pk, flush, dev, reps=20):
     return res
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def time_prefill(pk, flush, dev, reps=20):
+    """Ragged paged prefill (pdattn_prefill, one launch per call; the tile
+    map is built once per batch on the host, outside the timing): the three
+    prefill workloads with bf16 pools, and the ragged batch with fp8 pools.
+    Caches flushed before every call. TFLOP/s = algorithmic flops (4 d per
+    (query row, head, visible position)) / mean call time, against the dense
+    bf16 MFMA peak (both products run on bf16 MFMA; fp8 codes are widened)."""
+    import torch
+    import synth
+    res = {}
+    runs = [(name, "bf16") for name in sorted(synth.PREFILL_WORKLOADS)] + [("llama3_8b_prefill", "fp8_e4m3")]
+    for name, kv in runs:
+        inp = synth.prefill_workload(name, kv_dtype=kv)
+        src = synth.to_hnd(inp)
+        d = {k: (src[k].to(dev) if src.get(k) is not None else None)
+             for k in ("q", "qo_indptr", "k_pages", "v_pages", "k_scale", "v_scale", "block_table", "context_lens")}
+        prob = pk._prefill_problem(d["q"], d["k_pages"], d["block_table"], pk.LAYOUT_HND, None)
+        rt = pk.prefill_rows_per_tile(prob)
+        tb, ti = pk.prefill_tiles(inp["qo_indptr"], rt, context_lens_host=inp["context_lens"])
+        tb, ti = tb.to(dev), ti.to(dev)
+        out = torch.empty(d["q"].shape, dtype=torch.float32, device=dev)
+        lse = torch.empty(d["q"].shape[:2], dtype=torch.float32, device=dev)
+
+        def call():
+            pk.prefill(prob, d["q"], d["qo_indptr"], tb, ti, d["k_pages"], d["v_pages"], d["k_scale"],
+                       d["v_scale"], d["block_table"], d["context_lens"], out, lse)
+        for _ in range(3):
+            call()
+        ts = []
+        for i in range(reps):
+            flush.fill_(i & 0xFF)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        us = statistics.fmean(ts)
+        flops = synth.prefill_flops(inp["q_lens"], inp["context_lens"], prob.num_q_heads, prob.head_dim)
+        tf = flops / (us * 1e-6) / 1e12
+        res[f"{name}_{kv}"] = {
+            "q_rows": int(inp["q_lens"].sum()), "q_lens": inp["q_lens"].tolist(),
+            "context_lens": inp["context_lens"].tolist(), "tiles": int(tb.numel()), "rows_per_tile": rt,
+            "workgroups": int(tb.numel()) * prob.num_kv_heads, "flops": flops, "us_per_call": round(us, 2),
+            "tflops": round(tf, 1), "roofline": {"bound": "mfma", "achieved": round(tf, 1),
+                                                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                                 "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)},
+            "outputs_finite": bool(torch.isfinite(out).all())}
+        del d, out, lse, inp, src
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -303,6 +358,7 @@ def main():
     ap.add_argument("--no-append", action="store_true", help="skip the KV-append timings")
     ap.add_argument("--no-merge", action="store_true", help="skip the partial-state merge timings")
     ap.add_argument("--no-multi-query", action="store_true", help="skip the multi-query decode timing")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the ragged paged prefill timing")
     ap.add_argument("--no-d256", action="store_true", help="skip the head_dim 256 timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run 3 device copies of 256 MiB (a plain copy kernel of known "
@@ -437,6 +493,7 @@ def main():
     merge = None if args.no_merge else time_merge(pk, flush, dev)
     multi = None if args.no_multi_query else time_multi_query(pk, w, inp, args, flush, dev)
     d256 = None if args.no_d256 else time_d256(pk, w, args, flush, dev)
+    prefill = None if args.no_prefill else time_prefill(pk, flush, dev)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -523,6 +580,7 @@ def main():
         "merge": merge,
         "multi_query": multi,
         "head_dim_256": d256,
+        "prefill": prefill,
     }
     print(json.dumps(rec), flush=True)
 

@@ -215,31 +215,39 @@ __device__ __forceinline__ void read_v(VPieces<C, P_>& v, uint32_t av) {
   }
 }
 
-// The V^T operand of d-block e: element e of the eight k slots' pieces.
+// The V^T operand of d-block e: element e of the eight k slots' pieces,
+// gathered with byte permutes (perm(s0, s1, sel): selector bytes 0-3 pick
+// bytes of s1, 4-7 bytes of s0).
 template <bool FP8, typename VP>
 __device__ __forceinline__ bf16x8 v_operand(const VP& v, int e) {
   if constexpr (FP8) {
-    const int wd = e >> 2, sh = 8 * (e & 3);
+    const int wd = e >> 2, b = e & 3;
+    const uint32_t pick2 = (uint32_t)(((4 + b) << 8) | b);  // byte b of s1, then byte b of s0
     uint32_t x[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      x[h] = ((v.w[4 * h + 0][wd] >> sh) & 0xffu) | (((v.w[4 * h + 1][wd] >> sh) & 0xffu) << 8) |
-             (((v.w[4 * h + 2][wd] >> sh) & 0xffu) << 16) | (((v.w[4 * h + 3][wd] >> sh) & 0xffu) << 24);
+      const uint32_t lo = __builtin_amdgcn_perm(v.w[4 * h + 1][wd], v.w[4 * h + 0][wd], pick2);
+      const uint32_t hi = __builtin_amdgcn_perm(v.w[4 * h + 3][wd], v.w[4 * h + 2][wd], pick2);
+      x[h] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
     }
     return __builtin_bit_cast(bf16x8, dev::fp8x8_to_bf16x8(x[0], x[1]));
   } else {
-    const int wd = e >> 1, sh = 16 * (e & 1);
+    const int wd = e >> 1;
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of s1 then s0
     u32x4 r;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      r[q] = ((v.w[2 * q][wd] >> sh) & 0xffffu) | (((v.w[2 * q + 1][wd] >> sh) & 0xffffu) << 16);
+    for (int q = 0; q < 4; ++q) r[q] = __builtin_amdgcn_perm(v.w[2 * q + 1][wd], v.w[2 * q][wd], sel);
     return __builtin_bit_cast(bf16x8, r);
   }
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats as bf16 (round to nearest even), a in the low half: one
+// v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  const __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
 }
 
 template <int D, bool FP8>
@@ -389,7 +397,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     issue(0, 0, e0, e1);
     if (T > 1) load_pages(C::NT, e0, e1);
   }
-  for (int it = 0; it < T; ++it) {
+  // one K/V tile: wait for its loads, start the next tile's, then compute.
+  // MASKED (a compile-time flag) applies the columns' limits; the tiles that
+  // need it come last, in a loop of their own, so that neither loop merges
+  // masked and unmasked scores before the max (a merge would make the
+  // compiler re-canonicalise every score)
+  auto tile_step = [&](int it, auto masked_c) {
+    constexpr bool MASKED = decltype(masked_c)::value;
     dev::wait_vmcnt<0>();
     __syncthreads();  // every wave's loads of tile it landed; stage (it + 1) & 1 is free
     const int tb = it * C::NT;
@@ -436,36 +450,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         // to one element of a vector (every element reads as element 0)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          ksc[mb][j] = __uint_as_float(s2[0][j]);
+          ksc[mb][j] = __uint_as_float(s2[0][j]) * p.qk_scale_log2;
           vsc[mb][j] = __uint_as_float(s2[1][j]);
         }
       });
     }
 
-    // online softmax per column block; P as the B operand of p.V
-    const bool need_mask = tb + C::NT > mask_from;
+    // online softmax per column block in base 2; P as the B operand of
+    // p.V. Scores x = q.k * scale * log2 e (fp8: times the k scale, folded
+    // into the scale reads); the multiply also gives the max canonical
+    // inputs, which a raw MFMA result is not known to be
     bf16x8 pop[C::NB][C::PS];
 #pragma unroll
     for (int bb = 0; bb < C::NB; ++bb) {
       float x[C::MB][4];
-      float mx = -__builtin_inff();
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float s = S[mb][bb][j] * p.qk_scale_log2;
-          if constexpr (FP8) s *= ksc[mb][j];
-          if (need_mask && tb + 16 * mb + 4 * g + j >= lim[bb]) s = -__builtin_inff();
-          x[mb][j] = s;
-          mx = fmaxf(mx, s);
-        }
+        for (int j = 0; j < 4; ++j) x[mb][j] = S[mb][bb][j] * (FP8 ? ksc[mb][j] : p.qk_scale_log2);
+      if constexpr (MASKED) {
+        // only tiles that reach past some column's limit: token
+        // tb + 16 mb + 4 r + j is visible iff 16 mb + j < rel
+        const int rel = lim[bb] - (tb + 4 * g);
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (16 * mb + j >= rel) x[mb][j] = -__builtin_inff();
+      }
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb)
+        mx = fmaxf(fmaxf(mx, fmaxf(x[mb][0], x[mb][1])), fmaxf(x[mb][2], x[mb][3]));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m[bb], mx);
+      // the running max moves only when a column's max exceeds it by more
+      // than 8 in the exponent (or it is still -inf): every weight stays
+      // below 2^8, and since numerator and denominator are taken against
+      // the same m the result does not depend on it. A NaN max leaves m
+      // alone (and the NaN reaches l and the output through the weights)
+      const float m_old = m[bb];
+      const bool up = mx - m_old > 8.0f;
+      const float m_new = up ? mx : m_old;
       // a column with nothing visible yet keeps m = -inf; its weights are
       // then taken against 0 and are exactly 0
       const float m_ref = m_new == -__builtin_inff() ? 0.0f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m[bb] - m_ref);
+      if (__any(up)) {
+        const float alpha = __builtin_amdgcn_exp2f(m_old - m_ref);  // 1 where m stays
+        l[bb] *= alpha;
+#pragma unroll
+        for (int e = 0; e < C::DB; ++e) acc[bb][e] *= alpha;
+      }
+      m[bb] = m_new;
       float sum = 0.0f;
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb)
@@ -474,13 +510,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
           x[mb][j] = __builtin_amdgcn_exp2f(x[mb][j] - m_ref);
           sum += x[mb][j];
         }
-      l[bb] = l[bb] * alpha + sum;
-      const bool grew = m_new > m[bb];
-      m[bb] = m_new;
-      if (__any(grew)) {
-#pragma unroll
-        for (int e = 0; e < C::DB; ++e) acc[bb][e] *= alpha;
-      }
+      l[bb] += sum;
 #pragma unroll
       for (int pp = 0; pp < C::PS; ++pp) {
         float y[8];
@@ -513,7 +543,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
           acc[bb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop[bb][pp], acc[bb][e], 0, 0, 0);
       }
     });
-  }
+  };
+  // tiles entirely below every column's limit, then the rest
+  const int T_open = min(T, mask_from / C::NT);
+  int it = 0;
+  for (; it < T_open; ++it) tile_step(it, std::false_type{});
+  for (; it < T; ++it) tile_step(it, std::true_type{});
 
   // totals over the four lane rows (disjoint tokens), then the outputs:
   // lane (r, c) holds d = (4 r + j) DB + e of its column

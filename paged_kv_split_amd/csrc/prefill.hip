@@ -350,10 +350,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     return ((long long)page * P * p.num_kv_heads) + (long long)(pos & (P - 1)) * p.slot_stride +
            (long long)kvh * p.head_stride;
   };
+  // Per-lane byte offsets of the loads inside the wave's 16-token group,
+  // fixed for the whole call: the group's token x sits x * slot_stride rows
+  // after the group's first row, when the group lies in one page.
+  const uint32_t slot_bytes = (uint32_t)p.slot_stride * C::ROW;
+  uint32_t koff[C::KI], voff[C::VI];
+#pragma unroll
+  for (int i = 0; i < C::KI; ++i) koff[i] = n * slot_bytes + 16 * g + 64 * ((w * C::KI + i) % C::QK);
+#pragma unroll
+  for (int i = 0; i < C::VI; ++i) {
+    const int cv = (w * C::VI + i) * 64 + lane;
+    voff[i] = (uint32_t)(cv * 16 / C::ROW - 16 * mbK) * slot_bytes + (cv * 16) % C::ROW;
+  }
+  const uint32_t soff = (uint32_t)((lane & 15) * p.slot_stride) * 4u;
+  const float* sbase_lane = lane < 16 ? p.k_scale : p.v_scale;
   auto issue = [&](int tb, int stage, int raw0, int raw1) {
     const int e0 = check_page(raw0), e1 = check_page(raw1);
     unsigned char* st = smem + stage * C::STAGE;
     const int first = group_first(tb);
+    if (P >= 16 && tb + C::NT <= L) {
+      // the group is 16-aligned and inside one page, every position < L:
+      // a wave-uniform row base plus the fixed lane offsets
+      const int tg = tb + 16 * mbK;
+      const long long rb = (long long)e0 * P * p.num_kv_heads + (long long)(tg & (P - 1)) * p.slot_stride +
+                           (long long)kvh * p.head_stride;
+      const uint8_t* kb = p.k + rb * C::ROW;
+      const uint8_t* vb = p.v + rb * C::ROW;
+#pragma unroll
+      for (int i = 0; i < C::KI; ++i) dev::dma16(kb + koff[i], st + (w * C::KI + i) * 1024);
+#pragma unroll
+      for (int i = 0; i < C::VI; ++i) dev::dma16(vb + voff[i], st + C::K_T + (w * C::VI + i) * 1024);
+      if constexpr (FP8) {
+        if ((w * C::KI) % C::QK == 0 && lane < 32)
+          dev::dma4(reinterpret_cast<const uint8_t*>(sbase_lane + rb) + soff, st + C::K_T + C::V_T + mbK * 128);
+      }
+      return;
+    }
     {
       const int pos = min(tb + 16 * mbK + n, L - 1);
       const uint8_t* src = p.k + row_of(pos, first, e0, e1) * C::ROW + 16 * g;

@@ -154,9 +154,10 @@ __device__ __forceinline__ void lds_b32x8(uint32_t (&r)[8], uint32_t a) {
       : "memory");
 }
 
-// The K chunks of M-block MB_ (QK 16-byte reads from the lane's slot).
+// The K chunks of M-block MB_ and the ones after it (QK 16-byte reads from
+// the lane's slot per M-block, one LDS wait for all of them).
 template <typename C, int MB_, size_t... I>
-__device__ __forceinline__ void read_k(u32x4 (&r)[C::QK], uint32_t ak, std::index_sequence<I...>) {
+__device__ __forceinline__ void read_k(u32x4 (&r)[sizeof...(I)], uint32_t ak, std::index_sequence<I...>) {
   lds_b128<(int)((MB_ * C::QK + I) * 1024)...>(r, ak);
 }
 
@@ -239,6 +240,17 @@ __device__ __forceinline__ bf16x8 v_operand(const VP& v, int e) {
     for (int q = 0; q < 4; ++q) r[q] = __builtin_amdgcn_perm(v.w[2 * q + 1][wd], v.w[2 * q][wd], sel);
     return __builtin_bit_cast(bf16x8, r);
   }
+}
+
+// Maximum over the four 16-lane rows, for every lane (the lane's column
+// in each row): gfx950's row swaps (permlane16 pairs rows 0-1 and 2-3,
+// permlane32 the two halves; with both operands x, the two results of a
+// lane are its own value and its partner's), plain VALU, no LDS trip.
+__device__ __forceinline__ float max_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -445,12 +457,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
     const uint32_t sb = lds0 + (it & 1) * C::STAGE;
 
+    // the MFMA phases run at raised wave priority, so that the other waves
+    // of the SIMD fill the VALU around them instead of competing for issue
+    __builtin_amdgcn_s_setprio(1);
     // S^T = K . Q^T
     f32x4 S[C::MB][C::NB];
+    constexpr int KG = 2 * C::QK <= 8 ? 2 : 1;  // M-blocks per LDS wait
+    u32x4 kcg[KG * C::QK];
     dev::static_for<0, C::MB>([&](auto mbc) {
       constexpr int mb = decltype(mbc)::value;
-      u32x4 kc[C::QK];
-      read_k<C, mb>(kc, sb + lane * 16, std::make_index_sequence<C::QK>{});
+      if constexpr (mb % KG == 0) read_k<C, mb>(kcg, sb + lane * 16, std::make_index_sequence<KG * C::QK>{});
+      const u32x4* kc = kcg + (mb % KG) * C::QK;
 #pragma unroll
       for (int bb = 0; bb < C::NB; ++bb) S[mb][bb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -472,6 +489,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       }
     });
 
+    __builtin_amdgcn_s_setprio(0);
     float ksc[C::MB][4], vsc[C::MB][4];
     if constexpr (FP8) {
       dev::static_for<0, C::MB>([&](auto mbc) {
@@ -514,8 +532,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb)
         mx = fmaxf(fmaxf(mx, fmaxf(x[mb][0], x[mb][1])), fmaxf(x[mb][2], x[mb][3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_rows(mx);
       // the running max moves only when a column's max exceeds it by more
       // than 8 in the exponent (or it is still -inf): every weight stays
       // below 2^8, and since numerator and denominator are taken against
@@ -561,6 +578,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       }
     }
 
+    __builtin_amdgcn_s_setprio(1);
     // O^T += V^T . P
     const uint32_t av = sb + C::K_T + 4 * g * C::ROW + n * C::VR;
     dev::static_for<0, C::PS>([&](auto ppc) {
@@ -575,6 +593,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
           acc[bb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop[bb][pp], acc[bb][e], 0, 0, 0);
       }
     });
+    __builtin_amdgcn_s_setprio(0);
   };
   // tiles entirely below every column's limit, then the rest
   const int T_open = min(T, mask_from / C::NT);

@@ -23,6 +23,11 @@ MI355X's 8 TB/s HBM peak. traffic = measured HBM bytes per launch of that kernel
 committed rocprofv3 counter summary, or null when the kernel's sources have
 changed since the counters were taken. cpu_baseline = the CPU fp64 oracle
 timed on this host's cores on the same step's inputs.
+
+prefill = the ragged paged prefill (pdattn_prefill) on its three workloads
+(synth.PREFILL_WORKLOADS) and the ragged batch with fp8 pools, each call
+timed alone after a cache flush; roofline there = algorithmic flops / mean
+call time against the dense bf16 MFMA peak.
 """
 import argparse
 import hashlib

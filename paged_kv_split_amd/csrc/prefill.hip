@@ -65,11 +65,6 @@ struct Cfg {
   static constexpr int VI = V_T / (kWaves * 64 * 16);
   static constexpr int VR = DB * ESZ;               // bytes of a lane's V piece of one token
   static constexpr int COLS = kWaves * 16 * NB;
-  // 128-byte V rows (bf16 d64, fp8 d128): rows t and t + 4 would sit on the
-  // same 32 LDS banks, and the p.V reads of lane rows 0 and 1 (tokens 4
-  // apart) share a phase; rows with bit 2 of t set store their two 64-byte
-  // halves swapped
-  static constexpr int VSW = ROW == 128 ? 64 : 0;
   static_assert(COLS == prefill_columns(D), "columns");
   static_assert(KI >= 1 && QK % KI == 0 && VI >= 1, "load split");
   static_assert(MB * QK == kWaves * KI, "K image");
@@ -377,8 +372,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
   for (int i = 0; i < C::VI; ++i) {
     const int cv = (w * C::VI + i) * 64 + lane;
-    const int t = cv * 16 / C::ROW;  // token of the tile; its bytes at ((cv * 16) mod ROW) ^ swizzle
-    voff[i] = (uint32_t)(t - 16 * mbK) * slot_bytes + (((cv * 16) % C::ROW) ^ ((t & 4) ? C::VSW : 0));
+    voff[i] = (uint32_t)(cv * 16 / C::ROW - 16 * mbK) * slot_bytes + (cv * 16) % C::ROW;
   }
   const uint32_t soff = (uint32_t)((lane & 15) * p.slot_stride) * 4u;
   const float* sbase_lane = lane < 16 ? p.k_scale : p.v_scale;
@@ -417,8 +411,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     for (int i = 0; i < C::VI; ++i) {
       const int cv = (w * C::VI + i) * 64 + lane;
       const int pos = min(tb + cv * 16 / C::ROW, L - 1);
-      const int t = cv * 16 / C::ROW;
-      dev::dma16(p.v + row_of(pos, first, e0, e1) * C::ROW + (((cv * 16) % C::ROW) ^ ((t & 4) ? C::VSW : 0)),
+      dev::dma16(p.v + row_of(pos, first, e0, e1) * C::ROW + (cv * 16) % C::ROW,
                  st + C::K_T + (w * C::VI + i) * 1024);
     }
     if constexpr (FP8) {
@@ -587,8 +580,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
     __builtin_amdgcn_s_setprio(1);
     // O^T += V^T . P
-    // the tokens a lane reads have bit 2 equal to its row's bit 0
-    const uint32_t av = sb + C::K_T + 4 * g * C::ROW + ((n * C::VR) ^ ((g & 1) ? C::VSW : 0));
+    const uint32_t av = sb + C::K_T + 4 * g * C::ROW + n * C::VR;
     dev::static_for<0, C::PS>([&](auto ppc) {
       constexpr int pp = decltype(ppc)::value;
       VPieces<C, pp> vp;

@@ -100,8 +100,22 @@ typedef enum pdattn_status {
 
 typedef enum pdattn_kv_dtype {
   PDATTN_KV_BF16 = 0,
-  PDATTN_KV_FP8_E4M3 = 1 /* OCP e4m3fn codes with one fp32 scale per (token, kv head) */
+  PDATTN_KV_FP8_E4M3 = 1, /* OCP e4m3fn codes with one fp32 scale per (token, kv head) */
+  PDATTN_KV_FP8_E4M3_INLINE = 2 /* the same codes and scales, each row's scale stored after its codes */
 } pdattn_kv_dtype;
+
+/*
+ * PDATTN_KV_FP8_E4M3_INLINE (DeepGEMM documentation section 6.1: the paged
+ * cache of its indexer keeps each token's fp32 scale in the byte cache,
+ * after the token's value bytes): a pool row is d e4m3fn code bytes followed
+ * by 4 bytes holding the row's fp32 scale (little-endian), so rows are
+ * d + 4 bytes apart and 4-byte aligned; the row order inside a page is
+ * problem->kv_layout's, as for the other dtypes. k_scale and v_scale are
+ * NULL. The stored value of element i is e4m3fn(code_i) * scale, as for
+ * PDATTN_KV_FP8_E4M3. Served by static decode plans (one-token and
+ * multi-query) and by pdattn_kv_append; balanced plans and pdattn_prefill
+ * return PDATTN_ERR_UNSUPPORTED.
+ */
 
 /* The order of the (slot, kv head) rows inside one page of the K and V
  * pools (and of the fp8 scales). The paged addressing (FlashQuant wiki "CUDA

@@ -15,10 +15,11 @@ import torch
 __all__ = ["Problem", "Plan", "PdattnError", "plan", "decode", "reduce", "workspace", "workspace_init",
            "paged_decode", "KV_BF16", "KV_FP8_E4M3", "PLAN_BALANCED", "library_path", "stream_read",
            "stream_read_sink", "kv_append", "APPEND_POW2_SCALES", "fp8_conversion_check", "merge", "LAYOUT_NHD", "LAYOUT_HND",
-           "pool_dims", "prefill_rows_per_tile", "prefill_tiles", "prefill", "paged_prefill", "TILES_LONGEST_FIRST"]
+           "pool_dims", "kv_kind", "KV_FP8_E4M3_INLINE", "prefill_rows_per_tile", "prefill_tiles", "prefill", "paged_prefill", "TILES_LONGEST_FIRST"]
 
 KV_BF16 = 0
 KV_FP8_E4M3 = 1
+KV_FP8_E4M3_INLINE = 2   # uint8 pools, rows of d codes then the row's fp32 scale
 PLAN_BALANCED = 2
 LAYOUT_NHD = 0   # pool rows [page][slot][kv head]
 LAYOUT_HND = 1   # pool rows [page][kv head][slot]
@@ -132,6 +133,14 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def kv_kind(pages):
+    """The kv dtype of a pool tensor: bf16; float8_e4m3fn (separate scale
+    arrays); uint8 (inline-scale fp8 rows of d codes and 4 scale bytes)."""
+    if pages.dtype == torch.uint8:
+        return KV_FP8_E4M3_INLINE
+    return KV_FP8_E4M3 if pages.dtype == torch.float8_e4m3fn else KV_BF16
+
+
 def pool_dims(pages, layout=LAYOUT_NHD):
     """(num_pages, P, Hkv, d) of a pool tensor in the given layout."""
     n, a, b, d = pages.shape
@@ -198,12 +207,14 @@ def kv_append(k_new, v_new, token_seq, token_pos, block_table, k_pages, v_pages,
 
     k_new/v_new: bf16 [N,Hkv,d]; token_seq/token_pos: int32 [N]; block_table
     int32 [B,max_pages]; k_pages/v_pages: bf16 or float8_e4m3fn, [num_pages,P,Hkv,d]
-    (NHD) or [num_pages,Hkv,P,d] (HND); k_scale/v_scale: fp32, one per row, for
-    fp8 pools. ``batch`` defaults to the block table's row count.
+    (NHD) or [num_pages,Hkv,P,d] (HND), or uint8 rows of d + 4 bytes
+    (inline-scale fp8); k_scale/v_scale: fp32, one per row, for float8 pools
+    (None otherwise). ``batch`` defaults to the block table's row count.
     """
     N = k_new.shape[0]
-    num_pages, P, Hkv, D = pool_dims(k_pages, layout)
-    kv = KV_FP8_E4M3 if k_pages.dtype == torch.float8_e4m3fn else KV_BF16
+    num_pages, P, Hkv, _ = pool_dims(k_pages, layout)
+    D = k_new.shape[-1]
+    kv = kv_kind(k_pages)
     B = block_table.shape[0] if batch is None else batch
     prob = Problem(B, Hkv, Hkv, D, P, block_table.shape[1], num_pages, kv, 0.0, layout, 1)
     flags = APPEND_POW2_SCALES if pow2_scales else 0
@@ -242,15 +253,17 @@ def paged_decode(q, k_pages, v_pages, block_table, context_lens, *, context_lens
     q: bf16 [B,Hq,d], or [B,n,Hq,d] for multi-query decode (n query rows per
     sequence, the last n positions of its context; outputs then [B,n,Hq,d]
     and [B,n,Hq]); k_pages/v_pages: bf16 or float8_e4m3fn, [num_pages,P,Hkv,d]
-    (NHD) or [num_pages,Hkv,P,d] (HND); block_table int32 [B,max_pages];
-    context_lens int32 [B] on the device.
+    (NHD) or [num_pages,Hkv,P,d] (HND), or uint8 with rows of d + 4 bytes
+    (inline-scale fp8: the codes, then the row's fp32 scale; k_scale and
+    v_scale None); block_table int32 [B,max_pages]; context_lens int32 [B]
+    on the device.
     """
     n = q.shape[1] if q.dim() == 4 else 1
     B, Hq, D = q.shape[0], q.shape[-2], q.shape[-1]
     num_pages, P, Hkv, _ = pool_dims(k_pages, layout)
     if context_lens_host is None:
         context_lens_host = context_lens.cpu()
-    kv = KV_FP8_E4M3 if k_pages.dtype == torch.float8_e4m3fn else KV_BF16
+    kv = kv_kind(k_pages)
     pl = plan(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=P,
               max_pages_per_seq=block_table.shape[1], num_pages=num_pages, kv_dtype=kv,
               scale=0.0 if scale is None else scale, context_lens_host=context_lens_host,
@@ -268,7 +281,7 @@ def paged_decode(q, k_pages, v_pages, block_table, context_lens, *, context_lens
 def _prefill_problem(q, k_pages, block_table, layout, scale):
     Hq, D = q.shape[1], q.shape[2]
     num_pages, P, Hkv, _ = pool_dims(k_pages, layout)
-    kv = KV_FP8_E4M3 if k_pages.dtype == torch.float8_e4m3fn else KV_BF16
+    kv = kv_kind(k_pages)
     return Problem(block_table.shape[0], Hq, Hkv, D, P, block_table.shape[1], num_pages, kv,
                    0.0 if scale is None else float(scale), layout, 1)
 

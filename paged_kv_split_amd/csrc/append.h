@@ -14,9 +14,9 @@ struct AppendParams {
   const int32_t* token_seq;   // [num_tokens]
   const int32_t* token_pos;   // [num_tokens]
   const int32_t* block_table; // [B][max_pages_per_seq]
-  void* k_pages;              // pool rows of D * esize bytes
+  void* k_pages;              // pool rows of D * esize bytes (D + 4 with inline scales)
   void* v_pages;
-  float* k_scale;             // fp8 pools: one per row
+  float* k_scale;             // fp8 pools with separate scales: one per row
   float* v_scale;
   int32_t num_tokens;
   int32_t batch;
@@ -25,6 +25,7 @@ struct AppendParams {
   int32_t max_pages_per_seq;
   int32_t num_pages;
   int32_t pow2_scales;        // fp8: power-of-two scales instead of absmax / 448
+  int32_t inline_scales;      // fp8: rows of D codes then the fp32 scale (D + 4 bytes apart)
   int32_t slot_stride;        // row index = page * P * Hkv + slot * slot_stride + kvh * head_stride
   int32_t head_stride;
 };

@@ -66,10 +66,10 @@ __device__ __forceinline__ void worker_range(long long w, long long nw, long lon
 
 // fp8 d128 with up to 4 columns: the LDS holds four workgroups per CU; the
 // register budget is held to the 128 VGPRs that let four waves share a SIMD
-template <int D, int G, bool FP8>
+template <int D, int G, bool FP8, bool INL = false>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FP8 && D == 128 && G <= 4 ? 4 : 1)))
 void decode_kernel(DecodeParams p) {
-  using TL = Tile<D, G, FP8>;
+  using TL = Tile<D, G, FP8, INL>;
   constexpr int C = TL::C;
   constexpr int NT = kWaves * 64;
   constexpr int S = kStages;
@@ -401,42 +401,56 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(MergeParams p) 
   }
 }
 
-template <int D, int G, bool FP8>
+template <int D, int G, bool FP8, bool INL>
 hipError_t launch_one(const DecodeParams& p, uint32_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, G, FP8>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
+  hipLaunchKernelGGL((decode_kernel<D, G, FP8, INL>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, int G, bool FP8>
+template <int D, int G, bool FP8, bool INL>
 int occupancy_one() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, G, FP8>, kWaves * 64, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, G, FP8, INL>, kWaves * 64, 0) != hipSuccess)
     return 0;
   return n;
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool INL>
 int occupancy_group(int group) {
   switch (group) {
-    case 1: return occupancy_one<D, 1, FP8>();
-    case 2: return occupancy_one<D, 2, FP8>();
-    case 4: return occupancy_one<D, 4, FP8>();
-    case 8: return occupancy_one<D, 8, FP8>();
-    case 16: return occupancy_one<D, 16, FP8>();
+    case 1: return occupancy_one<D, 1, FP8, INL>();
+    case 2: return occupancy_one<D, 2, FP8, INL>();
+    case 4: return occupancy_one<D, 4, FP8, INL>();
+    case 8: return occupancy_one<D, 8, FP8, INL>();
+    case 16: return occupancy_one<D, 16, FP8, INL>();
     default: return 0;
   }
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool INL>
 hipError_t launch_group(const DecodeParams& p, int group, uint32_t grid, hipStream_t stream) {
   switch (group) {
-    case 1: return launch_one<D, 1, FP8>(p, grid, stream);
-    case 2: return launch_one<D, 2, FP8>(p, grid, stream);
-    case 4: return launch_one<D, 4, FP8>(p, grid, stream);
-    case 8: return launch_one<D, 8, FP8>(p, grid, stream);
-    case 16: return launch_one<D, 16, FP8>(p, grid, stream);
+    case 1: return launch_one<D, 1, FP8, INL>(p, grid, stream);
+    case 2: return launch_one<D, 2, FP8, INL>(p, grid, stream);
+    case 4: return launch_one<D, 4, FP8, INL>(p, grid, stream);
+    case 8: return launch_one<D, 8, FP8, INL>(p, grid, stream);
+    case 16: return launch_one<D, 16, FP8, INL>(p, grid, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+// kind: 0 bf16, 1 fp8 with separate scales, 2 fp8 with inline scales
+template <int D>
+int occupancy_kind(int group, int kind) {
+  return kind == 0 ? occupancy_group<D, false, false>(group)
+                   : kind == 1 ? occupancy_group<D, true, false>(group) : occupancy_group<D, true, true>(group);
+}
+
+template <int D>
+hipError_t launch_kind(const DecodeParams& p, int group, int kind, uint32_t grid, hipStream_t stream) {
+  return kind == 0 ? launch_group<D, false, false>(p, group, grid, stream)
+                   : kind == 1 ? launch_group<D, true, false>(p, group, grid, stream)
+                               : launch_group<D, true, true>(p, group, grid, stream);
 }
 
 template <int D>
@@ -455,21 +469,19 @@ hipError_t launch_merge_d(const MergeParams& p, int group, uint32_t grid, hipStr
 
 }  // namespace
 
-int decode_wgs_per_cu(int head_dim, int group, bool fp8) {
-  if (head_dim == 64) return fp8 ? occupancy_group<64, true>(group) : occupancy_group<64, false>(group);
-  if (head_dim == 128) return fp8 ? occupancy_group<128, true>(group) : occupancy_group<128, false>(group);
-  if (head_dim == 256) return fp8 ? occupancy_group<256, true>(group) : occupancy_group<256, false>(group);
+int decode_wgs_per_cu(int head_dim, int group, int kind) {
+  if (head_dim == 64) return occupancy_kind<64>(group, kind);
+  if (head_dim == 128) return occupancy_kind<128>(group, kind);
+  if (head_dim == 256) return occupancy_kind<256>(group, kind);
   return 0;
 }
 
-hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, bool fp8, uint32_t grid,
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, int kind, uint32_t grid,
                          hipStream_t stream) {
-  if (head_dim == 64) return fp8 ? launch_group<64, true>(p, group, grid, stream)
-                                 : launch_group<64, false>(p, group, grid, stream);
-  if (head_dim == 128) return fp8 ? launch_group<128, true>(p, group, grid, stream)
-                                  : launch_group<128, false>(p, group, grid, stream);
-  if (head_dim == 256) return fp8 ? launch_group<256, true>(p, group, grid, stream)
-                                  : launch_group<256, false>(p, group, grid, stream);
+  if (kind < 0 || kind > 2) return hipErrorInvalidValue;
+  if (head_dim == 64) return launch_kind<64>(p, group, kind, grid, stream);
+  if (head_dim == 128) return launch_kind<128>(p, group, kind, grid, stream);
+  if (head_dim == 256) return launch_kind<256>(p, group, kind, grid, stream);
   return hipErrorInvalidValue;
 }
 

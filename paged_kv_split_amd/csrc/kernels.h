@@ -129,12 +129,16 @@ struct MergeParams {
   int32_t num_cols;
 };
 
+// KV kinds of the static decode kernel: bf16, fp8 with separate scale
+// arrays, fp8 with each row's scale after its codes.
+constexpr int kKindBf16 = 0, kKindFp8 = 1, kKindFp8Inline = 2;
+
 // Resident workgroups per compute unit of one decode instantiation, from the
 // runtime's occupancy query; 0 when it cannot be asked.
-int decode_wgs_per_cu(int head_dim, int group, bool fp8);
+int decode_wgs_per_cu(int head_dim, int group, int kind);
 
 // Returns hipErrorInvalidValue for an instantiation that is not built.
-hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, bool fp8, uint32_t grid,
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, int kind, uint32_t grid,
                          hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int head_dim, int group, uint32_t grid, hipStream_t stream);
 int dynamic_wgs_per_cu(int head_dim, int group, bool fp8);

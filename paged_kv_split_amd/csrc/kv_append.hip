@@ -187,7 +187,20 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
           float ks, vs;
           const u32x2 kc = quantise_chunk<D>(in ? kx[u] : u32x4{0, 0, 0, 0}, p.pow2_scales, &ks);
           const u32x2 vc = quantise_chunk<D>(in ? vx[u] : u32x4{0, 0, 0, 0}, p.pow2_scales, &vs);
-          if (in) {
+          if (in && p.inline_scales) {
+            // rows D + 4 bytes apart are 4-byte aligned: dword stores; the
+            // row's first lane also writes its scale after the codes
+            unsigned char* kr = kpool + r * (D + 4);
+            unsigned char* vr = vpool + r * (D + 4);
+            reinterpret_cast<uint32_t*>(kr + within / 2)[0] = kc.x;
+            reinterpret_cast<uint32_t*>(kr + within / 2)[1] = kc.y;
+            reinterpret_cast<uint32_t*>(vr + within / 2)[0] = vc.x;
+            reinterpret_cast<uint32_t*>(vr + within / 2)[1] = vc.y;
+            if ((lane & (D / 8 - 1)) == 0) {
+              *reinterpret_cast<float*>(kr + D) = ks;
+              *reinterpret_cast<float*>(vr + D) = vs;
+            }
+          } else if (in) {
             *reinterpret_cast<u32x2*>(kpool + r * D + within / 2) = kc;
             *reinterpret_cast<u32x2*>(vpool + r * D + within / 2) = vc;
             if ((lane & (D / 8 - 1)) == 0) {

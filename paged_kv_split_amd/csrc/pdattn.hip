@@ -63,7 +63,7 @@ pdattn_status check_problem(const pdattn_problem* p) {
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "negative block table or pool size");
   if ((int64_t)p->max_pages_per_seq * p->page_size > INT32_MAX)
     return fail(PDATTN_ERR_UNSUPPORTED, "max_pages_per_seq * page_size exceeds 2^31 - 1 tokens");
-  if (p->kv_dtype != PDATTN_KV_BF16 && p->kv_dtype != PDATTN_KV_FP8_E4M3)
+  if (p->kv_dtype != PDATTN_KV_BF16 && p->kv_dtype != PDATTN_KV_FP8_E4M3 && p->kv_dtype != PDATTN_KV_FP8_E4M3_INLINE)
     return fail(PDATTN_ERR_UNSUPPORTED, "kv_dtype %d unknown", p->kv_dtype);
   if (!std::isfinite(p->scale)) return fail(PDATTN_ERR_INVALID_ARGUMENT, "scale is not finite");
   if (p->kv_layout != PDATTN_LAYOUT_NHD && p->kv_layout != PDATTN_LAYOUT_HND)
@@ -72,6 +72,23 @@ pdattn_status check_problem(const pdattn_problem* p) {
 }
 
 int qlen_of(const pdattn_problem& p) { return p.q_len > 1 ? p.q_len : 1; }
+// 0 bf16, 1 fp8 with separate scale arrays, 2 fp8 with inline scales
+int kind_of(const pdattn_problem& p) {
+  return p.kv_dtype == PDATTN_KV_FP8_E4M3_INLINE ? pdattn::kKindFp8Inline
+                                                 : p.kv_dtype == PDATTN_KV_FP8_E4M3 ? pdattn::kKindFp8 : pdattn::kKindBf16;
+}
+// The scale arguments a dtype takes: both for fp8 with separate scales,
+// none otherwise.
+pdattn_status check_scales(const pdattn_problem& p, const float* k_scale, const float* v_scale) {
+  if (kind_of(p) == pdattn::kKindFp8) {
+    if (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4))
+      return fail(PDATTN_ERR_INVALID_ARGUMENT, "fp8 pools need 4-byte aligned k_scale and v_scale");
+  } else if (k_scale || v_scale) {
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "k_scale / v_scale must be NULL for %s pools",
+                kind_of(p) == pdattn::kKindBf16 ? "bf16" : "inline-scale fp8");
+  }
+  return PDATTN_OK;
+}
 int heads_per_kv(const pdattn_problem& p) { return p.num_q_heads / p.num_kv_heads; }
 // Valid columns: the (query row, head) pairs of one kv head; a kernel
 // instantiation has the next power of two (the rest are padding).
@@ -128,14 +145,15 @@ uint64_t workspace_for(const pdattn_problem& p, int64_t workers, int32_t flags) 
 // Resident workgroups per CU of one kernel instantiation on the current
 // device, from the runtime's occupancy query (cached: the query costs
 // milliseconds), 0 if it cannot be asked.
-int wgs_per_cu_cached(int device, int head_dim, int group, bool fp8, bool dyn) {
-  static std::atomic<int> cache[64][3][5][2][2];
+int wgs_per_cu_cached(int device, int head_dim, int group, int kind, bool dyn) {
+  static std::atomic<int> cache[64][3][5][3][2];
   if (device < 0 || device >= 64) return 0;
   const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : group == 8 ? 3 : 4;
-  std::atomic<int>& slot = cache[device][head_dim == 256 ? 2 : head_dim == 128 ? 1 : 0][gi][fp8][dyn];
+  std::atomic<int>& slot = cache[device][head_dim == 256 ? 2 : head_dim == 128 ? 1 : 0][gi][kind][dyn];
   int v = slot.load(std::memory_order_relaxed);
   if (v > 0) return v;
-  v = dyn ? pdattn::dynamic_wgs_per_cu(head_dim, group, fp8) : pdattn::decode_wgs_per_cu(head_dim, group, fp8);
+  v = dyn ? pdattn::dynamic_wgs_per_cu(head_dim, group, kind != pdattn::kKindBf16)
+          : pdattn::decode_wgs_per_cu(head_dim, group, kind);
   if (v > 0) slot.store(v, std::memory_order_relaxed);
   return v;
 }
@@ -193,6 +211,8 @@ PDATTN_API pdattn_status pdattn_plan(const pdattn_problem* problem, const int32_
   if (dyn && problem->head_dim == 256) return fail(PDATTN_ERR_UNSUPPORTED, "head_dim 256 needs a static plan");
   if (dyn && !pow2_heads(*problem))
     return fail(PDATTN_ERR_UNSUPPORTED, "a group size that is not a power of two needs a static plan");
+  if (dyn && problem->kv_dtype == PDATTN_KV_FP8_E4M3_INLINE)
+    return fail(PDATTN_ERR_UNSUPPORTED, "inline-scale fp8 pools need a static plan");
 
   const int64_t cap = (int64_t)problem->max_pages_per_seq * problem->page_size;
   int64_t tiles = 0, max_len = 0;
@@ -208,7 +228,8 @@ PDATTN_API pdattn_status pdattn_plan(const pdattn_problem* problem, const int32_
   tiles *= problem->num_kv_heads;
   if (max_len > 0 && problem->num_pages <= 0) return fail(PDATTN_ERR_INVALID_ARGUMENT, "empty page pool");
 
-  const bool fp8 = problem->kv_dtype == PDATTN_KV_FP8_E4M3;
+  const int kind = kind_of(*problem);
+  const bool fp8 = kind != pdattn::kKindBf16;
   // resident workgroups per CU: the runtime's occupancy figure for this
   // instantiation when the device is asked, else a conservative estimate
   int per_cu = 0;
@@ -218,7 +239,7 @@ PDATTN_API pdattn_status pdattn_plan(const pdattn_problem* problem, const int32_
     if (e == hipSuccess) e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess || num_cus <= 0)
       return fail(PDATTN_ERR_DEVICE, "cannot query the compute-unit count: %s", hipGetErrorString(e));
-    per_cu = wgs_per_cu_cached(dev, problem->head_dim, group_of(*problem), fp8, dyn);
+    per_cu = wgs_per_cu_cached(dev, problem->head_dim, group_of(*problem), kind, dyn);
   }
   if (per_cu <= 0) per_cu = pdattn::decode_wgs_per_cu_estimate(problem->head_dim, group_of(*problem), fp8, dyn);
 
@@ -279,11 +300,10 @@ PDATTN_API pdattn_status pdattn_decode(const pdattn_plan_t* plan, const void* q,
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "q, k_pages, v_pages and out must be 16-byte aligned");
   if (!aligned(block_table, 4) || !aligned(context_lens, 4) || (lse && !aligned(lse, 4)))
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "block_table, context_lens and lse must be 4-byte aligned");
-  const bool fp8 = pr.kv_dtype == PDATTN_KV_FP8_E4M3;
-  if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
-    return fail(PDATTN_ERR_INVALID_ARGUMENT, "fp8 pools need 4-byte aligned k_scale and v_scale");
-  if (!fp8 && (k_scale || v_scale))
-    return fail(PDATTN_ERR_INVALID_ARGUMENT, "k_scale / v_scale must be NULL for bf16 pools");
+  st = check_scales(pr, k_scale, v_scale);
+  if (st != PDATTN_OK) return st;
+  const int kind = kind_of(pr);
+  const bool fp8 = kind != pdattn::kKindBf16;
   if (!workspace || workspace_bytes < plan->workspace_bytes)
     return fail(PDATTN_ERR_WORKSPACE, "workspace needs %llu bytes, got %llu at %p",
                 (unsigned long long)plan->workspace_bytes, (unsigned long long)workspace_bytes, workspace);
@@ -352,7 +372,7 @@ PDATTN_API pdattn_status pdattn_decode(const pdattn_plan_t* plan, const void* q,
   p.head_stride = head_stride_of(pr);
   p.qk_scale_log2 = pr.scale * 1.44269504088896340736f;
 
-  hipError_t e = pdattn::launch_decode(p, pr.head_dim, group_of(pr), fp8, (uint32_t)plan->num_workgroups,
+  hipError_t e = pdattn::launch_decode(p, pr.head_dim, group_of(pr), kind, (uint32_t)plan->num_workgroups,
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "decode kernel launch: %s", hipGetErrorString(e));
   return PDATTN_OK;
@@ -422,7 +442,8 @@ PDATTN_API pdattn_status pdattn_kv_append(const pdattn_problem* problem, int32_t
   if (num_tokens < 0) return fail(PDATTN_ERR_INVALID_ARGUMENT, "num_tokens %d is negative", num_tokens);
   if ((flags & ~PDATTN_APPEND_POW2_SCALES) != 0)
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "unknown append flags %d", flags);
-  const bool fp8 = problem->kv_dtype == PDATTN_KV_FP8_E4M3;
+  const int kind = kind_of(*problem);
+  const bool fp8 = kind != pdattn::kKindBf16;
   if (!fp8 && (flags & PDATTN_APPEND_POW2_SCALES))
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "PDATTN_APPEND_POW2_SCALES applies to fp8 pools only");
   if ((int64_t)problem->num_kv_heads * problem->head_dim > (1 << 19))
@@ -436,10 +457,8 @@ PDATTN_API pdattn_status pdattn_kv_append(const pdattn_problem* problem, int32_t
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "k_new, v_new, k_pages and v_pages must be 16-byte aligned");
   if (!aligned(token_seq, 4) || !aligned(token_pos, 4) || !aligned(block_table, 4))
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "token_seq, token_pos and block_table must be 4-byte aligned");
-  if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
-    return fail(PDATTN_ERR_INVALID_ARGUMENT, "fp8 pools need 4-byte aligned k_scale and v_scale");
-  if (!fp8 && (k_scale || v_scale))
-    return fail(PDATTN_ERR_INVALID_ARGUMENT, "k_scale / v_scale must be NULL for bf16 pools");
+  st = check_scales(*problem, k_scale, v_scale);
+  if (st != PDATTN_OK) return st;
 
   pdattn::AppendParams p;
   std::memset(&p, 0, sizeof p);
@@ -459,6 +478,7 @@ PDATTN_API pdattn_status pdattn_kv_append(const pdattn_problem* problem, int32_t
   p.max_pages_per_seq = problem->max_pages_per_seq;
   p.num_pages = problem->num_pages;
   p.pow2_scales = (flags & PDATTN_APPEND_POW2_SCALES) ? 1 : 0;
+  p.inline_scales = kind == pdattn::kKindFp8Inline ? 1 : 0;
   p.slot_stride = slot_stride_of(*problem);
   p.head_stride = head_stride_of(*problem);
   // one wave per token, four tokens per workgroup; a larger append is
@@ -598,11 +618,11 @@ PDATTN_API pdattn_status pdattn_prefill(const pdattn_problem* problem, int32_t c
   if (!aligned(qo_indptr, 4) || !aligned(tile_batch, 4) || !aligned(tile_index, 4) || !aligned(block_table, 4) ||
       !aligned(context_lens, 4) || (lse && !aligned(lse, 4)))
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "index arrays and lse must be 4-byte aligned");
+  if (problem->kv_dtype == PDATTN_KV_FP8_E4M3_INLINE)
+    return fail(PDATTN_ERR_UNSUPPORTED, "the prefill reads bf16 or separate-scale fp8 pools");
+  st = check_scales(*problem, k_scale, v_scale);
+  if (st != PDATTN_OK) return st;
   const bool fp8 = problem->kv_dtype == PDATTN_KV_FP8_E4M3;
-  if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
-    return fail(PDATTN_ERR_INVALID_ARGUMENT, "fp8 pools need 4-byte aligned k_scale and v_scale");
-  if (!fp8 && (k_scale || v_scale))
-    return fail(PDATTN_ERR_INVALID_ARGUMENT, "k_scale / v_scale must be NULL for bf16 pools");
 
   pdattn::PrefillParams p;
   std::memset(&p, 0, sizeof p);

@@ -307,14 +307,24 @@ __device__ __forceinline__ long long uniform64(long long x) {
 }
 
 // The per-wave tile machinery for head_dim D, group size G and pool type.
-template <int D, int G, bool FP8>
+// INL (fp8 only): each pool row holds its D codes and then its fp32 scale
+// (DeepGEMM documentation 6.1, the paged cache with the scale fused per
+// token), D + 4 bytes, so rows are only 4-byte aligned: the tile is fetched
+// with 4-byte direct-to-LDS loads into the same LDS image as the 16-byte
+// loads of separate-scale pools build, and everything after the loads is
+// shared.
+template <int D, int G, bool FP8, bool INL = false>
 struct Tile {
+  static_assert(!INL || FP8, "inline scales are an fp8 layout");
   static constexpr int ESZ = FP8 ? 1 : 2;             // bytes per stored element
-  static constexpr int ROW_BYTES = D * ESZ;           // one (token, kv head) row
+  static constexpr int ROW_BYTES = D * ESZ;           // one (token, kv head) row's values
+  static constexpr int PITCH = ROW_BYTES + (INL ? 4 : 0);  // pool bytes per row
   static constexpr int KSTEPS = D / 32;               // MFMA k-steps over head_dim
   static constexpr int K_LD = ROW_BYTES / 64;         // 16-byte loads per lane per tile, K
   static constexpr int V_LD = ROW_BYTES / 64;         // and V (a tile is 16 rows)
-  static constexpr int C = K_LD + V_LD + (FP8 ? 1 : 0);  // direct-to-LDS loads per tile
+  // direct-to-LDS loads per tile: each 16-byte load is four 4-byte ones
+  // with inline scales
+  static constexpr int C = (INL ? 4 : 1) * (K_LD + V_LD) + (FP8 ? 1 : 0);
   static constexpr int VE = D / 16;                   // V elements per lane per row
   static constexpr int VB = VE * ESZ;                 // V bytes per lane per row
   // one ring stage: K tile in MFMA-operand lane order, V tile row-major,
@@ -421,6 +431,39 @@ struct Tile {
   __device__ static void issue(unsigned char* st, const uint8_t* k, const uint8_t* v, const float* k_scale,
                                const float* v_scale, RowOf&& row_of, int tb, int last, int lane, int row,
                                int col) {
+    if constexpr (INL) {
+      // Same LDS image from 4-byte loads: load (jj, q) fills bytes
+      // [jj * 1024 + q * 256, +256), lane i the dword at + 4 i.
+      // K: that dword is dword i mod 4 of the 16-byte fragment of MFMA lane
+      // 16 q + i / 4, i.e. row q, column i / 4: token tile_token(i / 4),
+      // bytes 64 jj + 16 q + 4 (i mod 4) of its row
+      {
+        const int pos = min(tb + tile_token(lane >> 2), last);
+        const unsigned char* src = k + row_of(pos) * PITCH + 4 * (lane & 3);
+#pragma unroll
+        for (int jj = 0; jj < K_LD; ++jj)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) dma4(src + jj * 64 + q * 16, st + jj * 1024 + q * 256);
+      }
+      // V: row-major, the dword at byte b of the tile is byte b mod ROW of
+      // token b / ROW
+#pragma unroll
+      for (int jj = 0; jj < V_LD; ++jj)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int byte = jj * 1024 + q * 256 + lane * 4;
+          const int pos = min(tb + byte / ROW_BYTES, last);
+          dma4(v + row_of(pos) * PITCH + (byte % ROW_BYTES), st + K_TILE + jj * 1024 + q * 256);
+        }
+      // scales: slot m < 16 the k scale of token tile_token(m), 16 + m its
+      // v scale (the dword after the row's codes); lanes 32..63 repeat
+      {
+        const int m = lane & 15;
+        const int pos = min(tb + tile_token(m), last);
+        dma4(((lane & 16) ? v : k) + row_of(pos) * PITCH + ROW_BYTES, st + K_TILE + V_TILE);
+      }
+      return;
+    }
     {
       // K: lane (row, col) fetches bytes [j*64 + row*16, +16) of token
       // tile_token(col); it lands at j*1024 + lane*16, the lane's own

@@ -28,7 +28,7 @@ import math
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "kv_bytes", "make_append_inputs", "append_bytes", "to_hnd",
-           "make_prefill_inputs", "prefill_flops", "PREFILL_WORKLOADS", "prefill_workload",
+           "make_prefill_inputs", "prefill_flops", "PREFILL_WORKLOADS", "prefill_workload", "to_inline", "from_inline",
            "from_hnd"]
 
 E4M3_MAX = 448.0
@@ -371,3 +371,26 @@ def prefill_workload(name, **overrides):
     inp = make_prefill_inputs(**kw)
     inp["description"] = desc
     return inp
+
+
+def to_inline(inp):
+    """A copy of an fp8 input dict whose pools carry each row's fp32 scale
+    after its codes (uint8 rows of d + 4 bytes, the scale's 4 bytes in
+    memory order), and no separate scale arrays: the same values laid out
+    as one byte cache. Works on either row order (NHD or HND)."""
+    out = dict(inp)
+    for pages, scale in (("k_pages", "k_scale"), ("v_pages", "v_scale")):
+        codes = inp[pages].view(torch.uint8)
+        sb = inp[scale].contiguous().view(torch.uint8).reshape(tuple(inp[scale].shape) + (4,))
+        out[pages] = torch.cat([codes, sb], dim=-1).contiguous()
+        out[scale] = None
+    return out
+
+
+def from_inline(pages):
+    """(codes float8_e4m3fn [..., d], scales float32 [...]) of an inline
+    pool (uint8 [..., d + 4])."""
+    d = pages.shape[-1] - 4
+    codes = pages[..., :d].contiguous().view(torch.float8_e4m3fn)
+    scales = pages[..., d:].contiguous().view(torch.float32).reshape(pages.shape[:-1])
+    return codes, scales

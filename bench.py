@@ -27,7 +27,8 @@ timed on this host's cores on the same step's inputs.
 prefill = the ragged paged prefill (pdattn_prefill) on its three workloads
 (synth.PREFILL_WORKLOADS) and the ragged batch with fp8 pools, each call
 timed alone after a cache flush; roofline there = algorithmic flops / mean
-call time against the dense bf16 MFMA peak.
+call time against the dense bf16 MFMA peak. fp8_kv_scales = the FP8 KV
+workload's step with separate scale arrays and with inline scales.
 """
 import argparse
 import hashlib
@@ -121,6 +122,51 @@ def time_other_layout(pk, w, inp, args, flush, dev, reps=30):
     del d, ws
     return {"kv_layout": "HND" if hnd else "NHD", "us_per_call": round(us, 2),
             "gbs": round(kvb / (us * 1e-6) / 1e9, 1)}
+
+
+def time_fp8_scales(pk, flush, dev, layout, reps=20):
+    """The FP8 KV workload (B32, 32 q / 8 kv heads, d128, P16, L~U[1024,8192])
+    with its scales in separate arrays and with each row's scale inline
+    after its codes (the same values and the same bytes): mean step time
+    (decode + reduce, one event pair) and KV GB/s for both."""
+    import torch
+    import synth
+    w = synth.WORKLOADS["fp8_kv"]
+    inp = synth.make_inputs(w)
+    kvb = synth.kv_bytes(w, inp["context_lens"])
+    res = {"workload": w.description, "kv_bytes": kvb, "kv_layout": layout.upper()}
+    for name, src in (("separate", inp), ("inline", synth.to_inline(inp))):
+        laid = synth.to_hnd(src) if layout == "hnd" else src
+        d = {k: (laid[k].to(dev) if laid.get(k) is not None else None)
+             for k in ("q", "k_pages", "v_pages", "k_scale", "v_scale", "block_table", "context_lens")}
+        pl = pk.plan(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                     page_size=w.page_size, max_pages_per_seq=inp["block_table"].shape[1],
+                     num_pages=inp["k_pages"].shape[0], kv_dtype=pk.kv_kind(d["k_pages"]),
+                     context_lens_host=inp["context_lens"],
+                     kv_layout=pk.LAYOUT_HND if layout == "hnd" else pk.LAYOUT_NHD)
+        out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+        lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=dev)
+        ws = pk.workspace(pl, dev)
+
+        def step():
+            pk.decode(pl, d["q"], d["k_pages"], d["v_pages"], d["k_scale"], d["v_scale"], d["block_table"],
+                      d["context_lens"], ws, out, lse)
+            pk.reduce(pl, ws, out, lse)
+        for _ in range(5):
+            step()
+        ts = []
+        for i in range(reps):
+            flush.fill_(i & 0xFF)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            step()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        us = statistics.fmean(ts)
+        res[name] = {"us_per_call": round(us, 2), "gbs": round(kvb / (us * 1e-6) / 1e9, 1)}
+        del d, ws, laid
+    return res
 
 
 def time_append(pk, w, flush, dev, layout, reps=20):
@@ -364,6 +410,7 @@ def main():
     ap.add_argument("--no-merge", action="store_true", help="skip the partial-state merge timings")
     ap.add_argument("--no-multi-query", action="store_true", help="skip the multi-query decode timing")
     ap.add_argument("--no-prefill", action="store_true", help="skip the ragged paged prefill timing")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 separate / inline scale timing")
     ap.add_argument("--no-d256", action="store_true", help="skip the head_dim 256 timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run 3 device copies of 256 MiB (a plain copy kernel of known "
@@ -499,6 +546,7 @@ def main():
     multi = None if args.no_multi_query else time_multi_query(pk, w, inp, args, flush, dev)
     d256 = None if args.no_d256 else time_d256(pk, w, args, flush, dev)
     prefill = None if args.no_prefill else time_prefill(pk, flush, dev)
+    fp8_scales = None if args.no_fp8 else time_fp8_scales(pk, flush, dev, args.layout)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -586,6 +634,7 @@ def main():
         "multi_query": multi,
         "head_dim_256": d256,
         "prefill": prefill,
+        "fp8_kv_scales": fp8_scales,
     }
     print(json.dumps(rec), flush=True)
 

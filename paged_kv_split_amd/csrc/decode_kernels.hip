@@ -66,7 +66,7 @@ __device__ __forceinline__ void worker_range(long long w, long long nw, long lon
 
 // fp8 d128 with up to 4 columns: the LDS holds four workgroups per CU; the
 // register budget is held to the 128 VGPRs that let four waves share a SIMD
-template <int D, int G, bool FP8, bool INL = false>
+template <int D, int G, bool FP8, int INL = 0>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(FP8 && D == 128 && G <= 4 ? 4 : 1)))
 void decode_kernel(DecodeParams p) {
   using TL = Tile<D, G, FP8, INL>;
@@ -237,7 +237,7 @@ void decode_kernel(DecodeParams p) {
           // tiles k+1 .. min(k+S-1, nk-1) may stay in flight
           wait_tiles<C, S>(min(S - 1, nk - 1 - k));
           typename TL::Frag f;
-          TL::read(f, ring + (k % S) * STAGE, lane, row, col);
+          TL::read(f, ring + (k % S) * STAGE, lane, row, col, s1 - (c0 + k * kTileTokens));
           // the stage's reads have returned (read_stage waits for them): refill it
           if (k + S < nk) issue(k + S);
           TL::compute(st, f, qop, c0 + k * kTileTokens, lim, p.qk_scale_log2, row);
@@ -401,13 +401,13 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(MergeParams p) 
   }
 }
 
-template <int D, int G, bool FP8, bool INL>
+template <int D, int G, bool FP8, int INL>
 hipError_t launch_one(const DecodeParams& p, uint32_t grid, hipStream_t stream) {
   hipLaunchKernelGGL((decode_kernel<D, G, FP8, INL>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, int G, bool FP8, bool INL>
+template <int D, int G, bool FP8, int INL>
 int occupancy_one() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, G, FP8, INL>, kWaves * 64, 0) != hipSuccess)
@@ -415,7 +415,7 @@ int occupancy_one() {
   return n;
 }
 
-template <int D, bool FP8, bool INL>
+template <int D, bool FP8, int INL>
 int occupancy_group(int group) {
   switch (group) {
     case 1: return occupancy_one<D, 1, FP8, INL>();
@@ -427,7 +427,7 @@ int occupancy_group(int group) {
   }
 }
 
-template <int D, bool FP8, bool INL>
+template <int D, bool FP8, int INL>
 hipError_t launch_group(const DecodeParams& p, int group, uint32_t grid, hipStream_t stream) {
   switch (group) {
     case 1: return launch_one<D, 1, FP8, INL>(p, grid, stream);
@@ -439,18 +439,28 @@ hipError_t launch_group(const DecodeParams& p, int group, uint32_t grid, hipStre
   }
 }
 
-// kind: 0 bf16, 1 fp8 with separate scales, 2 fp8 with inline scales
+// kinds: see kernels.h (bf16; fp8 separate scales; fp8 inline scales by
+// 4-byte loads; fp8 inline scales by raw-row blocks, head-major pools)
 template <int D>
 int occupancy_kind(int group, int kind) {
-  return kind == 0 ? occupancy_group<D, false, false>(group)
-                   : kind == 1 ? occupancy_group<D, true, false>(group) : occupancy_group<D, true, true>(group);
+  switch (kind) {
+    case kKindBf16: return occupancy_group<D, false, 0>(group);
+    case kKindFp8: return occupancy_group<D, true, 0>(group);
+    case kKindFp8Inline: return occupancy_group<D, true, 1>(group);
+    case kKindFp8InlineRows: return occupancy_group<D, true, 2>(group);
+    default: return 0;
+  }
 }
 
 template <int D>
 hipError_t launch_kind(const DecodeParams& p, int group, int kind, uint32_t grid, hipStream_t stream) {
-  return kind == 0 ? launch_group<D, false, false>(p, group, grid, stream)
-                   : kind == 1 ? launch_group<D, true, false>(p, group, grid, stream)
-                               : launch_group<D, true, true>(p, group, grid, stream);
+  switch (kind) {
+    case kKindBf16: return launch_group<D, false, 0>(p, group, grid, stream);
+    case kKindFp8: return launch_group<D, true, 0>(p, group, grid, stream);
+    case kKindFp8Inline: return launch_group<D, true, 1>(p, group, grid, stream);
+    case kKindFp8InlineRows: return launch_group<D, true, 2>(p, group, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int D>
@@ -478,7 +488,7 @@ int decode_wgs_per_cu(int head_dim, int group, int kind) {
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, int kind, uint32_t grid,
                          hipStream_t stream) {
-  if (kind < 0 || kind > 2) return hipErrorInvalidValue;
+  if (kind < kKindBf16 || kind > kKindFp8InlineRows) return hipErrorInvalidValue;
   if (head_dim == 64) return launch_kind<64>(p, group, kind, grid, stream);
   if (head_dim == 128) return launch_kind<128>(p, group, kind, grid, stream);
   if (head_dim == 256) return launch_kind<256>(p, group, kind, grid, stream);

@@ -130,8 +130,9 @@ struct MergeParams {
 };
 
 // KV kinds of the static decode kernel: bf16, fp8 with separate scale
-// arrays, fp8 with each row's scale after its codes.
-constexpr int kKindBf16 = 0, kKindFp8 = 1, kKindFp8Inline = 2;
+// arrays, fp8 with each row's scale after its codes (4-byte loads, any row
+// order; or, for head-major pools, 16-byte loads of the raw rows).
+constexpr int kKindBf16 = 0, kKindFp8 = 1, kKindFp8Inline = 2, kKindFp8InlineRows = 3;
 
 // Resident workgroups per compute unit of one decode instantiation, from the
 // runtime's occupancy query; 0 when it cannot be asked.

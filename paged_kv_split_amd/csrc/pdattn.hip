@@ -77,6 +77,12 @@ int kind_of(const pdattn_problem& p) {
   return p.kv_dtype == PDATTN_KV_FP8_E4M3_INLINE ? pdattn::kKindFp8Inline
                                                  : p.kv_dtype == PDATTN_KV_FP8_E4M3 ? pdattn::kKindFp8 : pdattn::kKindBf16;
 }
+// The decode instantiation of a problem: inline scales in head-major pools
+// take the raw-row loads (a tile's rows are one contiguous block).
+int decode_kind(const pdattn_problem& p) {
+  const int k = kind_of(p);
+  return k == pdattn::kKindFp8Inline && p.kv_layout == PDATTN_LAYOUT_HND ? pdattn::kKindFp8InlineRows : k;
+}
 // The scale arguments a dtype takes: both for fp8 with separate scales,
 // none otherwise.
 pdattn_status check_scales(const pdattn_problem& p, const float* k_scale, const float* v_scale) {
@@ -146,7 +152,7 @@ uint64_t workspace_for(const pdattn_problem& p, int64_t workers, int32_t flags) 
 // device, from the runtime's occupancy query (cached: the query costs
 // milliseconds), 0 if it cannot be asked.
 int wgs_per_cu_cached(int device, int head_dim, int group, int kind, bool dyn) {
-  static std::atomic<int> cache[64][3][5][3][2];
+  static std::atomic<int> cache[64][3][5][4][2];
   if (device < 0 || device >= 64) return 0;
   const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : group == 8 ? 3 : 4;
   std::atomic<int>& slot = cache[device][head_dim == 256 ? 2 : head_dim == 128 ? 1 : 0][gi][kind][dyn];
@@ -239,7 +245,7 @@ PDATTN_API pdattn_status pdattn_plan(const pdattn_problem* problem, const int32_
     if (e == hipSuccess) e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess || num_cus <= 0)
       return fail(PDATTN_ERR_DEVICE, "cannot query the compute-unit count: %s", hipGetErrorString(e));
-    per_cu = wgs_per_cu_cached(dev, problem->head_dim, group_of(*problem), kind, dyn);
+    per_cu = wgs_per_cu_cached(dev, problem->head_dim, group_of(*problem), dyn ? kind : decode_kind(*problem), dyn);
   }
   if (per_cu <= 0) per_cu = pdattn::decode_wgs_per_cu_estimate(problem->head_dim, group_of(*problem), fp8, dyn);
 
@@ -372,7 +378,7 @@ PDATTN_API pdattn_status pdattn_decode(const pdattn_plan_t* plan, const void* q,
   p.head_stride = head_stride_of(pr);
   p.qk_scale_log2 = pr.scale * 1.44269504088896340736f;
 
-  hipError_t e = pdattn::launch_decode(p, pr.head_dim, group_of(pr), kind, (uint32_t)plan->num_workgroups,
+  hipError_t e = pdattn::launch_decode(p, pr.head_dim, group_of(pr), decode_kind(pr), (uint32_t)plan->num_workgroups,
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "decode kernel launch: %s", hipGetErrorString(e));
   return PDATTN_OK;

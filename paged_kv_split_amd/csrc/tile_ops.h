@@ -283,6 +283,48 @@ __device__ __forceinline__ void read_stage(const unsigned char* kp, const unsign
   }
 }
 
+// 4-byte LDS reads at immediate offsets from one address and the wait for
+// them, in one asm block (as read_stage: no destination is touched before
+// its data lands, and no wait is added for the ring's direct-to-LDS loads).
+template <int... O>
+__device__ __forceinline__ void lds_b32(uint32_t (&r)[sizeof...(O)], uint32_t a) {
+  constexpr int o[] = {O...};
+  constexpr int N = sizeof...(O);
+  if constexpr (N == 4) {
+    asm volatile(
+        "ds_read_b32 %0, %4 offset:%5\n\t"
+        "ds_read_b32 %1, %4 offset:%6\n\t"
+        "ds_read_b32 %2, %4 offset:%7\n\t"
+        "ds_read_b32 %3, %4 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(a), "i"(o[0]), "i"(o[1]), "i"(o[2]), "i"(o[3])
+        : "memory");
+  } else {
+    static_assert(N == 8, "read count");
+    asm volatile(
+        "ds_read_b32 %0, %8 offset:%9\n\t"
+        "ds_read_b32 %1, %8 offset:%10\n\t"
+        "ds_read_b32 %2, %8 offset:%11\n\t"
+        "ds_read_b32 %3, %8 offset:%12\n\t"
+        "ds_read_b32 %4, %8 offset:%13\n\t"
+        "ds_read_b32 %5, %8 offset:%14\n\t"
+        "ds_read_b32 %6, %8 offset:%15\n\t"
+        "ds_read_b32 %7, %8 offset:%16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(a), "i"(o[0]), "i"(o[1]), "i"(o[2]), "i"(o[3]), "i"(o[4]), "i"(o[5]), "i"(o[6]), "i"(o[7])
+        : "memory");
+  }
+}
+
+// Reads dwords FIRST .. FIRST + N - 1 of a list whose dword i sits at byte
+// 4 * (i mod W) + STRIDE * (i / W) from the base (W dwords per group).
+template <int W, int STRIDE, int FIRST, size_t... I>
+__device__ __forceinline__ void lds_b32_groups(uint32_t (&r)[sizeof...(I)], uint32_t a, std::index_sequence<I...>) {
+  lds_b32<(int)(4 * ((FIRST + I) % W) + STRIDE * ((FIRST + I) / W))...>(r, a);
+}
+
 // Token order inside a 16-token tile. MFMA A-row m carries token
 // tile_token(m) = m / 4 + 4 (m mod 4), so the result row 4 r + v held by
 // 16-lane row r is token r + 4 v: every 16-lane row owns the tokens
@@ -307,31 +349,38 @@ __device__ __forceinline__ long long uniform64(long long x) {
 }
 
 // The per-wave tile machinery for head_dim D, group size G and pool type.
-// INL (fp8 only): each pool row holds its D codes and then its fp32 scale
-// (DeepGEMM documentation 6.1, the paged cache with the scale fused per
-// token), D + 4 bytes, so rows are only 4-byte aligned: the tile is fetched
-// with 4-byte direct-to-LDS loads into the same LDS image as the 16-byte
-// loads of separate-scale pools build, and everything after the loads is
-// shared.
-template <int D, int G, bool FP8, bool INL = false>
+// INL (fp8 only) != 0: each pool row holds its D codes and then its fp32
+// scale (DeepGEMM documentation 6.1, the paged cache with the scale fused
+// per token), D + 4 bytes, so rows are only 4-byte aligned.
+//   INL 1 (any row order): the tile is fetched with 4-byte direct-to-LDS
+//     loads into the same LDS image as the 16-byte loads of separate-scale
+//     pools build; everything after the loads is shared.
+//   INL 2 (head-major pools, rows [page][kv head][slot]): the tile's 16 rows
+//     are one contiguous 16-byte-aligned block (two of 8 rows when P = 8),
+//     fetched with 16-byte loads as raw rows; the operands are read back
+//     with 4-byte LDS reads at the rows' offsets into the same registers.
+template <int D, int G, bool FP8, int INL = 0>
 struct Tile {
-  static_assert(!INL || FP8, "inline scales are an fp8 layout");
+  static_assert(INL == 0 || FP8, "inline scales are an fp8 layout");
   static constexpr int ESZ = FP8 ? 1 : 2;             // bytes per stored element
   static constexpr int ROW_BYTES = D * ESZ;           // one (token, kv head) row's values
   static constexpr int PITCH = ROW_BYTES + (INL ? 4 : 0);  // pool bytes per row
   static constexpr int KSTEPS = D / 32;               // MFMA k-steps over head_dim
   static constexpr int K_LD = ROW_BYTES / 64;         // 16-byte loads per lane per tile, K
   static constexpr int V_LD = ROW_BYTES / 64;         // and V (a tile is 16 rows)
+  static constexpr int BLK = kTileTokens * PITCH;     // INL 2: bytes of a tile's raw rows
+  static constexpr int BLK_LD = (BLK / 16 + 63) / 64; // INL 2: 16-byte loads per lane per block
   // direct-to-LDS loads per tile: each 16-byte load is four 4-byte ones
-  // with inline scales
-  static constexpr int C = (INL ? 4 : 1) * (K_LD + V_LD) + (FP8 ? 1 : 0);
+  // with INL 1; INL 2 loads the two raw blocks (scales inside)
+  static constexpr int C = INL == 2 ? 2 * BLK_LD : (INL ? 4 : 1) * (K_LD + V_LD) + (FP8 ? 1 : 0);
   static constexpr int VE = D / 16;                   // V elements per lane per row
   static constexpr int VB = VE * ESZ;                 // V bytes per lane per row
   // one ring stage: K tile in MFMA-operand lane order, V tile row-major,
   // then (fp8) 64 scale slots: k scales 0..15, v scales 16..31
-  static constexpr int K_TILE = kTileTokens * ROW_BYTES;
-  static constexpr int V_TILE = kTileTokens * ROW_BYTES;
-  static constexpr int STAGE = K_TILE + V_TILE + (FP8 ? 256 : 0);
+  static constexpr int K_TILE = INL == 2 ? BLK : kTileTokens * ROW_BYTES;
+  static constexpr int V_TILE = K_TILE;
+  static constexpr int STAGE = K_TILE + V_TILE + (FP8 && INL != 2 ? 256 : 0);
+  static_assert(BLK % 16 == 0, "raw blocks are 16-byte multiples");
   static constexpr int RF = (int)record_floats(D, G);
   static constexpr int EPL = G * D / 64;  // accumulator elements per lane in the merge layout
   using VVec = typename VChunk<VB>::type;
@@ -431,7 +480,25 @@ struct Tile {
   __device__ static void issue(unsigned char* st, const uint8_t* k, const uint8_t* v, const float* k_scale,
                                const float* v_scale, RowOf&& row_of, int tb, int last, int lane, int row,
                                int col) {
-    if constexpr (INL) {
+    if constexpr (INL == 2) {
+      // raw rows: byte x of the tile's block is byte x mod (8 PITCH) of the
+      // 8-row run starting at row ra (x < 8 PITCH) or rb; with P >= 16 the
+      // 16 rows are one run (rb = ra + 8). Rows past `last` are read as they
+      // are (inside an allocated page) and never used: their scores are
+      // masked and read() zeroes their V values and v scales.
+      const long long ra = row_of(tb);
+      const long long rb = tb + 8 <= last ? row_of(tb + 8) : ra;
+#pragma unroll
+      for (int i = 0; i < BLK_LD; ++i) {
+        const int x = (i * 64 + lane) * 16;
+        if (i < BLK_LD - 1 || x < BLK) {
+          const long long off = x < 8 * PITCH ? ra * PITCH + x : rb * PITCH + (x - 8 * PITCH);
+          dma16(k + off, st + i * 1024);
+          dma16(v + off, st + K_TILE + i * 1024);
+        }
+      }
+      return;
+    } else if constexpr (INL == 1) {
       // Same LDS image from 4-byte loads: load (jj, q) fills bytes
       // [jj * 1024 + q * 256, +256), lane i the dword at + 4 i.
       // K: that dword is dword i mod 4 of the 16-byte fragment of MFMA lane
@@ -490,7 +557,77 @@ struct Tile {
     }
   }
 
-  __device__ static void read(Frag& f, const unsigned char* st, int lane, int row, int col) {
+  // `valid`: tokens of the tile that exist in the piece (INL 2 zeroes the V
+  // values and v scales of the others; the other modes load clamped rows)
+  __device__ static void read(Frag& f, const unsigned char* st, int lane, int row, int col,
+                              int valid = kTileTokens) {
+    if constexpr (INL == 2) {
+      const uint32_t kb = lds_addr(st), vb = lds_addr(st + K_TILE);
+      // K fragment jj: dwords q of bytes 64 jj + 16 row of token tile_token(col)
+      {
+        const uint32_t ak = kb + tile_token(col) * PITCH + 16 * row;
+        uint32_t r[4 * K_LD];
+        static_for<0, (4 * K_LD + 7) / 8>([&](auto hc) {
+          constexpr int h = decltype(hc)::value;
+          constexpr int n = 4 * K_LD - 8 * h < 8 ? 4 * K_LD - 8 * h : 8;
+          uint32_t t[n];
+          lds_b32_groups<4, 64, 8 * h>(t, ak, std::make_index_sequence<n>{});
+#pragma unroll
+          for (int i = 0; i < n; ++i) r[8 * h + i] = t[i];
+        });
+#pragma unroll
+        for (int jj = 0; jj < K_LD; ++jj) f.kf[jj] = u32x4{r[4 * jj], r[4 * jj + 1], r[4 * jj + 2], r[4 * jj + 3]};
+      }
+      // V chunk j: token row + 4 j, bytes col * VB .. + VB
+      {
+        constexpr int W = VB / 4;
+        const uint32_t av = vb + row * PITCH + col * VB;
+        uint32_t r[4 * W];
+        static_for<0, (4 * W + 7) / 8>([&](auto hc) {
+          constexpr int h = decltype(hc)::value;
+          constexpr int n = 4 * W - 8 * h < 8 ? 4 * W - 8 * h : 8;
+          uint32_t t[n];
+          lds_b32_groups<W, 4 * PITCH, 8 * h>(t, av, std::make_index_sequence<n>{});
+#pragma unroll
+          for (int i = 0; i < n; ++i) r[8 * h + i] = t[i];
+        });
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (W == 1) {
+            f.vf[j] = r[j];
+          } else {
+#pragma unroll
+            for (int w = 0; w < W; ++w) f.vf[j][w] = r[W * j + w];
+          }
+        }
+      }
+      // scales: tokens row + 4 v, the dword after the codes
+      {
+        uint32_t rk[4], rv[4];
+        lds_b32_groups<1, 4 * PITCH, 0>(rk, kb + row * PITCH + ROW_BYTES, std::make_index_sequence<4>{});
+        lds_b32_groups<1, 4 * PITCH, 0>(rv, vb + row * PITCH + ROW_BYTES, std::make_index_sequence<4>{});
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          f.ks[v] = __uint_as_float(rk[v]);
+          f.vs[v] = __uint_as_float(rv[v]);
+        }
+      }
+      // rows past the piece were loaded raw: their weights are exactly 0,
+      // and 0 times a NaN left in an unused slot would not be
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        if (row + 4 * v >= valid) {
+          f.vs[v] = 0.0f;
+          if constexpr (VB / 4 == 1) {
+            f.vf[v] = 0u;
+          } else {
+#pragma unroll
+            for (int w = 0; w < VB / 4; ++w) f.vf[v][w] = 0u;
+          }
+        }
+      }
+      return;
+    }
     read_stage<D, FP8>(st + lane * 16, st + K_TILE + row * ROW_BYTES + col * VB, st + K_TILE + V_TILE + row * 16,
                        f.kf, f.vf, f.ks, f.vs);
   }

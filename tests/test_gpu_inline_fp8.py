@@ -1,12 +1,15 @@
 """The inline-scale fp8 cache (PDATTN_KV_FP8_E4M3_INLINE: each pool row is
 its d e4m3fn codes followed by its fp32 scale) on the GPU.
 
-* decode and multi-query decode over inline pools against the oracle, fed
-  the same codes and scales unpacked (fp8 tolerances: max-abs 4e-2, mean-abs
-  1e-3, lse 1e-3);
+* decode and multi-query decode over inline pools (4-byte loads in
+  token-major pools, raw 16-byte row blocks in head-major pools) against
+  the oracle, fed the same codes and scales unpacked (fp8 tolerances:
+  max-abs 4e-2, mean-abs 1e-3, lse 1e-3);
 * the same calls on the separate-scale pools holding the same values give
-  the same outputs bit for bit: the inline loads build the same LDS image,
-  and everything after the loads is shared;
+  the same outputs bit for bit: both inline paths give the registers the
+  values the separate-scale path gives them, and the arithmetic is shared;
+* NaN codes and scales in the unused slots past a sequence's length (read
+  raw by the head-major path) do not reach the outputs;
 * the fp8 append into inline pools (plain and power-of-two scales) equals
   the append oracle's pools, packed, byte for byte; untouched rows stay;
 * the calls this layout does not serve return errors.
@@ -125,3 +128,29 @@ def test_inline_unsupported_calls_fail():
     with pytest.raises(pk.PdattnError):      # the prefill
         pk.paged_prefill(q, torch.tensor([0, 4] + [4] * 7, dtype=torch.int32, device=DEV), d["k_pages"],
                          d["v_pages"], d["block_table"], d["context_lens"])
+
+
+@pytest.mark.parametrize("layout", ["nhd", "hnd"])
+@pytest.mark.parametrize("P", [8, 16, 64])
+def test_inline_unused_tail_slots_do_not_leak(layout, P):
+    """The slots of a sequence's last page past its length hold NaN codes
+    and NaN scales; head-major inline pools read those rows raw (whole
+    blocks), and their zero weights must still give finite, correct
+    outputs."""
+    case = (32, 8, 128, P, (1, 9, 17, 100, 255, 300), 1)
+    inp = _inputs(case, seed=6400 + P)
+    bt, lens = inp["block_table"], inp["context_lens"]
+    for b, L in enumerate(lens.tolist()):
+        if L % P:
+            page = int(bt[b, L // P])
+            inp["k_pages"].view(torch.uint8)[page, L % P:] = 0x7F
+            inp["v_pages"].view(torch.uint8)[page, L % P:] = 0x7F
+            inp["k_scale"][page, L % P:] = float("nan")
+            inp["v_scale"][page, L % P:] = float("nan")
+    out, lse = _decode(synth.to_inline(inp), layout)
+    ref_o, ref_l = oracle.decode(inp["q"], inp["k_pages"], inp["v_pages"], bt, lens, k_scale=inp["k_scale"],
+                                 v_scale=inp["v_scale"])
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
+    diff = (out.double() - ref_o).abs()
+    assert float(diff.max()) <= 4e-2 and float(diff.mean()) <= 1e-3
+    assert float((lse.double() - ref_l).abs().max()) <= 1e-3

@@ -332,12 +332,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
   }
 
-  // page entries of the wave's 16-token group of the tile at tb: every
-  // position the wave loads lies in [first, first + 15] (clamped to L - 1),
-  // i.e. on at most two pages (P >= 8, groups 16-aligned)
-  // read-only for the whole call: through the constant address space the
-  // wave-uniform entries load with scalar loads, which the tile's vector-
-  // memory waits do not count
+  // Page entries. Every position a wave loads for the tile at tb lies in its
+  // 16-token group [first, first + 15] (clamped to L - 1), so on at most two
+  // pages (P >= 8, groups 16-aligned). The block table is read-only for the
+  // whole call: through the constant address space these wave-uniform
+  // entries load with scalar loads, which the tiles' vector-memory waits do
+  // not count.
   typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
   const const_i32_ptr bt = (const_i32_ptr)(p.block_table + (long long)b * p.max_pages_per_seq);
   const int mbK = w * C::KI / C::QK;

@@ -21,6 +21,11 @@ Recipe (every decode workload; the append inputs have their own recipe in
   * fp8 workload: each (token, kv head) row of K and of V gets
     scale = absmax(row) / 448 (fp32; 1 for an all-zero row) and
     code = e4m3fn(round-to-nearest-even(x / scale)) clamped to +-448.
+  * TQ4 workloads (``make_tq4_inputs``): the same lengths, block table and
+    q; the K and V rows of every valid position are handed over as new
+    tokens for a TQ4 append (the codec itself is not here); the cache starts
+    as 0xFF bytes (NaN norms); the rotation is a Haar-random orthogonal
+    matrix (``random_rotation``).
 """
 from dataclasses import dataclass
 import math
@@ -29,7 +34,7 @@ import torch
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "kv_bytes", "make_append_inputs", "append_bytes", "to_hnd",
            "make_prefill_inputs", "prefill_flops", "PREFILL_WORKLOADS", "prefill_workload", "to_inline", "from_inline",
-           "from_hnd"]
+           "from_hnd", "random_rotation", "make_tq4_inputs", "tq4_kv_bytes"]
 
 E4M3_MAX = 448.0
 
@@ -394,3 +399,61 @@ def from_inline(pages):
     codes = pages[..., :d].contiguous().view(torch.float8_e4m3fn)
     scales = pages[..., d:].contiguous().view(torch.float32).reshape(pages.shape[:-1])
     return codes, scales
+
+
+def random_rotation(d, seed):
+    """A Haar-distributed random orthogonal d x d matrix (float32): the Q of
+    the QR factorisation of a seeded standard Gaussian matrix, each column
+    multiplied by the sign of R's diagonal entry. The TQ4 codec draws its
+    rotation once; here the draw is an input."""
+    g = torch.Generator().manual_seed(int(seed))
+    a = torch.randn((d, d), generator=g, dtype=torch.float64)
+    qm, r = torch.linalg.qr(a)
+    qm = qm * torch.sign(torch.diagonal(r))[None, :]
+    return qm.to(torch.float32).contiguous()
+
+
+def make_tq4_inputs(w, *, seed=None):
+    """Inputs of a TQ4 decode step on the CPU, for a workload of WORKLOADS
+    (its kv_dtype is ignored): q bf16 [B,Hq,d]; k_new, v_new bf16
+    [T,Hkv,d] (every valid position of every sequence, sequence by
+    sequence; T = sum of the lengths), token_seq, token_pos int32 [T];
+    block_table int32 [B,max_pages]; context_lens int32 [B]; cache uint8
+    [num_pages,Hkv,P,d + 8] of 0xFF; rotation float32 [d,d]; scale."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    seed = w.seed if seed is None else seed
+    g = torch.Generator().manual_seed(int(seed) + 77)
+    B, Hq, Hkv, D, P = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size
+    lens = _lens(w, g)
+    needed = [(int(L) + P - 1) // P for L in lens.tolist()]
+    total_needed = sum(needed)
+    pool = max(total_needed if w.pool == "exact" else 2 * total_needed, 1)
+    max_pages = max(max(needed) if needed else 0, 1)
+    perm = torch.randperm(pool, generator=g).to(torch.int32)
+    block_table = torch.full((B, max_pages), -1, dtype=torch.int32)
+    off = 0
+    for b, n in enumerate(needed):
+        block_table[b, :n] = perm[off:off + n]
+        off += n
+    q = torch.randn((B, Hq, D), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    T = int(lens.to(torch.int64).sum())
+    k_new = torch.randn((T, Hkv, D), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    v_new = torch.randn((T, Hkv, D), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    n = lens.to(torch.int64)
+    token_seq = torch.repeat_interleave(torch.arange(B, dtype=torch.int64), n)
+    starts = torch.cumsum(n, 0) - n
+    token_pos = torch.arange(T, dtype=torch.int64) - starts[token_seq]
+    cache = torch.full((pool, Hkv, P, D + 8), 0xFF, dtype=torch.uint8)
+    return dict(q=q, k_new=k_new, v_new=v_new, token_seq=token_seq.to(torch.int32),
+                token_pos=token_pos.to(torch.int32), block_table=block_table, context_lens=lens, cache=cache,
+                rotation=random_rotation(D, int(seed) + 78), workload=w, scale=1.0 / math.sqrt(D))
+
+
+def tq4_kv_bytes(w, context_lens) -> int:
+    """Algorithmic bytes of a TQ4 decode step: the d + 8 cache bytes of every
+    valid (token, kv head) once."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    tokens = int(torch.as_tensor(context_lens).to(torch.int64).sum())
+    return tokens * w.num_kv_heads * (w.head_dim + 8)

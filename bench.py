@@ -28,7 +28,9 @@ prefill = the ragged paged prefill (pdattn_prefill) on its three workloads
 (synth.PREFILL_WORKLOADS) and the ragged batch with fp8 pools, each call
 timed alone after a cache flush; roofline there = algorithmic flops / mean
 call time against the dense bf16 MFMA peak. fp8_kv_scales = the FP8 KV
-workload's step with separate scale arrays and with inline scales.
+workload's step with separate scale arrays and with inline scales. tq4 =
+the Llama-3-8B-shaped step over a TQ4 compressed cache (pdattn_tq4_decode:
+q rotation, chunk kernel, merge and back-rotation), GB/s of cache bytes.
 """
 import argparse
 import hashlib
@@ -167,6 +169,60 @@ def time_fp8_scales(pk, flush, dev, layout, reps=20):
         res[name] = {"us_per_call": round(us, 2), "gbs": round(kvb / (us * 1e-6) / 1e9, 1)}
         del d, ws, laid
     return res
+
+
+def time_tq4(pk, flush, dev, reps=20):
+    """The Llama-3-8B-shaped decode step over a TQ4 compressed cache (B32,
+    32 q / 8 kv heads, d128, P16 head-major, L~U[512,4096]): the cache is
+    filled by pdattn_tq4_append from the workload's bf16 rows (timed once,
+    flushed), with the library's codebook; then the decode step
+    (pdattn_tq4_decode: q rotation, the chunk kernel, the merge with the
+    back-rotation; one event pair, caches flushed before every call). GB/s
+    counts the d + 8 cache bytes of every valid (token, kv head) once."""
+    import torch
+    import synth
+    w = synth.WORKLOADS["llama3_8b"]
+    inp = synth.make_tq4_inputs(w)
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    ck, bk = pk.tq4_codebook(w.head_dim)
+    ck, bk = ck.to(dev), bk.to(dev)
+    cache = d["cache"]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    flush.fill_(1)
+    a.record()
+    pk.tq4_append(d["k_new"], d["v_new"], d["token_seq"], d["token_pos"], d["block_table"], d["rotation"], bk, bk,
+                  cache, num_q_heads=w.num_q_heads)
+    b.record()
+    torch.cuda.synchronize()
+    append_us = a.elapsed_time(b) * 1e3
+    nbytes = synth.tq4_kv_bytes(w, inp["context_lens"])
+    prob = pk.tq4_problem(d["q"], cache, d["block_table"])
+    pl = pk.tq4_plan(prob, inp["context_lens"])
+    ws = torch.empty(int(pl.workspace_bytes), dtype=torch.uint8, device=dev)
+    out = torch.empty(d["q"].shape, dtype=torch.float32, device=dev)
+    lse = torch.empty(d["q"].shape[:2], dtype=torch.float32, device=dev)
+
+    def step():
+        pk.tq4_decode(pl, d["q"], cache, d["rotation"], ck, ck, d["block_table"], d["context_lens"], ws, out, lse)
+    for _ in range(5):
+        step()
+    ts = []
+    for i in range(reps):
+        flush.fill_(i & 0xFF)
+        a.record()
+        step()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3)
+    us = statistics.fmean(ts)
+    if not bool(torch.isfinite(out).all()):
+        raise RuntimeError("TQ4 decode produced non-finite outputs")
+    tokens = int(inp["context_lens"].sum())
+    return {"workload": "Llama-3-8B-shaped TQ4 decode B32, 32 q / 8 kv heads, d128, P16 head-major, L~U[512,4096]",
+            "cache_bytes": nbytes, "bf16_equivalent_bytes": synth.kv_bytes(w, inp["context_lens"]),
+            "chunk_tiles": int(pl.chunk_tiles), "max_chunks": int(pl.max_chunks),
+            "us_per_call": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "append_us": round(append_us, 2), "append_tokens": tokens}
 
 
 def time_append(pk, w, flush, dev, layout, reps=20):
@@ -411,6 +467,7 @@ def main():
     ap.add_argument("--no-multi-query", action="store_true", help="skip the multi-query decode timing")
     ap.add_argument("--no-prefill", action="store_true", help="skip the ragged paged prefill timing")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8 separate / inline scale timing")
+    ap.add_argument("--no-tq4", action="store_true", help="skip the TQ4 compressed-cache timing")
     ap.add_argument("--no-d256", action="store_true", help="skip the head_dim 256 timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run 3 device copies of 256 MiB (a plain copy kernel of known "
@@ -547,6 +604,7 @@ def main():
     d256 = None if args.no_d256 else time_d256(pk, w, args, flush, dev)
     prefill = None if args.no_prefill else time_prefill(pk, flush, dev)
     fp8_scales = None if args.no_fp8 else time_fp8_scales(pk, flush, dev, args.layout)
+    tq4 = None if args.no_tq4 else time_tq4(pk, flush, dev)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -635,6 +693,7 @@ def main():
         "head_dim_256": d256,
         "prefill": prefill,
         "fp8_kv_scales": fp8_scales,
+        "tq4": tq4,
     }
     print(json.dumps(rec), flush=True)
 

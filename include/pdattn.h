@@ -101,7 +101,8 @@ typedef enum pdattn_status {
 typedef enum pdattn_kv_dtype {
   PDATTN_KV_BF16 = 0,
   PDATTN_KV_FP8_E4M3 = 1, /* OCP e4m3fn codes with one fp32 scale per (token, kv head) */
-  PDATTN_KV_FP8_E4M3_INLINE = 2 /* the same codes and scales, each row's scale stored after its codes */
+  PDATTN_KV_FP8_E4M3_INLINE = 2, /* the same codes and scales, each row's scale stored after its codes */
+  PDATTN_KV_TQ4 = 3 /* TQ4 compressed rows (pdattn_tq4_* calls only; see below) */
 } pdattn_kv_dtype;
 
 /*
@@ -391,6 +392,90 @@ PDATTN_API pdattn_status pdattn_prefill(const pdattn_problem* problem, int32_t c
                                         const int32_t* block_table, const int32_t* context_lens, float* out,
                                         float* lse, void* stream);
 
+/*
+ * ---- TQ4 compressed KV cache (FlashQuant wiki "CUDA Kernels": compress.cu,
+ * decompress.cu, fused_tq_attention.cu, paged_decode.cu, split_k_reduce.cu)
+ *
+ * Codec. R is a d x d orthogonal rotation (float32, row-major, 16-byte
+ * aligned), the same for K and V; K and V each have 16 centroids and 15
+ * sorted boundaries (float32). A row x (bf16) is stored as its norm
+ * ||x||_2 (fp32) and d 4-bit codes: x_hat = x / (||x|| + 1e-10), y = R x_hat,
+ * code_i = #{boundaries b : b <= y_i}, byte j = code_2j << 4 | code_2j+1
+ * (compress.cu, What It Replaces and Algorithm). The row it stands for is
+ * R_seq^T c where c_j = centroid[high nibble of byte j] * norm and
+ * c_{d/2 + j} = centroid[low nibble of byte j] * norm (decompress.cu,
+ * Sequential Layout), R_seq being R with row j = R[2j], row d/2 + j =
+ * R[2j + 1].
+ *
+ * Cache (paged_decode.cu, KV Cache Byte Layout): problem->kv_dtype =
+ * PDATTN_KV_TQ4, kv_layout = PDATTN_LAYOUT_HND; one uint8 pool of
+ * num_pages * Hkv * P rows of d + 8 bytes, row (page * Hkv + kvh) * P + slot:
+ * [K codes d/2 | K norm fp32 | V codes d/2 | V norm fp32]. The pool is 16-byte
+ * aligned. Page sizes: powers of two in [8, 128]; q_len 0 or 1.
+ */
+
+/* The codebook pdattn_tq4_append / pdattn_tq4_decode expect for rotated
+ * unit vectors of head_dim coordinates (FlashQuant wiki index, Algorithm
+ * Deep Dive, Lloyd-Max via erfinv): the 16-level Lloyd-Max quantiser of
+ * N(0, 1/head_dim), by Lloyd's iteration in double precision from the
+ * Gaussian quantiles; centroids (16) and boundaries (15, the midpoints)
+ * written as float32 to host arrays. Any head_dim >= 1. Host only. */
+PDATTN_API pdattn_status pdattn_tq4_codebook(int32_t head_dim, float* centroids, float* boundaries);
+
+/* Compress num_tokens new rows per kv head (k_new, v_new: bf16
+ * [num_tokens][Hkv][d], 16-byte aligned) and write them at page
+ * block_table[token_seq[t]][token_pos[t] / P], slot token_pos[t] % P, of
+ * `cache` (compress.cu, fused into the scatter). Tokens whose sequence,
+ * position or page falls outside the tables are skipped. Rows that two
+ * tokens name race. rotation, k_boundaries, v_boundaries: device float32
+ * (rotation 16-byte aligned). One kernel on `stream`. */
+PDATTN_API pdattn_status pdattn_tq4_append(const pdattn_problem* problem, int32_t num_tokens, const void* k_new,
+                                           const void* v_new, const int32_t* token_seq, const int32_t* token_pos,
+                                           const int32_t* block_table, const float* rotation,
+                                           const float* k_boundaries, const float* v_boundaries, void* cache,
+                                           void* stream);
+
+/* A TQ4 decode plan: every (sequence, kv head) pair is cut into work items
+ * of about chunk_tiles 16-token tiles (paged_decode.cu, split-K; the count
+ * per pair from the plan, not fixed), one wave each on a persistent grid. */
+typedef struct pdattn_tq4_plan_t {
+  pdattn_problem problem;   /* copy of the problem, scale resolved */
+  int32_t num_cus;          /* compute units the plan was sized for */
+  int32_t num_workgroups;   /* grid of the decode kernel (8 waves each) */
+  int32_t chunk_tiles;      /* tiles per work item (a pair takes ceil(tiles / chunk_tiles) items, evenly split) */
+  int32_t max_chunks;       /* work items per pair at most (longer pairs split their tiles over this many) */
+  int64_t total_tiles;      /* Hkv * sum_b ceil(L_b / 16) over the host lengths */
+  int64_t max_context_len;  /* largest host context length planned for */
+  uint64_t workspace_bytes; /* rotated queries, merged rotated outputs, the work items' records */
+  uint32_t magic;
+  uint32_t reserved1;
+} pdattn_tq4_plan_t;
+
+/* Plan a TQ4 decode step (problem->kv_dtype = PDATTN_KV_TQ4). num_cus: 0
+ * queries the current device; chunk_tiles: 0 = adaptive, > 0 forces it
+ * (tests move the split points with it). Host only apart from the device
+ * query. */
+PDATTN_API pdattn_status pdattn_tq4_plan(const pdattn_problem* problem, const int32_t* context_lens_host,
+                                         int32_t num_cus, int32_t chunk_tiles, pdattn_tq4_plan_t* out);
+
+/* Enqueue a TQ4 decode step on `stream`: q (bf16 [B][Hq][d], model space,
+ * 16-byte aligned) is rotated into the codes' space and rounded to fp16
+ * (fused_tq_attention.cu, Input/Output: the rotated queries are 16-bit), so
+ * its rotated values must stay below 65504 in magnitude;
+ * attention runs there over the cache (fused_tq_attention.cu, Decode Path;
+ * paged_decode.cu), each work item leaving (m, l, acc) in the workspace;
+ * the merge (split_k_reduce.cu) then writes out (fp32 [B][Hq][d], rotated
+ * back to model space: R_seq^T o) and lse (fp32 [B][Hq], natural log, or
+ * NULL). Empty sequences give out = 0, lse = -inf; a length beyond the
+ * block table or a block-table entry outside [0, num_pages) gives NaN.
+ * workspace: plan->workspace_bytes, 16-byte aligned; concurrent calls on one
+ * workspace race. Four kernels on `stream`. */
+PDATTN_API pdattn_status pdattn_tq4_decode(const pdattn_tq4_plan_t* plan, const void* q, const void* cache,
+                                           const float* rotation, const float* k_centroids,
+                                           const float* v_centroids, const int32_t* block_table,
+                                           const int32_t* context_lens, void* workspace, uint64_t workspace_bytes,
+                                           float* out, float* lse, void* stream);
+
 /* Static description of a status code. */
 PDATTN_API const char* pdattn_status_string(pdattn_status status);
 
@@ -410,9 +495,11 @@ PDATTN_API pdattn_status pdattn_stream_read(const void* buffer, uint64_t bytes, 
                                             void* stream);
 PDATTN_API uint64_t pdattn_stream_read_sink_words(int32_t num_cus);
 
-/* sizeof(pdattn_problem) and sizeof(pdattn_plan_t), for binding checks. */
+/* sizeof(pdattn_problem), sizeof(pdattn_plan_t) and sizeof(pdattn_tq4_plan_t),
+ * for binding checks. */
 PDATTN_API uint64_t pdattn_problem_size(void);
 PDATTN_API uint64_t pdattn_plan_size(void);
+PDATTN_API uint64_t pdattn_tq4_plan_size(void);
 
 #ifdef __cplusplus
 }

@@ -340,3 +340,105 @@ def paged_prefill(q, qo_indptr, k_pages, v_pages, block_table, context_lens, *, 
     prefill(prob, q, qo_indptr, tb.to(dev), ti.to(dev), k_pages, v_pages, k_scale, v_scale, block_table,
             context_lens, out, lse, causal=causal)
     return out, lse
+
+
+# ---- TQ4 compressed cache ---------------------------------------------------
+
+KV_TQ4 = 3
+
+
+class Tq4Plan(ctypes.Structure):
+    """Mirror of ``pdattn_tq4_plan_t``."""
+    _fields_ = [
+        ("problem", Problem),
+        ("num_cus", ctypes.c_int32),
+        ("num_workgroups", ctypes.c_int32),
+        ("chunk_tiles", ctypes.c_int32),
+        ("max_chunks", ctypes.c_int32),
+        ("total_tiles", ctypes.c_int64),
+        ("max_context_len", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_uint64),
+        ("magic", ctypes.c_uint32),
+        ("reserved1", ctypes.c_uint32),
+    ]
+
+
+_lib.pdattn_tq4_codebook.restype = ctypes.c_int
+_lib.pdattn_tq4_codebook.argtypes = [ctypes.c_int32, _P, _P]
+_lib.pdattn_tq4_append.restype = ctypes.c_int
+_lib.pdattn_tq4_append.argtypes = [ctypes.POINTER(Problem), ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+_lib.pdattn_tq4_plan.restype = ctypes.c_int
+_lib.pdattn_tq4_plan.argtypes = [ctypes.POINTER(Problem), _P, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(Tq4Plan)]
+_lib.pdattn_tq4_decode.restype = ctypes.c_int
+_lib.pdattn_tq4_decode.argtypes = [ctypes.POINTER(Tq4Plan), _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint64, _P, _P,
+                                   _P]
+_lib.pdattn_tq4_plan_size.restype = ctypes.c_uint64
+if _lib.pdattn_tq4_plan_size() != ctypes.sizeof(Tq4Plan):
+    raise ImportError("libpdattn.so TQ4 plan layout does not match the binding")
+__all__ += ["KV_TQ4", "Tq4Plan", "tq4_codebook", "tq4_problem", "tq4_append", "tq4_plan", "tq4_decode",
+            "paged_decode_tq4"]
+
+
+def tq4_codebook(head_dim):
+    """pdattn_tq4_codebook: (centroids float32 [16], boundaries float32 [15])
+    CPU tensors."""
+    c = torch.empty(16, dtype=torch.float32)
+    b = torch.empty(15, dtype=torch.float32)
+    _check(_lib.pdattn_tq4_codebook(int(head_dim), _ptr(c), _ptr(b)), "pdattn_tq4_codebook")
+    return c, b
+
+
+def tq4_problem(q_or_heads, cache, block_table, scale=0.0):
+    """The pdattn_problem of a TQ4 cache uint8 [num_pages, Hkv, P, d + 8] and
+    q [B, Hq, d] (or (B, Hq) for an append, which needs no q)."""
+    if cache.dtype != torch.uint8 or cache.dim() != 4:
+        raise ValueError("a TQ4 cache is uint8 [num_pages, Hkv, P, d + 8]")
+    num_pages, Hkv, P, rb = cache.shape
+    B, Hq = (q_or_heads.shape[0], q_or_heads.shape[1]) if isinstance(q_or_heads, torch.Tensor) else q_or_heads
+    return Problem(int(B), int(Hq), int(Hkv), int(rb - 8), int(P), int(block_table.shape[1]), int(num_pages), KV_TQ4,
+                   float(scale), LAYOUT_HND, 1)
+
+
+def tq4_append(k_new, v_new, token_seq, token_pos, block_table, rotation, k_boundaries, v_boundaries, cache,
+               num_q_heads=None, stream=None):
+    """pdattn_tq4_append: compress k_new / v_new (bf16 [T, Hkv, d]) into the
+    cache rows their (sequence, position) name. All tensors on the device."""
+    Hkv = cache.shape[1]
+    prob = tq4_problem((block_table.shape[0], num_q_heads or Hkv), cache, block_table)
+    for t in (k_new, v_new, rotation, cache, token_seq, token_pos, block_table, k_boundaries, v_boundaries):
+        if not t.is_contiguous():
+            raise ValueError("tq4_append takes contiguous tensors")
+    _check(_lib.pdattn_tq4_append(ctypes.byref(prob), int(k_new.shape[0]), _ptr(k_new), _ptr(v_new), _ptr(token_seq),
+                                  _ptr(token_pos), _ptr(block_table), _ptr(rotation), _ptr(k_boundaries),
+                                  _ptr(v_boundaries), _ptr(cache), _stream(stream)), "pdattn_tq4_append")
+
+
+def tq4_plan(problem, context_lens_host, num_cus=0, chunk_tiles=0):
+    """pdattn_tq4_plan; context_lens_host: CPU int32 [B]."""
+    lens = context_lens_host.to(torch.int32).contiguous()
+    pl = Tq4Plan()
+    _check(_lib.pdattn_tq4_plan(ctypes.byref(problem), _ptr(lens), int(num_cus), int(chunk_tiles), ctypes.byref(pl)),
+           "pdattn_tq4_plan")
+    return pl
+
+
+def tq4_decode(pl, q, cache, rotation, k_centroids, v_centroids, block_table, context_lens, ws, out, lse,
+               stream=None):
+    """pdattn_tq4_decode with caller-owned workspace and outputs."""
+    _check(_lib.pdattn_tq4_decode(ctypes.byref(pl), _ptr(q), _ptr(cache), _ptr(rotation), _ptr(k_centroids),
+                                  _ptr(v_centroids), _ptr(block_table), _ptr(context_lens), _ptr(ws),
+                                  int(ws.numel()), _ptr(out), _ptr(lse), _stream(stream)), "pdattn_tq4_decode")
+
+
+def paged_decode_tq4(q, cache, block_table, context_lens, rotation, k_centroids, v_centroids, *,
+                     context_lens_host=None, scale=0.0, chunk_tiles=0, stream=None):
+    """Plan, allocate and run one TQ4 decode step; returns (out fp32
+    [B, Hq, d], lse fp32 [B, Hq]) in model space."""
+    lens_host = context_lens.cpu() if context_lens_host is None else context_lens_host
+    prob = tq4_problem(q, cache, block_table, scale)
+    pl = tq4_plan(prob, lens_host, chunk_tiles=chunk_tiles)
+    ws = torch.empty(max(int(pl.workspace_bytes), 16), dtype=torch.uint8, device=q.device)
+    out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    tq4_decode(pl, q, cache, rotation, k_centroids, v_centroids, block_table, context_lens, ws, out, lse, stream)
+    return out, lse

@@ -13,7 +13,7 @@ LIBRARY = os.path.join(HERE, "libpdattn.so")
 SOURCES = [os.path.join(CSRC, "pdattn.hip"), os.path.join(CSRC, "decode_kernels.hip"),
            os.path.join(CSRC, "decode_dynamic.hip"), os.path.join(CSRC, "stream_read.hip"),
            os.path.join(CSRC, "kv_append.hip"), os.path.join(CSRC, "merge.hip"),
-           os.path.join(CSRC, "prefill.hip")]
+           os.path.join(CSRC, "prefill.hip"), os.path.join(CSRC, "tq4.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -17,6 +17,7 @@
 #include "append.h"
 #include "merge.h"
 #include "prefill.h"
+#include "tq4.h"
 
 namespace {
 
@@ -41,7 +42,8 @@ int ilog2(int64_t x) {
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
 
-pdattn_status check_problem(const pdattn_problem* p) {
+// TQ4 problems are accepted only by the pdattn_tq4_* calls (allow_tq4).
+pdattn_status check_problem(const pdattn_problem* p, bool allow_tq4 = false) {
   if (p == nullptr) return fail(PDATTN_ERR_INVALID_ARGUMENT, "problem is NULL");
   if (p->batch < 0 || p->batch > 65535)
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "batch %d outside [0, 65535]", p->batch);
@@ -63,8 +65,12 @@ pdattn_status check_problem(const pdattn_problem* p) {
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "negative block table or pool size");
   if ((int64_t)p->max_pages_per_seq * p->page_size > INT32_MAX)
     return fail(PDATTN_ERR_UNSUPPORTED, "max_pages_per_seq * page_size exceeds 2^31 - 1 tokens");
-  if (p->kv_dtype != PDATTN_KV_BF16 && p->kv_dtype != PDATTN_KV_FP8_E4M3 && p->kv_dtype != PDATTN_KV_FP8_E4M3_INLINE)
+  if (p->kv_dtype == PDATTN_KV_TQ4) {
+    if (!allow_tq4) return fail(PDATTN_ERR_UNSUPPORTED, "TQ4 caches are served by the pdattn_tq4_* calls only");
+  } else if (p->kv_dtype != PDATTN_KV_BF16 && p->kv_dtype != PDATTN_KV_FP8_E4M3 &&
+             p->kv_dtype != PDATTN_KV_FP8_E4M3_INLINE) {
     return fail(PDATTN_ERR_UNSUPPORTED, "kv_dtype %d unknown", p->kv_dtype);
+  }
   if (!std::isfinite(p->scale)) return fail(PDATTN_ERR_INVALID_ARGUMENT, "scale is not finite");
   if (p->kv_layout != PDATTN_LAYOUT_NHD && p->kv_layout != PDATTN_LAYOUT_HND)
     return fail(PDATTN_ERR_UNSUPPORTED, "kv_layout %d unknown", p->kv_layout);
@@ -199,6 +205,7 @@ PDATTN_API const char* pdattn_last_error(void) { return g_last_error; }
 
 PDATTN_API uint64_t pdattn_problem_size(void) { return sizeof(pdattn_problem); }
 PDATTN_API uint64_t pdattn_plan_size(void) { return sizeof(pdattn_plan_t); }
+PDATTN_API uint64_t pdattn_tq4_plan_size(void) { return sizeof(pdattn_tq4_plan_t); }
 
 PDATTN_API pdattn_status pdattn_plan(const pdattn_problem* problem, const int32_t* context_lens_host,
                                      int32_t num_cus, int32_t force_workers, int32_t flags, pdattn_plan_t* out) {
@@ -675,6 +682,255 @@ PDATTN_API pdattn_status pdattn_stream_read(const void* buffer, uint64_t bytes, 
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "buffer must be 16-byte aligned and a multiple of 4096 bytes");
   hipError_t e = pdattn::launch_stream_read(buffer, bytes, sink, (uint32_t)num_cus * 2, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "stream-read kernel launch: %s", hipGetErrorString(e));
+  return PDATTN_OK;
+}
+
+}  // extern "C"
+
+// ---- TQ4 compressed cache ----------------------------------------------------
+
+namespace {
+
+constexpr uint32_t kTq4PlanMagic = 0x70645434u;  // "pdT4"
+
+double std_normal_cdf(double z) { return 0.5 * std::erfc(-z / std::sqrt(2.0)); }
+double std_normal_pdf(double z) { return std::isinf(z) ? 0.0 : std::exp(-0.5 * z * z) / std::sqrt(2.0 * M_PI); }
+
+// Lloyd-Max quantiser of N(0, 1): start at the quantiles (i + 1/2) / 16
+// (found by bisection on the cdf), then alternate midpoint boundaries and
+// cell means until no centroid moves by more than 1e-13.
+void lloyd_max16(double (&c)[16], double (&b)[15]) {
+  for (int i = 0; i < 16; ++i) {
+    const double u = (i + 0.5) / 16.0;
+    double lo = -12.0, hi = 12.0;
+    for (int it = 0; it < 200; ++it) {
+      const double mid = 0.5 * (lo + hi);
+      (std_normal_cdf(mid) < u ? lo : hi) = mid;
+    }
+    c[i] = 0.5 * (lo + hi);
+  }
+  for (int it = 0; it < 100000; ++it) {
+    for (int i = 0; i < 15; ++i) b[i] = 0.5 * (c[i] + c[i + 1]);
+    double moved = 0.0;
+    for (int i = 0; i < 16; ++i) {
+      const double a = i == 0 ? -INFINITY : b[i - 1];
+      const double z = i == 15 ? INFINITY : b[i];
+      // cell mass as a difference of upper tails (accurate in both tails)
+      const double mass = 0.5 * (std::erfc(a / std::sqrt(2.0)) - std::erfc(z / std::sqrt(2.0)));
+      const double m = (std_normal_pdf(a) - std_normal_pdf(z)) / mass;
+      moved = std::max(moved, std::fabs(m - c[i]));
+      c[i] = m;
+    }
+    if (moved <= 1e-13) break;
+  }
+  for (int i = 0; i < 15; ++i) b[i] = 0.5 * (c[i] + c[i + 1]);
+}
+
+pdattn_status check_tq4_problem(const pdattn_problem* p) {
+  pdattn_status st = check_problem(p, true);
+  if (st != PDATTN_OK) return st;
+  if (p->kv_dtype != PDATTN_KV_TQ4) return fail(PDATTN_ERR_INVALID_ARGUMENT, "kv_dtype must be PDATTN_KV_TQ4");
+  if (p->kv_layout != PDATTN_LAYOUT_HND) return fail(PDATTN_ERR_UNSUPPORTED, "TQ4 caches are head-major (HND) only");
+  if (qlen_of(*p) != 1) return fail(PDATTN_ERR_UNSUPPORTED, "TQ4 decode takes one query row per sequence");
+  return PDATTN_OK;
+}
+
+uint64_t tq4_qseq_bytes(const pdattn_problem& p) {
+  return round_up((uint64_t)p.batch * p.num_q_heads * p.head_dim * 2, 256);
+}
+// workspace: rotated q (fp16), merged outputs (fp32, rotated space), records
+uint64_t tq4_oseq_bytes(const pdattn_problem& p) {
+  return round_up((uint64_t)p.batch * p.num_q_heads * p.head_dim * 4, 256);
+}
+uint64_t tq4_workspace(const pdattn_problem& p, int32_t max_chunks) {
+  return tq4_qseq_bytes(p) + tq4_oseq_bytes(p) +
+         (uint64_t)max_chunks * p.batch * p.num_kv_heads *
+             (uint64_t)pdattn::tq4_record_floats(heads_per_kv(p), p.head_dim) * 4;
+}
+
+pdattn_status check_tq4_plan(const pdattn_tq4_plan_t* plan) {
+  if (plan == nullptr) return fail(PDATTN_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (plan->magic != kTq4PlanMagic) return fail(PDATTN_ERR_PLAN_MISMATCH, "plan was not produced by pdattn_tq4_plan");
+  pdattn_status st = check_tq4_problem(&plan->problem);
+  if (st != PDATTN_OK) return fail(PDATTN_ERR_PLAN_MISMATCH, "plan holds an invalid problem: %s", g_last_error);
+  if (plan->num_workgroups < 0 || plan->chunk_tiles < 1 || plan->max_chunks < 1 ||
+      plan->workspace_bytes != tq4_workspace(plan->problem, plan->max_chunks))
+    return fail(PDATTN_ERR_PLAN_MISMATCH, "plan fields are inconsistent");
+  return PDATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+PDATTN_API pdattn_status pdattn_tq4_codebook(int32_t head_dim, float* centroids, float* boundaries) {
+  g_last_error[0] = '\0';
+  if (head_dim < 1) return fail(PDATTN_ERR_INVALID_ARGUMENT, "head_dim %d must be positive", head_dim);
+  if (!centroids || !boundaries) return fail(PDATTN_ERR_INVALID_ARGUMENT, "centroids and boundaries required");
+  double c[16], b[15];
+  lloyd_max16(c, b);
+  const double sigma = 1.0 / std::sqrt((double)head_dim);
+  for (int i = 0; i < 16; ++i) centroids[i] = (float)(c[i] * sigma);
+  for (int i = 0; i < 15; ++i) boundaries[i] = (float)(b[i] * sigma);
+  return PDATTN_OK;
+}
+
+PDATTN_API pdattn_status pdattn_tq4_append(const pdattn_problem* problem, int32_t num_tokens, const void* k_new,
+                                           const void* v_new, const int32_t* token_seq, const int32_t* token_pos,
+                                           const int32_t* block_table, const float* rotation,
+                                           const float* k_boundaries, const float* v_boundaries, void* cache,
+                                           void* stream) {
+  g_last_error[0] = '\0';
+  pdattn_status st = check_problem(problem, true);
+  if (st != PDATTN_OK) return st;
+  if (problem->kv_dtype != PDATTN_KV_TQ4) return fail(PDATTN_ERR_INVALID_ARGUMENT, "kv_dtype must be PDATTN_KV_TQ4");
+  if (problem->kv_layout != PDATTN_LAYOUT_HND) return fail(PDATTN_ERR_UNSUPPORTED, "TQ4 caches are head-major (HND) only");
+  if (num_tokens < 0) return fail(PDATTN_ERR_INVALID_ARGUMENT, "num_tokens %d is negative", num_tokens);
+  if (num_tokens == 0 || problem->batch == 0 || problem->max_pages_per_seq == 0 || problem->num_pages == 0)
+    return PDATTN_OK;
+  if (!k_new || !v_new || !token_seq || !token_pos || !block_table || !rotation || !k_boundaries || !v_boundaries ||
+      !cache)
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(cache, 16) || !aligned(rotation, 16))
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "k_new, v_new, cache and rotation must be 16-byte aligned");
+  if (!aligned(token_seq, 4) || !aligned(token_pos, 4) || !aligned(block_table, 4) || !aligned(k_boundaries, 4) ||
+      !aligned(v_boundaries, 4))
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "index arrays and boundaries must be 4-byte aligned");
+  pdattn::Tq4AppendParams p;
+  std::memset(&p, 0, sizeof p);
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.token_seq = token_seq;
+  p.token_pos = token_pos;
+  p.block_table = block_table;
+  p.rotation = rotation;
+  p.k_bounds = k_boundaries;
+  p.v_bounds = v_boundaries;
+  p.cache = static_cast<uint8_t*>(cache);
+  p.num_tokens = num_tokens;
+  p.batch = problem->batch;
+  p.num_kv_heads = problem->num_kv_heads;
+  p.page_log2 = ilog2(problem->page_size);
+  p.max_pages_per_seq = problem->max_pages_per_seq;
+  p.num_pages = problem->num_pages;
+  // one wave per (token, kv head), four per workgroup, grid-stride beyond 2^20 workgroups
+  const int64_t wgs = ceil_div((int64_t)num_tokens * problem->num_kv_heads, 4);
+  const uint32_t grid = (uint32_t)std::min<int64_t>(wgs, (int64_t)1 << 20);
+  hipError_t e = pdattn::launch_tq4_append(p, problem->head_dim, grid, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "TQ4 append kernel launch: %s", hipGetErrorString(e));
+  return PDATTN_OK;
+}
+
+PDATTN_API pdattn_status pdattn_tq4_plan(const pdattn_problem* problem, const int32_t* context_lens_host,
+                                         int32_t num_cus, int32_t chunk_tiles, pdattn_tq4_plan_t* out) {
+  g_last_error[0] = '\0';
+  pdattn_status st = check_tq4_problem(problem);
+  if (st != PDATTN_OK) return st;
+  if (out == nullptr) return fail(PDATTN_ERR_INVALID_ARGUMENT, "out is NULL");
+  if (problem->batch > 0 && context_lens_host == nullptr)
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "context_lens_host is NULL");
+  if (num_cus < 0 || chunk_tiles < 0) return fail(PDATTN_ERR_INVALID_ARGUMENT, "num_cus and chunk_tiles must be >= 0");
+  const int64_t cap = (int64_t)problem->max_pages_per_seq * problem->page_size;
+  int64_t total = 0, max_len = 0, max_tiles = 0;
+  for (int b = 0; b < problem->batch; ++b) {
+    const int64_t L = context_lens_host[b];
+    if (L < 0 || L > cap)
+      return fail(PDATTN_ERR_INVALID_ARGUMENT, "context length %lld of sequence %d outside [0, %lld]", (long long)L, b,
+                  (long long)cap);
+    const int64_t nt = ceil_div(L, pdattn::kTileTokens);
+    total += nt;
+    max_len = std::max(max_len, L);
+    max_tiles = std::max(max_tiles, nt);
+  }
+  total *= problem->num_kv_heads;
+  if (max_len > 0 && problem->num_pages <= 0) return fail(PDATTN_ERR_INVALID_ARGUMENT, "empty page pool");
+  int dev = 0;
+  if (num_cus == 0) {
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || num_cus <= 0)
+      return fail(PDATTN_ERR_DEVICE, "cannot query the compute-unit count: %s", hipGetErrorString(e));
+  }
+  int wpc = pdattn::tq4_decode_wgs_per_cu(problem->head_dim);
+  if (wpc <= 0) wpc = problem->head_dim == 256 ? 1 : 2;
+  const int64_t wgs = (int64_t)num_cus * wpc;
+  const int64_t waves = wgs * pdattn::kTq4Waves;
+  const int64_t pairs = (int64_t)problem->batch * problem->num_kv_heads;
+  int64_t ct = chunk_tiles;
+  if (ct == 0) {
+    // about one work item per resident wave: a pair's item count rounds up,
+    // so the pairs' rounding is taken off the waves first
+    const int64_t slots = std::max<int64_t>(waves - pairs, waves / 2);
+    ct = std::max<int64_t>(pdattn::kTq4MinChunkTiles, ceil_div(std::max<int64_t>(total, 1), slots));
+  }
+  ct = std::min<int64_t>(ct, 1 << 24);
+  const int64_t mc = std::max<int64_t>(1, ceil_div(std::max<int64_t>(max_tiles, 1), ct));
+  if (mc * pairs >= ((int64_t)1 << 31)) return fail(PDATTN_ERR_UNSUPPORTED, "too many work items");
+  std::memset(out, 0, sizeof *out);
+  out->problem = *problem;
+  if (out->problem.scale <= 0.0f) out->problem.scale = 1.0f / std::sqrt((float)problem->head_dim);
+  out->num_cus = num_cus;
+  out->num_workgroups = (int32_t)std::min<int64_t>(wgs, std::max<int64_t>(1, ceil_div(mc * pairs, pdattn::kTq4Waves)));
+  out->chunk_tiles = (int32_t)ct;
+  out->max_chunks = (int32_t)mc;
+  out->total_tiles = total;
+  out->max_context_len = max_len;
+  out->workspace_bytes = tq4_workspace(out->problem, out->max_chunks);
+  out->magic = kTq4PlanMagic;
+  return PDATTN_OK;
+}
+
+PDATTN_API pdattn_status pdattn_tq4_decode(const pdattn_tq4_plan_t* plan, const void* q, const void* cache,
+                                           const float* rotation, const float* k_centroids,
+                                           const float* v_centroids, const int32_t* block_table,
+                                           const int32_t* context_lens, void* workspace, uint64_t workspace_bytes,
+                                           float* out, float* lse, void* stream) {
+  g_last_error[0] = '\0';
+  pdattn_status st = check_tq4_plan(plan);
+  if (st != PDATTN_OK) return st;
+  const pdattn_problem& pr = plan->problem;
+  if (pr.batch == 0) return PDATTN_OK;
+  if (!q || !rotation || !out || !context_lens || !workspace || !block_table)
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if (pr.num_pages > 0 && (!cache || !k_centroids || !v_centroids))
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "cache and centroids required");
+  if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(rotation, 16) || !aligned(out, 16) ||
+      !aligned(workspace, 16))
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "q, cache, rotation, out and workspace must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(context_lens, 4) || !aligned(lse, 4) || !aligned(k_centroids, 4) ||
+      !aligned(v_centroids, 4))
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "block_table, context_lens, lse and centroids must be 4-byte aligned");
+  if (workspace_bytes < plan->workspace_bytes)
+    return fail(PDATTN_ERR_WORKSPACE, "workspace needs %llu bytes, got %llu",
+                (unsigned long long)plan->workspace_bytes, (unsigned long long)workspace_bytes);
+  pdattn::Tq4DecodeParams p;
+  std::memset(&p, 0, sizeof p);
+  p.q = static_cast<const uint16_t*>(q);
+  p.q_seq = static_cast<uint16_t*>(workspace);
+  p.cache = static_cast<const uint8_t*>(cache);
+  p.rotation = rotation;
+  p.k_cent = k_centroids;
+  p.v_cent = v_centroids;
+  p.block_table = block_table;
+  p.context_lens = context_lens;
+  p.o_seq = reinterpret_cast<float*>(static_cast<char*>(workspace) + tq4_qseq_bytes(pr));
+  p.rec = reinterpret_cast<float*>(static_cast<char*>(workspace) + tq4_qseq_bytes(pr) + tq4_oseq_bytes(pr));
+  p.out = out;
+  p.lse = lse;
+  p.batch = pr.batch;
+  p.num_q_heads = pr.num_q_heads;
+  p.num_kv_heads = pr.num_kv_heads;
+  p.heads_per_kv = heads_per_kv(pr);
+  p.page_log2 = ilog2(pr.page_size);
+  p.max_pages_per_seq = pr.max_pages_per_seq;
+  p.num_pages = pr.num_pages;
+  p.chunk_tiles = plan->chunk_tiles;
+  p.max_chunks = plan->max_chunks;
+  const uint32_t grid = pr.num_pages > 0 && pr.max_pages_per_seq > 0 ? (uint32_t)plan->num_workgroups : 0;
+  p.num_waves = (int32_t)(grid * pdattn::kTq4Waves);
+  p.qk_scale_log2 = pr.scale * 1.44269504088896340736f;
+  hipError_t e = pdattn::launch_tq4_decode(p, pr.head_dim, grid, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "TQ4 decode launch: %s", hipGetErrorString(e));
   return PDATTN_OK;
 }
 

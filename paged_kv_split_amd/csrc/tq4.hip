@@ -74,6 +74,17 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), f16x2));
 }
 
+// Max over the four 16-lane groups (lanes c, c + 16, c + 32, c + 48) by the
+// gfx950 lane swaps (permlane16 swaps the middle groups' halves, permlane32
+// the two halves: with both operands x, a lane's two results are its own
+// value and its partner's): plain VALU, no LDS round trip.
+__device__ __forceinline__ float max_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
@@ -349,6 +360,21 @@ void tq4_decode_kernel(const Tq4DecodeParams p) {
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
 
+      // V codes first (independent of the scores): lane (d row m = col,
+      // group r), tokens 4 r + jj,
+      // code bytes m KB .. m KB + KB - 1 of each
+      constexpr int VW = KB >= 4 ? KB / 4 : 1;  // code dwords per lane and token
+      uint32_t vw[4][VW];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const unsigned char* vr = buf + (4 * grp + jj) * RB + H + 4 + col * KB;
+        if constexpr (KB == 2) {
+          vw[jj][0] = *reinterpret_cast<const uint16_t*>(vr);
+        } else {
+#pragma unroll
+          for (int q = 0; q < VW; ++q) vw[jj][q] = *reinterpret_cast<const uint32_t*>(vr + 4 * q);
+        }
+      }
       // S = K . Q^T: lane (token m = col, group r)
       f32x4 S = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       {
@@ -373,9 +399,7 @@ void tq4_decode_kernel(const Tq4DecodeParams p) {
         const float xs = S[j] * kn * p.qk_scale_log2;
         x[j] = tok0 + j < L ? xs : -__builtin_inff();
       }
-      float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mx = max_groups(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
       // the running max moves only when a tile's max exceeds it by more
       // than 8 (log2 units), so every weight stays below 2^8 and the
       // accumulators are rescaled rarely; numerator and denominator share
@@ -384,6 +408,9 @@ void tq4_decode_kernel(const Tq4DecodeParams p) {
       const float m_new = up ? mx : m_run;
       const float m_ref = m_new == -__builtin_inff() ? 0.0f : m_new;
       if (__any(up)) {
+        // a real branch (the marker keeps the compiler from executing the
+        // rescale on every tile with a select)
+        asm volatile("; tq4 rescale" ::: "memory");
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
         l_part *= alpha;
 #pragma unroll
@@ -399,20 +426,7 @@ void tq4_decode_kernel(const Tq4DecodeParams p) {
       }
       const bf16x4 pop = __builtin_bit_cast(bf16x4, u32x2{pack_bf16(pw[0], pw[1]), pack_bf16(pw[2], pw[3])});
 
-      // O^T += V^T . P: lane (d row m = col, group r), tokens 4 r + jj,
-      // code bytes m KB .. m KB + KB - 1 of each
-      constexpr int VW = KB >= 4 ? KB / 4 : 1;  // code dwords per lane and token
-      uint32_t vw[4][VW];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const unsigned char* vr = buf + (4 * grp + jj) * RB + H + 4 + col * KB;
-        if constexpr (KB == 2) {
-          vw[jj][0] = *reinterpret_cast<const uint16_t*>(vr);
-        } else {
-#pragma unroll
-          for (int q = 0; q < VW; ++q) vw[jj][q] = *reinterpret_cast<const uint32_t*>(vr + 4 * q);
-        }
-      }
+      // O^T += V^T . P
 #pragma unroll
       for (int i = 0; i < KB; ++i) {
         uint32_t lk[4];

@@ -423,7 +423,9 @@ def make_tq4_inputs(w, *, seed=None):
     if isinstance(w, str):
         w = WORKLOADS[w]
     seed = w.seed if seed is None else seed
-    g = torch.Generator().manual_seed(int(seed) + 77)
+    # the same generator start as make_inputs: the same lengths, block table
+    # and q as the workload's bf16 / fp8 step
+    g = torch.Generator().manual_seed(int(seed))
     B, Hq, Hkv, D, P = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size
     lens = _lens(w, g)
     needed = [(int(L) + P - 1) // P for L in lens.tolist()]

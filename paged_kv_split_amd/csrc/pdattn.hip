@@ -813,8 +813,9 @@ PDATTN_API pdattn_status pdattn_tq4_append(const pdattn_problem* problem, int32_
   p.page_log2 = ilog2(problem->page_size);
   p.max_pages_per_seq = problem->max_pages_per_seq;
   p.num_pages = problem->num_pages;
-  // one wave per (token, kv head), four per workgroup, grid-stride beyond 2^20 workgroups
-  const int64_t wgs = ceil_div((int64_t)num_tokens * problem->num_kv_heads, 4);
+  // 16 row vectors (K and V of 8 (token, kv head) pairs) per workgroup,
+  // grid-stride beyond 2^20 workgroups
+  const int64_t wgs = ceil_div((int64_t)num_tokens * problem->num_kv_heads * 2, 16);
   const uint32_t grid = (uint32_t)std::min<int64_t>(wgs, (int64_t)1 << 20);
   hipError_t e = pdattn::launch_tq4_append(p, problem->head_dim, grid, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "TQ4 append kernel launch: %s", hipGetErrorString(e));

@@ -16,9 +16,11 @@
 // d/2 + j is R[2j + 1]. Attention runs in that space (fused_tq_attention.cu,
 // Input/Output: q pre-rotated, output rotated back).
 //
-// tq4_append_kernel: one wave per (token, kv head), K then V: norm by a wave
-//   reduction, x_hat in LDS, lane j forms y_2j and y_2j+1 (rotation rows
-//   from L2), counts the boundaries and stores byte j; lane 0 stores the norm.
+// tq4_append_kernel: 16 row vectors (the K and V rows of 8 (token, kv head)
+//   pairs) per workgroup: norms by wave reductions and x_hat in LDS; thread
+//   t forms rotated coordinate t mod D of several vectors (each rotation row
+//   read once per 16 vectors) and counts the boundaries; then the packed
+//   bytes and the norms are stored.
 // tq4_rotate_q_kernel: q into the sequential rotated space, rounded to fp16
 //   (the pages' rotated queries are 16-bit; fp16 keeps 11 significant bits).
 // tq4_decode_kernel: a persistent grid; a work item is a run of 16-token
@@ -101,77 +103,107 @@ __device__ __forceinline__ uint32_t code_of(float y, const float* bnd) {
 
 // ---- compress and scatter --------------------------------------------------
 
+constexpr int kAppendVecs = 16;  // row vectors per append workgroup
+
+// Vector v of the append is (token v / (2 Hkv), kv head (v / 2) mod Hkv,
+// K if v is even else V). A workgroup compresses kAppendVecs of them:
+// wave w normalises vectors w, w + 4, ... into LDS (norm by a wave
+// reduction); thread t then owns rotated coordinate i = t mod D of vectors
+// t / D, t / D + 256 / D, ..., reading rotation row R[i] once for them, and
+// leaves the codes in LDS; last, the packed bytes and norms are stored.
 template <int D>
 __global__ __launch_bounds__(256) void tq4_append_kernel(const Tq4AppendParams p) {
   constexpr int H = D / 2;
   constexpr int RB = D + 8;
-  constexpr int EPL = D / 64;                 // elements per lane
-  constexpr int PPL = (H + 63) / 64;          // code bytes (element pairs) per lane
-  __shared__ float s_x[4][D];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  constexpr int EPL = D / 64;
+  constexpr int TPC = 256 / D;                 // threads per coordinate
+  constexpr int VPT = kAppendVecs / TPC;       // vectors per thread
+  __shared__ __attribute__((aligned(16))) float s_x[kAppendVecs][D];
+  __shared__ float s_norm[kAppendVecs];
+  __shared__ uint8_t s_code[kAppendVecs][D];
+  __shared__ long long s_row[kAppendVecs];     // destination byte offset, or -1
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int P = 1 << p.page_log2;
-  const long long items = (long long)p.num_tokens * p.num_kv_heads;
-  float kb[15], vb[15];
-#pragma unroll
-  for (int i = 0; i < 15; ++i) {
-    kb[i] = p.k_bounds[i];
-    vb[i] = p.v_bounds[i];
-  }
-  for (long long it = (long long)blockIdx.x * 4 + wave; it < items; it += (long long)gridDim.x * 4) {
-    const int t = (int)(it / p.num_kv_heads);
-    const int kvh = (int)(it % p.num_kv_heads);
-    const int s = p.token_seq[t];
-    const int pos = p.token_pos[t];
-    if (s < 0 || s >= p.batch || pos < 0 || (pos >> p.page_log2) >= p.max_pages_per_seq) continue;
-    const int page = p.block_table[(long long)s * p.max_pages_per_seq + (pos >> p.page_log2)];
-    if (page < 0 || page >= p.num_pages) continue;
-    uint8_t* row = p.cache + (((long long)page * p.num_kv_heads + kvh) * P + (pos & (P - 1))) * RB;
-#pragma unroll
-    for (int kv = 0; kv < 2; ++kv) {
-      const uint16_t* src = (kv == 0 ? p.k_new : p.v_new) + ((long long)t * p.num_kv_heads + kvh) * D;
+  const long long nvec = (long long)p.num_tokens * p.num_kv_heads * 2;
+  for (long long v0 = (long long)blockIdx.x * kAppendVecs; v0 < nvec; v0 += (long long)gridDim.x * kAppendVecs) {
+    // 1. norms and x_hat
+    for (int lv = wave; lv < kAppendVecs; lv += 4) {
+      const long long v = v0 + lv;
+      long long dst = -1;
       float x[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) x[e] = 0.0f;
+      if (v < nvec) {
+        const int kind = (int)(v & 1);
+        const long long th = v >> 1;           // token * Hkv + kv head
+        const int t = (int)(th / p.num_kv_heads);
+        const int kvh = (int)(th % p.num_kv_heads);
+        const int s = p.token_seq[t];
+        const int pos = p.token_pos[t];
+        if (s >= 0 && s < p.batch && pos >= 0 && (pos >> p.page_log2) < p.max_pages_per_seq) {
+          const int page = p.block_table[(long long)s * p.max_pages_per_seq + (pos >> p.page_log2)];
+          if (page >= 0 && page < p.num_pages)
+            dst = (((long long)page * p.num_kv_heads + kvh) * P + (pos & (P - 1))) * RB + (kind ? H + 4 : 0);
+        }
+        const uint16_t* src = (kind ? p.v_new : p.k_new) + th * D;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) x[e] = __uint_as_float((uint32_t)src[lane + 64 * e] << 16);
+      }
       float ss = 0.0f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        x[e] = __uint_as_float((uint32_t)src[lane + 64 * e] << 16);
-        ss += x[e] * x[e];
-      }
+      for (int e = 0; e < EPL; ++e) ss += x[e] * x[e];
       const float norm = sqrtf(wave_sum(ss));
       const float den = norm + kNormEps;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s_x[wave][lane + 64 * e] = x[e] / den;
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      uint8_t* dst = row + (kv == 0 ? 0 : H + 4);
-#pragma unroll
-      for (int q = 0; q < PPL; ++q) {
-        const int j = lane + 64 * q;
-        if (j < H) {
-          const float* r0 = p.rotation + (long long)(2 * j) * D;
-          const float* r1 = r0 + D;
-          float y0 = 0.0f, y1 = 0.0f;
-#pragma unroll 8
-          for (int k = 0; k < D; k += 4) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(r0 + k);
-            const f32x4 b = *reinterpret_cast<const f32x4*>(r1 + k);
-            const f32x4 xv = *reinterpret_cast<const f32x4*>(&s_x[wave][k]);
-            y0 = fmaf(a[0], xv[0], y0);
-            y0 = fmaf(a[1], xv[1], y0);
-            y0 = fmaf(a[2], xv[2], y0);
-            y0 = fmaf(a[3], xv[3], y0);
-            y1 = fmaf(b[0], xv[0], y1);
-            y1 = fmaf(b[1], xv[1], y1);
-            y1 = fmaf(b[2], xv[2], y1);
-            y1 = fmaf(b[3], xv[3], y1);
-          }
-          const float* bnd = kv == 0 ? kb : vb;
-          dst[j] = (uint8_t)((code_of(y0, bnd) << 4) | code_of(y1, bnd));
-        }
+      for (int e = 0; e < EPL; ++e) s_x[lv][lane + 64 * e] = x[e] / den;
+      if (lane == 0) {
+        s_norm[lv] = norm;
+        s_row[lv] = dst;
       }
-      if (lane == 0) *reinterpret_cast<float*>(dst + H) = norm;
-      __builtin_amdgcn_wave_barrier();  // s_x is rewritten by the next vector
     }
+    __syncthreads();
+    // 2. y_i = R[i] . x_hat and its code, for this thread's vectors
+    {
+      const int i = tid % D;
+      const int vs = tid / D;
+      const float* rrow = p.rotation + (long long)i * D;
+      float y[VPT];
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) y[u] = 0.0f;
+#pragma unroll 1
+      for (int k0 = 0; k0 < D; k0 += 32) {
+        f32x4 a[8];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) a[w] = *reinterpret_cast<const f32x4*>(rrow + k0 + 4 * w);
+#pragma unroll
+        for (int w = 0; w < 8; ++w)
+#pragma unroll
+          for (int u = 0; u < VPT; ++u) {
+            const f32x4 xv = *reinterpret_cast<const f32x4*>(&s_x[vs + u * TPC][k0 + 4 * w]);
+            y[u] = fmaf(a[w][0], xv[0], y[u]);
+            y[u] = fmaf(a[w][1], xv[1], y[u]);
+            y[u] = fmaf(a[w][2], xv[2], y[u]);
+            y[u] = fmaf(a[w][3], xv[3], y[u]);
+          }
+      }
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        const int lv = vs + u * TPC;
+        // vectors alternate K, V: lv's kind is the parity of v0 + lv (v0 is even)
+        s_code[lv][i] = (uint8_t)code_of(y[u], (lv & 1) ? p.v_bounds : p.k_bounds);
+      }
+    }
+    __syncthreads();
+    // 3. packed bytes and norms
+    for (int e = tid; e < kAppendVecs * H; e += 256) {
+      const int lv = e / H, j = e % H;
+      const long long dst = s_row[lv];
+      if (dst >= 0) p.cache[dst + j] = (uint8_t)((s_code[lv][2 * j] << 4) | s_code[lv][2 * j + 1]);
+    }
+    if (tid < kAppendVecs && s_row[tid] >= 0) *reinterpret_cast<float*>(p.cache + s_row[tid] + H) = s_norm[tid];
+    __syncthreads();  // the LDS is rewritten by the next batch
   }
 }
 

@@ -446,7 +446,7 @@ typedef struct pdattn_tq4_plan_t {
   int32_t max_chunks;       /* work items per pair at most (longer pairs split their tiles over this many) */
   int64_t total_tiles;      /* Hkv * sum_b ceil(L_b / 16) over the host lengths */
   int64_t max_context_len;  /* largest host context length planned for */
-  uint64_t workspace_bytes; /* rotated queries, merged rotated outputs, the work items' records */
+  uint64_t workspace_bytes; /* rotated queries, then the work items' records */
   uint32_t magic;
   uint32_t reserved1;
 } pdattn_tq4_plan_t;
@@ -469,7 +469,7 @@ PDATTN_API pdattn_status pdattn_tq4_plan(const pdattn_problem* problem, const in
  * NULL). Empty sequences give out = 0, lse = -inf; a length beyond the
  * block table or a block-table entry outside [0, num_pages) gives NaN.
  * workspace: plan->workspace_bytes, 16-byte aligned; concurrent calls on one
- * workspace race. Four kernels on `stream`. */
+ * workspace race. Three kernels on `stream`. */
 PDATTN_API pdattn_status pdattn_tq4_decode(const pdattn_tq4_plan_t* plan, const void* q, const void* cache,
                                            const float* rotation, const float* k_centroids,
                                            const float* v_centroids, const int32_t* block_table,

@@ -738,14 +738,10 @@ pdattn_status check_tq4_problem(const pdattn_problem* p) {
 uint64_t tq4_qseq_bytes(const pdattn_problem& p) {
   return round_up((uint64_t)p.batch * p.num_q_heads * p.head_dim * 2, 256);
 }
-// workspace: rotated q (fp16), merged outputs (fp32, rotated space), records
-uint64_t tq4_oseq_bytes(const pdattn_problem& p) {
-  return round_up((uint64_t)p.batch * p.num_q_heads * p.head_dim * 4, 256);
-}
+// workspace: rotated q (fp16), then the work items' records
 uint64_t tq4_workspace(const pdattn_problem& p, int32_t max_chunks) {
-  return tq4_qseq_bytes(p) + tq4_oseq_bytes(p) +
-         (uint64_t)max_chunks * p.batch * p.num_kv_heads *
-             (uint64_t)pdattn::tq4_record_floats(heads_per_kv(p), p.head_dim) * 4;
+  return tq4_qseq_bytes(p) + (uint64_t)max_chunks * p.batch * p.num_kv_heads *
+                                 (uint64_t)pdattn::tq4_record_floats(heads_per_kv(p), p.head_dim) * 4;
 }
 
 pdattn_status check_tq4_plan(const pdattn_tq4_plan_t* plan) {
@@ -914,8 +910,7 @@ PDATTN_API pdattn_status pdattn_tq4_decode(const pdattn_tq4_plan_t* plan, const 
   p.v_cent = v_centroids;
   p.block_table = block_table;
   p.context_lens = context_lens;
-  p.o_seq = reinterpret_cast<float*>(static_cast<char*>(workspace) + tq4_qseq_bytes(pr));
-  p.rec = reinterpret_cast<float*>(static_cast<char*>(workspace) + tq4_qseq_bytes(pr) + tq4_oseq_bytes(pr));
+  p.rec = reinterpret_cast<float*>(static_cast<char*>(workspace) + tq4_qseq_bytes(pr));
   p.out = out;
   p.lse = lse;
   p.batch = pr.batch;

@@ -39,7 +39,7 @@ struct Tq4AppendParams {
   int32_t num_pages;
 };
 
-// Decode: q rotation, the chunk kernel, the merge, the back-rotation.
+// Decode: q rotation, the chunk kernel, the merge with the back-rotation.
 struct Tq4DecodeParams {
   const uint16_t* q;           // bf16 bits [B][Hq][D], model space
   uint16_t* q_seq;             // workspace: fp16 [B][Hq][D], rotated, sequential order
@@ -50,7 +50,6 @@ struct Tq4DecodeParams {
   const int32_t* block_table;
   const int32_t* context_lens;
   float* rec;                  // workspace: [max_chunks][B * Hkv][tq4_record_floats(G, D)]
-  float* o_seq;                // workspace: fp32 [B][Hq][D], merged outputs in the rotated space
   float* out;                  // [B][Hq][D]
   float* lse;                  // [B][Hq] or null
   int32_t batch;
@@ -70,7 +69,7 @@ struct Tq4DecodeParams {
 // 0 when it cannot be asked.
 int tq4_decode_wgs_per_cu(int head_dim);
 hipError_t launch_tq4_append(const Tq4AppendParams& p, int head_dim, uint32_t grid, hipStream_t stream);
-// The four decode launches on one stream.
+// The three decode launches on one stream.
 hipError_t launch_tq4_decode(const Tq4DecodeParams& p, int head_dim, uint32_t decode_grid, hipStream_t stream);
 
 }  // namespace pdattn

@@ -48,9 +48,9 @@
 //       A operands of two d blocks (the high nibble's element j, the low
 //       nibble's d/2 + j).
 //   Each work item leaves (m, l, acc) per head in the workspace.
-// tq4_merge_kernel: one wave per (sequence, q head): the log-sum-exp merge
-//   of the pair's work items (split_k_reduce.cu, Algorithm), in the rotated
-//   space; tq4_rotate_out_kernel: the outputs rotated back to model space.
+// tq4_merge_out_kernel: 8 (sequence, q head) rows per workgroup: one wave
+//   per row merges the pair's work items by log-sum-exp (split_k_reduce.cu,
+//   Algorithm) into LDS, then the rows are rotated back to model space.
 
 #include "tq4.h"
 
@@ -538,15 +538,12 @@ __device__ __forceinline__ int acc_index(int d) {
   return 16 * (2 * i + half) + 4 * (m / 4) + (m % 4);
 }
 
-// One wave per (sequence, q head): the log-sum-exp merge of its pair's work
-// items (split_k_reduce.cu, Algorithm), written in the rotated space to the
-// workspace (o_seq) with lse.
+// The log-sum-exp merge of one (sequence, q head) row's work items
+// (split_k_reduce.cu, Algorithm) by one wave, into `os` (D floats, the
+// rotated space), and its lse.
 template <int D>
-__global__ __launch_bounds__(256) void tq4_merge_kernel(const Tq4DecodeParams p) {
+__device__ __forceinline__ void merge_row(const Tq4DecodeParams& p, long long row, int lane, float* os) {
   constexpr int EPL = D / 64;
-  const int lane = threadIdx.x & 63;
-  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= (long long)p.batch * p.num_q_heads) return;
   const int G = p.heads_per_kv;
   const int b = (int)(row / p.num_q_heads);
   const int h = (int)(row % p.num_q_heads);
@@ -555,7 +552,6 @@ __global__ __launch_bounds__(256) void tq4_merge_kernel(const Tq4DecodeParams p)
   const long long pair = (long long)b * p.num_kv_heads + h / G;
   const long long cap = (long long)p.max_pages_per_seq << p.page_log2;
   const int L = p.context_lens[b];
-  float* os = p.o_seq + row * D;
   if (L <= 0 || (long long)L > cap) {
     const float v = L <= 0 ? 0.0f : __builtin_nanf("");
 #pragma unroll
@@ -613,22 +609,23 @@ __global__ __launch_bounds__(256) void tq4_merge_kernel(const Tq4DecodeParams p)
   if (p.lse != nullptr && lane == 0) p.lse[row] = (M + __builtin_log2f(lsum)) * kLn2;
 }
 
-// out[r][e] = sum_d R_seq[d][e] o_seq[r][d], kRotRows rows per workgroup:
-// the rows sit in LDS; thread t owns column e = t mod D of rows t / D,
-// t / D + 256 / D, ..., and reads R_seq[d][e] (row d of R_seq: coalesced
-// across the threads) once for them.
+// tq4_merge_out_kernel: 8 rows (sequence, q head) per workgroup of 8
+// waves: wave w merges row w into LDS; then thread t owns column e = t mod D
+// of rows t / D, t / D + 512 / D, ... and forms out[r][e] = sum_d
+// R_seq[d][e] o[r][d], reading R_seq row d coalesced across the threads, once
+// for its rows.
 template <int D>
-__global__ __launch_bounds__(256) void tq4_rotate_out_kernel(const Tq4DecodeParams p) {
+__global__ __launch_bounds__(512) void tq4_merge_out_kernel(const Tq4DecodeParams p) {
   constexpr int H = D / 2;
-  constexpr int TPC = 256 / D;
+  constexpr int TPC = 512 / D;
   constexpr int RPT = kRotRows / TPC;
   __shared__ __attribute__((aligned(16))) float s_o[kRotRows][D];
   const int tid = threadIdx.x;
   const long long rows = (long long)p.batch * p.num_q_heads;
   const long long r0 = (long long)blockIdx.x * kRotRows;
-  for (int e = tid; e < kRotRows * D; e += 256) {
-    const long long r = r0 + e / D;
-    s_o[e / D][e % D] = r < rows ? p.o_seq[r * D + e % D] : 0.0f;
+  {
+    const int w = tid >> 6;
+    if (r0 + w < rows) merge_row<D>(p, r0 + w, tid & 63, s_o[w]);
   }
   __syncthreads();
   const int e = tid % D;
@@ -669,10 +666,7 @@ hipError_t launch_all(const Tq4DecodeParams& p, uint32_t decode_grid, hipStream_
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(tq4_merge_kernel<D>, dim3((uint32_t)((rows + 3) / 4)), dim3(256), 0, stream, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(tq4_rotate_out_kernel<D>, dim3((uint32_t)((rows + kRotRows - 1) / kRotRows)), dim3(256), 0,
+  hipLaunchKernelGGL(tq4_merge_out_kernel<D>, dim3((uint32_t)((rows + kRotRows - 1) / kRotRows)), dim3(512), 0,
                      stream, p);
   return hipGetLastError();
 }

@@ -40,8 +40,7 @@ def test_tq4_plan_sizes_and_checks():
     G, D, pairs = 4, 128, 32
     rec = ((2 * G + 3) // 4 * 4 + G * D) * 4
     qseq = -(-(4 * 32 * D * 2) // 256) * 256
-    oseq = -(-(4 * 32 * D * 4) // 256) * 256
-    assert pl.workspace_bytes == qseq + oseq + pl.max_chunks * pairs * rec
+    assert pl.workspace_bytes == qseq + pl.max_chunks * pairs * rec
     forced = pk.tq4_plan(prob, lens, num_cus=256, chunk_tiles=3)
     assert forced.chunk_tiles == 3 and forced.max_chunks == 22
     with pytest.raises(pk.PdattnError):        # a length beyond the block table

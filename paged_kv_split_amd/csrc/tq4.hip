@@ -34,19 +34,20 @@
 //       shared memory); the table is held in 16 copies, entry v of copy c at
 //       word 16 v + c, lane l reading copy l mod 16;
 //     * S = K . Q^T on v_mfma_f32_16x16x32_f16 (K centroids and q in fp16,
-//       whose 2^-11 rounding keeps the scores close; the norm is applied
-//       in fp32): lane (token m, group r)
-//       builds its A operand from 4 code bytes per 32-wide k-block (each
-//       lookup fills two k slots); Q's B operand takes the same elements;
+//       whose 2^-11 rounding keeps the scores close; the norm is applied in
+//       fp32): lane (token m, group r) builds its A operand from 4 code
+//       bytes per 32-wide k-block (each lookup fills two k slots); Q's B
+//       operand takes the same elements;
 //     * the norms scale the scores (k) and the probabilities (v) instead of
 //       the elements (fused_tq_attention.cu, the decompress * norm step);
-//       online softmax in base 2 (flash_attention.cu, Online Softmax);
+//       online softmax in base 2 (flash_attention.cu, Online Softmax) with
+//       a lazily moved running max;
 //     * O^T += V^T . P on v_mfma_f32_16x16x16_bf16 (V centroids and the
-//       norm-weighted probabilities in bf16, for its range): the probabilities are
-//       already in B-operand order; lane (d row m, group r) looks up the code
-//       bytes m * d/32 .. of tokens 4 r .. 4 r + 3, and each lookup feeds the
-//       A operands of two d blocks (the high nibble's element j, the low
-//       nibble's d/2 + j).
+//       norm-weighted probabilities in bf16, for the norms' range): the
+//       probabilities are already in B-operand order; lane (d row m, group
+//       r) looks up the code bytes m * d/32 .. of tokens 4 r .. 4 r + 3,
+//       and each lookup feeds the A operands of two d blocks (the high
+//       nibble's element j, the low nibble's d/2 + j).
 //   Each work item leaves (m, l, acc) per head in the workspace.
 // tq4_merge_out_kernel: 8 (sequence, q head) rows per workgroup: one wave
 //   per row merges the pair's work items by log-sum-exp (split_k_reduce.cu,

@@ -10,10 +10,11 @@ Bars:
   (d + 8) 2^-23 bounds the fp32 error of the rotated value: a d-term dot
   product of a unit vector with a unit row, plus the normalisation);
   untouched rows keep their bytes.
-* decode: out within max-abs 4e-2 / mean-abs 2e-3 and lse within 4e-3 of
-  the fp64 oracle: the kernel rounds the rotated q, the centroids and the
-  probabilities to bf16 for the MFMAs (each within 2^-9 relative; the
-  scores' error grows with sqrt(d) terms of that size).
+* decode: out within max-abs 4e-2 / mean-abs 1e-3 and lse within 2e-3 of
+  the fp64 oracle: the kernel rounds the rotated q and the K centroids to
+  fp16 (2^-11 relative; the scores' error grows with sqrt(d) such terms)
+  and the V centroids and the probabilities to bf16 (2^-8 relative, as the
+  fp8 path's elements).
 """
 import math
 
@@ -131,10 +132,10 @@ def _compare(out, lse, ref_o, ref_l, tag):
     print(f"{tag}: max-abs {float(diff.max()):.2e} mean-abs {float(diff.mean()):.2e} "
           f"lse {float((lse.double()[fin] - ref_l[fin]).abs().max()) if bool(fin.any()) else 0:.2e}")
     assert bool(torch.isfinite(out).all())
-    assert float(diff.max()) <= 4e-2 and float(diff.mean()) <= 2e-3
+    assert float(diff.max()) <= 4e-2 and float(diff.mean()) <= 1e-3
     assert torch.equal(torch.isneginf(lse.double()), torch.isneginf(ref_l))
     if bool(fin.any()):
-        assert float((lse.double()[fin] - ref_l[fin]).abs().max()) <= 4e-3
+        assert float((lse.double()[fin] - ref_l[fin]).abs().max()) <= 2e-3
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}_G{c[1] // c[2]}_d{c[3]}_P{c[4]}_ct{c[6]}" for c in CASES])

@@ -204,3 +204,43 @@ def test_tq4_full_size_sampled_sequences():
     ref_o, ref_l = otq.decode(sub["q"], cache, sub["block_table"], sub["context_lens"], inp["rotation"], ck, cv)
     _compare(out[pick], lse[pick], ref_o, ref_l, "llama3_8b tq4 sampled")
     assert bool(torch.isfinite(out).all())
+
+
+def test_tq4_decode_captured_graph_replays_bitwise():
+    """pdattn_tq4_decode (q rotation, chunk kernel, merge with back-rotation)
+    captured in one HIP graph: every replay, with eager work between, equals
+    the eager call bit for bit."""
+    pk = _pk()
+    inp = synth.make_tq4_inputs(_workload(4, 32, 8, 128, 16, (5, 260, 700, 33), seed=8400))
+    ck, bk, cv, bv = _tables(128)
+    cache = _dev(_oracle_cache(inp, bk, bv))
+    q, bt, lens, rot = _dev(inp["q"]), _dev(inp["block_table"]), _dev(inp["context_lens"]), _dev(inp["rotation"])
+    ckd, cvd = _dev(ck), _dev(cv)
+    pl = pk.tq4_plan(pk.tq4_problem(q, cache, bt), inp["context_lens"], chunk_tiles=4)
+    ws = torch.empty(int(pl.workspace_bytes), dtype=torch.uint8, device=DEV)
+    out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=DEV)
+
+    def step():
+        pk.tq4_decode(pl, q, cache, rot, ckd, cvd, bt, lens, ws, out, lse)
+
+    step()
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(0.0)
+        ws.fill_(0xFF)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {r}"

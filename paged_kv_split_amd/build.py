@@ -11,10 +11,19 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libpdattn.so")
 SOURCES = [os.path.join(CSRC, "pdattn.hip"), os.path.join(CSRC, "decode_kernels.hip"),
+           os.path.join(CSRC, "decode_stream.hip"),
            os.path.join(CSRC, "decode_dynamic.hip"), os.path.join(CSRC, "stream_read.hip"),
            os.path.join(CSRC, "kv_append.hip"), os.path.join(CSRC, "merge.hip"),
            os.path.join(CSRC, "prefill.hip"), os.path.join(CSRC, "tq4.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# Per-source flags. The decode kernels keep their MFMA accumulators in VGPRs:
+# the tile loop rescales them on the VALU, and with AGPR accumulators the
+# compiler copies all of them between register files on every tile.
+SOURCE_FLAGS = {
+    "decode_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "decode_stream.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "decode_dynamic.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 FLAGS = [
     "--offload-arch=gfx950",
@@ -52,7 +61,9 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     objs = [os.path.join(objdir, os.path.basename(src) + ".o") for src in SOURCES]
     cflags = [f for f in FLAGS if f != "-shared"] + list(extra_flags)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        futs = [ex.submit(_run, [HIPCC] + cflags + ["-c", src, "-o", obj], verbose) for src, obj in zip(SOURCES, objs)]
+        futs = [ex.submit(_run, [HIPCC] + cflags + SOURCE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj],
+                          verbose)
+                for src, obj in zip(SOURCES, objs)]
         for f in futs:
             f.result()
     tmp = LIBRARY + ".tmp"

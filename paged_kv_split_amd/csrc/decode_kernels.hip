@@ -1,6 +1,8 @@
 // gfx950 kernels for paged split-KV GQA decode attention.
 //
-// decode_kernel: a persistent grid sized to the GPU's resident capacity. The
+// decode_kernel: the general decode kernel (every pool type and page size;
+// decode_stream.hip holds the default one for the common pools). A
+// persistent grid sized to the GPU's resident capacity. The
 // KV work of one step is the list of (sequence b, kv head) pairs, each cut
 // into 16-token tiles; the pairs are laid end to end (b major, kv head minor)
 // and every wave of the grid takes an equal contiguous range of that tile
@@ -35,13 +37,11 @@
 //     a fragment is the same for Q and K, so the contraction is exact.
 //   * softmax on the MFMA result layout (lane: one head, four tokens):
 //     tile max by a 4-way local max and two cross-row exchanges, exp2.
-//   * p . V on the VALU with fp32 accumulators: lane (row r, chunk c) owns
-//     d-chunk c for tokens r, r+4, r+8, r+12 of each tile; their
-//     probabilities for head g sit in lane g of the same 16-lane row and
-//     arrive with a DPP row broadcast.
+//   * p . V on the matrix cores (tile_ops.h: the weights as three bf16
+//     terms, fp32 accumulation).
 //
-// fp8 pools: e4m3fn bytes are widened in registers (hardware convert; exact
-// in bf16 for the K operand, fp32 for V); the per-(token, kv head) scales are
+// fp8 pools: e4m3fn bytes are widened in registers (hardware convert, exact
+// in bf16 for both operands); the per-(token, kv head) scales are
 // folded into the score (k) and the probability (v) instead of being
 // multiplied into the elements (OASR "Kernel Layer", FP8 KV variants: one
 // fp32 scale per token and kv head).
@@ -225,8 +225,19 @@ void decode_kernel(DecodeParams p) {
         };
         const int nk = (c1 - c0 + kTileTokens - 1) / kTileTokens;
         auto issue = [&](int k) {
-          TL::issue(ring + (k % S) * STAGE, p.k, p.v, p.k_scale, p.v_scale, row_of, c0 + k * kTileTokens, s1 - 1,
-                    lane, row, col);
+          const int tb = c0 + k * kTileTokens;
+          unsigned char* stg = ring + (k % S) * STAGE;
+          if constexpr (INL == 0) {
+            // pages of 16 tokens or more: a whole tile's rows share one page,
+            // so one scalar base addresses it
+            if (lp >= 4 && tb + kTileTokens <= s1) {
+              const long long row0 = (long long)uniform(pages[(tb >> lp) - pg0]) * page_rows +
+                                     (long long)((tb & (P - 1)) * p.slot_stride) + kvh_off;
+              TL::issue_rows(stg, p.k, p.v, p.k_scale, p.v_scale, row0, p.slot_stride, lane, row, col);
+              return;
+            }
+          }
+          TL::issue(stg, p.k, p.v, p.k_scale, p.v_scale, row_of, tb, s1 - 1, lane, row, col);
         };
 
 #pragma unroll

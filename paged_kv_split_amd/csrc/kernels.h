@@ -23,6 +23,11 @@ constexpr int kPagesPerWave = 256;
 constexpr int kMinTilesPerWorker = 4;
 // Words of one worker's merge descriptor.
 constexpr int kDescWords = 8;
+// Waves per workgroup of the streaming decode kernel.
+constexpr int kStreamWaves = 4;
+// Largest batch the streaming decode kernel takes (its workgroups hold the
+// tile prefix sums of all sequences in LDS).
+constexpr int kStreamMaxBatch = 512;
 // Tiles of one balancing unit of the dynamic kernel (a pair longer than this
 // is cut into several units, merged once more at the end).
 constexpr int kUnitTiles = 512;
@@ -137,6 +142,13 @@ constexpr int kKindBf16 = 0, kKindFp8 = 1, kKindFp8Inline = 2, kKindFp8InlineRow
 // Resident workgroups per compute unit of one decode instantiation, from the
 // runtime's occupancy query; 0 when it cannot be asked.
 int decode_wgs_per_cu(int head_dim, int group, int kind);
+
+// The streaming decode kernel (decode_stream.hip): bf16 pools or fp8 pools
+// with separate scale arrays, page_size >= 16, batch <= kStreamMaxBatch.
+int stream_wgs_per_cu(int head_dim, int group, bool fp8);
+bool stream_built(int head_dim, int group, bool fp8);  // instantiation within the LDS
+hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, int group, bool fp8, uint32_t grid,
+                                hipStream_t stream);
 
 // Returns hipErrorInvalidValue for an instantiation that is not built.
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, int kind, uint32_t grid,

@@ -118,6 +118,21 @@ int slot_stride_of(const pdattn_problem& p) { return p.kv_layout == PDATTN_LAYOU
 int head_stride_of(const pdattn_problem& p) { return p.kv_layout == PDATTN_LAYOUT_HND ? p.page_size : 1; }
 
 bool balanced(int32_t flags) { return (flags & PDATTN_PLAN_BALANCED) != 0; }
+
+// The streaming decode kernel serves bf16 pools and fp8 pools with separate
+// scale arrays whose pages hold whole 16-token tiles, at batches whose tile
+// prefix sums fit its workgroup's LDS, when every tile index it can meet
+// (any device lengths the block table admits) fits in 31 bits; the general
+// kernel (decode_kernels.hip) serves the rest.
+bool use_stream(const pdattn_problem& p) {
+  if (p.kv_dtype != PDATTN_KV_BF16 && p.kv_dtype != PDATTN_KV_FP8_E4M3) return false;
+  if (p.page_size < pdattn::kTileTokens || p.batch > pdattn::kStreamMaxBatch) return false;
+  const double cap_tiles = std::ceil((double)p.max_pages_per_seq * p.page_size / pdattn::kTileTokens);
+  if ((double)p.batch * cap_tiles * p.num_kv_heads >= 2147483648.0) return false;
+  // its output stores address the out array with 32-bit byte offsets
+  if ((double)p.batch * qlen_of(p) * p.num_q_heads * p.head_dim * 4.0 >= 2147483648.0) return false;
+  return pdattn::stream_built(p.head_dim, group_of(p), p.kv_dtype == PDATTN_KV_FP8_E4M3);
+}
 uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
 // Default-mode workspace: 2 partial records per worker, then
@@ -154,18 +169,33 @@ uint64_t workspace_for(const pdattn_problem& p, int64_t workers, int32_t flags) 
   return dyn_layout(p, workers).total;
 }
 
+// Waves per workgroup of the kernel a plan launches.
+int waves_of(const pdattn_problem& p, int32_t flags) {
+  return !balanced(flags) && use_stream(p) ? pdattn::kStreamWaves : pdattn::kWaves;
+}
+
+// Occupancy-cache kinds: the general kernel's kinds (kernels.h) and the
+// streaming kernel's two.
+constexpr int kKindStreamBf16 = 4, kKindStreamFp8 = 5, kKindSlots = 6;
+int engine_kind(const pdattn_problem& p) {
+  if (!use_stream(p)) return decode_kind(p);
+  return p.kv_dtype == PDATTN_KV_FP8_E4M3 ? kKindStreamFp8 : kKindStreamBf16;
+}
+
 // Resident workgroups per CU of one kernel instantiation on the current
 // device, from the runtime's occupancy query (cached: the query costs
 // milliseconds), 0 if it cannot be asked.
 int wgs_per_cu_cached(int device, int head_dim, int group, int kind, bool dyn) {
-  static std::atomic<int> cache[64][3][5][4][2];
+  static std::atomic<int> cache[64][3][5][kKindSlots][2];
   if (device < 0 || device >= 64) return 0;
   const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : group == 8 ? 3 : 4;
   std::atomic<int>& slot = cache[device][head_dim == 256 ? 2 : head_dim == 128 ? 1 : 0][gi][kind][dyn];
   int v = slot.load(std::memory_order_relaxed);
   if (v > 0) return v;
-  v = dyn ? pdattn::dynamic_wgs_per_cu(head_dim, group, kind != pdattn::kKindBf16)
-          : pdattn::decode_wgs_per_cu(head_dim, group, kind);
+  v = dyn                        ? pdattn::dynamic_wgs_per_cu(head_dim, group, kind != pdattn::kKindBf16)
+      : kind == kKindStreamBf16 ? pdattn::stream_wgs_per_cu(head_dim, group, false)
+      : kind == kKindStreamFp8  ? pdattn::stream_wgs_per_cu(head_dim, group, true)
+                                : pdattn::decode_wgs_per_cu(head_dim, group, kind);
   if (v > 0) slot.store(v, std::memory_order_relaxed);
   return v;
 }
@@ -176,7 +206,7 @@ pdattn_status check_plan(const pdattn_plan_t* plan) {
   pdattn_status st = check_problem(&plan->problem);
   if (st != PDATTN_OK) return fail(PDATTN_ERR_PLAN_MISMATCH, "plan holds an invalid problem: %s", g_last_error);
   if (plan->num_workers < 1 || plan->num_workgroups < 1 ||
-      (int64_t)plan->num_workgroups * pdattn::kWaves < plan->num_workers ||
+      (int64_t)plan->num_workgroups * waves_of(plan->problem, plan->flags) < plan->num_workers ||
       (plan->flags & ~PDATTN_PLAN_BALANCED) != 0 ||
       (balanced(plan->flags) &&
        (qlen_of(plan->problem) > 1 || plan->problem.head_dim == 256 || !pow2_heads(plan->problem))) ||
@@ -252,14 +282,14 @@ PDATTN_API pdattn_status pdattn_plan(const pdattn_problem* problem, const int32_
     if (e == hipSuccess) e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess || num_cus <= 0)
       return fail(PDATTN_ERR_DEVICE, "cannot query the compute-unit count: %s", hipGetErrorString(e));
-    per_cu = wgs_per_cu_cached(dev, problem->head_dim, group_of(*problem), dyn ? kind : decode_kind(*problem), dyn);
+    per_cu = wgs_per_cu_cached(dev, problem->head_dim, group_of(*problem), dyn ? kind : engine_kind(*problem), dyn);
   }
   if (per_cu <= 0) per_cu = pdattn::decode_wgs_per_cu_estimate(problem->head_dim, group_of(*problem), fp8, dyn);
 
   // Flash-decoding: as many worker waves as the device holds at once (the
   // grid is persistent: no workgroup waits for a free slot), each with at
   // least kMinTilesPerWorker tiles, so a small step is not spread thinner.
-  const int64_t capacity = (int64_t)num_cus * per_cu * pdattn::kWaves;
+  const int64_t capacity = (int64_t)num_cus * per_cu * waves_of(*problem, flags);
   int64_t workers;
   if (force_workers > 0) {
     workers = force_workers;
@@ -287,7 +317,7 @@ PDATTN_API pdattn_status pdattn_plan(const pdattn_problem* problem, const int32_
   if (!(plan.problem.scale > 0.0f)) plan.problem.scale = 1.0f / std::sqrt((float)problem->head_dim);
   plan.num_cus = num_cus;
   plan.num_workers = (int32_t)workers;
-  plan.num_workgroups = (int32_t)ceil_div(workers, pdattn::kWaves);
+  plan.num_workgroups = (int32_t)ceil_div(workers, waves_of(*problem, flags));
   plan.total_tiles = tiles;
   plan.max_context_len = max_len;
   plan.flags = flags;
@@ -385,8 +415,11 @@ PDATTN_API pdattn_status pdattn_decode(const pdattn_plan_t* plan, const void* q,
   p.head_stride = head_stride_of(pr);
   p.qk_scale_log2 = pr.scale * 1.44269504088896340736f;
 
-  hipError_t e = pdattn::launch_decode(p, pr.head_dim, group_of(pr), decode_kind(pr), (uint32_t)plan->num_workgroups,
-                                       static_cast<hipStream_t>(stream));
+  hipError_t e = use_stream(pr) ? pdattn::launch_decode_stream(p, pr.head_dim, group_of(pr), fp8,
+                                                                (uint32_t)plan->num_workgroups,
+                                                                static_cast<hipStream_t>(stream))
+                                : pdattn::launch_decode(p, pr.head_dim, group_of(pr), decode_kind(pr),
+                                                        (uint32_t)plan->num_workgroups, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "decode kernel launch: %s", hipGetErrorString(e));
   return PDATTN_OK;
 }

@@ -13,22 +13,22 @@
 //     base 2 with the scale pre-multiplied by log2(e) (same page, utils.cuh):
 //     lane (row r, column g) holds head g for tokens r, r+4, r+8, r+12; the
 //     tile max comes from a local max and two cross-row exchanges.
-//   * p . V, G <= 8: on the VALU with fp32 accumulators and fp32
-//     probabilities: lane (row r, chunk c) owns d-chunk c of tokens r + 4j;
-//     their probabilities for head g sit in lane g of the same 16-lane row
-//     and arrive by DPP row broadcast.
-//   * p . V, G = 16 (a 16-head group, or query rows x heads = 16): the
-//     probabilities of a tile form a full 16-column x 16-token operand, so
-//     the product runs on v_mfma_f32_16x16x16_bf16 (fp32 accumulation, the
-//     probabilities rounded to bf16: each weight within 2^-9 relative; the
-//     normaliser l and lse stay fp32). The operands need no data movement:
-//     the k index of the product is chosen as k = 4 r + j <-> token r + 4 j,
-//     which is where lane (r, c) already holds column c's probabilities
-//     (A operand) and its V chunk rows (B operand: MFMA number e takes
-//     element e of the lane's chunk, so its n = c stands for d = c VE + e).
-// fp8 pools: e4m3fn bytes widen exactly in registers (to bf16 for the MFMA
-// operand, to fp32 for V) and the per-(token, kv head) scales multiply the
-// score (k) and the probability (v) (OASR "Kernel Layer", FP8 KV variants).
+//   * p . V on the matrix cores (v_mfma_f32_16x16x32_bf16, fp32
+//     accumulation), for any group size: the G columns (padded to 16) x 16
+//     tokens x d product. Its operands need no data movement: the k index of
+//     the product is chosen so that k <-> token r + 4 j, which is where lane
+//     (r, c) already holds column c's weights (A operand) and its V chunk
+//     rows (B operand, V element e of the lane's chunk: n = c stands for
+//     d = c VE + e). Each weight enters as three bf16 terms (hi, mid, lo),
+//     so the product carries it to about 2^-24 relative, as fp32 does; the
+//     normaliser l and lse stay fp32. (On the VALU this product costs
+//     G x d/16 x 4 FMAs per lane per tile, which lengthened every tile
+//     step.)
+//   * the running maximum moves lazily (by more than kRescaleSlack, base
+//     2), so the accumulators are rescaled only when a score jumps.
+// fp8 pools: e4m3fn bytes widen exactly in registers (to bf16 for both MFMA
+// operands) and the per-(token, kv head) scales multiply the score (k) and
+// the weight (v) (OASR "Kernel Layer", FP8 KV variants).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -51,19 +51,15 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
 
+// Base-2 headroom of the lazily raised running maximum (weights < 2^8).
+constexpr float kRescaleSlack = 8.0f;
+
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (I < N) {
     f(std::integral_constant<int, I>{});
     static_for<I + 1, N>(f);
   }
-}
-
-// Value of lane SRC of the caller's 16-lane row (DPP row_newbcast).
-template <int SRC>
-__device__ __forceinline__ float row_bcast(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + SRC, 0xf, 0xf, false));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
@@ -111,6 +107,20 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
   asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n (clamped to 63: waiting for fewer
+// outstanding operations than allowed is always safe), by a binary dispatch
+// over the immediate forms.
+template <int LO = 0, int HI = 63>
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  if constexpr (LO == HI) {
+    wait_vmcnt<LO>();
+  } else {
+    constexpr int MID = (LO + HI + 1) / 2;
+    if (n >= MID) wait_vmcnt_le<MID, HI>(n);
+    else wait_vmcnt_le<LO, MID - 1>(n);
+  }
 }
 
 // Wait until at most `ahead` tiles of C loads each are still in flight (the
@@ -325,6 +335,56 @@ __device__ __forceinline__ void lds_b32_groups(uint32_t (&r)[sizeof...(I)], uint
   lds_b32<(int)(4 * ((FIRST + I) % W) + STRIDE * ((FIRST + I) / W))...>(r, a);
 }
 
+// 16-byte LDS reads at immediate offsets from one address, and the wait for
+// them, in one asm block (as read_stage).
+template <int... O>
+__device__ __forceinline__ void lds_b128(u32x4 (&r)[sizeof...(O)], uint32_t a) {
+  constexpr int o[] = {O...};
+  constexpr int N = sizeof...(O);
+  if constexpr (N == 2) {
+    asm volatile(
+        "ds_read_b128 %0, %2 offset:%3\n\t"
+        "ds_read_b128 %1, %2 offset:%4\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1])
+        : "v"(a), "i"(o[0]), "i"(o[1])
+        : "memory");
+  } else if constexpr (N == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:%5\n\t"
+        "ds_read_b128 %1, %4 offset:%6\n\t"
+        "ds_read_b128 %2, %4 offset:%7\n\t"
+        "ds_read_b128 %3, %4 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(a), "i"(o[0]), "i"(o[1]), "i"(o[2]), "i"(o[3])
+        : "memory");
+  } else {
+    static_assert(N == 8, "read count");
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:%9\n\t"
+        "ds_read_b128 %1, %8 offset:%10\n\t"
+        "ds_read_b128 %2, %8 offset:%11\n\t"
+        "ds_read_b128 %3, %8 offset:%12\n\t"
+        "ds_read_b128 %4, %8 offset:%13\n\t"
+        "ds_read_b128 %5, %8 offset:%14\n\t"
+        "ds_read_b128 %6, %8 offset:%15\n\t"
+        "ds_read_b128 %7, %8 offset:%16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(a), "i"(o[0]), "i"(o[1]), "i"(o[2]), "i"(o[3]), "i"(o[4]), "i"(o[5]), "i"(o[6]), "i"(o[7])
+        : "memory");
+  }
+}
+
+// One dword of LDS at a wave-uniform address, read in an asm block that also
+// waits for it, returned as a wave-uniform value.
+__device__ __forceinline__ int lds_uniform_i32(const void* p) {
+  int r;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(lds_addr(p)) : "memory");
+  return __builtin_amdgcn_readfirstlane(r);
+}
+
 // Token order inside a 16-token tile. MFMA A-row m carries token
 // tile_token(m) = m / 4 + 4 (m mod 4), so the result row 4 r + v held by
 // 16-lane row r is token r + 4 v: every 16-lane row owns the tokens
@@ -384,23 +444,21 @@ struct Tile {
   static constexpr int RF = (int)record_floats(D, G);
   static constexpr int EPL = G * D / 64;  // accumulator elements per lane in the merge layout
   using VVec = typename VChunk<VB>::type;
-  // p . V on the matrix cores at 16 columns (see the header): there the
-  // VALU form (G x d/16 x 4 FMAs per lane per tile) makes the step
-  // compute-bound; up to 8 columns it stays memory-bound and exact in fp32
-  static constexpr bool PV_MFMA = G == 16;
+  // buffer stores of one finished pair (out and lse) and of one record
+  // (acc, then m and l): a fixed count, whatever the lanes that write
+  static constexpr int N_OUT_STORES = VE + 1;
+  static constexpr int N_REC_STORES = VE + 2;
   static_assert(K_LD >= 1 && (D == 64 || D == 128 || D == 256), "head_dim");
   static_assert(G >= 1 && G <= 16, "group size");
   static_assert(EPL >= 1 && D % EPL == 0, "merge lane slice");
 
   // Online-softmax state of one piece: running max m (base 2) and sum l of
-  // head `col` (every row holds the same after reduce_rows), and acc[g][e]:
-  // head g, d = col * VE + e, summed over this row's tokens.
-  // MFMA p . V: cacc[e][v] is column 4 row + v at d = col * VE + e, summed
-  // over all tokens of the piece (acc is then unused, and the reverse).
+  // column `col` (every row holds the same after reduce_rows), and
+  // cacc[e][v]: column 4 row + v at d = col * VE + e, summed over all tokens
+  // of the piece by the matrix cores.
   struct State {
     float m, l;
-    float acc[PV_MFMA ? 1 : G][VE];
-    f32x4 cacc[PV_MFMA ? VE : 1];
+    f32x4 cacc[VE];
   };
   // One stage read back into registers.
   struct Frag {
@@ -412,44 +470,46 @@ struct Tile {
   __device__ static void reset(State& s) {
     s.m = -__builtin_inff();
     s.l = 0.0f;
-    if constexpr (PV_MFMA) {
 #pragma unroll
-      for (int e = 0; e < VE; ++e) s.cacc[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    } else {
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int e = 0; e < VE; ++e) s.acc[g][e] = 0.0f;
-    }
+    for (int e = 0; e < VE; ++e) s.cacc[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
   // Value of x in lane (row, 4 row + v): column 4 row + v's copy of a
   // per-column quantity (m, l, alpha: every row holds the same).
   __device__ static float col_of_row(float x, int row, int v) { return __shfl(x, 20 * row + v); }
 
-  // Element e of each of the lane's four V chunk rows as the MFMA B operand
-  // (bf16; fp8 codes widen exactly).
-  __device__ static bf16x4 v_operand(const Frag& f, int e) {
-    uint32_t lo, hi;
+  // The MFMA B operands of the lane's four V chunk rows (rows row + 4 j):
+  // operand e holds element e of each, as bf16 (fp8 codes widen exactly).
+  // Two source dwords are interleaved by one byte permute (v_perm_b32:
+  // selector bytes 0-3 pick bytes of the second source, 4-7 of the first).
+  __device__ static void v_operands(const Frag& f, bf16x4 (&b)[VE]) {
     if constexpr (FP8) {
-      const int sh = 8 * (e & 3);
-      const uint32_t b0 = (dword(f.vf[0], e >> 2) >> sh) & 0xffu;
-      const uint32_t b1 = (dword(f.vf[1], e >> 2) >> sh) & 0xffu;
-      const uint32_t b2 = (dword(f.vf[2], e >> 2) >> sh) & 0xffu;
-      const uint32_t b3 = (dword(f.vf[3], e >> 2) >> sh) & 0xffu;
-      const uint32_t w = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
-      lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
-      hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+      // elements e, e + 1 (e even) sit in bytes e & 3, (e & 3) + 1 of dword
+      // e / 4; one permute gathers them from two rows, then two converts
+      // widen the low and the high byte pairs
+#pragma unroll
+      for (int e = 0; e < VE; e += 2) {
+        const uint32_t x = e & 3;
+        const uint32_t sel = x | ((4 + x) << 8) | ((x + 1) << 16) | ((5 + x) << 24);
+        const uint32_t a01 = __builtin_amdgcn_perm(dword(f.vf[1], e >> 2), dword(f.vf[0], e >> 2), sel);
+        const uint32_t a23 = __builtin_amdgcn_perm(dword(f.vf[3], e >> 2), dword(f.vf[2], e >> 2), sel);
+        const uint32_t l0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(a01, 1.0f, false));
+        const uint32_t l1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(a23, 1.0f, false));
+        const uint32_t h0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(a01, 1.0f, true));
+        const uint32_t h1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(a23, 1.0f, true));
+        b[e] = __builtin_bit_cast(bf16x4, u32x2{l0, l1});
+        b[e + 1] = __builtin_bit_cast(bf16x4, u32x2{h0, h1});
+      }
     } else {
-      const int sh = 16 * (e & 1);
-      const uint32_t h0 = (dword(f.vf[0], e >> 1) >> sh) & 0xffffu;
-      const uint32_t h1 = (dword(f.vf[1], e >> 1) >> sh) & 0xffffu;
-      const uint32_t h2 = (dword(f.vf[2], e >> 1) >> sh) & 0xffffu;
-      const uint32_t h3 = (dword(f.vf[3], e >> 1) >> sh) & 0xffffu;
-      lo = h0 | (h1 << 16);
-      hi = h2 | (h3 << 16);
+      // element e is the low (e even) or high half of dword e / 2
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t lo = __builtin_amdgcn_perm(dword(f.vf[1], e >> 1), dword(f.vf[0], e >> 1), sel);
+        const uint32_t hi = __builtin_amdgcn_perm(dword(f.vf[3], e >> 1), dword(f.vf[2], e >> 1), sel);
+        b[e] = __builtin_bit_cast(bf16x4, u32x2{lo, hi});
+      }
     }
-    return __builtin_bit_cast(bf16x4, u32x2{lo, hi});
   }
 
   // head_dim position of element 0 of lane (row, ·)'s fragment at k-step kk;
@@ -557,6 +617,111 @@ struct Tile {
     }
   }
 
+  // Issue for a tile whose 16 rows lie in one page and all belong to the
+  // piece: row0 (wave-uniform) is the row index of its first token, and
+  // consecutive tokens are slot_stride rows apart. The same LDS image as
+  // issue(), from one scalar base plus per-lane offsets that do not change
+  // from tile to tile.
+  __device__ static void issue_rows(unsigned char* st, const uint8_t* k, const uint8_t* v, const float* k_scale,
+                                    const float* v_scale, long long row0, int slot_stride, int lane, int row,
+                                    int col) {
+    static_assert(INL == 0, "separate-scale or bf16 pools");
+    const uint32_t rs = (uint32_t)slot_stride * ROW_BYTES;  // bytes between consecutive tokens
+    const long long base = row0 * ROW_BYTES;
+    {
+      // K: lane (row, col) fetches bytes [jj * 64 + row * 16, +16) of token
+      // tile_token(col)
+      const uint8_t* kb = k + base;
+      const uint32_t ko = (uint32_t)tile_token(col) * rs + (uint32_t)row * 16u;
+#pragma unroll
+      for (int jj = 0; jj < K_LD; ++jj) dma16(kb + ko + jj * 64, st + jj * 1024);
+    }
+    {
+      // V: byte jj * 1024 + lane * 16 of the row-major tile
+      constexpr int TPJ = 1024 / ROW_BYTES;  // tokens per 1024 bytes
+      const uint8_t* vb = v + base;
+      const uint32_t lb = (uint32_t)lane * 16u;
+      const uint32_t vo = (lb / ROW_BYTES) * rs + lb % ROW_BYTES;
+#pragma unroll
+      for (int jj = 0; jj < V_LD; ++jj) dma16(vb + vo + (uint32_t)(jj * TPJ) * rs, st + K_TILE + jj * 1024);
+    }
+    if constexpr (FP8) {
+      // scale slot m < 16: k_scale of token tile_token(m); 16 + m: its v_scale
+      const int m = lane & 15;
+      const float* src = ((lane & 16) ? v_scale : k_scale) + row0 + (long long)tile_token(m) * slot_stride;
+      dma4(src, st + K_TILE + V_TILE);
+    }
+  }
+
+  // issue_rows for the pair's last tile when it is partial: tokens past
+  // `last` (0..15, the last valid token of the tile) are fetched as the
+  // last valid one (finite data, masked by the softmax), all inside the
+  // tile's page.
+  __device__ static void issue_rows_clamped(unsigned char* st, const uint8_t* k, const uint8_t* v, const float* k_scale,
+                                            const float* v_scale, long long row0, int slot_stride, int last, int lane,
+                                            int row, int col) {
+    static_assert(INL == 0, "separate-scale or bf16 pools");
+    const uint32_t rs = (uint32_t)slot_stride * ROW_BYTES;
+    const long long base = row0 * ROW_BYTES;
+    {
+      const uint8_t* kb = k + base;
+      const uint32_t ko = (uint32_t)min(tile_token(col), last) * rs + (uint32_t)row * 16u;
+#pragma unroll
+      for (int jj = 0; jj < K_LD; ++jj) dma16(kb + ko + jj * 64, st + jj * 1024);
+    }
+    {
+      constexpr int TPJ = 1024 / ROW_BYTES;
+      const uint8_t* vb = v + base;
+      const int lb = lane * 16;
+#pragma unroll
+      for (int jj = 0; jj < V_LD; ++jj) {
+        const uint32_t tok = (uint32_t)min(jj * TPJ + lb / ROW_BYTES, last);
+        dma16(vb + tok * rs + (uint32_t)(lb % ROW_BYTES), st + K_TILE + jj * 1024);
+      }
+    }
+    if constexpr (FP8) {
+      const int m = lane & 15;
+      const float* src =
+          ((lane & 16) ? v_scale : k_scale) + row0 + (long long)min(tile_token(m), last) * slot_stride;
+      dma4(src, st + K_TILE + V_TILE);
+    }
+  }
+
+  // A pair's query rows as direct-to-LDS loads into a slot of QSLOT bytes:
+  // column c's row lands at slot + c * D * 2 (padding columns fetch a valid
+  // row; q_read zeroes them). qrow_of(c) is column c's query row index.
+  static constexpr int Q_LPR = D * 2 / 16;                 // lanes per query row
+  static constexpr int Q_RPL = 64 / Q_LPR;                 // rows per load
+  static constexpr int CQ = (G + Q_RPL - 1) / Q_RPL;       // loads per pair
+  static constexpr int QSLOT = CQ * 1024;
+  template <typename QRowOf>
+  __device__ static void q_issue(unsigned char* slot, const uint16_t* q, QRowOf&& qrow_of, int ncols, int lane) {
+#pragma unroll
+    for (int i = 0; i < CQ; ++i) {
+      const int c = min(i * Q_RPL + lane / Q_LPR, ncols - 1);
+      dma16(reinterpret_cast<const unsigned char*>(q + qrow_of(c) * D) + (lane % Q_LPR) * 16, slot + i * 1024);
+    }
+  }
+  // Q as the MFMA B operand from a slot (as load_q).
+  __device__ static void q_read(bf16x8 (&qop)[KSTEPS], const unsigned char* slot, int row, int col, int ncols) {
+    // byte offset of dpos(kk, row): row * RS + QO(kk)
+    constexpr int RS = FP8 ? 32 : 16;
+    const uint32_t a = lds_addr(slot) + (uint32_t)(min(col, G - 1) * D * 2 + row * RS);
+    u32x4 r[KSTEPS];
+    if constexpr (FP8) {
+      if constexpr (KSTEPS == 2) lds_b128<0, 16>(r, a);
+      else if constexpr (KSTEPS == 4) lds_b128<0, 16, 128, 144>(r, a);
+      else lds_b128<0, 16, 128, 144, 256, 272, 384, 400>(r, a);
+    } else {
+      if constexpr (KSTEPS == 2) lds_b128<0, 64>(r, a);
+      else if constexpr (KSTEPS == 4) lds_b128<0, 64, 128, 192>(r, a);
+      else lds_b128<0, 64, 128, 192, 256, 320, 384, 448>(r, a);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+      qop[kk] = __builtin_bit_cast(bf16x8, col < ncols ? r[kk] : u32x4{0u, 0u, 0u, 0u});
+  }
+
   // `valid`: tokens of the tile that exist in the piece (INL 2 zeroes the V
   // values and v scales of the others; the other modes load clamped rows)
   __device__ static void read(Frag& f, const unsigned char* st, int lane, int row, int col,
@@ -634,7 +799,14 @@ struct Tile {
 
   // One tile of the online softmax: tokens tb .. tb+15 of the pair, those
   // at or past L masked (L may differ between columns: lane (row, col)
-  // passes its column's limit).
+  // passes its column's limit). FULL: every token of the tile is visible to
+  // every column (no masking).
+  //
+  // The running maximum moves lazily: it is raised (and the accumulators
+  // rescaled) only when a score exceeds it by more than kRescaleSlack (base
+  // 2), so weights stay below 2^kRescaleSlack; m, l and acc stay mutually
+  // consistent, which is all the final division and the merge need.
+  template <bool FULL = false>
   __device__ static void compute(State& s, const Frag& f, const bf16x8 (&qop)[KSTEPS], int tb, int L,
                                  float qk_scale_log2, int row) {
     // S[t][g]: lane (row, col) holds head col for tokens row + 4 v
@@ -655,132 +827,89 @@ struct Tile {
     for (int v = 0; v < 4; ++v) {
       float x = Sacc[v] * qk_scale_log2;
       if constexpr (FP8) x *= f.ks[v];
-      sc[v] = (tb + row + 4 * v < L) ? x : -__builtin_inff();
+      if constexpr (FULL) sc[v] = x;
+      else sc[v] = (tb + row + 4 * v < L) ? x : -__builtin_inff();
     }
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(s.m, mx);
-    // a column with no visible token yet keeps m = -inf; exponents are then
-    // taken against 0, so every weight is exactly 0 (never -inf - -inf)
-    const float m_ref = m_new == -__builtin_inff() ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(s.m - m_ref);
+    // a column that has seen no score keeps m = -inf (and never grows on an
+    // all-masked tile: -inf > -inf + slack is false)
+    const bool grow = mx > s.m + kRescaleSlack;
+    if (__any(grow)) {
+      const float m_new = grow ? mx : s.m;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(s.m - m_new) : 1.0f;  // exp2(-inf) = 0
+      s.l *= alpha;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float a = col_of_row(alpha, row, v);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) s.cacc[e][v] *= a;
+      }
+      s.m = m_new;
+    }
+    // exponents against m, or against 0 while m = -inf (every weight is then
+    // exactly 0: never -inf - -inf)
+    const float m_ref = s.m == -__builtin_inff() ? 0.0f : s.m;
     float pr[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) pr[v] = __builtin_amdgcn_exp2f(sc[v] - m_ref);
-    s.l = s.l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    const bool grew = m_new > s.m;
-    s.m = m_new;
-    if (__any(grew)) {
-      if constexpr (PV_MFMA) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float a = col_of_row(alpha, row, v);
-#pragma unroll
-          for (int e = 0; e < VE; ++e) s.cacc[e][v] *= a;
-        }
-      } else {
-        static_for<0, G>([&](auto gc) {
-          constexpr int g = decltype(gc)::value;
-          const float a = row_bcast<g>(alpha);
-#pragma unroll
-          for (int e = 0; e < VE; ++e) s.acc[g][e] *= a;
-        });
-      }
-    }
+    s.l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
     if constexpr (FP8) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) pr[v] *= f.vs[v];
     }
-    if constexpr (PV_MFMA) {
-      // A: column col's probabilities for tokens row + 4 j, k = 4 row + j
-      const bf16x4 pa = {(__bf16)pr[0], (__bf16)pr[1], (__bf16)pr[2], (__bf16)pr[3]};
+    // p . V on the matrix cores. Each weight enters as three bf16 terms
+    // (hi, mid, lo: about 2^-24 relative, as fp32). One 16x16x32 product per
+    // V element e takes hi and mid: k = 8 row + j carries hi of token
+    // row + 4 j and k = 8 row + 4 + j its mid, against the same V element
+    // twice (B: V element e of tokens row + 4 j, n = col <-> d = col * VE + e);
+    // a second one of the same shape takes lo (its other half zero).
+    bf16x4 vb[VE];
+    v_operands(f, vb);
+    const bf16x4 ph = {(__bf16)pr[0], (__bf16)pr[1], (__bf16)pr[2], (__bf16)pr[3]};
+    float r1[4];
 #pragma unroll
-      for (int e = 0; e < VE; ++e)
-        s.cacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, v_operand(f, e), s.cacc[e], 0, 0, 0);
-      return;
-    }
-    // p . V: lane (row, col) takes V row (token) row + 4 j, d-chunk col
+    for (int v = 0; v < 4; ++v) r1[v] = pr[v] - (float)ph[v];
+    const bf16x4 pm = {(__bf16)r1[0], (__bf16)r1[1], (__bf16)r1[2], (__bf16)r1[3]};
+    const bf16x4 pl = {(__bf16)(r1[0] - (float)pm[0]), (__bf16)(r1[1] - (float)pm[1]),
+                       (__bf16)(r1[2] - (float)pm[2]), (__bf16)(r1[3] - (float)pm[3])};
+    const bf16x4 z4 = {(__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f};
+    const bf16x8 a8 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(ph, pm, 0, 1, 2, 3, 4, 5, 6, 7));
+    const bf16x8 l8 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(pl, z4, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      float vf[VE];
-      if constexpr (FP8) {
-#pragma unroll
-        for (int w = 0; w < VB / 4; ++w) {
-          const uint32_t x = dword(f.vf[jj], w);
-          auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(x, false);
-          auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(x, true);
-          vf[4 * w + 0] = lo[0];
-          vf[4 * w + 1] = lo[1];
-          vf[4 * w + 2] = hi[0];
-          vf[4 * w + 3] = hi[1];
-        }
-      } else {
-#pragma unroll
-        for (int w = 0; w < VB / 4; ++w) {
-          const uint32_t x = dword(f.vf[jj], w);
-          vf[2 * w + 0] = bf16_lo(x);
-          vf[2 * w + 1] = bf16_hi(x);
-        }
-      }
-      const float pj = pr[jj];
-      static_for<0, G>([&](auto gc) {
-        constexpr int g = decltype(gc)::value;
-        const float pg = row_bcast<g>(pj);
-#pragma unroll
-        for (int e = 0; e < VE; ++e) s.acc[g][e] = fmaf(pg, vf[e], s.acc[g][e]);
-      });
+    for (int e = 0; e < VE; ++e) {
+      const bf16x8 b8 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vb[e], vb[e], 0, 1, 2, 3, 4, 5, 6, 7));
+      s.cacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, s.cacc[e], 0, 0, 0);
+      s.cacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(l8, b8, s.cacc[e], 0, 0, 0);
     }
   }
 
-  // Sum l and acc over the four rows (disjoint tokens); every row then holds
-  // the totals.
+  // Sum l over the four rows (disjoint tokens); every row then holds the
+  // total (the matrix cores already summed acc over the tile's tokens).
   __device__ static void reduce_rows(State& s) {
     s.l += __shfl_xor(s.l, 16);
     s.l += __shfl_xor(s.l, 32);
-    if constexpr (PV_MFMA) return;  // the MFMA already summed over the tile's tokens
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int e = 0; e < VE; ++e) {
-        float a = s.acc[g][e];
-        a += __shfl_xor(a, 16);
-        a += __shfl_xor(a, 32);
-        s.acc[g][e] = a;
-      }
   }
 
   // A whole pair after reduce_rows: out = acc / l, lse = ln 2 (m + log2 l);
   // a column that saw no token (l = 0) gets out = 0, lse = -inf (a NaN l
   // stays NaN). Column c < ncols has its output row at o + row_of(c) * D and
   // its lse at lo[row_of(c)] (lo may be null); padding columns are not
-  // written; row r writes the columns c with c mod 4 == r.
+  // written. Lane (row, col) holds columns 4 row + v at d = col * VE + e.
   template <typename RowOfCol>
   __device__ static void store_out(const State& s, float* o, float* lo, RowOfCol&& row_of, int ncols, bool poisoned,
                                    int row, int col) {
     const float nan = __builtin_nanf("");
-    if constexpr (PV_MFMA) {
-      // lane (row, col) holds columns 4 row + v at d = col * VE + e
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float lg = col_of_row(s.l, row, v);
-        const int c = 4 * row + v;
-        if (c < ncols) {
-          float* d = o + (long long)row_of(c) * D + col * VE;
+    for (int v = 0; v < 4; ++v) {
+      const float lg = col_of_row(s.l, row, v);
+      const int c = 4 * row + v;
+      if (c < ncols) {
+        float* d = o + (long long)row_of(c) * D + col * VE;
 #pragma unroll
-          for (int e = 0; e < VE; ++e) d[e] = poisoned ? nan : (lg != 0.0f ? s.cacc[e][v] / lg : 0.0f);
-        }
+        for (int e = 0; e < VE; ++e) d[e] = poisoned ? nan : (lg != 0.0f ? s.cacc[e][v] / lg : 0.0f);
       }
-    } else {
-      static_for<0, G>([&](auto gc) {
-        constexpr int g = decltype(gc)::value;
-        const float lg = row_bcast<g>(s.l);
-        if (row == (g & 3) && g < ncols) {
-          float* d = o + (long long)row_of(g) * D + col * VE;
-#pragma unroll
-          for (int e = 0; e < VE; ++e) d[e] = poisoned ? nan : (lg != 0.0f ? s.acc[g][e] / lg : 0.0f);
-        }
-      });
     }
     if (lo != nullptr && row == 0 && col < ncols)
       lo[row_of(col)] = poisoned ? nan : (s.l != 0.0f ? (s.m + log2f(s.l)) * kLn2 : -__builtin_inff());
@@ -793,40 +922,72 @@ struct Tile {
   template <bool COHERENT = false>
   __device__ static void store_record(const State& s, float* r, bool poisoned, int row, int col) {
     const float nan = __builtin_nanf("");
-    if constexpr (PV_MFMA) {
-      // every lane holds distinct values: columns 4 row + v, d = col * VE + e
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int c = 4 * row + v;
-        if (c < G) {
+    for (int v = 0; v < 4; ++v) {
+      const int c = 4 * row + v;
+      if (c < G) {
 #pragma unroll
-          for (int e = 0; e < VE; ++e) put<COHERENT>(r + 2 * G + c * D + col * VE + e, poisoned ? nan : s.cacc[e][v]);
-        }
+        for (int e = 0; e < VE; ++e) put<COHERENT>(r + 2 * G + c * D + col * VE + e, poisoned ? nan : s.cacc[e][v]);
       }
-    } else if constexpr (COHERENT) {
-      // every row holds the totals: row 0 writes all heads (lane-dependent
-      // head choices would move the accumulators to scratch memory here)
-      if (row == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int e = 0; e < VE; ++e) put<true>(r + 2 * G + g * D + col * VE + e, poisoned ? nan : s.acc[g][e]);
-      }
-    } else {
-      // row r writes the heads g with g mod 4 == r
-      static_for<0, G>([&](auto gc) {
-        constexpr int g = decltype(gc)::value;
-        if (row == (g & 3)) {
-          float* d = r + 2 * G + g * D + col * VE;
-#pragma unroll
-          for (int e = 0; e < VE; ++e) d[e] = poisoned ? nan : s.acc[g][e];
-        }
-      });
     }
     if (row == 0 && col < G) {
       put<COHERENT>(r + col, poisoned ? 0.0f : s.m);
       put<COHERENT>(r + G + col, poisoned ? nan : s.l);
     }
+  }
+
+  // The same two stores as buffer stores whose count does not depend on the
+  // data: exactly N_OUT_STORES (N_REC_STORES) instructions, every lane
+  // taking part; a lane with nothing to write addresses past the buffer's
+  // end, which the hardware drops. (The streaming kernel counts them in its
+  // vmcnt waits.) out_rs / lse_rs cover the output and lse arrays (lse_rs
+  // with no records when there is no lse), rec_rs the records; row_of(c) is
+  // column c's row index, rec_off the record's float offset.
+  template <typename RowOfCol>
+  __device__ static void store_out_counted(const State& s, __amdgpu_buffer_rsrc_t out_rs, __amdgpu_buffer_rsrc_t lse_rs,
+                                           RowOfCol&& row_of, int ncols, bool poisoned, int row, int col) {
+    const float nan = __builtin_nanf("");
+    constexpr uint32_t kDrop = 0x80000000u;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float lg = col_of_row(s.l, row, v);
+      const int c = 4 * row + v;
+      const uint32_t off = c < ncols ? (uint32_t)(row_of(c) * D + col * VE) * 4u : kDrop;
+#pragma unroll
+      for (int i = 0; i < VE / 4; ++i) {
+        f32x4 x;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[t] = poisoned ? nan : (lg != 0.0f ? s.cacc[4 * i + t][v] / lg : 0.0f);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), out_rs, off == kDrop ? kDrop : off + 16u * i,
+                                               0, 0);
+      }
+    }
+    const float ls = poisoned ? nan : (s.l != 0.0f ? (s.m + log2f(s.l)) * kLn2 : -__builtin_inff());
+    const uint32_t loff = row == 0 && col < ncols ? (uint32_t)row_of(col) * 4u : kDrop;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, ls), lse_rs, loff, 0, 0);
+  }
+  __device__ static void store_record_counted(const State& s, __amdgpu_buffer_rsrc_t rec_rs, uint32_t rec_off,
+                                              bool poisoned, int row, int col) {
+    const float nan = __builtin_nanf("");
+    constexpr uint32_t kDrop = 0x80000000u;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int c = 4 * row + v;
+      const uint32_t off = c < G ? (rec_off + 2 * G + c * D + col * VE) * 4u : kDrop;
+#pragma unroll
+      for (int i = 0; i < VE / 4; ++i) {
+        f32x4 x;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[t] = poisoned ? nan : s.cacc[4 * i + t][v];
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rec_rs, off == kDrop ? kDrop : off + 16u * i,
+                                               0, 0);
+      }
+    }
+    const bool w = row == 0 && col < G;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, poisoned ? 0.0f : s.m), rec_rs,
+                                          w ? (rec_off + col) * 4u : kDrop, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, poisoned ? nan : s.l), rec_rs,
+                                          w ? (rec_off + G + col) * 4u : kDrop, 0, 0);
   }
   template <bool COHERENT>
   __device__ static void put(float* a, float v) {

@@ -231,6 +231,29 @@ PDATTN_API pdattn_status pdattn_decode(const pdattn_plan_t* plan, const void* q,
 PDATTN_API pdattn_status pdattn_reduce(const pdattn_plan_t* plan, const void* workspace,
                                        uint64_t workspace_bytes, float* out, float* lse, void* stream);
 
+/* Bytes of device scratch behind pdattn_decode_noalloc, per device. */
+#define PDATTN_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * default-mode decode followed by its reduce, as pdattn_decode then
+ * pdattn_reduce, with the workspace taken from a static device array of
+ * PDATTN_NOALLOC_SCRATCH_BYTES bytes that the library holds on each device
+ * it runs on until the process ends (no workspace argument). Arguments as for
+ * pdattn_decode; writes every output. Allocates nothing: no hipMalloc, no
+ * hipFree. Errors: PDATTN_ERR_UNSUPPORTED for balanced plans,
+ * PDATTN_ERR_WORKSPACE when plan->workspace_bytes exceeds the scratch,
+ * PDATTN_ERR_DEVICE when the scratch's device address cannot be resolved.
+ * Every call on one device shares that device's scratch: calls that overlap
+ * on one device (on different streams, or from different threads) race and
+ * must be serialised by the caller.
+ */
+PDATTN_API pdattn_status pdattn_decode_noalloc(const pdattn_plan_t* plan, const void* q, const void* k_pages,
+                                               const void* v_pages, const float* k_scale, const float* v_scale,
+                                               const int32_t* block_table, const int32_t* context_lens, float* out,
+                                               float* lse, void* stream);
+
 /* Append flags. */
 #define PDATTN_APPEND_POW2_SCALES 1 /* fp8 pools: power-of-two scales */
 

@@ -12,7 +12,8 @@ import os
 
 import torch
 
-__all__ = ["Problem", "Plan", "PdattnError", "plan", "decode", "reduce", "workspace", "workspace_init",
+__all__ = ["Problem", "Plan", "PdattnError", "plan", "decode", "reduce", "decode_noalloc", "NOALLOC_SCRATCH_BYTES",
+           "workspace", "workspace_init",
            "paged_decode", "KV_BF16", "KV_FP8_E4M3", "PLAN_BALANCED", "library_path", "stream_read",
            "stream_read_sink", "kv_append", "APPEND_POW2_SCALES", "fp8_conversion_check", "merge", "LAYOUT_NHD", "LAYOUT_HND",
            "pool_dims", "kv_kind", "KV_FP8_E4M3_INLINE", "prefill_rows_per_tile", "prefill_tiles", "prefill", "paged_prefill", "TILES_LONGEST_FIRST"]
@@ -78,6 +79,8 @@ _lib.pdattn_decode.restype = ctypes.c_int
 _lib.pdattn_decode.argtypes = [ctypes.POINTER(Plan), _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint64, _P, _P, _P]
 _lib.pdattn_reduce.restype = ctypes.c_int
 _lib.pdattn_reduce.argtypes = [ctypes.POINTER(Plan), _P, ctypes.c_uint64, _P, _P, _P]
+_lib.pdattn_decode_noalloc.restype = ctypes.c_int
+_lib.pdattn_decode_noalloc.argtypes = [ctypes.POINTER(Plan), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.pdattn_status_string.restype = ctypes.c_char_p
 _lib.pdattn_status_string.argtypes = [ctypes.c_int]
 _lib.pdattn_last_error.restype = ctypes.c_char_p
@@ -175,6 +178,17 @@ def reduce(pl: Plan, workspace, out, lse=None, stream=None):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.pdattn_reduce(ctypes.byref(pl), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
                               _stream(stream)), "pdattn_reduce")
+
+
+def decode_noalloc(pl: Plan, q, k_pages, v_pages, k_scale, v_scale, block_table, context_lens, out, lse=None,
+                   stream=None):
+    """``pdattn_decode_noalloc``: decode and reduce on the library's static device scratch."""
+    _check(_lib.pdattn_decode_noalloc(ctypes.byref(pl), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
+                                      _ptr(v_scale), _ptr(block_table), _ptr(context_lens), _ptr(out), _ptr(lse),
+                                      _stream(stream)), "pdattn_decode_noalloc")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def workspace_init(pl: Plan, workspace, stream=None):

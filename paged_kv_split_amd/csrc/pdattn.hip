@@ -7,6 +7,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -18,6 +19,11 @@
 #include "merge.h"
 #include "prefill.h"
 #include "tq4.h"
+
+// The workspace of pdattn_decode_noalloc: one copy per device, held until the
+// process ends. Host code never takes this name as an address: the device
+// address comes from hipGetSymbolAddress (scratch_for_current_device).
+static __device__ __align__(256) unsigned char scratch[PDATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -215,6 +221,111 @@ pdattn_status check_plan(const pdattn_plan_t* plan) {
   return PDATTN_OK;
 }
 
+// Pointer, alignment and scale checks shared by the decode entry points.
+pdattn_status check_decode_args(const pdattn_plan_t* plan, const void* q, const void* k_pages, const void* v_pages,
+                                const float* k_scale, const float* v_scale, const int32_t* block_table,
+                                const int32_t* context_lens, const float* out, const float* lse) {
+  pdattn_status st = check_plan(plan);
+  if (st != PDATTN_OK) return st;
+  const pdattn_problem& pr = plan->problem;
+  if (pr.batch == 0) return PDATTN_OK;
+  if (!q || !k_pages || !v_pages || !block_table || !context_lens || !out)
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(out, 16))
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "q, k_pages, v_pages and out must be 16-byte aligned");
+  if (!aligned(block_table, 4) || !aligned(context_lens, 4) || (lse && !aligned(lse, 4)))
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "block_table, context_lens and lse must be 4-byte aligned");
+  return check_scales(pr, k_scale, v_scale);
+}
+
+// The default-mode decode launch on a checked workspace: records at its
+// start, then the descriptors.
+pdattn_status launch_static_decode(const pdattn_plan_t* plan, const void* q, const void* k_pages, const void* v_pages,
+                                   const float* k_scale, const float* v_scale, const int32_t* block_table,
+                                   const int32_t* context_lens, void* workspace, float* out, float* lse,
+                                   void* stream) {
+  const pdattn_problem& pr = plan->problem;
+  const bool fp8 = kind_of(pr) != pdattn::kKindBf16;
+  pdattn::DecodeParams p;
+  std::memset(&p, 0, sizeof p);
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint8_t*>(k_pages);
+  p.v = static_cast<const uint8_t*>(v_pages);
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.block_table = block_table;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.lse = lse;
+  p.rec = static_cast<float*>(workspace);
+  p.desc = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(workspace) + records_bytes(pr, plan->num_workers));
+  p.batch = pr.batch;
+  p.num_q_heads = pr.num_q_heads;
+  p.num_kv_heads = pr.num_kv_heads;
+  p.page_log2 = ilog2(pr.page_size);
+  p.max_pages_per_seq = pr.max_pages_per_seq;
+  p.num_pages = pr.num_pages;
+  p.num_workers = plan->num_workers;
+  p.q_len = qlen_of(pr);
+  p.heads_per_kv = heads_per_kv(pr);
+  p.num_cols = cols_of(pr);
+  p.slot_stride = slot_stride_of(pr);
+  p.head_stride = head_stride_of(pr);
+  p.qk_scale_log2 = pr.scale * 1.44269504088896340736f;
+
+  hipError_t e = use_stream(pr) ? pdattn::launch_decode_stream(p, pr.head_dim, group_of(pr), fp8,
+                                                                (uint32_t)plan->num_workgroups,
+                                                                static_cast<hipStream_t>(stream))
+                                : pdattn::launch_decode(p, pr.head_dim, group_of(pr), decode_kind(pr),
+                                                        (uint32_t)plan->num_workgroups, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "decode kernel launch: %s", hipGetErrorString(e));
+  return PDATTN_OK;
+}
+
+// The default-mode reduce launch on a checked workspace.
+pdattn_status launch_static_reduce(const pdattn_plan_t* plan, const void* workspace, float* out, float* lse,
+                                   void* stream) {
+  const pdattn_problem& pr = plan->problem;
+  pdattn::MergeParams p;
+  std::memset(&p, 0, sizeof p);
+  p.rec = static_cast<const float*>(workspace);
+  p.desc = reinterpret_cast<const int32_t*>(static_cast<const unsigned char*>(workspace) +
+                                            records_bytes(pr, plan->num_workers));
+  p.out = out;
+  p.lse = lse;
+  p.num_q_heads = pr.num_q_heads;
+  p.num_workers = plan->num_workers;
+  p.q_len = qlen_of(pr);
+  p.heads_per_kv = heads_per_kv(pr);
+  p.num_cols = cols_of(pr);
+  hipError_t e = pdattn::launch_merge(p, pr.head_dim, group_of(pr), (uint32_t)plan->num_workers,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "reduce kernel launch: %s", hipGetErrorString(e));
+  return PDATTN_OK;
+}
+
+// Device address of `scratch` on the current device, resolved once per device
+// (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+pdattn_status scratch_for_current_device(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PDATTN_ERR_DEVICE, "device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || addr == nullptr)
+      return fail(PDATTN_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = addr;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PDATTN_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -333,20 +444,11 @@ PDATTN_API pdattn_status pdattn_decode(const pdattn_plan_t* plan, const void* q,
                                        void* workspace, uint64_t workspace_bytes, float* out, float* lse,
                                        void* stream) {
   g_last_error[0] = '\0';
-  pdattn_status st = check_plan(plan);
+  pdattn_status st = check_decode_args(plan, q, k_pages, v_pages, k_scale, v_scale, block_table, context_lens, out, lse);
   if (st != PDATTN_OK) return st;
   const pdattn_problem& pr = plan->problem;
   if (pr.batch == 0) return PDATTN_OK;
-  if (!q || !k_pages || !v_pages || !block_table || !context_lens || !out)
-    return fail(PDATTN_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
-  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(out, 16))
-    return fail(PDATTN_ERR_INVALID_ARGUMENT, "q, k_pages, v_pages and out must be 16-byte aligned");
-  if (!aligned(block_table, 4) || !aligned(context_lens, 4) || (lse && !aligned(lse, 4)))
-    return fail(PDATTN_ERR_INVALID_ARGUMENT, "block_table, context_lens and lse must be 4-byte aligned");
-  st = check_scales(pr, k_scale, v_scale);
-  if (st != PDATTN_OK) return st;
-  const int kind = kind_of(pr);
-  const bool fp8 = kind != pdattn::kKindBf16;
+  const bool fp8 = kind_of(pr) != pdattn::kKindBf16;
   if (!workspace || workspace_bytes < plan->workspace_bytes)
     return fail(PDATTN_ERR_WORKSPACE, "workspace needs %llu bytes, got %llu at %p",
                 (unsigned long long)plan->workspace_bytes, (unsigned long long)workspace_bytes, workspace);
@@ -388,40 +490,8 @@ PDATTN_API pdattn_status pdattn_decode(const pdattn_plan_t* plan, const void* q,
     return PDATTN_OK;
   }
 
-  pdattn::DecodeParams p;
-  std::memset(&p, 0, sizeof p);
-  p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint8_t*>(k_pages);
-  p.v = static_cast<const uint8_t*>(v_pages);
-  p.k_scale = k_scale;
-  p.v_scale = v_scale;
-  p.block_table = block_table;
-  p.context_lens = context_lens;
-  p.out = out;
-  p.lse = lse;
-  p.rec = static_cast<float*>(workspace);
-  p.desc = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(workspace) + records_bytes(pr, plan->num_workers));
-  p.batch = pr.batch;
-  p.num_q_heads = pr.num_q_heads;
-  p.num_kv_heads = pr.num_kv_heads;
-  p.page_log2 = ilog2(pr.page_size);
-  p.max_pages_per_seq = pr.max_pages_per_seq;
-  p.num_pages = pr.num_pages;
-  p.num_workers = plan->num_workers;
-  p.q_len = qlen_of(pr);
-  p.heads_per_kv = heads_per_kv(pr);
-  p.num_cols = cols_of(pr);
-  p.slot_stride = slot_stride_of(pr);
-  p.head_stride = head_stride_of(pr);
-  p.qk_scale_log2 = pr.scale * 1.44269504088896340736f;
-
-  hipError_t e = use_stream(pr) ? pdattn::launch_decode_stream(p, pr.head_dim, group_of(pr), fp8,
-                                                                (uint32_t)plan->num_workgroups,
-                                                                static_cast<hipStream_t>(stream))
-                                : pdattn::launch_decode(p, pr.head_dim, group_of(pr), decode_kind(pr),
-                                                        (uint32_t)plan->num_workgroups, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "decode kernel launch: %s", hipGetErrorString(e));
-  return PDATTN_OK;
+  return launch_static_decode(plan, q, k_pages, v_pages, k_scale, v_scale, block_table, context_lens, workspace, out,
+                              lse, stream);
 }
 
 PDATTN_API pdattn_status pdattn_reduce(const pdattn_plan_t* plan, const void* workspace,
@@ -438,23 +508,32 @@ PDATTN_API pdattn_status pdattn_reduce(const pdattn_plan_t* plan, const void* wo
     return fail(PDATTN_ERR_WORKSPACE, "workspace needs %llu bytes", (unsigned long long)plan->workspace_bytes);
   if (!aligned(workspace, 16)) return fail(PDATTN_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
   if (balanced(plan->flags)) return PDATTN_OK;  // merged inside pdattn_decode
+  return launch_static_reduce(plan, workspace, out, lse, stream);
+}
 
-  pdattn::MergeParams p;
-  std::memset(&p, 0, sizeof p);
-  p.rec = static_cast<const float*>(workspace);
-  p.desc = reinterpret_cast<const int32_t*>(static_cast<const unsigned char*>(workspace) +
-                                            records_bytes(pr, plan->num_workers));
-  p.out = out;
-  p.lse = lse;
-  p.num_q_heads = pr.num_q_heads;
-  p.num_workers = plan->num_workers;
-  p.q_len = qlen_of(pr);
-  p.heads_per_kv = heads_per_kv(pr);
-  p.num_cols = cols_of(pr);
-  hipError_t e = pdattn::launch_merge(p, pr.head_dim, group_of(pr), (uint32_t)plan->num_workers,
-                                      static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "reduce kernel launch: %s", hipGetErrorString(e));
-  return PDATTN_OK;
+PDATTN_API pdattn_status pdattn_decode_noalloc(const pdattn_plan_t* plan, const void* q, const void* k_pages,
+                                               const void* v_pages, const float* k_scale, const float* v_scale,
+                                               const int32_t* block_table, const int32_t* context_lens, float* out,
+                                               float* lse, void* stream) {
+  g_last_error[0] = '\0';
+  pdattn_status st = check_decode_args(plan, q, k_pages, v_pages, k_scale, v_scale, block_table, context_lens, out, lse);
+  if (st != PDATTN_OK) return st;
+  if (plan->problem.batch == 0) return PDATTN_OK;
+  if (balanced(plan->flags))
+    return fail(PDATTN_ERR_UNSUPPORTED, "pdattn_decode_noalloc takes default-mode plans (balanced plans need a "
+                                        "prepared workspace)");
+  if (plan->workspace_bytes > PDATTN_NOALLOC_SCRATCH_BYTES)
+    return fail(PDATTN_ERR_WORKSPACE, "plan needs %llu bytes of scratch; the static scratch holds %llu",
+                (unsigned long long)plan->workspace_bytes, (unsigned long long)PDATTN_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != PDATTN_OK) return st;
+  // every descriptor and every record the reduce reads is written by this
+  // decode, so the scratch needs no clearing between calls
+  st = launch_static_decode(plan, q, k_pages, v_pages, k_scale, v_scale, block_table, context_lens, ws, out, lse,
+                            stream);
+  if (st != PDATTN_OK) return st;
+  return launch_static_reduce(plan, ws, out, lse, stream);
 }
 
 PDATTN_API pdattn_status pdattn_workspace_init(const pdattn_plan_t* plan, void* workspace, uint64_t workspace_bytes,

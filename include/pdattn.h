@@ -162,7 +162,7 @@ typedef struct pdattn_plan_t {
   int32_t flags;            /* PDATTN_PLAN_* flags the plan was made with */
   int64_t total_tiles;      /* Hkv * sum_b ceil(L_b / 16) over the host lengths */
   int64_t max_context_len;  /* largest host context length planned for */
-  uint64_t workspace_bytes; /* partial records, merge descriptors or counters */
+  uint64_t workspace_bytes; /* partial records and the tile prefix, or counters */
   uint32_t magic;           /* set by pdattn_plan; checked by decode / reduce */
   uint32_t reserved1;
 } pdattn_plan_t;
@@ -209,7 +209,7 @@ PDATTN_API pdattn_status pdattn_workspace_init(const pdattn_plan_t* plan, void* 
  * plan->workspace_bytes bytes, prepared by pdattn_workspace_init for
  * balanced plans (default-mode plans need no preparation). Default mode:
  * writes `out` (and `lse`) for every (b, kvh) pair that one worker covers
- * and for empty or invalid sequences, and leaves partials and descriptors
+ * and for empty or invalid sequences, and leaves partials and the tile prefix
  * in the workspace for the cut pairs, which pdattn_reduce completes.
  * Balanced mode: writes every output.
  */

@@ -21,8 +21,8 @@
 // in base 2 with the scale pre-multiplied by log2(e) (same page, utils.cuh,
 // the exp2/log2(e) trick). A pair the wave covers whole is finished and
 // written to out; a pair cut by a wave boundary leaves an (m, l, acc) record
-// per piece, and the wave holding the pair's last tile leaves a descriptor
-// that the merge kernel follows.
+// per piece, and workgroup 0 leaves the tile prefix of the sequences, from
+// which the merge kernel finds every cut pair's pieces.
 //
 // Per tile and wave:
 //   * page gather (page = block_table[pos >> log2 P], slot = pos & (P - 1);
@@ -46,10 +46,12 @@
 // multiplied into the elements (OASR "Kernel Layer", FP8 KV variants: one
 // fp32 scale per token and kv head).
 //
-// merge_kernel: one wave per descriptor: M = max m_s, out = sum 2^(m_s - M)
+// merge_kernel: per cut pair, M = max m_s, out = sum 2^(m_s - M)
 // acc_s / sum 2^(m_s - M) l_s, lse = ln 2 (M + log2 sum 2^(m_s - M) l_s)
 // (FlashQuant wiki, split_k_reduce.cu, Algorithm and Numerical Stability,
 // on un-normalised accumulators).
+
+#include <algorithm>
 
 #include "tile_ops.h"
 
@@ -117,6 +119,15 @@ void decode_kernel(DecodeParams p) {
   }
   const long long T = total * Hkv;             // tiles of all (b, kv head) pairs
   const long long pre = before + incl - mine;  // tiles per kv head before b_lo
+  if (blockIdx.x == 0) {
+    // the prefix for the split reduce
+    long long run = pre;
+    for (int b = b_lo; b < b_hi; ++b) {
+      p.pre[b] = run;
+      run += tiles_of(p.context_lens[b]);
+    }
+    if (tid == 0) p.pre[B] = total;
+  }
 
   // ---- 2. place the waves of this workgroup; empty or over-long sequences
   // get their outputs here (out = 0, lse = -inf; NaN when the length does
@@ -160,8 +171,6 @@ void decode_kernel(DecodeParams p) {
   if (gw >= NW) return;
   long long t0, t1;
   worker_range(gw, NW, T, t0, t1);
-  int dsc[kDescWords] = {0, 0, 0, 0, 0, 0, 0, 0};
-
   unsigned char* ring = &s_ring[wave][0];
   int* pages = &s_pages[wave][0];
   if (t0 >= t1) {
@@ -266,22 +275,6 @@ void decode_kernel(DecodeParams p) {
         // a piece of a cut pair: record (m, l, acc); slot 0 for the wave's
         // first piece, 1 for its last
         TL::store_record(st, p.rec + (gw * 2 + (first ? 0 : 1)) * RF, poisoned, row, col);
-        if (cut_start && reaches_end) {
-          // this wave holds the pair's last tile (only possible for its first
-          // piece): describe the pieces for the merge
-          const long long pair_start = t0 - j;
-          // first worker whose range reaches pair_start
-          const long long wf = ((pair_start + 1) * NW + T - 1) / T - 1;
-          long long wf0, wf1;
-          worker_range(wf, NW, T, wf0, wf1);
-          dsc[0] = 1;
-          dsc[1] = b;
-          dsc[2] = kvh;
-          dsc[3] = (int)wf;
-          dsc[4] = wf0 == pair_start ? 0 : 1;
-          dsc[5] = (int)(T & 0xffffffffll);
-          dsc[6] = (int)(T >> 32);
-        }
       }
 
       remaining -= seg;
@@ -297,118 +290,217 @@ void decode_kernel(DecodeParams p) {
       }
     }
   }
-  // lane i writes word i (selected, not indexed: an indexed register array
-  // would live in scratch memory)
-  int dword_i = 0;
-#pragma unroll
-  for (int i = 0; i < kDescWords; ++i) dword_i = lane == i ? dsc[i] : dword_i;
-  if (lane < kDescWords) p.desc[gw * kDescWords + lane] = dword_i;
 }
 
-// Waves of a merge workgroup, and the pieces one merge wave loads per step.
-constexpr int kMergeWaves = kWaves;
-constexpr int kMergeUnroll = 4;
-
-// One workgroup per worker descriptor; only the descriptors of cut pairs
-// are valid. Every worker wf .. w holds a record for the pair (a worker
-// with an empty tile range holds the empty record m = -inf, l = acc = 0).
-// One pass: each of the kMergeWaves waves merges every kMergeWaves-th piece
-// with the online rule (a
-// running maximum M, l and acc rescaled by 2^(M_old - M_new)), loading
-// kMergeUnroll pieces per step so their loads overlap; each lane keeps its
-// own slice of one head's accumulator. The four waves' (M, l, acc) meet in LDS and are
-// merged by the same rule.
+// Pieces one merge wave loads per step: fewer when a lane's slice is long
+// (loads beyond a pair's pieces are wasted, so this stays small).
 template <int D, int G>
-__global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(MergeParams p) {
-  constexpr int RF = (int)record_floats(D, G);
-  constexpr int NT = kMergeWaves * 64;
-  constexpr int EPL = G * D / 64;      // accumulator elements per lane
-  constexpr int LPH = D / EPL;         // lanes per head
-  static_assert(EPL >= 1 && D % EPL == 0, "lane slice");
-  __shared__ float s_m[kMergeWaves][G];
-  __shared__ float s_l[kMergeWaves][G];
-  __shared__ __attribute__((aligned(16))) float s_acc[kMergeWaves][G * D];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const long long w = blockIdx.x;
-  if (w >= p.num_workers) return;
-  const int* dsc = p.desc + w * kDescWords;
-  if (dsc[0] != 1) return;
-  const int b = dsc[1];
-  const int kvh = dsc[2];
-  const long long wf = dsc[3];
-  const int slot_first = dsc[4];
-  const long long n = w - wf + 1;  // pieces: workers wf .. w
-  auto piece = [&](long long i) -> const float* {
-    return p.rec + ((wf + i) * 2 + (i == 0 ? slot_first : 0)) * RF;
-  };
+constexpr int merge_unroll() {
+  return G * D / 64 >= 64 ? 1 : (G * D / 64 >= 16 ? 2 : 4);
+}
+// A merge workgroup of W waves meets in LDS: W * G * D floats, held to 64 KB.
+template <int D, int G, int W>
+constexpr bool merge_fits() {
+  return W * G * D * 4 <= 65536;
+}
+// Workgroup size (waves) of the one-pair-per-wave merge.
+constexpr int kMergePairWaves = 4;
 
-  const int g = lane / LPH;   // this lane's head
-  const int e0 = lane * EPL;  // first element of its slice (g * D + ...)
-  float M = -__builtin_inff(), L = 0.0f, A[EPL];
-#pragma unroll
-  for (int k = 0; k < EPL; ++k) A[k] = 0.0f;
-  // fold one piece (m, l, acc slice) into the running state
-  auto fold = [&](float mi, float li, const float (&ai)[EPL]) {
-    const float Mn = fmaxf(M, mi);
-    // equal maxima (including both -inf: an empty record) scale by 1
-    const float so = M == Mn ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
-    const float si = mi == Mn ? 1.0f : __builtin_amdgcn_exp2f(mi - Mn);
-    L = L * so + li * si;
-#pragma unroll
-    for (int k = 0; k < EPL; ++k) A[k] = A[k] * so + ai[k] * si;
-    M = Mn;
-  };
-  // pieces in flight per step: fewer when a lane's slice is long
-  constexpr int U = EPL >= 64 ? 1 : (EPL >= 16 ? 2 : kMergeUnroll);
-  for (long long i = wave; i < n; i += U * kMergeWaves) {
-    // U pieces per step (every fourth piece from i), all loads issued first
+// floor(x / d) for 0 <= x, 0 < d: below 2^53 the fp64 quotient, corrected by
+// one step (its error is below one); the integer division beyond
+__device__ __forceinline__ long long floor_div(long long x, long long d) {
+  if (x >= (1ll << 53)) return x / d;
+  long long q = (long long)((double)x / (double)d);
+  if (q * d > x) --q;
+  else if ((q + 1) * d <= x) ++q;
+  return q;
+}
+
+// The split reduce over the (sequence b, kv head) pairs. A pair's tiles
+// [ps, ps + nt) sit in the tile list at ps = Hkv * pre[b] + kvh * nt (nt =
+// pre[b + 1] - pre[b]); with the decode's equal ranges (worker w holds
+// [floor(w T / NW), floor((w + 1) T / NW))), the workers holding its first
+// and last tiles are wf = ceil((ps + 1) NW / T) - 1 and wl = ceil((ps + nt)
+// NW / T) - 1. A pair with wf == wl was finished by the decode. Otherwise
+// workers wf .. wl each left one record of it: wf in slot 0 when its range
+// starts at ps, else in slot 1 (its last piece); every later worker in slot
+// 0 (its first piece; a worker with an empty range holds the empty record
+// m = -inf, l = acc = 0).
+struct CutPair {
+  long long wf;  // first worker
+  long long n;   // pieces (workers wf .. wf + n - 1); 0: nothing to merge
+  int slot_first;
+  int b, kvh;
+};
+
+__device__ __forceinline__ CutPair cut_pair(const MergeParams& p, int pair) {
+  CutPair c;
+  const int Hkv = p.num_kv_heads;
+  c.b = pair / Hkv;
+  c.kvh = pair - c.b * Hkv;
+  c.wf = 0;
+  c.n = 0;
+  c.slot_first = 0;
+  const long long NW = p.num_workers;
+  const long long T = p.pre[p.batch] * Hkv;
+  const long long pb = p.pre[c.b];
+  const long long nt = p.pre[c.b + 1] - pb;
+  if (nt <= 0) return c;  // empty or invalid: written by the decode
+  const long long ps = Hkv * pb + c.kvh * nt;
+  const long long wf = floor_div((ps + 1) * NW + T - 1, T) - 1;
+  const long long wl = floor_div((ps + nt) * NW + T - 1, T) - 1;
+  if (wf == wl) return c;  // one worker finished it
+  c.wf = wf;
+  c.n = wl - wf + 1;
+  c.slot_first = floor_div(wf * T, NW) == ps ? 0 : 1;
+  return c;
+}
+
+// Pieces i0, i0 + S, i0 + 2 S, ... of a cut pair folded into one lane's
+// running (M, L, A slice) with the online rule (a running maximum M, l and
+// acc rescaled by 2^(M_old - M_new)); U pieces per step, their loads issued
+// first so they overlap. Lane: head lane / (D / EPL), elements lane * EPL ..
+template <int D, int G>
+__device__ __forceinline__ void fold_pieces(const MergeParams& p, const CutPair& c, long long i0, long long S,
+                                            int lane, float& M, float& L, float (&A)[G * D / 64]) {
+  constexpr int RF = (int)record_floats(D, G);
+  constexpr int EPL = G * D / 64;
+  constexpr int LPH = D / EPL;
+  constexpr int U = merge_unroll<D, G>();
+  static_assert(EPL >= 1 && D % EPL == 0, "lane slice");
+  const int g = lane / LPH;
+  const int e0 = lane * EPL;
+  for (long long i = i0; i < c.n; i += (long long)U * S) {
     float mu[U], lu[U], au[U][EPL];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const long long iu = i + (long long)u * kMergeWaves;
-      const float* r = piece(iu < n ? iu : i);
+      const long long iu0 = i + (long long)u * S;
+      const long long iu = iu0 < c.n ? iu0 : i;
+      const float* r = p.rec + ((c.wf + iu) * 2 + (iu == 0 ? c.slot_first : 0)) * RF;
       mu[u] = r[g];
       lu[u] = r[G + g];
 #pragma unroll
       for (int k = 0; k < EPL; ++k) au[u][k] = r[2 * G + e0 + k];
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (i + (long long)u * kMergeWaves < n) fold(mu[u], lu[u], au[u]);
-  }
+    for (int u = 0; u < U; ++u) {
+      if (i + (long long)u * S < c.n) {
+        const float Mn = fmaxf(M, mu[u]);
+        // equal maxima (including both -inf: an empty record) scale by 1
+        const float so = M == Mn ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
+        const float si = mu[u] == Mn ? 1.0f : __builtin_amdgcn_exp2f(mu[u] - Mn);
+        L = L * so + lu[u] * si;
 #pragma unroll
-  for (int k = 0; k < EPL; ++k) s_acc[wave][e0 + k] = A[k];
-  if (lane % LPH == 0) {
-    s_m[wave][g] = M;
-    s_l[wave][g] = L;
-  }
-  __syncthreads();
-  for (int e = tid; e < G * D; e += NT) {
-    const int gg = e / D;
-    float Mx = s_m[0][gg];
-#pragma unroll
-    for (int q = 1; q < kMergeWaves; ++q) Mx = fmaxf(Mx, s_m[q][gg]);
-    float Av = 0.0f, Ls = 0.0f;
-#pragma unroll
-    for (int q = 0; q < kMergeWaves; ++q) {
-      const float mq = s_m[q][gg];
-      // a wave without pieces holds M = -inf, l = acc = 0: weight 0
-      const float wq = mq == Mx ? 1.0f : __builtin_amdgcn_exp2f(mq - Mx);
-      Av += wq * s_acc[q][e];
-      Ls += wq * s_l[q][gg];
+        for (int k = 0; k < EPL; ++k) A[k] = A[k] * so + au[u][k] * si;
+        M = Mn;
+      }
     }
-    // column gg < num_cols: query row gg / Gh of head kvh * Gh + gg % Gh
-    // (padding columns are not written); a column that saw no token
-    // (Ls = 0) gets 0 and -inf
-    if (gg >= p.num_cols) continue;
-    const int Gh = p.heads_per_kv;
-    const long long bh = (long long)b * p.q_len * p.num_q_heads + (long long)kvh * Gh +
-                         (long long)(gg / Gh) * p.num_q_heads + gg % Gh;
-    // (a NaN sum, from a poisoned piece, stays NaN)
-    p.out[bh * D + (e % D)] = Ls != 0.0f ? Av / Ls : 0.0f;
-    if (e % D == 0 && p.lse != nullptr) p.lse[bh] = Ls != 0.0f ? (Mx + log2f(Ls)) * kLn2 : -__builtin_inff();
+  }
+}
+
+// Output row of column c < num_cols of pair (b, kvh): query row c / Gh of
+// head kvh * Gh + c % Gh.
+__device__ __forceinline__ long long merge_row(const MergeParams& p, int b, int kvh, int c) {
+  const int Gh = p.heads_per_kv;
+  return (long long)b * p.q_len * p.num_q_heads + (long long)kvh * Gh + (long long)(c / Gh) * p.num_q_heads + c % Gh;
+}
+
+// A lane's N consecutive output floats at dst (aligned to N floats when N
+// is 2 or a multiple of 4: out is 16-byte aligned and slices start at
+// multiples of N), in the widest stores that alignment allows.
+template <int N>
+__device__ __forceinline__ void store_slice(float* dst, const float (&v)[N]) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int k = 0; k < N; k += 4)
+      *reinterpret_cast<float4*>(dst + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+  } else if constexpr (N == 2) {
+    *reinterpret_cast<float2*>(dst) = make_float2(v[0], v[1]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < N; ++k) dst[k] = v[k];
+  }
+}
+
+// Short pairs: one pair per wave, kMergePairWaves pairs per workgroup; the
+// grid strides over the pairs.
+template <int D, int G>
+__global__ __launch_bounds__(kMergePairWaves * 64) void merge_wave_kernel(MergeParams p) {
+  constexpr int EPL = G * D / 64;
+  constexpr int LPH = D / EPL;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane / LPH;
+  const int e0 = lane * EPL;
+  for (int pair = blockIdx.x * kMergePairWaves + wave; pair < p.batch * p.num_kv_heads;
+       pair += gridDim.x * kMergePairWaves) {
+    const CutPair c = cut_pair(p, pair);
+    if (c.n == 0) continue;
+    float M = -__builtin_inff(), L = 0.0f, A[EPL];
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) A[k] = 0.0f;
+    fold_pieces<D, G>(p, c, 0, 1, lane, M, L, A);
+    if (g >= p.num_cols) continue;  // padding columns are not written
+    const long long bh = merge_row(p, c.b, c.kvh, g);
+    // a column that saw no token (L = 0) gets 0 and -inf; a NaN sum, from a
+    // poisoned piece, stays NaN
+    float o[EPL];
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) o[k] = L != 0.0f ? A[k] / L : 0.0f;
+    store_slice<EPL>(p.out + bh * D + (e0 % D), o);
+    if (lane % LPH == 0 && p.lse != nullptr) p.lse[bh] = L != 0.0f ? (M + log2f(L)) * kLn2 : -__builtin_inff();
+  }
+}
+
+// Longer pairs: one pair per workgroup of W waves, each wave taking every
+// W-th piece; the waves' states meet in LDS under the same rule. The grid
+// strides over the pairs.
+template <int D, int G, int W>
+__global__ __launch_bounds__(W * 64) void merge_kernel(MergeParams p) {
+  constexpr int EPL = G * D / 64;
+  constexpr int LPH = D / EPL;
+  __shared__ float s_m[W][G];
+  __shared__ float s_l[W][G];
+  __shared__ __attribute__((aligned(16))) float s_acc[W][G * D];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane / LPH;
+  const int e0 = lane * EPL;
+  for (int pair = blockIdx.x; pair < p.batch * p.num_kv_heads; pair += gridDim.x) {
+    const CutPair c = cut_pair(p, pair);
+    if (c.n == 0) continue;  // uniform over the workgroup
+    float M = -__builtin_inff(), L = 0.0f, A[EPL];
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) A[k] = 0.0f;
+    fold_pieces<D, G>(p, c, wave, W, lane, M, L, A);
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) s_acc[wave][e0 + k] = A[k];
+    if (lane % LPH == 0) {
+      s_m[wave][g] = M;
+      s_l[wave][g] = L;
+    }
+    __syncthreads();
+    for (int e = tid; e < G * D; e += W * 64) {
+      const int gg = e / D;
+      if (gg >= p.num_cols) continue;
+      float Mx = s_m[0][gg];
+#pragma unroll
+      for (int q = 1; q < W; ++q) Mx = fmaxf(Mx, s_m[q][gg]);
+      float Av = 0.0f, Ls = 0.0f;
+#pragma unroll
+      for (int q = 0; q < W; ++q) {
+        const float mq = s_m[q][gg];
+        // a wave without pieces holds M = -inf, l = acc = 0: weight 0
+        const float wq = mq == Mx ? 1.0f : __builtin_amdgcn_exp2f(mq - Mx);
+        Av += wq * s_acc[q][e];
+        Ls += wq * s_l[q][gg];
+      }
+      const long long bh = merge_row(p, c.b, c.kvh, gg);
+      p.out[bh * D + (e % D)] = Ls != 0.0f ? Av / Ls : 0.0f;
+      if (e % D == 0 && p.lse != nullptr) p.lse[bh] = Ls != 0.0f ? (Mx + log2f(Ls)) * kLn2 : -__builtin_inff();
+    }
+    __syncthreads();  // the LDS is reused by the next pair
   }
 }
 
@@ -474,18 +566,66 @@ hipError_t launch_kind(const DecodeParams& p, int group, int kind, uint32_t grid
   }
 }
 
-template <int D>
-hipError_t launch_merge_d(const MergeParams& p, int group, uint32_t grid, hipStream_t stream) {
-  // one workgroup per worker descriptor
-  switch (group) {
-    case 1: hipLaunchKernelGGL((merge_kernel<D, 1>), dim3(grid), dim3(kMergeWaves * 64), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((merge_kernel<D, 2>), dim3(grid), dim3(kMergeWaves * 64), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((merge_kernel<D, 4>), dim3(grid), dim3(kMergeWaves * 64), 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((merge_kernel<D, 8>), dim3(grid), dim3(kMergeWaves * 64), 0, stream, p); break;
-    case 16: hipLaunchKernelGGL((merge_kernel<D, 16>), dim3(grid), dim3(kMergeWaves * 64), 0, stream, p); break;
+template <int D, int G, int W>
+hipError_t launch_merge_w(const MergeParams& p, uint32_t max_grid, hipStream_t stream) {
+  const int64_t pairs = (int64_t)p.batch * p.num_kv_heads;
+  if constexpr (W == 1) {
+    const uint32_t grid = (uint32_t)std::min<int64_t>((pairs + kMergePairWaves - 1) / kMergePairWaves, max_grid);
+    hipLaunchKernelGGL((merge_wave_kernel<D, G>), dim3(grid), dim3(kMergePairWaves * 64), 0, stream, p);
+    return hipGetLastError();
+  } else if constexpr (merge_fits<D, G, W>()) {
+    const uint32_t grid = (uint32_t)std::min<int64_t>(pairs, max_grid);
+    hipLaunchKernelGGL((merge_kernel<D, G, W>), dim3(grid), dim3(W * 64), 0, stream, p);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
+template <int D, int G>
+hipError_t launch_merge_g(const MergeParams& p, int waves, uint32_t max_grid, hipStream_t stream) {
+  switch (waves) {
+    case 1: return launch_merge_w<D, G, 1>(p, max_grid, stream);
+    case 4: return launch_merge_w<D, G, 4>(p, max_grid, stream);
+    case 8: return launch_merge_w<D, G, 8>(p, max_grid, stream);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_merge_d(const MergeParams& p, int group, int waves, uint32_t max_grid, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_merge_g<D, 1>(p, waves, max_grid, stream);
+    case 2: return launch_merge_g<D, 2>(p, waves, max_grid, stream);
+    case 4: return launch_merge_g<D, 4>(p, waves, max_grid, stream);
+    case 8: return launch_merge_g<D, 8>(p, waves, max_grid, stream);
+    case 16: return launch_merge_g<D, 16>(p, waves, max_grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// One pair per wave when one step of a wave covers the longest pair; four
+// waves per pair up to four steps' worth; eight beyond (as LDS allows).
+// Measured on MI355X: wider workgroups, or more pieces in flight per wave
+// than a pair has, only lengthen the reduce.
+template <int D, int G>
+int merge_waves_g(int64_t max_pieces) {
+  constexpr int U = merge_unroll<D, G>();
+  if (max_pieces <= U) return 1;
+  if (max_pieces <= 4 * U || !merge_fits<D, G, 8>()) return 4;
+  return 8;
+}
+
+template <int D>
+int merge_waves_d(int group, int64_t max_pieces) {
+  switch (group) {
+    case 1: return merge_waves_g<D, 1>(max_pieces);
+    case 2: return merge_waves_g<D, 2>(max_pieces);
+    case 4: return merge_waves_g<D, 4>(max_pieces);
+    case 8: return merge_waves_g<D, 8>(max_pieces);
+    case 16: return merge_waves_g<D, 16>(max_pieces);
+    default: return 1;
+  }
 }
 
 }  // namespace
@@ -506,11 +646,19 @@ hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, int kin
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_merge(const MergeParams& p, int head_dim, int group, uint32_t grid, hipStream_t stream) {
-  if (head_dim == 64) return launch_merge_d<64>(p, group, grid, stream);
-  if (head_dim == 128) return launch_merge_d<128>(p, group, grid, stream);
-  if (head_dim == 256) return launch_merge_d<256>(p, group, grid, stream);
+hipError_t launch_merge(const MergeParams& p, int head_dim, int group, int waves, uint32_t max_grid,
+                        hipStream_t stream) {
+  if (head_dim == 64) return launch_merge_d<64>(p, group, waves, max_grid, stream);
+  if (head_dim == 128) return launch_merge_d<128>(p, group, waves, max_grid, stream);
+  if (head_dim == 256) return launch_merge_d<256>(p, group, waves, max_grid, stream);
   return hipErrorInvalidValue;
+}
+
+int merge_waves(int head_dim, int group, int64_t max_pieces) {
+  if (head_dim == 64) return merge_waves_d<64>(group, max_pieces);
+  if (head_dim == 128) return merge_waves_d<128>(group, max_pieces);
+  if (head_dim == 256) return merge_waves_d<256>(group, max_pieces);
+  return 1;
 }
 
 }  // namespace pdattn

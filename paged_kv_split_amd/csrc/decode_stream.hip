@@ -22,8 +22,9 @@
 //   * a tile's K and V rows are addressed from one wave-uniform base (its
 //     page's row index) plus per-lane offsets that never change.
 // The per-tile step (q.K on MFMA, online softmax in base 2, p.V) and the
-// finish of a pair (out, or an (m, l, acc) record of a cut pair with the
-// merge descriptor) are those of decode_kernel, from tile_ops.h.
+// finish of a pair (out, or an (m, l, acc) record of a cut pair; workgroup 0
+// leaves the tile prefix the merge walks) are those of decode_kernel, from
+// tile_ops.h.
 
 #include "tile_ops.h"
 
@@ -98,8 +99,17 @@ void decode_stream_kernel(DecodeParams p) {
     total += x;
   }
   const int pre = before + incl - n0 - n1;
-  if (2 * tid <= B) s_pre[2 * tid] = pre;
-  if (2 * tid + 1 <= B) s_pre[2 * tid + 1] = pre + n0;
+  // entries 0 .. B - 1 here, entry B (the total) by thread 0: at B =
+  // kStreamMaxBatch no thread's pair of sequences reaches it
+  if (2 * tid < B) s_pre[2 * tid] = pre;
+  if (2 * tid + 1 < B) s_pre[2 * tid + 1] = pre + n0;
+  if (tid == 0) s_pre[B] = total;
+  if (blockIdx.x == 0) {
+    // the prefix for the split reduce
+    if (2 * tid < B) p.pre[2 * tid] = pre;
+    if (2 * tid + 1 < B) p.pre[2 * tid + 1] = pre + n0;
+    if (tid == 0) p.pre[B] = total;
+  }
   // empty or over-long sequences get their outputs here (out = 0,
   // lse = -inf; NaN when the length does not fit the block table)
   if (blockIdx.x == 0) {
@@ -132,7 +142,6 @@ void decode_stream_kernel(DecodeParams p) {
   };
   const int t0 = range_start(gw), t1 = range_start(gw + 1);
   const int n = t1 - t0;
-  int dsc[kDescWords] = {0, 0, 0, 0, 0, 0, 0, 0};
   unsigned char* ring = &s_ring[wave][0];
   unsigned char* qs = &s_q[wave][0];
 
@@ -290,15 +299,13 @@ void decode_stream_kernel(DecodeParams p) {
     typename TL::State sta;
     TL::reset(sta);
     bool poisoned = false, first_piece = true, cut_start = false;
-    int cb = 0, ckvh = 0, lim = 0;
+    int lim = 0;
     long long base_row = 0;
     // tile k's arithmetic, f holding its fragments; g receives tile k + 1's
     auto step = [&](int k, typename TL::Frag& f, typename TL::Frag& g) {
       const int jf = njf;
       const int j = jf & kJMask;
       if (jf & kPieceStart) {
-        cb = nb;
-        ckvh = nkvh;
         base_row = (long long)nb * p.q_len * Hq + (long long)nkvh * Gh;
         const int cl = min(col, p.num_cols - 1);
         lim = nL - (p.q_len - 1 - cl / Gh);
@@ -335,19 +342,6 @@ void decode_stream_kernel(DecodeParams p) {
           TL::store_record_counted(sta, rec_rs, (uint32_t)((gw * 2 + (first_piece ? 0 : 1)) * RF), poisoned, row,
                                    col);
           st_now = TL::N_REC_STORES;
-          if (cut_start && reaches_end) {
-            // this wave holds the pair's last tile: describe the pieces
-            const long long pair_start = (long long)t0 + k - j;
-            // first worker whose range reaches pair_start
-            const long long wf = ((pair_start + 1) * NW + T - 1) / T - 1;
-            dsc[0] = 1;
-            dsc[1] = cb;
-            dsc[2] = ckvh;
-            dsc[3] = (int)wf;
-            dsc[4] = range_start(wf) == pair_start ? 0 : 1;
-            dsc[5] = T;
-            dsc[6] = 0;
-          }
         }
         first_piece = false;
       }
@@ -365,11 +359,6 @@ void decode_stream_kernel(DecodeParams p) {
       if (k + 1 < n) step(k + 1, fb, fa);
     }
   }
-  // lane i writes word i (selected, not indexed)
-  int dword_i = 0;
-#pragma unroll
-  for (int i = 0; i < kDescWords; ++i) dword_i = lane == i ? dsc[i] : dword_i;
-  if (lane < kDescWords) p.desc[gw * kDescWords + lane] = dword_i;
 }
 
 // LDS of one workgroup; instantiations beyond the 160 KB of a CU are not

@@ -21,8 +21,6 @@ constexpr int kStages = PDATTN_STAGES;
 constexpr int kPagesPerWave = 256;
 // Fewest tiles the planner gives one worker wave.
 constexpr int kMinTilesPerWorker = 4;
-// Words of one worker's merge descriptor.
-constexpr int kDescWords = 8;
 // Waves per workgroup of the streaming decode kernel.
 constexpr int kStreamWaves = 4;
 // Largest batch the streaming decode kernel takes (its workgroups hold the
@@ -77,7 +75,7 @@ struct DecodeParams {
   float* out;                 // [B][Hq][D]
   float* lse;                 // [B][Hq] or null
   float* rec;                 // [num_workers][2][record_floats]
-  int32_t* desc;              // [num_workers][kDescWords]
+  int64_t* pre;               // [batch + 1]: tiles per kv head before sequence b (workgroup 0 writes it)
   int32_t batch;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -123,10 +121,12 @@ struct DynParams {
 };
 
 struct MergeParams {
-  const float* rec;
-  const int32_t* desc;
+  const float* rec;           // the decode's records
+  const int64_t* pre;         // the decode's tile prefix [batch + 1]
   float* out;
   float* lse;
+  int32_t batch;
+  int32_t num_kv_heads;
   int32_t num_q_heads;
   int32_t num_workers;
   int32_t q_len;              // as in DecodeParams
@@ -153,7 +153,13 @@ hipError_t launch_decode_stream(const DecodeParams& p, int head_dim, int group, 
 // Returns hipErrorInvalidValue for an instantiation that is not built.
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int group, int kind, uint32_t grid,
                          hipStream_t stream);
-hipError_t launch_merge(const MergeParams& p, int head_dim, int group, uint32_t grid, hipStream_t stream);
+// The split reduce: `waves` 1 (one pair per wave), 4 or 8 (one pair per
+// workgroup of that many waves), from merge_waves; at most max_grid
+// workgroups, striding over the pairs.
+hipError_t launch_merge(const MergeParams& p, int head_dim, int group, int waves, uint32_t max_grid,
+                        hipStream_t stream);
+// The merge shape for pairs of at most max_pieces pieces.
+int merge_waves(int head_dim, int group, int64_t max_pieces);
 int dynamic_wgs_per_cu(int head_dim, int group, bool fp8);
 hipError_t launch_dynamic(const DynParams& p, int head_dim, int group, bool fp8, uint32_t grid, hipStream_t stream);
 hipError_t launch_workspace_init(uint32_t* ctl, uint64_t words, uint32_t* header, uint32_t units_max,

@@ -28,6 +28,8 @@ static __device__ __align__(256) unsigned char scratch[PDATTN_NOALLOC_SCRATCH_BY
 namespace {
 
 constexpr uint32_t kPlanMagic = 0x70644132u;  // "pdA2"
+// Largest grid of the split reduce (its workgroups stride over the pairs).
+constexpr int64_t kMaxMergeWorkgroups = 8192;
 
 thread_local char g_last_error[512] = "";
 
@@ -141,8 +143,8 @@ bool use_stream(const pdattn_problem& p) {
 }
 uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
-// Default-mode workspace: 2 partial records per worker, then
-// kDescWords descriptor words per worker.
+// Default-mode workspace: 2 partial records per worker, then the tile
+// prefix of the sequences (batch + 1 int64 words).
 uint64_t records_bytes(const pdattn_problem& p, int64_t workers) {
   return (uint64_t)workers * 2 * pdattn::record_floats(p.head_dim, group_of(p)) * 4;
 }
@@ -171,7 +173,7 @@ DynLayout dyn_layout(const pdattn_problem& p, int64_t workers) {
 }
 
 uint64_t workspace_for(const pdattn_problem& p, int64_t workers, int32_t flags) {
-  if (!balanced(flags)) return records_bytes(p, workers) + (uint64_t)workers * pdattn::kDescWords * 4;
+  if (!balanced(flags)) return records_bytes(p, workers) + ((uint64_t)p.batch + 1) * 8;
   return dyn_layout(p, workers).total;
 }
 
@@ -258,7 +260,7 @@ pdattn_status launch_static_decode(const pdattn_plan_t* plan, const void* q, con
   p.out = out;
   p.lse = lse;
   p.rec = static_cast<float*>(workspace);
-  p.desc = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(workspace) + records_bytes(pr, plan->num_workers));
+  p.pre = reinterpret_cast<int64_t*>(static_cast<unsigned char*>(workspace) + records_bytes(pr, plan->num_workers));
   p.batch = pr.batch;
   p.num_q_heads = pr.num_q_heads;
   p.num_kv_heads = pr.num_kv_heads;
@@ -289,16 +291,24 @@ pdattn_status launch_static_reduce(const pdattn_plan_t* plan, const void* worksp
   pdattn::MergeParams p;
   std::memset(&p, 0, sizeof p);
   p.rec = static_cast<const float*>(workspace);
-  p.desc = reinterpret_cast<const int32_t*>(static_cast<const unsigned char*>(workspace) +
-                                            records_bytes(pr, plan->num_workers));
+  p.pre = reinterpret_cast<const int64_t*>(static_cast<const unsigned char*>(workspace) +
+                                           records_bytes(pr, plan->num_workers));
   p.out = out;
   p.lse = lse;
+  p.batch = pr.batch;
+  p.num_kv_heads = pr.num_kv_heads;
   p.num_q_heads = pr.num_q_heads;
   p.num_workers = plan->num_workers;
   p.q_len = qlen_of(pr);
   p.heads_per_kv = heads_per_kv(pr);
   p.num_cols = cols_of(pr);
-  hipError_t e = pdattn::launch_merge(p, pr.head_dim, group_of(pr), (uint32_t)plan->num_workers,
+  // pieces of the longest pair under the host lengths: its tiles span at
+  // most floor((nt - 1) NW / T) + 2 worker ranges
+  const int64_t nt_max = ceil_div(plan->max_context_len, (int64_t)pdattn::kTileTokens);
+  const int64_t max_pieces =
+      plan->total_tiles > 0 && nt_max > 0 ? (nt_max - 1) * plan->num_workers / plan->total_tiles + 2 : 1;
+  const int waves = pdattn::merge_waves(pr.head_dim, group_of(pr), max_pieces);
+  hipError_t e = pdattn::launch_merge(p, pr.head_dim, group_of(pr), waves, (uint32_t)kMaxMergeWorkgroups,
                                       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "reduce kernel launch: %s", hipGetErrorString(e));
   return PDATTN_OK;

@@ -100,7 +100,8 @@ def test_plan_for_each_workload(name, flags):
     if flags:
         assert pl.workspace_bytes == dyn_workspace_bytes(pl)
     else:
-        assert pl.workspace_bytes == pl.num_workers * (2 * rec + 8 * 4)
+        # two records per worker, then the tile prefix (batch + 1 int64 words)
+        assert pl.workspace_bytes == pl.num_workers * 2 * rec + (w.batch + 1) * 8
     assert 1 <= pl.num_workers <= 4 * pl.num_workgroups
     assert pl.num_workers <= max(1, tiles // 4)
     assert abs(pl.problem.scale - 1.0 / math.sqrt(w.head_dim)) < 1e-7

@@ -193,6 +193,31 @@ def test_many_sequences_exercise_the_chunked_length_scan():
     assert_parity(out, lse, *oracle_run(inp), tag="B2048")
 
 
+def test_streaming_kernel_at_its_largest_batch():
+    # 512 sequences, the streaming kernel's largest batch: the tile prefix's
+    # last entry (the total) is one no pair of sequences per thread reaches
+    w = small(B=512, Hq=8, Hkv=2, D=64, P=16, lens=("uniform", 1, 300), seed=316)
+    inp = synth.make_inputs(w)
+    out, lse = gpu_run(inp)
+    assert_parity(out, lse, *oracle_run(inp), tag="B512")
+
+
+MERGE_STRIDE = [(4500, 8, ("uniform", 0, 40), 0), (1100, 8, ("uniform", 64, 160), 30000),
+                (512, 32, ("uniform", 16, 400), 30000)]
+
+
+@pytest.mark.parametrize("B,Hkv,lens,force", MERGE_STRIDE,
+                         ids=["pair-per-wave", "pair-per-workgroup", "pair-per-workgroup-stream"])
+def test_more_pairs_than_reduce_workgroups(B, Hkv, lens, force):
+    # more (sequence, kv head) pairs than the reduce launches workgroups (8192
+    # at most), so its grid strides over them; short pairs are merged one per
+    # wave, pairs cut into more pieces (many forced workers) one per workgroup
+    w = small(B=B, Hq=Hkv, Hkv=Hkv, D=64, P=16, lens=lens, seed=315 + B)
+    inp = synth.make_inputs(w)
+    out, lse = gpu_run(inp, force_workers=force)
+    assert_parity(out, lse, *oracle_run(inp), tag=f"B{B} Hkv{Hkv} workers {force}")
+
+
 def test_long_single_sequence_with_one_worker_crosses_page_buffer_refills():
     # one worker walks 3000 pages (more than one 256-entry page buffer)
     w = small(B=1, Hq=8, Hkv=1, D=64, P=8, lens=("fixed", (24000,)), seed=314)

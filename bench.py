@@ -16,13 +16,19 @@ HBM.
 
 Prints ONE JSON line. value = KV algorithmic bytes (every K and V element of
 every valid (token, kv head) once, plus the fp8 scales) / mean step time, in
-GB/s, the step timed by one event pair around decode + reduce. roofline =
-the same bytes / the mean duration of the decode kernel alone (an event pair
+GB/s, the step timed by one event pair around decode + reduce. Warm-up runs
+the timed loops' own work (flush, event records, launches). roofline = the
+same bytes / the mean duration of the decode kernel alone (an event pair
 around that launch on its stream, in a second flushed loop), against
-MI355X's 8 TB/s HBM peak. traffic = measured HBM bytes per launch of that kernel from the
-committed rocprofv3 counter summary, or null when the kernel's sources have
-changed since the counters were taken. cpu_baseline = the CPU fp64 oracle
-timed on this host's cores on the same step's inputs.
+MI355X's 8 TB/s HBM peak. traffic = measured HBM bytes per launch of that
+kernel from the committed rocprofv3 counter summary, or null when the
+kernel's sources have changed since the counters were taken. cpu_baseline =
+the CPU fp64 oracle timed on this host's cores on the same step's inputs;
+oracle_check = the headline outputs against that oracle's (max- and
+mean-abs). configs = the tiny, long-context, many-short and FP8 KV
+workloads, each timed the same way (mean, median, p10/p90, GB/s, fraction
+of peak, decode and reduce kernels alone) and checked against the oracle.
+device = name, gfx arch, compute units, HIP and ROCm versions.
 
 prefill = the ragged paged prefill (pdattn_prefill) on its three workloads
 (synth.PREFILL_WORKLOADS) and the ragged batch with fp8 pools, each call
@@ -48,9 +54,15 @@ CSRC = os.path.join(ROOT, "paged_kv_split_amd", "csrc")
 # the sources each mode's decode kernel is built from
 KERNEL_SOURCES = {
     "balanced": ["decode_dynamic.hip", "tile_ops.h", "kernels.h"],
-    "static": ["decode_kernels.hip", "tile_ops.h", "kernels.h"],
+    "static": ["decode_stream.hip", "tile_ops.h", "kernels.h"],
 }
-KERNEL_NAMES = {"balanced": "decode_dynamic_kernel", "static": "decode_kernel"}
+# the static mode's decode kernel for bf16 / fp8 pools with page_size >= 16 and
+# batch <= 512 (every benchmark workload)
+KERNEL_NAMES = {"balanced": "decode_dynamic_kernel", "static": "decode_stream_kernel"}
+# the configurations timed beside the headline, each as its own sub-record
+SUB_WORKLOADS = ("tiny", "long_ctx", "many_short", "fp8_kv")
+# parity bars of the decode against the oracle (out max-abs, out mean-abs, lse max-abs)
+TOL = {"bf16": (1e-2, 1e-3, 1e-3), "fp8_e4m3": (4e-2, 1e-3, 1e-3)}
 METRIC = "decode-attn achieved HBM GB/s + µs/call, Llama-3-8B shape, 1×MI355X"
 
 
@@ -448,6 +460,125 @@ def time_prefill(pk, flush, dev, reps=20):
     return res
 
 
+def device_info():
+    """Name, gfx architecture, compute units and the HIP / ROCm versions."""
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    rocm = None
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        if os.path.exists(path):
+            with open(path) as f:
+                rocm = f.read().strip()
+            break
+    return {"name": torch.cuda.get_device_name(0), "gfx_arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "hbm_bytes": props.total_memory,
+            "hip_runtime": torch.version.hip, "rocm": rocm, "torch": torch.__version__}
+
+
+def time_step(pk, w, inp, layout, balanced, flush, dev, steps, warmup, no_flush=False):
+    """One workload's decode step on the device: plan, warm up, then time.
+
+    Warm-up runs exactly the timed loops' work (the cache flush, the event
+    records and the launches). The timed steps: a 512 MiB flush before each
+    (outside its events), then one event pair around decode + reduce. Then
+    each launch alone between its own events, after the same flush: the
+    decode kernel's duration (for the roofline) and the reduce's. Returns the
+    figures, the outputs of the last step and the plan."""
+    import torch
+    import synth
+    laid = synth.to_hnd(inp) if layout == pk.LAYOUT_HND else inp
+    d = {k: (laid[k].to(dev) if laid[k] is not None else None)
+         for k in ("q", "k_pages", "v_pages", "k_scale", "v_scale", "block_table", "context_lens")}
+    pl = pk.plan(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                 page_size=w.page_size, max_pages_per_seq=inp["block_table"].shape[1],
+                 num_pages=inp["k_pages"].shape[0],
+                 kv_dtype=pk.KV_BF16 if w.kv_dtype == "bf16" else pk.KV_FP8_E4M3,
+                 context_lens_host=inp["context_lens"], balanced=balanced, kv_layout=layout)
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=dev)
+    ws = pk.workspace(pl, dev)
+    if balanced:
+        pk.workspace_init(pl, ws)
+
+    def decode():
+        pk.decode(pl, d["q"], d["k_pages"], d["v_pages"], d["k_scale"], d["v_scale"], d["block_table"],
+                  d["context_lens"], ws, out, lse)
+
+    def reduce():
+        pk.reduce(pl, ws, out, lse)
+
+    def step_loop(n):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+        for i in range(n):
+            if not no_flush:
+                flush.fill_(i & 0xFF)
+            ev[i][0].record()
+            decode()
+            reduce()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) * 1e3 for a, b in ev]
+
+    def split_loop(n):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+        for i in range(n):
+            if not no_flush:
+                flush.fill_(i & 0xFF)
+            ev[i][0].record()
+            decode()
+            ev[i][1].record()
+            ev[i][2].record()
+            reduce()
+            ev[i][3].record()
+        torch.cuda.synchronize()
+        return ([e[0].elapsed_time(e[1]) * 1e3 for e in ev], [e[2].elapsed_time(e[3]) * 1e3 for e in ev])
+
+    if warmup > 0:
+        step_loop(warmup)
+        split_loop(warmup)
+    wall0 = time.perf_counter()
+    step_us = step_loop(steps)
+    wall = time.perf_counter() - wall0
+    dec_us, red_us = split_loop(steps)
+    kvb = synth.kv_bytes(w, inp["context_lens"])
+    mean_step = statistics.fmean(step_us)
+    med_step = statistics.median(step_us)
+    qs = statistics.quantiles(step_us, n=10) if len(step_us) > 1 else [step_us[0]] * 9
+    mean_dec = statistics.fmean(dec_us)
+    res = {
+        "workload": w.description, "batch": w.batch, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+        "head_dim": w.head_dim, "page_size": w.page_size, "kv_dtype": w.kv_dtype, "seed": w.seed,
+        "kv_layout": "HND" if layout == pk.LAYOUT_HND else "NHD", "mode": "balanced" if balanced else "static",
+        "workers": pl.num_workers, "workgroups": pl.num_workgroups, "kv_bytes": kvb, "steps": steps,
+        "us_per_call_mean": round(mean_step, 2), "us_per_call_median": round(med_step, 2),
+        "us_per_call_p10_p90": [round(qs[0], 2), round(qs[-1], 2)],
+        "gbs": round(kvb / (mean_step * 1e-6) / 1e9, 1),
+        "frac": round(kvb / (mean_step * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "frac_median": round(kvb / (med_step * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "decode_kernel_us": round(mean_dec, 2), "decode_kernel_us_median": round(statistics.median(dec_us), 2),
+        "decode_kernel_frac": round(kvb / (mean_dec * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "reduce_kernel_us": round(statistics.fmean(red_us), 2),
+        "reduce_kernel_us_median": round(statistics.median(red_us), 2),
+        "timed_wall_s": round(wall, 4),
+        "outputs_finite": bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all()),
+    }
+    torch.cuda.synchronize()
+    return res, out.cpu(), lse.cpu(), pl
+
+
+def oracle_compare(out, lse, ref_out, ref_lse, kv_dtype):
+    """Max- and mean-abs differences of the device outputs from the oracle's."""
+    import torch
+    diff = (out.to(torch.float64) - ref_out).abs()
+    fin = torch.isfinite(ref_lse)
+    ldiff = float((lse.to(torch.float64)[fin] - ref_lse[fin]).abs().max()) if bool(fin.any()) else 0.0
+    mx_tol, mean_tol, lse_tol = TOL[kv_dtype]
+    mx, mean = float(diff.max()), float(diff.mean())
+    return {"out_max_abs": mx, "out_mean_abs": mean, "lse_max_abs": ldiff,
+            "tolerance": {"out_max_abs": mx_tol, "out_mean_abs": mean_tol, "lse_max_abs": lse_tol},
+            "within_tolerance": bool(mx <= mx_tol and mean <= mean_tol and ldiff <= lse_tol)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -455,12 +586,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="CPU time budget of the oracle baseline (0 skips it)")
+                    help="CPU time budget of the oracle baseline (0 skips it, and the oracle checks)")
     ap.add_argument("--no-flush", action="store_true", help="time with warm caches")
     ap.add_argument("--balanced", action="store_true",
                     help="time the on-device balanced kernel instead of the static split + reduce")
     ap.add_argument("--layout", choices=("hnd", "nhd"), default="hnd",
                     help="KV pool rows [page][kv head][slot] (hnd, the default) or [page][slot][kv head] (nhd)")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other configurations' sub-records")
     ap.add_argument("--no-other-layout", action="store_true", help="skip the other-layout step timing")
     ap.add_argument("--no-append", action="store_true", help="skip the KV-append timings")
     ap.add_argument("--no-merge", action="store_true", help="skip the partial-state merge timings")
@@ -487,91 +619,34 @@ def main():
     inp = synth.make_inputs(w)
     dev = torch.device("cuda:0")
     layout = pk.LAYOUT_HND if args.layout == "hnd" else pk.LAYOUT_NHD
-    laid = synth.to_hnd(inp) if args.layout == "hnd" else inp
-    d = {k: (laid[k].to(dev) if laid[k] is not None else None)
-         for k in ("q", "k_pages", "v_pages", "k_scale", "v_scale", "block_table", "context_lens")}
-    kv_bytes = synth.kv_bytes(w, inp["context_lens"])
     mode = "balanced" if args.balanced else "static"
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
+    # host planning cost (the first plan on a device also queries its occupancy)
     def make_plan():
         return pk.plan(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
                        head_dim=w.head_dim, page_size=w.page_size,
                        max_pages_per_seq=inp["block_table"].shape[1], num_pages=inp["k_pages"].shape[0],
                        kv_dtype=pk.KV_BF16 if w.kv_dtype == "bf16" else pk.KV_FP8_E4M3,
                        context_lens_host=inp["context_lens"], balanced=args.balanced, kv_layout=layout)
-
     t0 = time.perf_counter()
-    pl = make_plan()  # the first plan on a device also queries its occupancy
+    make_plan()
     plan_first_us = (time.perf_counter() - t0) * 1e6
     t0 = time.perf_counter()
     for _ in range(20):
-        pl = make_plan()
+        make_plan()
     plan_us = (time.perf_counter() - t0) * 1e6 / 20
-    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
-    lse = torch.empty((w.batch, w.num_q_heads), dtype=torch.float32, device=dev)
-    ws = pk.workspace(pl, dev)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
-    def step():
-        pk.decode(pl, d["q"], d["k_pages"], d["v_pages"], d["k_scale"], d["v_scale"], d["block_table"],
-                  d["context_lens"], ws, out, lse)
-        pk.reduce(pl, ws, out, lse)
+    head, out, lse, pl = time_step(pk, w, inp, layout, args.balanced, flush, dev, args.steps, args.warmup,
+                                   no_flush=args.no_flush)
+    kv_bytes = head["kv_bytes"]
+    mean_step = head["us_per_call_mean"]
+    mean_dec = head["decode_kernel_us"]
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # the timed steps: one event pair around decode + reduce (an event between
-    # the two launches would itself add a few microseconds to the step)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for i in range(args.steps):
-        if not args.no_flush:
-            flush.fill_(i & 0xFF)
-        ev[i][0].record()
-        step()
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    step_us = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
-    mean_step = statistics.fmean(step_us)
-    qs = statistics.quantiles(step_us, n=10)
-
-    # each kernel alone between events, on the stream it runs on, after the
-    # same flush: the decode kernel's duration for the roofline, and the
-    # reduce's
-    dec_us, red_us = [], []
-    for i in range(args.steps):
-        if not args.no_flush:
-            flush.fill_(i & 0xFF)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        pk.decode(pl, d["q"], d["k_pages"], d["v_pages"], d["k_scale"], d["v_scale"], d["block_table"],
-                  d["context_lens"], ws, out, lse)
-        b.record()
-        c, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c.record()
-        pk.reduce(pl, ws, out, lse)
-        e.record()
-        torch.cuda.synchronize()
-        dec_us.append(a.elapsed_time(b) * 1e3)
-        red_us.append(c.elapsed_time(e) * 1e3)
-    mean_dec = statistics.fmean(dec_us)
-
-    # warm-cache figure (secondary): same steps without the flush
-    warm = []
-    for _ in range(10):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        step()
-        b.record()
-        torch.cuda.synchronize()
-        warm.append(a.elapsed_time(b) * 1e3)
-    ok = bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
+    # warm-cache figure (secondary): the same step without the flush
+    warm, _, _, _ = time_step(pk, w, inp, layout, args.balanced, flush, dev, 10, 3, no_flush=True)
 
     # streaming-read reference over a buffer of the step's KV size
-    ceiling = None
     num_cus = torch.cuda.get_device_properties(0).multi_processor_count
     rbytes = (kv_bytes // 4096) * 4096
     rbuf = torch.ones(rbytes, dtype=torch.uint8, device=dev)
@@ -597,6 +672,21 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # the other configurations, each timed like the headline
+    configs = {}
+    sub_out = {}
+    if not args.no_configs:
+        for name in SUB_WORKLOADS:
+            if name == args.workload:
+                continue
+            sw = synth.WORKLOADS[name]
+            sinp = synth.make_inputs(sw)
+            res, so, sl, _ = time_step(pk, sw, sinp, layout, args.balanced, flush, dev, max(args.steps, 20),
+                                       args.warmup, no_flush=args.no_flush)
+            configs[name] = res
+            sub_out[name] = (sw, sinp, so, sl)
+            torch.cuda.empty_cache()
+
     other = None if args.no_other_layout else time_other_layout(pk, w, inp, args, flush, dev)
     append = None if args.no_append else time_append(pk, w, flush, dev, layout)
     merge = None if args.no_merge else time_merge(pk, flush, dev)
@@ -606,7 +696,10 @@ def main():
     fp8_scales = None if args.no_fp8 else time_fp8_scales(pk, flush, dev, args.layout)
     tq4 = None if args.no_tq4 else time_tq4(pk, flush, dev)
 
+    # the cpu_baseline leg: the CPU fp64 oracle, timed on this host's cores on
+    # the headline step's inputs; its outputs also check the device's
     cpu = None
+    parity = None
     if args.cpu_seconds > 0:
         import oracle
         times = []
@@ -614,9 +707,9 @@ def main():
         start = time.perf_counter()
         while True:
             t = time.perf_counter()
-            _, _, threads = oracle.decode(inp["q"], inp["k_pages"], inp["v_pages"], inp["block_table"],
-                                          inp["context_lens"], k_scale=inp["k_scale"],
-                                          v_scale=inp["v_scale"], return_threads=True)
+            ref_out, ref_lse, threads = oracle.decode(inp["q"], inp["k_pages"], inp["v_pages"], inp["block_table"],
+                                                      inp["context_lens"], k_scale=inp["k_scale"],
+                                                      v_scale=inp["v_scale"], return_threads=True)
             times.append(time.perf_counter() - t)
             if time.perf_counter() - start >= args.cpu_seconds:
                 break
@@ -625,22 +718,32 @@ def main():
                "kind": "oracle",
                "sample": f"the full {w.name} step ({w.batch} sequences) repeated {len(times)} times "
                          f"({sum(times):.1f} s); median {per_call * 1e6:.0f} us/call"}
-        # the same oracle on one thread, over a bounded prefix of the batch
-        nb = max(1, min(w.batch, 4))
-        sub = {k: inp[k] for k in ("q", "k_pages", "v_pages", "k_scale", "v_scale", "block_table", "context_lens")}
-        sub["q"], sub["block_table"], sub["context_lens"] = inp["q"][:nb], inp["block_table"][:nb], inp["context_lens"][:nb]
-        t1 = []
-        start = time.perf_counter()
-        while True:
-            t = time.perf_counter()
-            oracle.decode(sub["q"], sub["k_pages"], sub["v_pages"], sub["block_table"], sub["context_lens"],
-                          k_scale=sub["k_scale"], v_scale=sub["v_scale"], threads=1)
-            t1.append(time.perf_counter() - t)
-            if time.perf_counter() - start >= min(3.0, args.cpu_seconds):
-                break
-        sub_bytes = synth.kv_bytes(w, inp["context_lens"][:nb])
-        cpu["single_thread"] = {"value": round(sub_bytes / statistics.median(t1) / 1e9, 4), "unit": "GB/s",
-                                "cores": 1, "sample": f"the first {nb} sequences of the step, {len(t1)} calls"}
+        parity = oracle_compare(out, lse, ref_out, ref_lse, w.kv_dtype)
+
+        def single_thread(sw, sinp, budget):
+            # the same oracle on one thread, over a bounded prefix of the batch
+            nb = max(1, min(sw.batch, 4))
+            t1 = []
+            begin = time.perf_counter()
+            while True:
+                t = time.perf_counter()
+                oracle.decode(sinp["q"][:nb], sinp["k_pages"], sinp["v_pages"], sinp["block_table"][:nb],
+                              sinp["context_lens"][:nb], k_scale=sinp["k_scale"], v_scale=sinp["v_scale"],
+                              threads=1)
+                t1.append(time.perf_counter() - t)
+                if time.perf_counter() - begin >= budget:
+                    break
+            sub_bytes = synth.kv_bytes(sw, sinp["context_lens"][:nb])
+            return {"value": round(sub_bytes / statistics.median(t1) / 1e9, 4), "unit": "GB/s", "cores": 1,
+                    "kind": "oracle", "sample": f"the first {nb} sequences of the step, {len(t1)} calls"}
+
+        cpu["single_thread"] = single_thread(w, inp, min(3.0, args.cpu_seconds))
+        for name, (sw, sinp, so, sl) in sub_out.items():
+            ro, rl = oracle.decode(sinp["q"], sinp["k_pages"], sinp["v_pages"], sinp["block_table"],
+                                   sinp["context_lens"], k_scale=sinp["k_scale"], v_scale=sinp["v_scale"])
+            configs[name]["oracle_check"] = oracle_compare(so, sl, ro, rl, sw.kv_dtype)
+            if name in ("tiny", "many_short"):
+                configs[name]["cpu_single_thread"] = single_thread(sw, sinp, min(3.0, args.cpu_seconds))
 
     traffic = read_traffic(mode, w.name, args.layout)
     # fp8 pools: the two fp32 scales per (token, kv head) inside kv_bytes
@@ -649,7 +752,7 @@ def main():
     achieved = kv_bytes / (mean_dec * 1e-6) / 1e9
     rec = {
         "metric": METRIC,
-        "value": round(kv_bytes / (mean_step * 1e-6) / 1e9, 1),
+        "value": head["gbs"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -668,12 +771,19 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "cpu_baseline": cpu,
+        "oracle_check": parity,
         "us_per_call": round(mean_step, 2),
-        "us_per_call_p10_p50_p90": [round(qs[0], 2), round(statistics.median(step_us), 2), round(qs[-1], 2)],
+        "us_per_call_median": head["us_per_call_median"],
+        "us_per_call_p10_p50_p90": [head["us_per_call_p10_p90"][0], head["us_per_call_median"],
+                                    head["us_per_call_p10_p90"][1]],
+        "frac_of_peak_step_mean": head["frac"],
+        "frac_of_peak_step_median": head["frac_median"],
         "mode": mode,
-        "decode_kernel_us": round(mean_dec, 2),
-        "reduce_kernel_us": round(statistics.fmean(red_us), 2),
-        "warm_cache_us_per_call": round(statistics.median(warm), 2),
+        "decode_kernel_us": head["decode_kernel_us"],
+        "decode_kernel_us_median": head["decode_kernel_us_median"],
+        "reduce_kernel_us": head["reduce_kernel_us"],
+        "reduce_kernel_us_median": head["reduce_kernel_us_median"],
+        "warm_cache_us_per_call": warm["us_per_call_median"],
         "kv_bytes_per_call": kv_bytes,
         "kv_payload_bytes_per_call": kv_bytes - scale_bytes,
         "value_payload_only_gbs": round((kv_bytes - scale_bytes) / (mean_step * 1e-6) / 1e9, 1),
@@ -681,11 +791,12 @@ def main():
         "frac_of_stream_read_ceiling": round(kv_bytes / (mean_step * 1e-6) / 1e9 / ceiling, 4),
         "plan_host_us": round(plan_us, 1),
         "plan_host_first_call_us": round(plan_first_us, 1),
-        "timed_wall_s": round(wall, 4),
+        "timed_wall_s": head["timed_wall_s"],
         "cache_flush_between_steps": not args.no_flush,
-        "outputs_finite": ok,
-        "device": torch.cuda.get_device_name(0),
+        "outputs_finite": head["outputs_finite"],
+        "device": device_info(),
         "kernel_source_sha256_16": source_digest(mode),
+        "configs": configs,
         "other_layout": other,
         "kv_append": append,
         "merge": merge,

@@ -35,6 +35,7 @@ FLAGS = [
     # packed fp32 VALU forms stay off: ordinary scalar fp32 code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
+    "-Werror=array-bounds",
     "-I", os.path.join(ROOT, "include"),
     "-I", CSRC,
 ]

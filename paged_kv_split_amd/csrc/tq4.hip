@@ -213,13 +213,19 @@ __global__ __launch_bounds__(256) void tq4_append_kernel(const Tq4AppendParams p
 constexpr int kRotRows = 8;  // q rows per rotation workgroup
 
 // y_seq[i] = sum_k R_seq[i][k] q[k] for kRotRows rows per workgroup: the
-// rows sit in LDS, thread t owns output column i = t mod D for the rows
-// t / D, t / D + 256 / D, ... and reads rotation row R_seq[i] once for them.
+// rows sit in LDS; KP adjacent threads share output column i, each taking a
+// D / KP slice of rotation row R_seq[i] for all the rows, so a thread's part
+// of the row is one round trip of independent 16-byte loads (four for d 256);
+// the KP partial sums meet by lane exchanges.
+// (fewer workgroups than compute units: occupancy does not matter, and the
+// loads are scheduled all ahead)
 template <int D>
-__global__ __launch_bounds__(256) void tq4_rotate_q_kernel(const Tq4DecodeParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void tq4_rotate_q_kernel(
+    const Tq4DecodeParams p) {
   constexpr int H = D / 2;
-  constexpr int TPC = 256 / D;                // threads per column (1, 2 or 4)
-  constexpr int RPT = kRotRows / TPC;         // rows per thread (8, 4 or 2)
+  constexpr int KP = 256 / D;             // threads per output column (4, 2 or 1)
+  constexpr int KL = D / KP;              // k per thread (16, 64 or 256)
+  constexpr int KB = KL > 64 ? 64 : KL;   // k per round trip
   __shared__ __attribute__((aligned(16))) float s_q[kRotRows][D];
   const int tid = threadIdx.x;
   const long long rows = (long long)p.batch * p.num_q_heads;
@@ -229,23 +235,22 @@ __global__ __launch_bounds__(256) void tq4_rotate_q_kernel(const Tq4DecodeParams
     s_q[e / D][e % D] = r < rows ? __uint_as_float((uint32_t)p.q[r * D + e % D] << 16) : 0.0f;
   }
   __syncthreads();
-  const int i = tid % D;
-  const int rs = tid / D;
-  const float* rrow = p.rotation + (long long)(i < H ? 2 * i : 2 * (i - H) + 1) * D;
-  float y[RPT];
+  const int i = tid / KP;
+  const int kp = tid % KP;
+  const float* rrow = p.rotation + (long long)(i < H ? 2 * i : 2 * (i - H) + 1) * D + kp * KL;
+  float y[kRotRows];
 #pragma unroll
-  for (int u = 0; u < RPT; ++u) y[u] = 0.0f;
-  // 32 columns of the row per round trip
+  for (int u = 0; u < kRotRows; ++u) y[u] = 0.0f;
 #pragma unroll 1
-  for (int k0 = 0; k0 < D; k0 += 32) {
-    f32x4 a[8];
+  for (int kb = 0; kb < KL; kb += KB) {
+    f32x4 a[KB / 4];
 #pragma unroll
-    for (int v = 0; v < 8; ++v) a[v] = *reinterpret_cast<const f32x4*>(rrow + k0 + 4 * v);
+    for (int v = 0; v < KB / 4; ++v) a[v] = *reinterpret_cast<const f32x4*>(rrow + kb + 4 * v);
 #pragma unroll
-    for (int v = 0; v < 8; ++v)
+    for (int v = 0; v < KB / 4; ++v)
 #pragma unroll
-      for (int u = 0; u < RPT; ++u) {
-        const f32x4 xv = *reinterpret_cast<const f32x4*>(&s_q[rs + u * TPC][k0 + 4 * v]);
+      for (int u = 0; u < kRotRows; ++u) {
+        const f32x4 xv = *reinterpret_cast<const f32x4*>(&s_q[u][kp * KL + kb + 4 * v]);
         y[u] = fmaf(a[v][0], xv[0], y[u]);
         y[u] = fmaf(a[v][1], xv[1], y[u]);
         y[u] = fmaf(a[v][2], xv[2], y[u]);
@@ -253,9 +258,14 @@ __global__ __launch_bounds__(256) void tq4_rotate_q_kernel(const Tq4DecodeParams
       }
   }
 #pragma unroll
-  for (int u = 0; u < RPT; ++u) {
-    const long long r = r0 + rs + u * TPC;
-    if (r < rows) p.q_seq[r * D + i] = (uint16_t)(pack_f16(y[u], 0.0f) & 0xffffu);
+  for (int o = 1; o < KP; o <<= 1)
+#pragma unroll
+    for (int u = 0; u < kRotRows; ++u) y[u] += __shfl_xor(y[u], o);
+  // every thread of the column holds the sums: thread kp writes rows kp, kp + KP, ...
+#pragma unroll
+  for (int u = 0; u < kRotRows; ++u) {
+    const long long r = r0 + u;
+    if (u % KP == kp && r < rows) p.q_seq[r * D + i] = (uint16_t)(pack_f16(y[u], 0.0f) & 0xffffu);
   }
 }
 
@@ -563,6 +573,19 @@ __device__ __forceinline__ void merge_row(const Tq4DecodeParams& p, long long ro
   const int nch = pair_chunks(pair_tiles(L, cap), p.chunk_tiles, p.max_chunks);
   const long long stride = (long long)pairs * tq4_record_floats(G, D);
   const float* rec0 = p.rec + pair * tq4_record_floats(G, D);
+  int aoff[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) aoff[e] = tq4_record_header(G) + n * D + acc_index<D>(lane + 64 * e);
+  // the accumulators of the first kPre items: their loads go out with the m
+  // loads below (one round trip for both; the sums keep the item order)
+  constexpr int kPre = 16;
+  float v0[kPre][EPL];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) {
+    const int c = u < nch ? u : nch - 1;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) v0[u][e] = rec0[c * stride + aoff[e]];
+  }
   // the items' m and l, 64 items per pass, one per lane
   float M = -__builtin_inff();
   for (int c0 = 0; c0 < nch; c0 += 64)
@@ -573,16 +596,26 @@ __device__ __forceinline__ void merge_row(const Tq4DecodeParams& p, long long ro
   float o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.0f;
-  int aoff[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) aoff[e] = tq4_record_header(G) + n * D + acc_index<D>(lane + 64 * e);
   for (int c0 = 0; c0 < nch; c0 += 64) {
     const int cl = c0 + lane;
     const float wl = cl < nch ? __builtin_amdgcn_exp2f(rec0[cl * stride + n] - M) : 0.0f;
     lsum += cl < nch ? wl * rec0[cl * stride + G + n] : 0.0f;
     const int cn = nch - c0 < 64 ? nch - c0 : 64;
-    // accumulators: eight items' loads in flight at a time
     int c = 0;
+    if (c0 == 0) {
+      // the prefetched items
+      const int np = cn < kPre ? cn : kPre;
+#pragma unroll
+      for (int u = 0; u < kPre; ++u) {
+        if (u < np) {
+          const float wgt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), u));
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[e] = fmaf(wgt, v0[u][e], o[e]);
+        }
+      }
+      c = np;
+    }
+    // the rest: eight items' loads in flight at a time
     for (; c + 8 <= cn; c += 8) {
       float v[8][EPL];
 #pragma unroll
@@ -612,15 +645,20 @@ __device__ __forceinline__ void merge_row(const Tq4DecodeParams& p, long long ro
 
 // tq4_merge_out_kernel: 8 rows (sequence, q head) per workgroup of 8
 // waves: wave w merges row w into LDS; then thread t owns column e = t mod D
-// of rows t / D, t / D + 512 / D, ... and forms out[r][e] = sum_d
-// R_seq[d][e] o[r][d], reading R_seq row d coalesced across the threads, once
-// for its rows.
+// and the d slice t / D of the back rotation out[r][e] = sum_d R_seq[d][e]
+// o[r][d] for all the rows (its column's entries of R_seq read coalesced
+// across the threads, one round trip of independent loads per 64 d); the
+// slices' partial sums meet in LDS.
 template <int D>
-__global__ __launch_bounds__(512) void tq4_merge_out_kernel(const Tq4DecodeParams p) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void tq4_merge_out_kernel(
+    const Tq4DecodeParams p) {
   constexpr int H = D / 2;
-  constexpr int TPC = 512 / D;
-  constexpr int RPT = kRotRows / TPC;
+  constexpr int DQ = 512 / D;             // d slices (8, 4 or 2)
+  constexpr int DL = D / DQ;              // d per thread (8, 32 or 128)
+  constexpr int DB = DL > 64 ? 64 : DL;   // d per round trip
+  static_assert(kRotRows == 8, "rows per workgroup");
   __shared__ __attribute__((aligned(16))) float s_o[kRotRows][D];
+  __shared__ float s_part[DQ][kRotRows][D];
   const int tid = threadIdx.x;
   const long long rows = (long long)p.batch * p.num_q_heads;
   const long long r0 = (long long)blockIdx.x * kRotRows;
@@ -630,27 +668,33 @@ __global__ __launch_bounds__(512) void tq4_merge_out_kernel(const Tq4DecodeParam
   }
   __syncthreads();
   const int e = tid % D;
-  const int rs = tid / D;
-  float y[RPT];
+  const int dq = tid / D;
+  float y[kRotRows];
 #pragma unroll
-  for (int u = 0; u < RPT; ++u) y[u] = 0.0f;
+  for (int u = 0; u < kRotRows; ++u) y[u] = 0.0f;
 #pragma unroll 1
-  for (int d0 = 0; d0 < D; d0 += 16) {
-    float r[16];
+  for (int db = 0; db < DL; db += DB) {
+    float r[DB];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int dd = d0 + v;
+    for (int v = 0; v < DB; ++v) {
+      const int dd = dq * DL + db + v;
       r[v] = p.rotation[(long long)(dd < H ? 2 * dd : 2 * (dd - H) + 1) * D + e];
     }
 #pragma unroll
-    for (int v = 0; v < 16; ++v)
+    for (int v = 0; v < DB; ++v)
 #pragma unroll
-      for (int u = 0; u < RPT; ++u) y[u] = fmaf(r[v], s_o[rs + u * TPC][d0 + v], y[u]);
+      for (int u = 0; u < kRotRows; ++u) y[u] = fmaf(r[v], s_o[u][dq * DL + db + v], y[u]);
   }
 #pragma unroll
-  for (int u = 0; u < RPT; ++u) {
-    const long long r = r0 + rs + u * TPC;
-    if (r < rows) p.out[r * D + e] = y[u];
+  for (int u = 0; u < kRotRows; ++u) s_part[dq][u][e] = y[u];
+  __syncthreads();
+  // thread t: column e of rows dq, dq + DQ, ...
+  for (int u = dq; u < kRotRows; u += DQ) {
+    float v = 0.0f;
+#pragma unroll
+    for (int q = 0; q < DQ; ++q) v += s_part[q][u][e];
+    const long long r = r0 + u;
+    if (r < rows) p.out[r * D + e] = v;
   }
 }
 

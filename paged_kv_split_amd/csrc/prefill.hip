@@ -65,6 +65,11 @@ struct Cfg {
   static constexpr int VI = V_T / (kWaves * 64 * 16);
   static constexpr int VR = DB * ESZ;               // bytes of a lane's V piece of one token
   static constexpr int COLS = kWaves * 16 * NB;
+  // bf16 d 128: V^T operands by transposing LDS reads from a chunk-swizzled
+  // V tile (16-byte chunk s of tile row t holds the row's chunk s ^ 2 (t mod
+  // 8)); d-block e of O^T is then d 16 e .. 16 e + 15
+  static constexpr bool TRV = !FP8 && D == 128;
+  static constexpr int CPR = ROW / 16;                     // 16-byte chunks per row
   static_assert(COLS == prefill_columns(D), "columns");
   static_assert(KI >= 1 && QK % KI == 0 && VI >= 1, "load split");
   static_assert(MB * QK == kWaves * KI, "K image");
@@ -112,6 +117,43 @@ __device__ __forceinline__ void lds_b128(u32x4 (&r)[sizeof...(O)], uint32_t a) {
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
         : "v"(a), "i"(o[0]), "i"(o[1]), "i"(o[2]), "i"(o[3]), "i"(o[4]), "i"(o[5]), "i"(o[6]), "i"(o[7])
+        : "memory");
+  }
+}
+
+// Eight transposing 8-byte LDS reads (ds_read_b64_tr_b16: in each 16-lane
+// group, lanes 4 r .. 4 r + 3 supply row r of a 4 x 16 block of 16-bit
+// values, 8 bytes each, and lane i receives column i: the four rows' values
+// of it), from eight base addresses at one immediate offset. WAIT closes the
+// block with the wait for every LDS read issued so far.
+template <int OFF, bool WAIT>
+__device__ __forceinline__ void lds_tr8(u32x2 (&r)[8], const uint32_t (&a)[8]) {
+  if constexpr (WAIT) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %1, %9 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %2, %10 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %3, %11 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %4, %12 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %5, %13 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %6, %14 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "i"(OFF)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %1, %9 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %2, %10 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %3, %11 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %4, %12 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %5, %13 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %6, %14 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %7, %15 offset:%16"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "i"(OFF)
         : "memory");
   }
 }
@@ -372,7 +414,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
   for (int i = 0; i < C::VI; ++i) {
     const int cv = (w * C::VI + i) * 64 + lane;
-    voff[i] = (uint32_t)(cv * 16 / C::ROW - 16 * mbK) * slot_bytes + (cv * 16) % C::ROW;
+    const int chunk = C::TRV ? (cv % C::CPR) ^ (2 * ((cv / C::CPR) % 8)) : cv % C::CPR;
+    voff[i] = (uint32_t)(cv * 16 / C::ROW - 16 * mbK) * slot_bytes + chunk * 16;
   }
   const uint32_t soff = (uint32_t)((lane & 15) * p.slot_stride) * 4u;
   const float* sbase_lane = lane < 16 ? p.k_scale : p.v_scale;
@@ -411,8 +454,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     for (int i = 0; i < C::VI; ++i) {
       const int cv = (w * C::VI + i) * 64 + lane;
       const int pos = min(tb + cv * 16 / C::ROW, L - 1);
-      dev::dma16(p.v + row_of(pos, first, e0, e1) * C::ROW + (cv * 16) % C::ROW,
-                 st + C::K_T + (w * C::VI + i) * 1024);
+      const int chunk = C::TRV ? (cv % C::CPR) ^ (2 * ((cv / C::CPR) % 8)) : cv % C::CPR;
+      dev::dma16(p.v + row_of(pos, first, e0, e1) * C::ROW + chunk * 16, st + C::K_T + (w * C::VI + i) * 1024);
     }
     if constexpr (FP8) {
       // the first wave of each M-block group stages its 16 k and 16 v scales
@@ -424,6 +467,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
   };
 
+  // transposing V reads: lane 4 r + q of 16-lane group g supplies tile row
+  // 4 g + r (+ 32 pp + 16 h, at the immediate offset), d 16 e + 4 q .. + 3,
+  // whose 32-byte pair e sits at pair slot e ^ ((4 g + r) mod 8)
+  uint32_t trv_off[8];
+  if constexpr (C::TRV) {
+    const int tr_r = n >> 2, tr_q = n & 3;
+    const int tr_x = (4 * g + tr_r) % 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      trv_off[e] = (uint32_t)(C::K_T + (4 * g + tr_r) * C::ROW + 32 * (e ^ tr_x) + 8 * tr_q);
+  }
   float m[C::NB], l[C::NB];
   f32x4 acc[C::NB][C::DB];
 #pragma unroll
@@ -580,19 +634,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
     __builtin_amdgcn_s_setprio(1);
     // O^T += V^T . P
-    const uint32_t av = sb + C::K_T + 4 * g * C::ROW + n * C::VR;
-    dev::static_for<0, C::PS>([&](auto ppc) {
-      constexpr int pp = decltype(ppc)::value;
-      VPieces<C, pp> vp;
-      read_v<C, pp>(vp, av);
+    if constexpr (C::TRV) {
+      // d-block e, k slots 8 g + j: tokens 32 pp + 16 (j / 4) + 4 g + j mod 4
+      // (the P operand's order); the two transposing reads of a block give
+      // tokens 32 pp + 4 g .. + 3 and 32 pp + 16 + 4 g .. + 3 of d 16 e + n
+      static_assert(C::DB == 8, "eight d-blocks");
+      uint32_t ab[8];
 #pragma unroll
-      for (int e = 0; e < C::DB; ++e) {
-        const bf16x8 va = v_operand<FP8>(vp, e);
+      for (int e = 0; e < 8; ++e) ab[e] = sb + trv_off[e];
+      dev::static_for<0, C::PS>([&](auto ppc) {
+        constexpr int pp = decltype(ppc)::value;
+        u32x2 t0[8], t1[8];
+        lds_tr8<32 * pp * C::ROW, false>(t0, ab);
+        lds_tr8<(32 * pp + 16) * C::ROW, true>(t1, ab);
 #pragma unroll
-        for (int bb = 0; bb < C::NB; ++bb)
-          acc[bb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop[bb][pp], acc[bb][e], 0, 0, 0);
-      }
-    });
+        for (int e = 0; e < 8; ++e) {
+          const u32x4 vw = {t0[e][0], t0[e][1], t1[e][0], t1[e][1]};
+          const bf16x8 va = __builtin_bit_cast(bf16x8, vw);
+#pragma unroll
+          for (int bb = 0; bb < C::NB; ++bb)
+            acc[bb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop[bb][pp], acc[bb][e], 0, 0, 0);
+        }
+      });
+    } else {
+      const uint32_t av = sb + C::K_T + 4 * g * C::ROW + n * C::VR;
+      dev::static_for<0, C::PS>([&](auto ppc) {
+        constexpr int pp = decltype(ppc)::value;
+        VPieces<C, pp> vp;
+        read_v<C, pp>(vp, av);
+#pragma unroll
+        for (int e = 0; e < C::DB; ++e) {
+          const bf16x8 va = v_operand<FP8>(vp, e);
+#pragma unroll
+          for (int bb = 0; bb < C::NB; ++bb)
+            acc[bb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop[bb][pp], acc[bb][e], 0, 0, 0);
+        }
+      });
+    }
     __builtin_amdgcn_s_setprio(0);
   };
   // tiles entirely below every column's limit, then the rest
@@ -611,14 +689,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     lt += __shfl_xor(lt, 32);
     if (orow[bb] < 0) continue;
     float* o = p.out + orow[bb] * D;
+    if constexpr (C::TRV) {
+      // lane (g, n) holds d 16 e + 4 g + j
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float r[C::DB];
+      for (int e = 0; e < C::DB; ++e) {
+        float r[4];
 #pragma unroll
-      for (int e = 0; e < C::DB; ++e) r[e] = poisoned ? nan : (lt != 0.0f ? acc[bb][e][j] / lt : 0.0f);
+        for (int j = 0; j < 4; ++j) r[j] = poisoned ? nan : (lt != 0.0f ? acc[bb][e][j] / lt : 0.0f);
+        *reinterpret_cast<f32x4*>(o + 16 * e + 4 * g) = f32x4{r[0], r[1], r[2], r[3]};
+      }
+    } else {
+      // lane (g, n) holds d (4 g + j) DB + e
 #pragma unroll
-      for (int e = 0; e < C::DB; e += 4)
-        *reinterpret_cast<f32x4*>(o + (4 * g + j) * C::DB + e) = f32x4{r[e], r[e + 1], r[e + 2], r[e + 3]};
+      for (int j = 0; j < 4; ++j) {
+        float r[C::DB];
+#pragma unroll
+        for (int e = 0; e < C::DB; ++e) r[e] = poisoned ? nan : (lt != 0.0f ? acc[bb][e][j] / lt : 0.0f);
+#pragma unroll
+        for (int e = 0; e < C::DB; e += 4)
+          *reinterpret_cast<f32x4*>(o + (4 * g + j) * C::DB + e) = f32x4{r[e], r[e + 1], r[e + 2], r[e + 3]};
+      }
     }
     if (p.lse != nullptr && g == 0)
       p.lse[orow[bb]] = poisoned ? nan : (lt != 0.0f ? (m[bb] + log2f(lt)) * dev::kLn2 : -__builtin_inff());

@@ -288,6 +288,12 @@ __device__ __forceinline__ bf16x8 v_operand(const VP& v, int e) {
 // in each row): gfx950's row swaps (permlane16 pairs rows 0-1 and 2-3,
 // permlane32 the two halves; with both operands x, the two results of a
 // lane are its own value and its partner's), plain VALU, no LDS trip.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ float max_rows(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
@@ -567,11 +573,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     bf16x8 pop[C::NB][C::PS];
 #pragma unroll
     for (int bb = 0; bb < C::NB; ++bb) {
+      // fp8: scores scaled here (the k scale varies per token); bf16: raw
+      // scores, the scale (positive) applied to their maximum and inside the
+      // exponent's fma
       float x[C::MB][4];
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) x[mb][j] = S[mb][bb][j] * (FP8 ? ksc[mb][j] : p.qk_scale_log2);
+        for (int j = 0; j < 4; ++j) x[mb][j] = FP8 ? S[mb][bb][j] * ksc[mb][j] : S[mb][bb][j];
       if constexpr (MASKED) {
         // only tiles that reach past some column's limit: token
         // tb + 16 mb + 4 r + j is visible iff 16 mb + j < rel
@@ -583,10 +592,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             if (16 * mb + j >= rel) x[mb][j] = -__builtin_inff();
       }
       float mx = -__builtin_inff();
+      if constexpr (FP8) {
 #pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb)
-        mx = fmaxf(fmaxf(mx, fmaxf(x[mb][0], x[mb][1])), fmaxf(x[mb][2], x[mb][3]));
+        for (int mb = 0; mb < C::MB; ++mb)
+          mx = fmaxf(fmaxf(mx, fmaxf(x[mb][0], x[mb][1])), fmaxf(x[mb][2], x[mb][3]));
+      } else {
+        // v_max3 on the raw MFMA results (fmaxf would first canonicalise
+        // each); it skips quiet NaNs as fmaxf does
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb) mx = max3(max3(mx, x[mb][0], x[mb][1]), x[mb][2], x[mb][3]);
+      }
       mx = max_rows(mx);
+      if constexpr (!FP8) mx *= p.qk_scale_log2;
       // the running max moves only when a column's max exceeds it by more
       // than 8 in the exponent (or it is still -inf): every weight stays
       // below 2^8, and since numerator and denominator are taken against
@@ -610,7 +627,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          x[mb][j] = __builtin_amdgcn_exp2f(x[mb][j] - m_ref);
+          x[mb][j] = __builtin_amdgcn_exp2f(FP8 ? x[mb][j] - m_ref : fmaf(x[mb][j], p.qk_scale_log2, -m_ref));
           sum += x[mb][j];
         }
       l[bb] += sum;
@@ -691,11 +708,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     float* o = p.out + orow[bb] * D;
     if constexpr (C::TRV) {
       // lane (g, n) holds d 16 e + 4 g + j
+      const float inv = lt != 0.0f ? 1.0f / lt : 0.0f;
 #pragma unroll
       for (int e = 0; e < C::DB; ++e) {
         float r[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) r[j] = poisoned ? nan : (lt != 0.0f ? acc[bb][e][j] / lt : 0.0f);
+        for (int j = 0; j < 4; ++j) r[j] = poisoned ? nan : acc[bb][e][j] * inv;
         *reinterpret_cast<f32x4*>(o + 16 * e + 4 * g) = f32x4{r[0], r[1], r[2], r[3]};
       }
     } else {

@@ -409,12 +409,16 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def time_prefill(pk, flush, dev, reps=20):
-    """Ragged paged prefill (pdattn_prefill, one launch per call; the tile
-    map is built once per batch on the host, outside the timing): the three
-    prefill workloads with bf16 pools, and the ragged batch with fp8 pools.
-    Caches flushed before every call. TFLOP/s = algorithmic flops (4 d per
-    (query row, head, visible position)) / mean call time, against the dense
-    bf16 MFMA peak (both products run on bf16 MFMA; fp8 codes are widened)."""
+    """Ragged paged prefill, one launch per call (tile maps built once per
+    batch on the host, outside the timing): the three prefill workloads with
+    bf16 pools, and the ragged batch with fp8 pools. Each through the split
+    call (pdattn_prefill_split_tiles on this device's slot count, which cuts
+    long tiles where its schedule simulation says the grid ends sooner, then
+    pdattn_prefill_split), and through the unsplit call (pdattn_prefill,
+    longest tiles first) beside it. Caches
+    flushed before every call. TFLOP/s = algorithmic flops (4 d per (query
+    row, head, visible position)) / mean call time, against the dense bf16
+    MFMA peak (both products run on bf16 MFMA; fp8 codes are widened)."""
     import torch
     import synth
     res = {}
@@ -428,35 +432,48 @@ def time_prefill(pk, flush, dev, reps=20):
         rt = pk.prefill_rows_per_tile(prob)
         tb, ti = pk.prefill_tiles(inp["qo_indptr"], rt, context_lens_host=inp["context_lens"])
         tb, ti = tb.to(dev), ti.to(dev)
+        st = pk.prefill_split_tiles(prob, inp["qo_indptr"], inp["context_lens"], slots=0)
+        sb, si, sk = st.tile_batch.to(dev), st.tile_index.to(dev), st.tile_kv.to(dev)
+        ws = pk.prefill_split_workspace(st, dev)
         out = torch.empty(d["q"].shape, dtype=torch.float32, device=dev)
         lse = torch.empty(d["q"].shape[:2], dtype=torch.float32, device=dev)
 
-        def call():
+        def plain():
             pk.prefill(prob, d["q"], d["qo_indptr"], tb, ti, d["k_pages"], d["v_pages"], d["k_scale"],
                        d["v_scale"], d["block_table"], d["context_lens"], out, lse)
-        for _ in range(3):
-            call()
-        ts = []
-        for i in range(reps):
-            flush.fill_(i & 0xFF)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            call()
-            b.record()
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b) * 1e3)
-        us = statistics.fmean(ts)
+
+        def split():
+            pk.prefill_split(prob, d["q"], d["qo_indptr"], sb, si, sk, st.num_slots, ws, d["k_pages"], d["v_pages"],
+                             d["k_scale"], d["v_scale"], d["block_table"], d["context_lens"], out, lse)
+
+        def timed(call):
+            for _ in range(3):
+                call()
+            ts = []
+            for i in range(reps):
+                flush.fill_(i & 0xFF)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                call()
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b) * 1e3)
+            return statistics.fmean(ts)
+        us_plain = timed(plain)
+        us = timed(split)
         flops = synth.prefill_flops(inp["q_lens"], inp["context_lens"], prob.num_q_heads, prob.head_dim)
         tf = flops / (us * 1e-6) / 1e12
         res[f"{name}_{kv}"] = {
             "q_rows": int(inp["q_lens"].sum()), "q_lens": inp["q_lens"].tolist(),
             "context_lens": inp["context_lens"].tolist(), "tiles": int(tb.numel()), "rows_per_tile": rt,
-            "workgroups": int(tb.numel()) * prob.num_kv_heads, "flops": flops, "us_per_call": round(us, 2),
+            "workgroups": st.num_tiles * prob.num_kv_heads, "flops": flops, "us_per_call": round(us, 2),
             "tflops": round(tf, 1), "roofline": {"bound": "mfma", "achieved": round(tf, 1),
                                                  "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                                  "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)},
+            "split": {"entries": st.num_tiles, "slots": st.num_slots, "workspace_bytes": st.workspace_bytes},
+            "unsplit_us_per_call": round(us_plain, 2),
             "outputs_finite": bool(torch.isfinite(out).all())}
-        del d, out, lse, inp, src
+        del d, out, lse, inp, src, ws
     return res
 
 

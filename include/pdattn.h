@@ -416,6 +416,92 @@ PDATTN_API pdattn_status pdattn_prefill(const pdattn_problem* problem, int32_t c
                                         float* lse, void* stream);
 
 /*
+ * Split-KV prefill. A query tile reads its context positions in order, one
+ * kernel tile after another, so a grid whose tiles differ much in length
+ * (one long causal prompt: the last tile of 32 rows reads 2048 positions,
+ * the first 32) runs as long as its longest tile. Splitting the K/V range
+ * when the grid cannot fill the machine is the flash-decoding remedy,
+ * applied to fused attention too (OASR "Kernel Layer", section "Fused
+ * attention", where the number of splits depends only on the shape and the
+ * device; FlashQuant wiki "CUDA Kernels", paged_decode.cu and
+ * split_k_reduce.cu, for the per-split (m, l, acc) states and their
+ * log-sum-exp merge). Here a long tile is cut into parts over consecutive
+ * position ranges; each part is one workgroup per kv head, which keeps its
+ * unnormalised state in a record of the caller's workspace, and the last
+ * part of a tile to finish merges the records in part order (the result does
+ * not depend on which part finished last) and writes the rows. The outputs
+ * are those of pdattn_prefill up to rounding.
+ */
+
+/*
+ * Build the split tile map on the host. problem: as for pdattn_prefill
+ * (batch = number of requests). qo_indptr: host int32 [batch + 1],
+ * non-decreasing from >= 0; context_lens: host int32 [batch], each within
+ * the block table (PDATTN_ERR_INVALID_ARGUMENT otherwise). slots: the
+ * workgroups the device runs at once, 0 for the current device's (compute
+ * units x resident prefill workgroups per unit; PDATTN_ERR_DEVICE without a
+ * device).
+ *
+ * A tile reads ceil(reach / T) kernel tiles (reach as for
+ * PDATTN_TILES_LONGEST_FIRST; T = 64 positions, 32 at d 256). For a cap c,
+ * a tile of more than c kernel tiles is cut into min(ceil(count / c), 16,
+ * floor(units / m)) parts, units = ceil(reach / 64) and m = the 64-position
+ * units of 4 kernel tiles: part q covers units [q units / parts, (q + 1)
+ * units / parts) (integer division), times 64, the last ending at reach.
+ * An entry's cost, in quarter kernel tiles: 4 per tile read, plus 1 per tile
+ * at or past the first row's causal limit, plus 20, plus 12 for a part;
+ * entries are listed by cost, most first (ties in request, tile, part
+ * order). The device starts workgroups in grid order as slots free up, so
+ * the planner simulates that list schedule (each entry's num_kv_heads
+ * workgroups in turn, each on the slot free first) for no cut and for
+ * c = ceil(k x longest / 16), k = 15 down to 3 (at least 4), and keeps the
+ * first that ends soonest. Outputs, for entry t < *num_tiles:
+ *   tile_batch[t], tile_index[t]  the query tile, as in pdattn_prefill_tiles
+ *   tile_kv[4t + 0], [4t + 1]     its positions [first, end)
+ *   tile_kv[4t + 2]               -1 for a whole tile; for a part, the first
+ *                                 of the tile's consecutive workspace slots
+ *   tile_kv[4t + 3]               part | parts << 16 (1 << 16 when whole)
+ * *num_slots receives the slots the parts use and *workspace_bytes the
+ * workspace pdattn_prefill_split needs for them (0 when nothing is cut).
+ * With any of tile_batch, tile_index, tile_kv NULL only the three counts
+ * are written; else tile_batch and tile_index hold `capacity` entries and
+ * tile_kv 4 * capacity, capacity >= *num_tiles. Host memory only.
+ */
+PDATTN_API pdattn_status pdattn_prefill_split_tiles(const pdattn_problem* problem, const int32_t* qo_indptr,
+                                                    const int32_t* context_lens, int32_t causal, int32_t slots,
+                                                    int32_t* tile_batch, int32_t* tile_index, int32_t* tile_kv,
+                                                    int32_t capacity, int32_t* num_tiles, int32_t* num_slots,
+                                                    uint64_t* workspace_bytes);
+
+/*
+ * Enqueue the split-KV prefill on `stream`: num_tiles x num_kv_heads
+ * workgroups. pdattn_prefill's arguments, plus
+ *   tile_kv      int32 [num_tiles][4], device, 16-byte aligned: from
+ *                pdattn_prefill_split_tiles with the same problem and lengths
+ *   num_slots    that call's *num_slots (0: nothing cut, workspace unused)
+ *   workspace    device, 256-byte aligned, at least that call's
+ *                *workspace_bytes: num_slots x num_kv_heads 32-bit counters
+ *                (the region rounded up to 256 bytes), then as many part
+ *                records. The counters must be zero before the first call
+ *                that uses the workspace (e.g. hipMemset once after
+ *                allocation); each call leaves them zero. Calls that share a
+ *                workspace must not overlap (order them on one stream).
+ * A part entry whose slots lie outside num_slots makes its tile's rows NaN
+ * without touching the workspace (the tile's other parts then leave their
+ * counter nonzero: zero the workspace again before reusing it). Bad lengths
+ * and page entries poison rows as in pdattn_prefill, across all parts of a
+ * tile. Allocates nothing, never synchronises, graph-capturable; validated
+ * before launch.
+ */
+PDATTN_API pdattn_status pdattn_prefill_split(const pdattn_problem* problem, int32_t causal, const void* q,
+                                              const int32_t* qo_indptr, const int32_t* tile_batch,
+                                              const int32_t* tile_index, const int32_t* tile_kv, int32_t num_tiles,
+                                              int32_t num_slots, void* workspace, uint64_t workspace_bytes,
+                                              const void* k_pages, const void* v_pages, const float* k_scale,
+                                              const float* v_scale, const int32_t* block_table,
+                                              const int32_t* context_lens, float* out, float* lse, void* stream);
+
+/*
  * ---- TQ4 compressed KV cache (FlashQuant wiki "CUDA Kernels": compress.cu,
  * decompress.cu, fused_tq_attention.cu, paged_decode.cu, split_k_reduce.cu)
  *

@@ -16,7 +16,8 @@ __all__ = ["Problem", "Plan", "PdattnError", "plan", "decode", "reduce", "decode
            "workspace", "workspace_init",
            "paged_decode", "KV_BF16", "KV_FP8_E4M3", "PLAN_BALANCED", "library_path", "stream_read",
            "stream_read_sink", "kv_append", "APPEND_POW2_SCALES", "fp8_conversion_check", "merge", "LAYOUT_NHD", "LAYOUT_HND",
-           "pool_dims", "kv_kind", "KV_FP8_E4M3_INLINE", "prefill_rows_per_tile", "prefill_tiles", "prefill", "paged_prefill", "TILES_LONGEST_FIRST"]
+           "pool_dims", "kv_kind", "KV_FP8_E4M3_INLINE", "prefill_rows_per_tile", "prefill_tiles", "prefill", "paged_prefill", "TILES_LONGEST_FIRST",
+           "SplitTiles", "prefill_split_tiles", "prefill_split", "prefill_split_workspace"]
 
 KV_BF16 = 0
 KV_FP8_E4M3 = 1
@@ -104,6 +105,12 @@ _lib.pdattn_prefill_tiles.argtypes = [_P, _P, ctypes.c_int32, ctypes.c_int32, ct
 _lib.pdattn_prefill.restype = ctypes.c_int
 _lib.pdattn_prefill.argtypes = [ctypes.POINTER(Problem), ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P,
                                 _P, _P, _P, _P, _P, _P]
+_lib.pdattn_prefill_split_tiles.restype = ctypes.c_int
+_lib.pdattn_prefill_split_tiles.argtypes = [ctypes.POINTER(Problem), _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P,
+                                            _P, ctypes.c_int32, _P, _P, _P]
+_lib.pdattn_prefill_split.restype = ctypes.c_int
+_lib.pdattn_prefill_split.argtypes = [ctypes.POINTER(Problem), ctypes.c_int32, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                      ctypes.c_int32, _P, ctypes.c_uint64, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.pdattn_problem_size.restype = ctypes.c_uint64
 _lib.pdattn_plan_size.restype = ctypes.c_uint64
 
@@ -335,22 +342,84 @@ def prefill(problem: Problem, q, qo_indptr, tile_batch, tile_index, k_pages, v_p
                                _stream(stream)), "pdattn_prefill")
 
 
+class SplitTiles:
+    """``pdattn_prefill_split_tiles``'s outputs: CPU int32 tile_batch,
+    tile_index [num_tiles] and tile_kv [num_tiles, 4], the workspace slots
+    and bytes."""
+
+    def __init__(self, tile_batch, tile_index, tile_kv, num_slots, workspace_bytes):
+        self.tile_batch, self.tile_index, self.tile_kv = tile_batch, tile_index, tile_kv
+        self.num_slots, self.workspace_bytes = int(num_slots), int(workspace_bytes)
+
+    @property
+    def num_tiles(self):
+        return int(self.tile_batch.numel())
+
+
+def prefill_split_tiles(problem: Problem, qo_indptr_host, context_lens_host, *, causal=True, slots=0) -> SplitTiles:
+    """``pdattn_prefill_split_tiles`` on host int32 arrays (slots 0: the
+    current device's resident prefill workgroups)."""
+    ptr = torch.as_tensor(qo_indptr_host, dtype=torch.int32).contiguous().cpu()
+    lens = torch.as_tensor(context_lens_host, dtype=torch.int32).contiguous().cpu()
+    nt, ns, wb = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_uint64(0)
+    args = (ctypes.byref(problem), _ptr(ptr), _ptr(lens), int(bool(causal)), int(slots))
+    counts = (ctypes.byref(nt), ctypes.byref(ns), ctypes.byref(wb))
+    _check(_lib.pdattn_prefill_split_tiles(*args, None, None, None, 0, *counts), "pdattn_prefill_split_tiles")
+    cap = max(nt.value, 1)
+    tb = torch.empty(cap, dtype=torch.int32)
+    ti = torch.empty(cap, dtype=torch.int32)
+    tk = torch.empty(cap, 4, dtype=torch.int32)
+    _check(_lib.pdattn_prefill_split_tiles(*args, _ptr(tb), _ptr(ti), _ptr(tk), cap, *counts),
+           "pdattn_prefill_split_tiles")
+    n = nt.value
+    return SplitTiles(tb[:n], ti[:n], tk[:n], ns.value, wb.value)
+
+
+def prefill_split(problem: Problem, q, qo_indptr, tile_batch, tile_index, tile_kv, num_slots, workspace, k_pages,
+                  v_pages, k_scale, v_scale, block_table, context_lens, out, lse=None, *, causal=True, stream=None):
+    """``pdattn_prefill_split``: every tensor on the device; the map from
+    ``prefill_split_tiles``; workspace a zero-initialised uint8 tensor of at
+    least its workspace_bytes (None when num_slots is 0)."""
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.pdattn_prefill_split(ctypes.byref(problem), int(bool(causal)), _ptr(q), _ptr(qo_indptr),
+                                     _ptr(tile_batch), _ptr(tile_index), _ptr(tile_kv), int(tile_batch.numel()),
+                                     int(num_slots), _ptr(workspace), wbytes, _ptr(k_pages), _ptr(v_pages),
+                                     _ptr(k_scale), _ptr(v_scale), _ptr(block_table), _ptr(context_lens), _ptr(out),
+                                     _ptr(lse), _stream(stream)), "pdattn_prefill_split")
+
+
+def prefill_split_workspace(tiles: SplitTiles, device):
+    """A zeroed workspace for ``prefill_split`` (None when nothing is split)."""
+    if tiles.num_slots == 0:
+        return None
+    return torch.zeros(tiles.workspace_bytes, dtype=torch.uint8, device=device)
+
+
 def paged_prefill(q, qo_indptr, k_pages, v_pages, block_table, context_lens, *, qo_indptr_host=None,
                   context_lens_host=None, k_scale=None, v_scale=None, scale=None, causal=True, layout=LAYOUT_NHD,
-                  longest_first=True, return_lse=True):
+                  longest_first=True, return_lse=True, split=False, slots=0):
     """Build the tile map, allocate (torch) and run one prefill; returns
     (out fp32 [total_q, Hq, d], lse fp32 [total_q, Hq]).
 
     q: bf16 [total_q, Hq, d] packed by qo_indptr (int32 [B + 1], device);
-    pools, block_table and context_lens as for ``paged_decode`` (device)."""
+    pools, block_table and context_lens as for ``paged_decode`` (device).
+    split: the split-KV map and kernel (slots as for
+    ``prefill_split_tiles``)."""
     prob = _prefill_problem(q, k_pages, block_table, layout, scale)
     ptr_h = qo_indptr.cpu() if qo_indptr_host is None else qo_indptr_host
     lens_h = context_lens.cpu() if context_lens_host is None else context_lens_host
-    tb, ti = prefill_tiles(ptr_h, prefill_rows_per_tile(prob), context_lens_host=lens_h, causal=causal,
-                           longest_first=longest_first)
     dev = q.device
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev) if return_lse else None
+    if split:
+        st = prefill_split_tiles(prob, ptr_h, lens_h, causal=causal, slots=slots)
+        ws = prefill_split_workspace(st, dev)
+        prefill_split(prob, q, qo_indptr, st.tile_batch.to(dev), st.tile_index.to(dev), st.tile_kv.to(dev),
+                      st.num_slots, ws, k_pages, v_pages, k_scale, v_scale, block_table, context_lens, out, lse,
+                      causal=causal)
+        return out, lse
+    tb, ti = prefill_tiles(ptr_h, prefill_rows_per_tile(prob), context_lens_host=lens_h, causal=causal,
+                           longest_first=longest_first)
     prefill(prob, q, qo_indptr, tb.to(dev), ti.to(dev), k_pages, v_pages, k_scale, v_scale, block_table,
             context_lens, out, lse, causal=causal)
     return out, lse

@@ -13,6 +13,8 @@
 #include <cstring>
 #include <algorithm>
 #include <vector>
+#include <queue>
+#include <limits>
 
 #include "kernels.h"
 #include "append.h"
@@ -732,27 +734,50 @@ PDATTN_API pdattn_status pdattn_prefill_tiles(const int32_t* qo_indptr, const in
   return PDATTN_OK;
 }
 
-PDATTN_API pdattn_status pdattn_prefill(const pdattn_problem* problem, int32_t causal, const void* q,
-                                        const int32_t* qo_indptr, const int32_t* tile_batch,
-                                        const int32_t* tile_index, int32_t num_tiles, const void* k_pages,
-                                        const void* v_pages, const float* k_scale, const float* v_scale,
-                                        const int32_t* block_table, const int32_t* context_lens, float* out,
-                                        float* lse, void* stream) {
-  g_last_error[0] = '\0';
+namespace {
+
+// Fewest kernel tiles (K/V tiles) of one part of a split tile, and most parts.
+constexpr int64_t kMinPartSteps = 4;
+constexpr int64_t kMaxParts = 16;
+// Positions per unit of a part boundary (a multiple of every kernel tile).
+constexpr int64_t kPartUnit = 64;
+
+uint64_t prefill_workspace_bytes(const pdattn_problem& problem, int64_t num_slots) {
+  const uint64_t records = (uint64_t)num_slots * (uint64_t)problem.num_kv_heads;
+  const uint64_t ctr = (records * 4 + 255) / 256 * 256;
+  return ctr + records * (uint64_t)pdattn::prefill_record_floats(problem.head_dim) * 4;
+}
+
+pdattn_status prefill_launch(const pdattn_problem* problem, int32_t causal, const void* q, const int32_t* qo_indptr,
+                             const int32_t* tile_batch, const int32_t* tile_index, const int32_t* tile_kv,
+                             int32_t num_tiles, int32_t num_slots, void* workspace, uint64_t workspace_bytes,
+                             const void* k_pages, const void* v_pages, const float* k_scale, const float* v_scale,
+                             const int32_t* block_table, const int32_t* context_lens, float* out, float* lse,
+                             void* stream) {
   pdattn_status st = check_problem(problem);
   if (st != PDATTN_OK) return st;
   if (causal != 0 && causal != 1) return fail(PDATTN_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
   if (num_tiles < 0) return fail(PDATTN_ERR_INVALID_ARGUMENT, "num_tiles %d is negative", num_tiles);
   if ((int64_t)num_tiles * problem->num_kv_heads > INT32_MAX)
     return fail(PDATTN_ERR_UNSUPPORTED, "num_tiles * num_kv_heads exceeds 2^31 - 1");
+  if (num_slots < 0) return fail(PDATTN_ERR_INVALID_ARGUMENT, "num_slots %d is negative", num_slots);
+  if (num_slots > 0) {
+    if (!workspace) return fail(PDATTN_ERR_WORKSPACE, "%d slots need a workspace", num_slots);
+    if (!aligned(workspace, 256))
+      return fail(PDATTN_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    const uint64_t need = prefill_workspace_bytes(*problem, num_slots);
+    if (workspace_bytes < need)
+      return fail(PDATTN_ERR_WORKSPACE, "workspace of %llu bytes; %d slots need %llu",
+                  (unsigned long long)workspace_bytes, num_slots, (unsigned long long)need);
+  }
   if (num_tiles == 0 || problem->batch == 0) return PDATTN_OK;
   if (!q || !qo_indptr || !tile_batch || !tile_index || !k_pages || !v_pages || !block_table || !context_lens || !out)
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
   if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(out, 16))
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "q, k_pages, v_pages and out must be 16-byte aligned");
   if (!aligned(qo_indptr, 4) || !aligned(tile_batch, 4) || !aligned(tile_index, 4) || !aligned(block_table, 4) ||
-      !aligned(context_lens, 4) || (lse && !aligned(lse, 4)))
-    return fail(PDATTN_ERR_INVALID_ARGUMENT, "index arrays and lse must be 4-byte aligned");
+      !aligned(context_lens, 4) || (lse && !aligned(lse, 4)) || (tile_kv && !aligned(tile_kv, 16)))
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "index arrays and lse must be 4-byte aligned, tile_kv 16-byte");
   if (problem->kv_dtype == PDATTN_KV_FP8_E4M3_INLINE)
     return fail(PDATTN_ERR_UNSUPPORTED, "the prefill reads bf16 or separate-scale fp8 pools");
   st = check_scales(*problem, k_scale, v_scale);
@@ -786,10 +811,197 @@ PDATTN_API pdattn_status pdattn_prefill(const pdattn_problem* problem, int32_t c
   p.causal = causal;
   const float scale = problem->scale > 0.0f ? problem->scale : 1.0f / std::sqrt((float)problem->head_dim);
   p.qk_scale_log2 = scale * 1.44269504088896340736f;
+  p.tile_kv = tile_kv;
+  if (num_slots > 0) {
+    const uint64_t records = (uint64_t)num_slots * (uint64_t)problem->num_kv_heads;
+    p.part_ctr = static_cast<uint32_t*>(workspace);
+    p.part_rec = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + (records * 4 + 255) / 256 * 256);
+    p.num_slots = num_slots;
+  }
   const uint32_t grid = (uint32_t)((int64_t)num_tiles * problem->num_kv_heads);
   hipError_t e = pdattn::launch_prefill(p, problem->head_dim, fp8, grid, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "prefill kernel launch: %s", hipGetErrorString(e));
   return PDATTN_OK;
+}
+
+}  // namespace
+
+PDATTN_API pdattn_status pdattn_prefill(const pdattn_problem* problem, int32_t causal, const void* q,
+                                        const int32_t* qo_indptr, const int32_t* tile_batch,
+                                        const int32_t* tile_index, int32_t num_tiles, const void* k_pages,
+                                        const void* v_pages, const float* k_scale, const float* v_scale,
+                                        const int32_t* block_table, const int32_t* context_lens, float* out,
+                                        float* lse, void* stream) {
+  g_last_error[0] = '\0';
+  return prefill_launch(problem, causal, q, qo_indptr, tile_batch, tile_index, nullptr, num_tiles, 0, nullptr, 0,
+                        k_pages, v_pages, k_scale, v_scale, block_table, context_lens, out, lse, stream);
+}
+
+PDATTN_API pdattn_status pdattn_prefill_split_tiles(const pdattn_problem* problem, const int32_t* qo_indptr,
+                                                    const int32_t* context_lens, int32_t causal, int32_t slots,
+                                                    int32_t* tile_batch, int32_t* tile_index, int32_t* tile_kv,
+                                                    int32_t capacity, int32_t* num_tiles, int32_t* num_slots,
+                                                    uint64_t* workspace_bytes) {
+  g_last_error[0] = '\0';
+  if (!num_tiles || !num_slots || !workspace_bytes)
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "num_tiles, num_slots and workspace_bytes must not be NULL");
+  *num_tiles = 0;
+  *num_slots = 0;
+  *workspace_bytes = 0;
+  pdattn_status st = check_problem(problem);
+  if (st != PDATTN_OK) return st;
+  if (causal != 0 && causal != 1) return fail(PDATTN_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  if (slots < 0) return fail(PDATTN_ERR_INVALID_ARGUMENT, "slots %d is negative", slots);
+  const int batch = problem->batch;
+  if (batch > 0 && (!qo_indptr || !context_lens))
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "qo_indptr and context_lens (host arrays) are required");
+  if (slots == 0) {
+    int dev = 0, num_cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || num_cus <= 0)
+      return fail(PDATTN_ERR_DEVICE, "cannot query the compute-unit count: %s", hipGetErrorString(e));
+    const int per_cu = pdattn::prefill_wgs_per_cu(problem->head_dim, problem->kv_dtype == PDATTN_KV_FP8_E4M3);
+    slots = num_cus * (per_cu > 0 ? per_cu : 1);
+  }
+  const int64_t H = problem->num_kv_heads;
+  const int64_t rows = pdattn::prefill_columns(problem->head_dim) / heads_per_kv(*problem);
+  const int64_t nt = pdattn::prefill_kv_tile(problem->head_dim);
+  const int64_t min_units = ceil_div(kMinPartSteps * nt, kPartUnit);  // smallest part, in 64-position units
+
+  struct Tile {
+    int64_t reach, open, steps;  // positions read; positions below every row's limit; kernel tiles
+    int32_t b, j;
+  };
+  struct Piece {
+    int64_t cost;
+    int32_t b, j, kv0, kv1, base, pq;
+  };
+  // Costs in quarter kernel tiles: 4 per tile read, 1 more per tile at or
+  // past the first row's causal limit (the masked loop), 20 per workgroup
+  // for its start and end (the dependent loads before the first tile, the
+  // output stores), 12 more per part for its record, counter and merge.
+  auto piece_cost = [&](const Tile& t, int64_t kv0, int64_t kv1, bool part) {
+    const int64_t i0 = kv0 / nt, i1 = ceil_div(kv1, nt);
+    const int64_t masked = std::max<int64_t>(0, i1 - std::max(i0, t.open / nt));
+    return 4 * (i1 - i0) + masked + 20 + (part ? 12 : 0);
+  };
+  std::vector<Tile> tiles;
+  int64_t max_steps = 0;
+  try {
+    for (int b = 0; b < batch; ++b) {
+      const int64_t n = (int64_t)qo_indptr[b + 1] - qo_indptr[b];
+      if (qo_indptr[b] < 0 || n < 0)
+        return fail(PDATTN_ERR_INVALID_ARGUMENT, "qo_indptr must start at >= 0 and not decrease (request %d)", b);
+      const int64_t L = context_lens[b];
+      if (L < 0 || L > (int64_t)problem->max_pages_per_seq * problem->page_size)
+        return fail(PDATTN_ERR_INVALID_ARGUMENT, "context_lens[%d] = %lld outside the block table", b, (long long)L);
+      for (int64_t j = 0; j < ceil_div(n, rows); ++j) {
+        const int64_t last = std::min<int64_t>((j + 1) * rows, n) - 1;
+        int64_t reach = causal ? L - n + last + 1 : L;
+        reach = reach < 0 ? 0 : (reach > L ? L : reach);
+        int64_t open = causal ? L - n + j * rows + 1 : L;
+        open = open < 0 ? 0 : (open > L ? L : open);
+        tiles.push_back(Tile{reach, open, ceil_div(reach, nt), b, (int32_t)j});
+        max_steps = std::max(max_steps, tiles.back().steps);
+        if ((int64_t)tiles.size() > INT32_MAX) return fail(PDATTN_ERR_UNSUPPORTED, "more than 2^31 - 1 query tiles");
+      }
+    }
+  } catch (const std::bad_alloc&) {
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "out of host memory for the tile map");
+  }
+
+  // The device starts the workgroups in grid order as slots free up (each
+  // entry's kv heads one after another): a list schedule. A tile of more
+  // than `cap` kernel tiles is cut into ceil(steps / cap) parts (at most
+  // 16, each of at least kMinPartSteps tiles, at multiples of 64
+  // positions, as even as those allow); entries are listed by cost, most
+  // first. The planner simulates that schedule on `slots` slots for no cut
+  // and for caps of k / 16 of the longest tile (k = 3 .. 15), and keeps
+  // the cap that ends first (the earlier candidate on a tie).
+  std::vector<Piece> pieces, trial;
+  int64_t slot_count = 0, best = -1;
+  auto cut = [&](int64_t cap, std::vector<Piece>& out, int64_t& nslots) {
+    out.clear();
+    nslots = 0;
+    for (const Tile& t : tiles) {
+      const int64_t units = ceil_div(t.reach, kPartUnit);
+      const int64_t parts =
+          t.steps > cap ? std::min<int64_t>({ceil_div(t.steps, cap), kMaxParts, units / min_units}) : 1;
+      if (parts < 2) {
+        out.push_back(Piece{piece_cost(t, 0, t.reach, false), t.b, t.j, 0, (int32_t)t.reach, -1, 1 << 16});
+        continue;
+      }
+      for (int64_t q = 0; q < parts; ++q) {
+        const int64_t kv0 = q * units / parts * kPartUnit;
+        const int64_t kv1 = q + 1 == parts ? t.reach : (q + 1) * units / parts * kPartUnit;
+        out.push_back(Piece{piece_cost(t, kv0, kv1, true), t.b, t.j, (int32_t)kv0, (int32_t)kv1,
+                            (int32_t)nslots, (int32_t)(q | (parts << 16))});
+      }
+      nslots += parts;
+    }
+    std::stable_sort(out.begin(), out.end(), [](const Piece& x, const Piece& y) { return x.cost > y.cost; });
+  };
+  auto makespan = [&](const std::vector<Piece>& list) {
+    std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
+    for (int64_t i = 0; i < std::min<int64_t>(slots, (int64_t)list.size() * H); ++i) free_at.push(0);
+    int64_t end = 0;
+    for (const Piece& it : list)
+      for (int64_t h = 0; h < H; ++h) {
+        const int64_t t = free_at.top() + it.cost;
+        free_at.pop();
+        free_at.push(t);
+        end = std::max(end, t);
+      }
+    return end;
+  };
+  try {
+    std::vector<int64_t> caps = {std::numeric_limits<int64_t>::max()};
+    for (int64_t k = 15; k >= 3; --k) caps.push_back(std::max<int64_t>(kMinPartSteps, ceil_div(max_steps * k, 16)));
+    for (int64_t cap : caps) {
+      int64_t nslots = 0;
+      cut(cap, trial, nslots);
+      if ((int64_t)trial.size() * H > INT32_MAX || nslots > INT32_MAX) continue;
+      const int64_t span = makespan(trial);
+      if (best < 0 || span < best) {
+        best = span;
+        pieces.swap(trial);
+        slot_count = nslots;
+      }
+    }
+  } catch (const std::bad_alloc&) {
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "out of host memory for the tile map");
+  }
+  if (!tiles.empty() && best < 0) return fail(PDATTN_ERR_UNSUPPORTED, "tiles * num_kv_heads exceeds 2^31 - 1");
+  *num_tiles = (int32_t)pieces.size();
+  *num_slots = (int32_t)slot_count;
+  *workspace_bytes = slot_count > 0 ? prefill_workspace_bytes(*problem, slot_count) : 0;
+  if (!tile_batch || !tile_index || !tile_kv) return PDATTN_OK;  // sizes only
+  if (capacity < (int64_t)pieces.size())
+    return fail(PDATTN_ERR_INVALID_ARGUMENT, "%zu entries do not fit in capacity %d", pieces.size(), capacity);
+  for (size_t i = 0; i < pieces.size(); ++i) {
+    tile_batch[i] = pieces[i].b;
+    tile_index[i] = pieces[i].j;
+    tile_kv[4 * i + 0] = pieces[i].kv0;
+    tile_kv[4 * i + 1] = pieces[i].kv1;
+    tile_kv[4 * i + 2] = pieces[i].base;
+    tile_kv[4 * i + 3] = pieces[i].pq;
+  }
+  return PDATTN_OK;
+}
+
+PDATTN_API pdattn_status pdattn_prefill_split(const pdattn_problem* problem, int32_t causal, const void* q,
+                                              const int32_t* qo_indptr, const int32_t* tile_batch,
+                                              const int32_t* tile_index, const int32_t* tile_kv, int32_t num_tiles,
+                                              int32_t num_slots, void* workspace, uint64_t workspace_bytes,
+                                              const void* k_pages, const void* v_pages, const float* k_scale,
+                                              const float* v_scale, const int32_t* block_table,
+                                              const int32_t* context_lens, float* out, float* lse, void* stream) {
+  g_last_error[0] = '\0';
+  if (num_tiles > 0 && !tile_kv) return fail(PDATTN_ERR_INVALID_ARGUMENT, "tile_kv is NULL");
+  return prefill_launch(problem, causal, q, qo_indptr, tile_batch, tile_index, tile_kv, num_tiles, num_slots,
+                        workspace, workspace_bytes, k_pages, v_pages, k_scale, v_scale, block_table, context_lens,
+                        out, lse, stream);
 }
 
 PDATTN_API uint64_t pdattn_stream_read_sink_words(int32_t num_cus) {

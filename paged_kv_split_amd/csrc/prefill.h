@@ -10,6 +10,11 @@ namespace pdattn {
 // (query row, head) columns one prefill workgroup computes: 4 waves of two
 // 16-column blocks (one block for head_dim 256).
 constexpr int prefill_columns(int head_dim) { return head_dim == 256 ? 64 : 128; }
+// Tokens of the kernel's K/V tiles.
+constexpr int prefill_kv_tile(int head_dim) { return head_dim == 256 ? 32 : 64; }
+// Floats of one part record of a split tile (per kv head): the unnormalised
+// accumulators of every column, then each column's (m, l).
+constexpr int64_t prefill_record_floats(int head_dim) { return (int64_t)prefill_columns(head_dim) * (head_dim + 2); }
 
 struct PrefillParams {
   const uint16_t* q;          // bf16 bits [total_q][Hq][D]
@@ -36,9 +41,16 @@ struct PrefillParams {
   int32_t head_stride;
   int32_t causal;
   float qk_scale_log2;        // softmax scale * log2(e)
+  // split tiles (null tile_kv: every tile whole)
+  const int32_t* tile_kv;     // [num_tiles][4]: first position, end position, first slot (-1: whole), part | parts << 16
+  float* part_rec;            // [num_slots][num_kv_heads][prefill_record_floats]
+  uint32_t* part_ctr;         // [num_slots][num_kv_heads]: parts finished (low 16 bits) and poisoned (high)
+  int32_t num_slots;
 };
 
 // grid: num_tiles * num_kv_heads workgroups of 256 threads.
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, bool fp8, uint32_t grid, hipStream_t stream);
+// Resident prefill workgroups per compute unit (0 when the runtime cannot say).
+int prefill_wgs_per_cu(int head_dim, bool fp8);
 
 }  // namespace pdattn

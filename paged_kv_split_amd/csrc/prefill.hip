@@ -71,6 +71,7 @@ struct Cfg {
   static constexpr bool TRV = !FP8 && D == 128;
   static constexpr int CPR = ROW / 16;                     // 16-byte chunks per row
   static_assert(COLS == prefill_columns(D), "columns");
+  static_assert(NT == prefill_kv_tile(D), "kv tile");
   static_assert(KI >= 1 && QK % KI == 0 && VI >= 1, "load split");
   static_assert(MB * QK == kWaves * KI, "K image");
 };
@@ -310,15 +311,116 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
 }
 
+// Part records cross workgroups on different XCDs. They are written and
+// read with device-scope (sc1) 16-byte buffer accesses, coherent at device
+// level without a write-back or invalidation of a whole L2; the writer's
+// stores complete before the counter update that publishes them.
+constexpr int kBufferWord3 = 0x00020000;  // word 3 of a raw buffer resource (gfx9 family)
+constexpr int kDeviceScope = 16;          // cache policy: sc1
+
+// One part of a split tile: store its record (the lane's accumulators in
+// its own layout, then per column m and the row-summed l), count the part
+// in, and return false unless it is the last to finish. The last one merges
+// every part's record in part order (its own from registers), so the result
+// does not depend on which part finished last, leaves the merged state in
+// acc, m, l, and resets the counter for the next call. A part that saw a bad
+// page poisons the tile through the counter's high half.
 template <int D, bool FP8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(const PrefillParams p) {
+__device__ __forceinline__ bool merge_parts(const PrefillParams& p, uint32_t& s_count,
+                                            f32x4 (&acc)[Cfg<D, FP8>::NB][Cfg<D, FP8>::DB],
+                                            float (&m)[Cfg<D, FP8>::NB], float (&l)[Cfg<D, FP8>::NB], bool& poisoned,
+                                            int slot0, int part, int parts, int kvh, int w, int lane) {
   using C = Cfg<D, FP8>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::STAGE];
+  constexpr long long RF = prefill_record_floats(D);
+  const int n = lane & 15, g = lane >> 4;
+  auto rec_of = [&](int q) {
+    return __builtin_amdgcn_make_buffer_rsrc(p.part_rec + ((long long)(slot0 + q) * p.num_kv_heads + kvh) * RF, 0,
+                                             (int)(RF * 4), kBufferWord3);
+  };
+  // byte offsets: accumulators [wave][block][d-block][lane][4], then
+  // [wave][block][column][m, l]
+  auto acc_off = [&](int bb, int e) { return (uint32_t)((((w * C::NB + bb) * C::DB + e) * 64 + lane) * 16); };
+  auto ml_off = [&](int bb) { return (uint32_t)((C::COLS * D + ((w * C::NB + bb) * 16 + n) * 2) * 4); };
+  {
+    const auto r = rec_of(part);
+#pragma unroll
+    for (int bb = 0; bb < C::NB; ++bb)
+#pragma unroll
+      for (int e = 0; e < C::DB; ++e)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[bb][e]), r, acc_off(bb, e), 0,
+                                               kDeviceScope);
+    if (g == 0) {
+#pragma unroll
+      for (int bb = 0; bb < C::NB; ++bb)
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(m[bb]), __float_as_uint(l[bb])}, r, ml_off(bb),
+                                              0, kDeviceScope);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  uint32_t* ctr = p.part_ctr + (long long)slot0 * p.num_kv_heads + kvh;
+  if (threadIdx.x == 0)
+    s_count = __hip_atomic_fetch_add(ctr, 1u + (poisoned ? 0x10000u : 0u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint32_t before = s_count;
+  if ((int)(before & 0xffffu) + 1 < parts) return false;
+  if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  poisoned = poisoned || (before >> 16) != 0;
+#pragma unroll
+  for (int bb = 0; bb < C::NB; ++bb) {
+    float M = m[bb];
+    for (int q = 0; q < parts; ++q) {
+      if (q == part) continue;
+      const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(rec_of(q), ml_off(bb), 0, kDeviceScope);
+      M = fmaxf(M, __uint_as_float(ml[0]));
+    }
+    // parts that saw nothing keep m = -inf, l = 0, acc = 0 and weigh 0
+    const float m_ref = M == -__builtin_inff() ? 0.0f : M;
+    f32x4 R[C::DB];
+#pragma unroll
+    for (int e = 0; e < C::DB; ++e) R[e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float L = 0.0f;
+    for (int q = 0; q < parts; ++q) {
+      float mq, lq;
+      f32x4 a[C::DB];
+      if (q == part) {
+        mq = m[bb];
+        lq = l[bb];
+#pragma unroll
+        for (int e = 0; e < C::DB; ++e) a[e] = acc[bb][e];
+      } else {
+        const auto r = rec_of(q);
+        const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(r, ml_off(bb), 0, kDeviceScope);
+        mq = __uint_as_float(ml[0]);
+        lq = __uint_as_float(ml[1]);
+#pragma unroll
+        for (int e = 0; e < C::DB; ++e)
+          a[e] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, acc_off(bb, e), 0, kDeviceScope));
+      }
+      const float sc = __builtin_amdgcn_exp2f(mq - m_ref);
+      L = fmaf(lq, sc, L);
+#pragma unroll
+      for (int e = 0; e < C::DB; ++e)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) R[e][j] = fmaf(a[e][j], sc, R[e][j]);
+    }
+#pragma unroll
+    for (int e = 0; e < C::DB; ++e) acc[bb][e] = R[e];
+    l[bb] = L;
+    m[bb] = M;
+  }
+  return true;
+}
+
+// One map entry (a whole query tile, or one part of a split one) for kv
+// head kvh, on the whole workgroup.
+template <int D, bool FP8>
+__device__ __forceinline__ void prefill_item(const PrefillParams& p, const int tile, const int kvh,
+                                             unsigned char (&smem)[2 * Cfg<D, FP8>::STAGE], uint32_t& s_count) {
+  using C = Cfg<D, FP8>;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, n = lane & 15;
-  const int kvh = blockIdx.x % p.num_kv_heads;
-  const int tile = blockIdx.x / p.num_kv_heads;
   const int b = p.tile_batch[tile];
   if (b < 0 || b >= p.batch) return;
   const int row_base = p.tile_index[tile] * p.rows_per_tile;
@@ -363,6 +465,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   int mask_from = p.causal ? L - nreq + row_base + 1 : L;
   mask_from = mask_from < 0 ? 0 : (mask_from > L ? L : mask_from);
   const int T = (kv_end + C::NT - 1) / C::NT;
+  // The tiles [it0, it1) this workgroup reads: all T, or the range of one
+  // part of a split tile. A part keeps its (m, l, acc) in a record; the last
+  // part to finish merges the records and writes the rows. An entry that
+  // does not fit the workspace poisons the tile instead.
+  int it0 = 0, it1 = T, slot0 = -1, part = 0, parts = 1;
+  bool bad_map = false;
+  if (p.tile_kv != nullptr) {
+    const int32_t* kv = p.tile_kv + 4 * (long long)tile;
+    const int kv_first = kv[0], kv_last = kv[1], s0 = kv[2], pq = kv[3];
+    it0 = kv_first <= 0 ? 0 : min(kv_first / C::NT, T);
+    it1 = kv_last <= 0 ? it0 : max(it0, min((int)(((long long)kv_last + C::NT - 1) / C::NT), T));
+    if (s0 >= 0) {
+      parts = pq >> 16;
+      part = pq & 0xffff;
+      if (parts < 2 || part >= parts || s0 > p.num_slots - parts) {
+        bad_map = true;
+        it1 = it0;
+      } else {
+        slot0 = s0;
+      }
+    }
+  }
 
   // Q as the B operand of q.K, zero for columns without a row; the head_dim
   // order inside a k-step matches the K chunks (bf16: 32 ks + 8 r + j; fp8:
@@ -496,10 +620,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
   const uint32_t lds0 = dev::lds_addr(smem);
   int e0 = 0, e1 = 0;
-  if (T > 0) {
-    load_pages(0, e0, e1);
-    issue(0, 0, e0, e1);
-    if (T > 1) load_pages(C::NT, e0, e1);
+  if (it0 < it1) {
+    load_pages(it0 * C::NT, e0, e1);
+    issue(it0 * C::NT, it0 & 1, e0, e1);
+    if (it0 + 1 < it1) load_pages((it0 + 1) * C::NT, e0, e1);
   }
   // one K/V tile: wait for its loads, start the next tile's, then compute.
   // MASKED (a compile-time flag) applies the columns' limits; the tiles that
@@ -511,9 +635,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     dev::wait_vmcnt<0>();
     __syncthreads();  // every wave's loads of tile it landed; stage (it + 1) & 1 is free
     const int tb = it * C::NT;
-    if (it + 1 < T) {
+    if (it + 1 < it1) {
       issue(tb + C::NT, (it + 1) & 1, e0, e1);
-      if (it + 2 < T) load_pages(tb + 2 * C::NT, e0, e1);
+      if (it + 2 < it1) load_pages(tb + 2 * C::NT, e0, e1);
     }
     const uint32_t sb = lds0 + (it & 1) * C::STAGE;
 
@@ -691,19 +815,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     __builtin_amdgcn_s_setprio(0);
   };
   // tiles entirely below every column's limit, then the rest
-  const int T_open = min(T, mask_from / C::NT);
-  int it = 0;
+  const int T_open = min(it1, max(it0, mask_from / C::NT));
+  int it = it0;
   for (; it < T_open; ++it) tile_step(it, std::false_type{});
-  for (; it < T; ++it) tile_step(it, std::true_type{});
+  for (; it < it1; ++it) tile_step(it, std::true_type{});
 
-  // totals over the four lane rows (disjoint tokens), then the outputs:
-  // lane (r, c) holds d = (4 r + j) DB + e of its column
-  const bool poisoned = __syncthreads_or(bad_page) != 0;
+  // totals over the four lane rows (disjoint tokens)
+  bool poisoned = __syncthreads_or(bad_page || bad_map) != 0;
 #pragma unroll
   for (int bb = 0; bb < C::NB; ++bb) {
-    float lt = l[bb];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    l[bb] += __shfl_xor(l[bb], 16);
+    l[bb] += __shfl_xor(l[bb], 32);
+  }
+  if (slot0 >= 0 && !merge_parts<D, FP8>(p, s_count, acc, m, l, poisoned, slot0, part, parts, kvh, w, lane)) return;
+
+  // the outputs: lane (r, c) holds d = (4 r + j) DB + e of its column
+#pragma unroll
+  for (int bb = 0; bb < C::NB; ++bb) {
+    const float lt = l[bb];
     if (orow[bb] < 0) continue;
     float* o = p.out + orow[bb] * D;
     if constexpr (C::TRV) {
@@ -733,13 +862,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   }
 }
 
+// Workgroup (t, kv head) with t = blockIdx / Hkv: map entry t.
+template <int D, bool FP8>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(const PrefillParams p) {
+  using C = Cfg<D, FP8>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::STAGE];
+  __shared__ uint32_t s_count;  // a split tile's parts counted in before this one
+  prefill_item<D, FP8>(p, blockIdx.x / p.num_kv_heads, blockIdx.x % p.num_kv_heads, smem, s_count);
+}
+
 template <int D, bool FP8>
 hipError_t launch_one(const PrefillParams& p, uint32_t grid, hipStream_t stream) {
   hipLaunchKernelGGL((prefill_kernel<D, FP8>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 
+template <int D, bool FP8>
+int wgs_one() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_kernel<D, FP8>, kWaves * 64, 0) != hipSuccess) return 0;
+  return n;
+}
+
 }  // namespace
+
+int prefill_wgs_per_cu(int head_dim, bool fp8) {
+  if (head_dim == 64) return fp8 ? wgs_one<64, true>() : wgs_one<64, false>();
+  if (head_dim == 128) return fp8 ? wgs_one<128, true>() : wgs_one<128, false>();
+  if (head_dim == 256) return fp8 ? wgs_one<256, true>() : wgs_one<256, false>();
+  return 0;
+}
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, bool fp8, uint32_t grid, hipStream_t stream) {
   if (head_dim == 64) return fp8 ? launch_one<64, true>(p, grid, stream) : launch_one<64, false>(p, grid, stream);

@@ -180,3 +180,154 @@ def test_prefill_full_size_sampled(name):
             rows += [ptr[b], ptr[b + 1] - 1] + rng.integers(ptr[b], ptr[b + 1], 2).tolist()
     ref_o, ref_l = _sampled(inp, rows)
     _compare(out[rows], lse[rows], ref_o, ref_l, False, name)
+
+
+# ---- split-KV prefill (pdattn_prefill_split_tiles + pdattn_prefill_split) ----
+
+# longer prefixes so that tiles read up to 34 kernel tiles and are cut into
+# several parts when the planner is given more slots than there is work
+SPLIT_PREFIX = (0, 37, 2000, 5, 9, 700)
+
+
+def _split_call(inp, *, layout="nhd", causal=True, slots=1 << 20, lens=None, ws=None, tiles=None):
+    pk = _pk()
+    src = synth.to_hnd(inp) if layout == "hnd" else inp
+    d = {k: (src[k].to(DEV) if src.get(k) is not None else None)
+         for k in ("q", "qo_indptr", "k_pages", "v_pages", "k_scale", "v_scale", "block_table")}
+    lay = pk.LAYOUT_HND if layout == "hnd" else pk.LAYOUT_NHD
+    prob = pk._prefill_problem(d["q"], d["k_pages"], d["block_table"], lay, None)
+    st = tiles if tiles is not None else pk.prefill_split_tiles(prob, inp["qo_indptr"], inp["context_lens"],
+                                                                causal=causal, slots=slots)
+    if ws is None:
+        ws = pk.prefill_split_workspace(st, DEV)
+    lens = (inp["context_lens"] if lens is None else lens).to(DEV)
+    out = torch.empty(d["q"].shape, dtype=torch.float32, device=DEV)
+    lse = torch.empty(d["q"].shape[:2], dtype=torch.float32, device=DEV)
+    pk.prefill_split(prob, d["q"], d["qo_indptr"], st.tile_batch.to(DEV), st.tile_index.to(DEV), st.tile_kv.to(DEV),
+                     st.num_slots, ws, d["k_pages"], d["v_pages"], d["k_scale"], d["v_scale"], d["block_table"], lens,
+                     out, lse, causal=causal)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu(), st, ws
+
+
+def _counters(st, ws, Hkv):
+    n = st.num_slots * Hkv
+    return ws[:4 * n].view(torch.int32).cpu() if n else torch.zeros(0, dtype=torch.int32)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"G{c[0] // c[1]}_d{c[2]}_P{c[3]}_{c[4]}" for c in CASES])
+def test_split_prefill_matches_oracle(case):
+    Hq, Hkv, D, P, kv = case
+    inp = synth.make_prefill_inputs(num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=P, q_lens=Q_LENS,
+                                    prefix_lens=SPLIT_PREFIX, kv_dtype=kv, seed=4600 + Hq + D + P)
+    layout = "hnd" if (Hq + D) % 2 == 0 else "nhd"
+    out, lse, st, ws = _split_call(inp, layout=layout)
+    parts = st.tile_kv[:, 3] >> 16
+    print(f"split G{Hq // Hkv} d{D}: {st.num_tiles} entries, {st.num_slots} slots, up to {int(parts.max())} parts",
+          flush=True)
+    assert st.num_slots > 0
+    _check(inp, out, lse, True, f"split G{Hq // Hkv} d{D} P{P} {kv} {layout}")
+    assert int(_counters(st, ws, Hkv).abs().sum()) == 0
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_split_prefill_is_deterministic_and_leaves_counters_zero(causal):
+    """Two calls on one workspace give the same bits (the last part merges
+    the records in part order, whatever order the parts finished in), leave
+    every counter at zero, and agree with the unsplit kernel to the bf16
+    rounding of the probabilities."""
+    inp = synth.make_prefill_inputs(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, q_lens=Q_LENS,
+                                    prefix_lens=SPLIT_PREFIX, seed=4700)
+    a_o, a_l, st, ws = _split_call(inp, causal=causal)
+    assert int(_counters(st, ws, 8).abs().sum()) == 0
+    b_o, b_l, _, _ = _split_call(inp, causal=causal, ws=ws, tiles=st)
+    assert torch.equal(a_o, b_o) and torch.equal(a_l, b_l)
+    assert int(_counters(st, ws, 8).abs().sum()) == 0
+    u_o, u_l = _run(inp, causal=causal)
+    # P is rounded to bf16 against each part's own running max, so the
+    # outputs agree to that rounding (the parity bar), l and lse to fp32's
+    diff = (a_o - u_o).abs()
+    assert float(diff.max()) <= 1e-2 and float(diff.mean()) <= 1e-4
+    fin = torch.isfinite(u_l)
+    assert torch.equal(fin, torch.isfinite(a_l)) and float((a_l[fin] - u_l[fin]).abs().max()) <= 1e-5
+    _check(inp, a_o, a_l, causal, f"split causal={causal}")
+
+
+def test_split_prefill_bad_inputs_give_nan_rows():
+    """A bad block-table entry read by one part of a split tile makes all of
+    that tile's rows NaN (the poison travels through the counter); a map entry
+    whose slots lie outside num_slots makes its tile's rows NaN without
+    touching the workspace; other rows are unaffected."""
+    pk = _pk()
+    inp = synth.make_prefill_inputs(num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16, q_lens=(40, 20, 30),
+                                    prefix_lens=(1000, 600, 0), seed=4800)
+    ref_o, ref_l = pf.prefill(inp["q"], inp["qo_indptr"], inp["k_pages"], inp["v_pages"], inp["block_table"],
+                              inp["context_lens"])
+    ptr = inp["qo_indptr"].tolist()
+    bad = dict(inp)
+    bt = inp["block_table"].clone()
+    bt[0, 2] = 1 << 30   # request 0, positions 32..47: the first part of its tiles
+    bad["block_table"] = bt
+    out, lse, st, ws = _split_call(bad)
+    assert int((st.tile_kv[:, 2] >= 0).sum()) > 0
+    assert bool(torch.isnan(out[ptr[0]:ptr[1]]).all()) and bool(torch.isnan(lse[ptr[0]:ptr[1]]).all())
+    _compare(out[ptr[1]:], lse[ptr[1]:], ref_o[ptr[1]:], ref_l[ptr[1]:], False, "split: rows of the good requests")
+    assert int(_counters(st, ws, 2).abs().sum()) == 0
+    # a part entry naming slots past num_slots (request 1's first split entry)
+    tk = st.tile_kv.clone()
+    t = [i for i in range(st.num_tiles) if int(st.tile_batch[i]) == 1 and int(tk[i, 2]) >= 0][0]
+    tk[t, 2] = st.num_slots
+    broken = pk.SplitTiles(st.tile_batch, st.tile_index, tk, st.num_slots, st.workspace_bytes)
+    out2, lse2, _, _ = _split_call(inp, tiles=broken, ws=pk.prefill_split_workspace(st, DEV))
+    rows = int(st.tile_index[t]) * 32
+    assert bool(torch.isnan(out2[ptr[1] + rows:min(ptr[1] + rows + 32, ptr[2])]).all())
+    _compare(out2[ptr[2]:], lse2[ptr[2]:], ref_o[ptr[2]:], ref_l[ptr[2]:], False, "split: other rows")
+
+
+def test_split_prefill_graph_replays():
+    """The split call captured in a HIP graph: every replay (with eager work
+    and synchronisation between them) gives the eager call's bits; the
+    counters restore themselves, no memset is recorded."""
+    pk = _pk()
+    inp = synth.make_prefill_inputs(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, q_lens=Q_LENS,
+                                    prefix_lens=SPLIT_PREFIX, seed=4900)
+    ref_o, ref_l, st, ws = _split_call(inp)
+    d = {k: (inp[k].to(DEV) if inp.get(k) is not None else None)
+         for k in ("q", "qo_indptr", "k_pages", "v_pages", "block_table", "context_lens")}
+    prob = pk._prefill_problem(d["q"], d["k_pages"], d["block_table"], pk.LAYOUT_NHD, None)
+    tb, ti, tk = st.tile_batch.to(DEV), st.tile_index.to(DEV), st.tile_kv.to(DEV)
+    out = torch.zeros(d["q"].shape, dtype=torch.float32, device=DEV)
+    lse = torch.zeros(d["q"].shape[:2], dtype=torch.float32, device=DEV)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        pk.prefill_split(prob, d["q"], d["qo_indptr"], tb, ti, tk, st.num_slots, ws, d["k_pages"], d["v_pages"],
+                         None, None, d["block_table"], d["context_lens"], out, lse, stream=s)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(0.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.cpu(), ref_o) and torch.equal(lse.cpu(), ref_l), rep
+        assert int(_counters(st, ws, 8).abs().sum()) == 0, rep
+
+
+@pytest.mark.parametrize("name", sorted(synth.PREFILL_WORKLOADS))
+def test_split_prefill_full_size_sampled(name):
+    """The bench's workloads at full size through the split call on this
+    device's slot count (the planner cuts only what the schedule needs):
+    sampled rows against the oracle, every output finite."""
+    inp = synth.prefill_workload(name)
+    out, lse, st, ws = _split_call(inp, layout="hnd", slots=0)
+    print(f"{name}: {st.num_tiles} entries, {st.num_slots} slots", flush=True)
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
+    ptr = inp["qo_indptr"].tolist()
+    rng = np.random.default_rng(12)
+    rows = []
+    for b in range(len(ptr) - 1):
+        if ptr[b + 1] > ptr[b]:
+            rows += [ptr[b], ptr[b + 1] - 1] + rng.integers(ptr[b], ptr[b + 1], 6).tolist()
+    ref_o, ref_l = _sampled(inp, rows)
+    _compare(out[rows], lse[rows], ref_o, ref_l, False, name + " split")

@@ -1,7 +1,8 @@
 """Host logic of the prefill boundary, on the CPU: the tile map that
 pdattn_prefill_tiles builds (against the pages' worked example and the
-oracle's tile map), its longest-first order, the rows-per-tile query and the
-argument checks. No device call is made."""
+oracle's tile map), its longest-first order, the split map of
+pdattn_prefill_split_tiles (against the rule its header states), the
+rows-per-tile query and the argument checks. No device call is made."""
 import json
 import os
 
@@ -104,3 +105,176 @@ def test_prefill_rejects_bad_arguments_before_launch():
     st = pk._lib.pdattn_prefill(ctypes.byref(prob), 1, None, None, None, None, 0, None, None, None, None, None, None,
                                 None, None, None)
     assert st == 0
+
+
+def _reach(ptr, L, b, j, rt, causal):
+    n = int(ptr[b + 1] - ptr[b])
+    last = min((j + 1) * rt, n) - 1
+    r = int(L[b]) - n + last + 1 if causal else int(L[b])
+    return min(max(r, 0), int(L[b]))
+
+
+def _split_problem(B, D=128, Hq=32, Hkv=8, P=16, max_len=1):
+    mp = max(1, -(-max_len // P))
+    return _pk().Problem(B, Hq, Hkv, D, P, mp, B * mp, 0, 0.0, 0, 1)
+
+
+def _map_by_rule(ptr, L, rows, nt, H, slots, causal):
+    """The split map as pdattn.h states the rule: for each candidate cap
+    (none, then ceil(k x longest / 16) for k = 15 .. 3, at least 4), cut the
+    long tiles evenly at multiples of 64 positions, list the entries by cost
+    (most first, stable), simulate the list schedule on `slots` slots and
+    keep the first cap that ends soonest. Returns entries as
+    [b, j, kv0, kv1, base, pq] and the slot count."""
+    import heapq
+    min_units = -(-4 * nt // 64)
+    tiles = []
+    for b in range(len(ptr) - 1):
+        n, Lb = int(ptr[b + 1] - ptr[b]), int(L[b])
+        for j in range(-(-n // rows)):
+            last = min((j + 1) * rows, n) - 1
+            reach = min(max(Lb - n + last + 1 if causal else Lb, 0), Lb)
+            opn = min(max(Lb - n + j * rows + 1 if causal else Lb, 0), Lb)
+            tiles.append((b, j, reach, opn, -(-reach // nt)))
+
+    def cost(t, kv0, kv1, part):
+        i0, i1 = kv0 // nt, -(-kv1 // nt)
+        return 4 * (i1 - i0) + max(0, i1 - max(i0, t[3] // nt)) + 20 + (12 if part else 0)
+
+    def cut(cap):
+        out, nslots = [], 0
+        for t in tiles:
+            units = -(-t[2] // 64)
+            parts = min(-(-t[4] // cap), 16, units // min_units) if t[4] > cap else 1
+            if parts < 2:
+                out.append((cost(t, 0, t[2], False), [t[0], t[1], 0, t[2], -1, 1 << 16]))
+                continue
+            for q in range(parts):
+                kv0 = q * units // parts * 64
+                kv1 = t[2] if q + 1 == parts else (q + 1) * units // parts * 64
+                out.append((cost(t, kv0, kv1, True), [t[0], t[1], kv0, kv1, nslots, q | (parts << 16)]))
+            nslots += parts
+        out.sort(key=lambda e: -e[0])
+        return out, nslots
+
+    def span(lst):
+        free = [0] * min(slots, len(lst) * H)
+        end = 0
+        for c, _ in lst:
+            for _ in range(H):
+                t = heapq.heappop(free) + c
+                heapq.heappush(free, t)
+                end = max(end, t)
+        return end
+    longest = max((t[4] for t in tiles), default=0)
+    best = None
+    for cap in [1 << 62] + [max(4, -(-longest * k // 16)) for k in range(15, 2, -1)]:
+        lst, nslots = cut(cap)
+        sp = span(lst)
+        if best is None or sp < best[0]:
+            best = (sp, [e for _, e in lst], nslots)
+    return (best[1], best[2]) if best else ([], 0)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_split_map_follows_the_rule_and_covers_every_position_once(causal):
+    """pdattn_prefill_split_tiles: entries equal the rule pdattn.h states;
+    every query tile appears, whole or as parts whose ranges join up to
+    [0, reach) in part order at multiples of 64 (each at least 4 kernel
+    tiles), the parts of a tile hold consecutive slots, no slot is shared,
+    and the workspace size follows the slot count."""
+    pk = _pk()
+    rng = np.random.default_rng(17)
+    cut_any = 0
+    for trial in range(40):
+        B = int(rng.integers(1, 10))
+        n = rng.integers(0, 700, B)
+        L = n + rng.integers(0, 3000, B)
+        if rng.random() < 0.3:
+            L = np.minimum(L, rng.integers(0, 300, B))
+        ptr = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+        D = int(rng.choice([64, 128, 256]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        Hkv = int(rng.choice([1, 2, 8]))
+        prob = _split_problem(B, D=D, Hq=G * Hkv, Hkv=Hkv, max_len=int(L.max()))
+        slots = int(rng.choice([8, 64, 512, 4096]))
+        st = pk.prefill_split_tiles(prob, ptr, L.astype(np.int32), causal=causal, slots=slots)
+        rt = pk.prefill_rows_per_tile(prob)
+        nt = 32 if D == 256 else 64
+        want, want_slots = _map_by_rule(ptr, L, rt, nt, Hkv, slots, causal)
+        got = [[b, j] + k for b, j, k in zip(st.tile_batch.tolist(), st.tile_index.tolist(), st.tile_kv.tolist())]
+        assert got == want and st.num_slots == want_slots
+        cut_any += st.num_slots > 0
+        ref_b, ref_i = pf.tile_map(ptr, rt)
+        parts_of = {}
+        for e in got:
+            parts_of.setdefault((e[0], e[1]), []).append(e[2:])
+        assert sorted(parts_of) == sorted(zip(ref_b, ref_i))
+        used = set()
+        for (b, j), ents in parts_of.items():
+            reach = _reach(ptr, L, b, j, rt, causal)
+            if len(ents) == 1 and ents[0][2] == -1:
+                assert ents[0] == [0, reach, -1, 1 << 16]
+                continue
+            parts = ents[0][3] >> 16
+            assert 2 <= parts <= 16 and len(ents) == parts
+            e = sorted(ents, key=lambda x: x[3] & 0xFFFF)
+            assert [x[3] & 0xFFFF for x in e] == list(range(parts))
+            assert all(x[3] >> 16 == parts and x[2] == e[0][2] for x in e)
+            assert e[0][0] == 0 and e[-1][1] == reach
+            for a, c in zip(e, e[1:]):
+                assert a[1] == c[0] and a[1] % 64 == 0 and a[1] - a[0] >= 4 * nt
+            assert e[-1][1] - e[-1][0] >= 4 * nt - 63
+            here = set(range(e[0][2], e[0][2] + parts))
+            assert not (here & used)
+            used |= here
+        assert used == set(range(st.num_slots))
+        rec = (64 if D == 256 else 128) * (D + 2) * 4
+        ws = 0 if st.num_slots == 0 else -(-st.num_slots * Hkv * 4 // 256) * 256 + st.num_slots * Hkv * rec
+        assert st.workspace_bytes == ws
+    assert cut_any >= 5
+
+
+def test_split_planner_cuts_the_long_prompt_only():
+    """One 2048-token causal prompt (64 tiles of 32 rows reading 1 to 32
+    kernel tiles) on 512 slots: the longest tiles are cut; the ragged and
+    chunked bench batches, whose tiles already spread over the slots, and a
+    prompt of 4 kernel tiles are not."""
+    pk = _pk()
+    import synth
+    prob = _split_problem(1, max_len=2048)
+    st = pk.prefill_split_tiles(prob, [0, 2048], [2048], causal=True, slots=512)
+    assert st.num_slots > 0 and st.num_tiles > 64
+    for name in ("llama3_8b_prefill", "llama3_8b_chunked_prefill"):
+        desc, dims, batch, qr, pr, seed = synth.PREFILL_WORKLOADS[name]
+        g = torch.Generator().manual_seed(seed + 2)
+        q = torch.randint(qr[0], qr[1] + 1, (batch,), generator=g)
+        pre = torch.randint(pr[0], pr[1] + 1, (batch,), generator=g)
+        lens = (q + pre).to(torch.int32)
+        ptr = torch.cat([torch.zeros(1, dtype=torch.int64), q.cumsum(0)]).to(torch.int32)
+        big = _split_problem(batch, max_len=int(lens.max()))
+        st = pk.prefill_split_tiles(big, ptr, lens, causal=True, slots=512)
+        assert st.num_slots == 0, name
+    short = pk.prefill_split_tiles(_split_problem(1, max_len=400), [0, 32], [256], causal=True, slots=1 << 20)
+    assert short.num_slots == 0 and short.num_tiles == 1
+
+
+def test_split_argument_checks():
+    pk = _pk()
+    import ctypes
+    prob = _split_problem(1, max_len=2048)
+    with pytest.raises(pk.PdattnError):
+        pk.prefill_split_tiles(prob, [0, 2048], [5000], slots=512)   # length beyond the block table
+    with pytest.raises(pk.PdattnError):
+        pk.prefill_split_tiles(prob, [0, 2048], [2048], slots=-1)
+    P = ctypes.c_void_p
+    call = pk._lib.pdattn_prefill_split
+    # parts but no workspace; a workspace too small; no tile_kv
+    assert call(ctypes.byref(prob), 1, P(16), P(16), P(16), P(16), P(16), 3, 2, None, 0, P(16), P(16), None, None,
+                P(16), P(16), P(16), None, None) == 3
+    assert call(ctypes.byref(prob), 1, P(16), P(16), P(16), P(16), P(16), 3, 2, P(256), 100, P(16), P(16), None,
+                None, P(16), P(16), P(16), None, None) == 3
+    assert call(ctypes.byref(prob), 1, P(16), P(16), P(16), P(16), None, 3, 0, None, 0, P(16), P(16), None, None,
+                P(16), P(16), P(16), None, None) == 1
+    assert call(ctypes.byref(prob), 1, None, None, None, None, None, 0, 0, None, 0, None, None, None, None, None,
+                None, None, None, None) == 0

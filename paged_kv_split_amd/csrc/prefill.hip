@@ -673,6 +673,22 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, const int t
       }
     });
 
+    // The bf16 softmax reads the raw S registers with inline-asm v_max3,
+    // and the compiler inserts no wait states between an MFMA and an asm
+    // operand it writes (the matrix core does not interlock its results).
+    // All of S passes through this block: every q.K product is issued
+    // before it (no pass can sink one towards its use), 19 wait states
+    // pass, and the reads below take its outputs.
+    if constexpr (!FP8) {
+      static_assert(C::MB * C::NB == 8 || C::MB * C::NB == 2, "S blocks");
+      if constexpr (C::MB * C::NB == 8) {
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2"
+                     : "+v"(S[0][0]), "+v"(S[0][1]), "+v"(S[1][0]), "+v"(S[1][1]), "+v"(S[2][0]), "+v"(S[2][1]),
+                       "+v"(S[3][0]), "+v"(S[3][1]));
+      } else {
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 2" : "+v"(S[0][0]), "+v"(S[1][0]));
+      }
+    }
     __builtin_amdgcn_s_setprio(0);
     float ksc[C::MB][4], vsc[C::MB][4];
     if constexpr (FP8) {

@@ -331,3 +331,24 @@ def test_split_prefill_full_size_sampled(name):
             rows += [ptr[b], ptr[b + 1] - 1] + rng.integers(ptr[b], ptr[b + 1], 6).tolist()
     ref_o, ref_l = _sampled(inp, rows)
     _compare(out[rows], lse[rows], ref_o, ref_l, False, name + " split")
+
+
+def test_prefill_full_size_fp8_sampled():
+    """The bench's ragged batch with fp8 pools at full size, through both
+    calls bench.py times (HND pools): sampled rows against the oracle at the
+    fp8 bar, every output finite, and the two calls within that bar of each
+    other."""
+    inp = synth.prefill_workload("llama3_8b_prefill", kv_dtype="fp8_e4m3")
+    out, lse = _run(inp, layout="hnd")
+    s_out, s_lse, st, _ = _split_call(inp, layout="hnd", slots=0)
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(s_out).all())
+    ptr = inp["qo_indptr"].tolist()
+    rng = np.random.default_rng(13)
+    rows = []
+    for b in range(len(ptr) - 1):
+        if ptr[b + 1] > ptr[b]:
+            rows += [ptr[b], ptr[b + 1] - 1] + rng.integers(ptr[b], ptr[b + 1], 3).tolist()
+    ref_o, ref_l = _sampled(inp, rows)
+    _compare(out[rows], lse[rows], ref_o, ref_l, True, "fp8 ragged, unsplit")
+    _compare(s_out[rows], s_lse[rows], ref_o, ref_l, True, f"fp8 ragged, split ({st.num_tiles} entries)")
+    assert float((out - s_out).abs().max()) <= 4e-2

@@ -671,6 +671,23 @@ PDATTN_API pdattn_status pdattn_prefill_rows_per_tile(const pdattn_problem* prob
   return PDATTN_OK;
 }
 
+namespace {
+
+// Positions a query tile reads: query tile j (rows j*rows .. of a request
+// with n new rows and L context positions) sees t < L - n + i + 1 for its
+// row i when causal, all t < L otherwise; `reach` is its last row's limit
+// and `open` its first row's (positions below it are visible to every row),
+// both clamped to [0, L].
+void tile_limits(int64_t L, int64_t n, int64_t j, int64_t rows, bool causal, int64_t& reach, int64_t& open) {
+  const int64_t last = std::min<int64_t>((j + 1) * rows, n) - 1;
+  reach = causal ? L - n + last + 1 : L;
+  reach = reach < 0 ? 0 : (reach > L ? L : reach);
+  open = causal ? L - n + j * rows + 1 : L;
+  open = open < 0 ? 0 : (open > L ? L : open);
+}
+
+}  // namespace
+
 PDATTN_API pdattn_status pdattn_prefill_tiles(const int32_t* qo_indptr, const int32_t* context_lens, int32_t batch,
                                               int32_t rows_per_tile, int32_t causal, int32_t flags,
                                               int32_t* tile_batch, int32_t* tile_index, int32_t capacity,
@@ -719,10 +736,8 @@ PDATTN_API pdattn_status pdattn_prefill_tiles(const int32_t* qo_indptr, const in
     for (int64_t i = 0; i < count; ++i) {
       const int b = tile_batch[i];
       const int64_t n = (int64_t)qo_indptr[b + 1] - qo_indptr[b];
-      const int64_t L = context_lens[b];
-      const int64_t last = std::min<int64_t>((int64_t)(tile_index[i] + 1) * rows_per_tile, n) - 1;
-      int64_t reach = causal ? L - n + last + 1 : L;
-      reach = reach < 0 ? 0 : (reach > L ? L : reach);
+      int64_t reach, open;
+      tile_limits(context_lens[b], n, tile_index[i], rows_per_tile, causal != 0, reach, open);
       items[i] = Item{reach, tile_batch[i], tile_index[i]};
     }
     std::stable_sort(items.begin(), items.end(), [](const Item& x, const Item& y) { return x.reach > y.reach; });
@@ -897,11 +912,8 @@ PDATTN_API pdattn_status pdattn_prefill_split_tiles(const pdattn_problem* proble
       if (L < 0 || L > (int64_t)problem->max_pages_per_seq * problem->page_size)
         return fail(PDATTN_ERR_INVALID_ARGUMENT, "context_lens[%d] = %lld outside the block table", b, (long long)L);
       for (int64_t j = 0; j < ceil_div(n, rows); ++j) {
-        const int64_t last = std::min<int64_t>((j + 1) * rows, n) - 1;
-        int64_t reach = causal ? L - n + last + 1 : L;
-        reach = reach < 0 ? 0 : (reach > L ? L : reach);
-        int64_t open = causal ? L - n + j * rows + 1 : L;
-        open = open < 0 ? 0 : (open > L ? L : open);
+        int64_t reach, open;
+        tile_limits(L, n, j, rows, causal != 0, reach, open);
         tiles.push_back(Tile{reach, open, ceil_div(reach, nt), b, (int32_t)j});
         max_steps = std::max(max_steps, tiles.back().steps);
         if ((int64_t)tiles.size() > INT32_MAX) return fail(PDATTN_ERR_UNSUPPORTED, "more than 2^31 - 1 query tiles");

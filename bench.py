@@ -411,7 +411,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 def time_prefill(pk, flush, dev, reps=20):
     """Ragged paged prefill, one launch per call (tile maps built once per
     batch on the host, outside the timing): the three prefill workloads with
-    bf16 pools, and the ragged batch with fp8 pools. Each through the split
+    bf16 pools, and the ragged batch with fp8 pools (separate scale arrays,
+    and each row's scale inline after its codes). Each through the split
     call (pdattn_prefill_split_tiles on this device's slot count, which cuts
     long tiles where its schedule simulation says the grid ends sooner, then
     pdattn_prefill_split), and through the unsplit call (pdattn_prefill,
@@ -422,9 +423,12 @@ def time_prefill(pk, flush, dev, reps=20):
     import torch
     import synth
     res = {}
-    runs = [(name, "bf16") for name in sorted(synth.PREFILL_WORKLOADS)] + [("llama3_8b_prefill", "fp8_e4m3")]
+    runs = [(name, "bf16") for name in sorted(synth.PREFILL_WORKLOADS)] + [("llama3_8b_prefill", "fp8_e4m3"),
+                                                                            ("llama3_8b_prefill", "fp8_inline")]
     for name, kv in runs:
-        inp = synth.prefill_workload(name, kv_dtype=kv)
+        inp = synth.prefill_workload(name, kv_dtype="bf16" if kv == "bf16" else "fp8_e4m3")
+        if kv == "fp8_inline":
+            inp = synth.to_inline(inp)
         src = synth.to_hnd(inp)
         d = {k: (src[k].to(dev) if src.get(k) is not None else None)
              for k in ("q", "qo_indptr", "k_pages", "v_pages", "k_scale", "v_scale", "block_table", "context_lens")}

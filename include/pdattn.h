@@ -114,8 +114,8 @@ typedef enum pdattn_kv_dtype {
  * problem->kv_layout's, as for the other dtypes. k_scale and v_scale are
  * NULL. The stored value of element i is e4m3fn(code_i) * scale, as for
  * PDATTN_KV_FP8_E4M3. Served by static decode plans (one-token and
- * multi-query) and by pdattn_kv_append; balanced plans and pdattn_prefill
- * return PDATTN_ERR_UNSUPPORTED.
+ * multi-query), by pdattn_kv_append and by the prefill calls; balanced
+ * plans return PDATTN_ERR_UNSUPPORTED.
  */
 
 /* The order of the (slot, kv head) rows inside one page of the K and V
@@ -392,7 +392,8 @@ PDATTN_API pdattn_status pdattn_prefill_tiles(const int32_t* qo_indptr, const in
 /*
  * Enqueue the prefill on `stream`.
  *   problem      pools and heads as for decode (q_len is not used; any G
- *                up to 16, d in {64, 128, 256}, both layouts, bf16 or fp8)
+ *                up to 16, d in {64, 128, 256}, both layouts, bf16 or fp8
+ *                with separate or inline scales)
  *   causal       1: causal mask as above; 0: every row sees all L_b positions
  *   q            bf16 [total_q][Hq][d], device, 16-byte aligned
  *   qo_indptr    int32 [batch + 1], device: the same values the tile map

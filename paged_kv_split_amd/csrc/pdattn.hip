@@ -757,6 +757,12 @@ constexpr int64_t kMaxParts = 16;
 // Positions per unit of a part boundary (a multiple of every kernel tile).
 constexpr int64_t kPartUnit = 64;
 
+int prefill_pool(const pdattn_problem& p) {
+  return p.kv_dtype == PDATTN_KV_FP8_E4M3_INLINE ? pdattn::kPrefillFp8Inline
+         : p.kv_dtype == PDATTN_KV_FP8_E4M3      ? pdattn::kPrefillFp8
+                                                 : pdattn::kPrefillBf16;
+}
+
 uint64_t prefill_workspace_bytes(const pdattn_problem& problem, int64_t num_slots) {
   const uint64_t records = (uint64_t)num_slots * (uint64_t)problem.num_kv_heads;
   const uint64_t ctr = (records * 4 + 255) / 256 * 256;
@@ -793,11 +799,8 @@ pdattn_status prefill_launch(const pdattn_problem* problem, int32_t causal, cons
   if (!aligned(qo_indptr, 4) || !aligned(tile_batch, 4) || !aligned(tile_index, 4) || !aligned(block_table, 4) ||
       !aligned(context_lens, 4) || (lse && !aligned(lse, 4)) || (tile_kv && !aligned(tile_kv, 16)))
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "index arrays and lse must be 4-byte aligned, tile_kv 16-byte");
-  if (problem->kv_dtype == PDATTN_KV_FP8_E4M3_INLINE)
-    return fail(PDATTN_ERR_UNSUPPORTED, "the prefill reads bf16 or separate-scale fp8 pools");
   st = check_scales(*problem, k_scale, v_scale);
   if (st != PDATTN_OK) return st;
-  const bool fp8 = problem->kv_dtype == PDATTN_KV_FP8_E4M3;
 
   pdattn::PrefillParams p;
   std::memset(&p, 0, sizeof p);
@@ -834,7 +837,8 @@ pdattn_status prefill_launch(const pdattn_problem* problem, int32_t causal, cons
     p.num_slots = num_slots;
   }
   const uint32_t grid = (uint32_t)((int64_t)num_tiles * problem->num_kv_heads);
-  hipError_t e = pdattn::launch_prefill(p, problem->head_dim, fp8, grid, static_cast<hipStream_t>(stream));
+  hipError_t e = pdattn::launch_prefill(p, problem->head_dim, prefill_pool(*problem), grid,
+                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "prefill kernel launch: %s", hipGetErrorString(e));
   return PDATTN_OK;
 }
@@ -876,7 +880,7 @@ PDATTN_API pdattn_status pdattn_prefill_split_tiles(const pdattn_problem* proble
     if (e == hipSuccess) e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess || num_cus <= 0)
       return fail(PDATTN_ERR_DEVICE, "cannot query the compute-unit count: %s", hipGetErrorString(e));
-    const int per_cu = pdattn::prefill_wgs_per_cu(problem->head_dim, problem->kv_dtype == PDATTN_KV_FP8_E4M3);
+    const int per_cu = pdattn::prefill_wgs_per_cu(problem->head_dim, prefill_pool(*problem));
     slots = num_cus * (per_cu > 0 ? per_cu : 1);
   }
   const int64_t H = problem->num_kv_heads;

@@ -21,9 +21,9 @@ struct PrefillParams {
   const int32_t* qo_indptr;   // [B + 1]
   const int32_t* tile_batch;  // [num_tiles]: request of each query tile
   const int32_t* tile_index;  // [num_tiles]: its tile index inside that request
-  const uint8_t* k;           // pool bytes, rows as in the decode kernels
+  const uint8_t* k;           // pool bytes, rows as in the decode kernels (inline fp8: D + 4 bytes each)
   const uint8_t* v;
-  const float* k_scale;       // fp8 pools: one per row
+  const float* k_scale;       // separate-scale fp8 pools: one per row
   const float* v_scale;
   const int32_t* block_table; // [B][max_pages_per_seq]
   const int32_t* context_lens;
@@ -48,9 +48,12 @@ struct PrefillParams {
   int32_t num_slots;
 };
 
+// Pool kinds of the prefill kernel.
+constexpr int kPrefillBf16 = 0, kPrefillFp8 = 1, kPrefillFp8Inline = 2;
+
 // grid: num_tiles * num_kv_heads workgroups of 256 threads.
-hipError_t launch_prefill(const PrefillParams& p, int head_dim, bool fp8, uint32_t grid, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, int pool, uint32_t grid, hipStream_t stream);
 // Resident prefill workgroups per compute unit (0 when the runtime cannot say).
-int prefill_wgs_per_cu(int head_dim, bool fp8);
+int prefill_wgs_per_cu(int head_dim, int pool);
 
 }  // namespace pdattn

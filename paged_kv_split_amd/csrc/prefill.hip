@@ -32,7 +32,9 @@
 //
 // fp8 pools: codes widen exactly to bf16 for the operand; the k scale
 // multiplies the score, the v scale the probability (OASR "Kernel Layer",
-// FP8 KV variants), as in the decode kernels.
+// FP8 KV variants), as in the decode kernels. Pools with the scale inline
+// (each row's D codes followed by its fp32 scale, DeepGEMM documentation
+// 6.1) are fetched with 4-byte loads into the same LDS image.
 
 #include "prefill.h"
 #include "tile_ops.h"
@@ -413,8 +415,8 @@ __device__ __forceinline__ bool merge_parts(const PrefillParams& p, uint32_t& s_
 }
 
 // One map entry (a whole query tile, or one part of a split one) for kv
-// head kvh, on the whole workgroup.
-template <int D, bool FP8>
+// head kvh, on the whole workgroup. INL: fp8 rows with their scale inline.
+template <int D, bool FP8, bool INL>
 __device__ __forceinline__ void prefill_item(const PrefillParams& p, const int tile, const int kvh,
                                              unsigned char (&smem)[2 * Cfg<D, FP8>::STAGE], uint32_t& s_count) {
   using C = Cfg<D, FP8>;
@@ -548,11 +550,80 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, const int t
     voff[i] = (uint32_t)(cv * 16 / C::ROW - 16 * mbK) * slot_bytes + chunk * 16;
   }
   const uint32_t soff = (uint32_t)((lane & 15) * p.slot_stride) * 4u;
+  // inline-scale rows (D + 4 bytes): the lane's K dword (token lane / 4 of
+  // the group, dword lane mod 4 of a fragment), its V dword (byte 4 lane of
+  // a 256-byte run of row-major rows) and its scale (token lane mod 16)
+  const uint32_t inl_slot = (uint32_t)p.slot_stride * (D + 4);
+  const uint32_t inl_k = (uint32_t)(lane >> 2) * inl_slot + 4 * (lane & 3);
+  const uint32_t inl_v = (uint32_t)(4 * lane / C::ROW) * inl_slot + (4 * lane) % C::ROW;
+  const uint32_t inl_s = (uint32_t)(lane & 15) * inl_slot + D;
   const float* sbase_lane = lane < 16 ? p.k_scale : p.v_scale;
   auto issue = [&](int tb, int stage, int raw0, int raw1) {
     const int e0 = check_page(raw0), e1 = check_page(raw1);
     unsigned char* st = smem + stage * C::STAGE;
     const int first = group_first(tb);
+    if constexpr (INL) {
+      // rows of D codes and the row's fp32 scale, D + 4 bytes apart and so
+      // only 4-byte aligned: load (i, qq) fills bytes [qq * 256, +256) of
+      // the wave's 1 KB piece i, lane x the dword at + 4 x
+      constexpr int PITCH = D + 4;
+      if (P >= 16 && tb + C::NT <= L) {
+        // the group inside one page, every position < L: a wave-uniform row
+        // base, the two fixed lane offsets and constant ones per load
+        const int tg = tb + 16 * mbK;
+        const long long rb = (long long)e0 * P * p.num_kv_heads + (long long)(tg & (P - 1)) * p.slot_stride +
+                             (long long)kvh * p.head_stride;
+        const uint8_t* kb = p.k + rb * PITCH + inl_k;
+        const uint8_t* vb = p.v + rb * PITCH + inl_v;
+#pragma unroll
+        for (int i = 0; i < C::KI; ++i) {
+          const int q = w * C::KI + i;
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) dev::dma4(kb + 64 * (q % C::QK) + 16 * qq, st + q * 1024 + qq * 256);
+        }
+#pragma unroll
+        for (int i = 0; i < C::VI; ++i)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const int t = ((w * C::VI + i) * 1024 + qq * 256) / C::ROW - 16 * mbK;
+            dev::dma4(vb + (uint32_t)t * inl_slot, st + C::K_T + (w * C::VI + i) * 1024 + qq * 256);
+          }
+        if ((w * C::KI) % C::QK == 0 && lane < 32)
+          dev::dma4((lane < 16 ? p.k : p.v) + rb * PITCH + inl_s, st + C::K_T + C::V_T + mbK * 128);
+        return;
+      }
+      {
+        // K: that dword is dword x mod 4 of the 16-byte operand fragment of
+        // lane 16 qq + x / 4, i.e. token x / 4 of the group, row bytes
+        // 64 (piece mod QK) + 16 qq + 4 (x mod 4)
+        const int pos = min(tb + 16 * mbK + (lane >> 2), L - 1);
+        const uint8_t* src = p.k + row_of(pos, first, e0, e1) * PITCH + 4 * (lane & 3);
+#pragma unroll
+        for (int i = 0; i < C::KI; ++i) {
+          const int q = w * C::KI + i;
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) dev::dma4(src + 64 * (q % C::QK) + 16 * qq, st + q * 1024 + qq * 256);
+        }
+      }
+      // V, row-major: byte y of the tile is byte y mod ROW of token y / ROW
+#pragma unroll
+      for (int i = 0; i < C::VI; ++i)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int y = (w * C::VI + i) * 1024 + qq * 256 + 4 * lane;
+          const int pos = min(tb + y / C::ROW, L - 1);
+          dev::dma4(p.v + row_of(pos, first, e0, e1) * PITCH + y % C::ROW,
+                    st + C::K_T + (w * C::VI + i) * 1024 + qq * 256);
+        }
+      // the first wave of each M-block group stages its 16 k and 16 v
+      // scales, the dwords after the rows' codes
+      if ((w * C::KI) % C::QK == 0 && lane < 32) {
+        const int pos = min(tb + 16 * mbK + (lane & 15), L - 1);
+        dev::dma4((lane < 16 ? p.k : p.v) + row_of(pos, first, e0, e1) * PITCH + D,
+                  st + C::K_T + C::V_T + mbK * 128);
+      }
+      return;
+    }
     if (P >= 16 && tb + C::NT <= L) {
       // the group is 16-aligned and inside one page, every position < L:
       // a wave-uniform row base plus the fixed lane offsets
@@ -879,40 +950,56 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, const int t
 }
 
 // Workgroup (t, kv head) with t = blockIdx / Hkv: map entry t.
-template <int D, bool FP8>
+template <int D, bool FP8, bool INL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(const PrefillParams p) {
   using C = Cfg<D, FP8>;
+  static_assert(FP8 || !INL, "inline scales are an fp8 layout");
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::STAGE];
   __shared__ uint32_t s_count;  // a split tile's parts counted in before this one
-  prefill_item<D, FP8>(p, blockIdx.x / p.num_kv_heads, blockIdx.x % p.num_kv_heads, smem, s_count);
+  prefill_item<D, FP8, INL>(p, blockIdx.x / p.num_kv_heads, blockIdx.x % p.num_kv_heads, smem, s_count);
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool INL>
 hipError_t launch_one(const PrefillParams& p, uint32_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_kernel<D, FP8>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
+  hipLaunchKernelGGL((prefill_kernel<D, FP8, INL>), dim3(grid), dim3(kWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool INL>
 int wgs_one() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_kernel<D, FP8>, kWaves * 64, 0) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_kernel<D, FP8, INL>, kWaves * 64, 0) != hipSuccess)
+    return 0;
   return n;
+}
+
+template <int D>
+int wgs_of(int pool) {
+  return pool == kPrefillFp8Inline ? wgs_one<D, true, true>()
+         : pool == kPrefillFp8     ? wgs_one<D, true, false>()
+                                   : wgs_one<D, false, false>();
+}
+
+template <int D>
+hipError_t launch_of(const PrefillParams& p, int pool, uint32_t grid, hipStream_t stream) {
+  return pool == kPrefillFp8Inline ? launch_one<D, true, true>(p, grid, stream)
+         : pool == kPrefillFp8     ? launch_one<D, true, false>(p, grid, stream)
+                                   : launch_one<D, false, false>(p, grid, stream);
 }
 
 }  // namespace
 
-int prefill_wgs_per_cu(int head_dim, bool fp8) {
-  if (head_dim == 64) return fp8 ? wgs_one<64, true>() : wgs_one<64, false>();
-  if (head_dim == 128) return fp8 ? wgs_one<128, true>() : wgs_one<128, false>();
-  if (head_dim == 256) return fp8 ? wgs_one<256, true>() : wgs_one<256, false>();
+int prefill_wgs_per_cu(int head_dim, int pool) {
+  if (head_dim == 64) return wgs_of<64>(pool);
+  if (head_dim == 128) return wgs_of<128>(pool);
+  if (head_dim == 256) return wgs_of<256>(pool);
   return 0;
 }
 
-hipError_t launch_prefill(const PrefillParams& p, int head_dim, bool fp8, uint32_t grid, hipStream_t stream) {
-  if (head_dim == 64) return fp8 ? launch_one<64, true>(p, grid, stream) : launch_one<64, false>(p, grid, stream);
-  if (head_dim == 128) return fp8 ? launch_one<128, true>(p, grid, stream) : launch_one<128, false>(p, grid, stream);
-  if (head_dim == 256) return fp8 ? launch_one<256, true>(p, grid, stream) : launch_one<256, false>(p, grid, stream);
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, int pool, uint32_t grid, hipStream_t stream) {
+  if (head_dim == 64) return launch_of<64>(p, pool, grid, stream);
+  if (head_dim == 128) return launch_of<128>(p, pool, grid, stream);
+  if (head_dim == 256) return launch_of<256>(p, pool, grid, stream);
   return hipErrorInvalidValue;
 }
 

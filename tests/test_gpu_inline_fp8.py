@@ -125,9 +125,9 @@ def test_inline_unsupported_calls_fail():
         pk.paged_decode(d["q"], d["k_pages"], d["v_pages"], d["block_table"], d["context_lens"],
                         context_lens_host=inp["context_lens"], k_scale=sc, v_scale=sc)
     q = torch.zeros((4, 32, 128), dtype=torch.bfloat16, device=DEV)
-    with pytest.raises(pk.PdattnError):      # the prefill
+    with pytest.raises(pk.PdattnError):      # the prefill with separate scale arrays too
         pk.paged_prefill(q, torch.tensor([0, 4] + [4] * 7, dtype=torch.int32, device=DEV), d["k_pages"],
-                         d["v_pages"], d["block_table"], d["context_lens"])
+                         d["v_pages"], d["block_table"], d["context_lens"], k_scale=sc, v_scale=sc)
 
 
 @pytest.mark.parametrize("layout", ["nhd", "hnd"])

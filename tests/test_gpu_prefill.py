@@ -7,7 +7,8 @@ Cases span several query tiles per request and a ragged tail (rows per tile
 = 128 / G, or 64 / G at head_dim 256), K/V tiles with a ragged tail, every
 group size class, both pool layouts, both KV dtypes, page sizes 8 to 128,
 causal and not, requests with no rows, contexts shorter than their rows,
-and the bench's workloads at full size on sampled rows."""
+and the bench's workloads at full size on sampled rows; inline-scale fp8 pools
+against the oracle and bit for bit against separate scales."""
 import numpy as np
 import pytest
 import torch
@@ -352,3 +353,58 @@ def test_prefill_full_size_fp8_sampled():
     _compare(out[rows], lse[rows], ref_o, ref_l, True, "fp8 ragged, unsplit")
     _compare(s_out[rows], s_lse[rows], ref_o, ref_l, True, f"fp8 ragged, split ({st.num_tiles} entries)")
     assert float((out - s_out).abs().max()) <= 4e-2
+
+
+INLINE_CASES = [
+    # Hq, Hkv, D, P
+    (32, 8, 128, 16),
+    (8, 2, 64, 8),     # two pages per 16-token group
+    (8, 1, 256, 16),   # d256, G 8: two waves per 16-token group
+    (8, 2, 128, 128),
+]
+
+
+@pytest.mark.parametrize("layout", ["nhd", "hnd"])
+@pytest.mark.parametrize("case", INLINE_CASES, ids=[f"G{c[0] // c[1]}_d{c[2]}_P{c[3]}" for c in INLINE_CASES])
+def test_inline_fp8_prefill_matches_oracle_and_separate_scales(case, layout):
+    """Pools with each row's scale after its codes (rows of d + 4 bytes,
+    only 4-byte aligned): the oracle's fp8 bar, and bit for bit the result
+    of the same values with separate scale arrays, unsplit and split (the
+    kernel builds the same LDS image from either layout)."""
+    Hq, Hkv, D, P = case
+    inp = synth.make_prefill_inputs(num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=P, q_lens=Q_LENS,
+                                    prefix_lens=SPLIT_PREFIX, kv_dtype="fp8_e4m3", seed=4900 + Hq + D + P)
+    il = synth.to_inline(inp)
+    tag = f"inline G{Hq // Hkv} d{D} P{P} {layout}"
+    out, lse = _run(inp, layout=layout)
+    i_out, i_lse = _run(il, layout=layout)
+    _check(inp, i_out, i_lse, True, tag)
+    assert torch.equal(i_out, out) and torch.equal(i_lse, lse), tag
+    s_out, s_lse, _, _ = _split_call(inp, layout=layout)
+    si_out, si_lse, st, ws = _split_call(il, layout=layout)
+    assert st.num_slots > 0, "the map splits the 2000-position prompt"
+    _check(inp, si_out, si_lse, True, tag + " split")
+    assert torch.equal(si_out, s_out) and torch.equal(si_lse, s_lse), tag
+    assert not bool(_counters(st, ws, Hkv).any())
+
+
+def test_inline_fp8_prefill_non_causal_and_bad_page():
+    """Inline pools without the causal mask, and a block-table entry outside
+    the pool: NaN rows for the tiles that read it, the rest as with
+    separate scales."""
+    inp = synth.make_prefill_inputs(num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, q_lens=Q_LENS,
+                                    prefix_lens=PREFIX, kv_dtype="fp8_e4m3", seed=4950)
+    il = synth.to_inline(inp)
+    out, lse = _run(il, causal=False)
+    _check(inp, out, lse, False, "inline non-causal")
+    bad = dict(il)
+    bt = il["block_table"].clone()
+    bt[2, 1] = 1 << 30   # request 2, positions 16..31: read by every tile of request 2
+    bad["block_table"] = bt
+    b_out, b_lse = _run(bad)
+    ptr = inp["qo_indptr"].tolist()
+    assert bool(torch.isnan(b_out[ptr[2]:ptr[3]]).all()) and bool(torch.isnan(b_lse[ptr[2]:ptr[3]]).all())
+    g_out, g_lse = _run(il)
+    keep = torch.ones(b_out.shape[0], dtype=torch.bool)
+    keep[ptr[2]:ptr[3]] = False
+    assert torch.equal(b_out[keep], g_out[keep]) and torch.equal(b_lse[keep], g_lse[keep])

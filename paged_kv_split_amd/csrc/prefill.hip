@@ -30,9 +30,11 @@
 // the last row's limit are not read (causal tile skipping, same page,
 // Causal Masking with Tile-Skipping).
 //
-// fp8 pools: codes widen exactly to bf16 for the operand; the k scale
-// multiplies the score, the v scale the probability (OASR "Kernel Layer",
-// FP8 KV variants), as in the decode kernels. Pools with the scale inline
+// fp8 pools: the staged codes are widened once per tile, by the whole
+// workgroup, into a bf16 image laid out as a bf16 tile is (exact: an e4m3
+// value fits bf16), which the products then read as for bf16 pools; the k
+// scale multiplies the score, the v scale the probability (OASR "Kernel
+// Layer", FP8 KV variants), as in the decode kernels. Pools with the scale inline
 // (each row's D codes followed by its fp32 scale, DeepGEMM documentation
 // 6.1) are fetched with 4-byte loads into the same LDS image.
 
@@ -72,6 +74,9 @@ struct Cfg {
   // 8)); d-block e of O^T is then d 16 e .. 16 e + 15
   static constexpr bool TRV = !FP8 && D == 128;
   static constexpr int CPR = ROW / 16;                     // 16-byte chunks per row
+  // fp8: the bf16 image of one tile after the two stages
+  static constexpr int IMG = FP8 ? 2 * NT * D * 2 : 0;
+  static constexpr int SMEM = 2 * STAGE + IMG;
   static_assert(COLS == prefill_columns(D), "columns");
   static_assert(NT == prefill_kv_tile(D), "kv tile");
   static_assert(KI >= 1 && QK % KI == 0 && VI >= 1, "load split");
@@ -180,22 +185,41 @@ __device__ __forceinline__ void lds_b64x8(u32x2 (&r)[8], uint32_t a) {
       : "memory");
 }
 
-template <int... O>
-__device__ __forceinline__ void lds_b32x8(uint32_t (&r)[8], uint32_t a) {
-  constexpr int o[] = {O...};
-  static_assert(sizeof...(O) == 8, "read count");
+// N 16-byte LDS reads from N addresses, and their wait.
+template <int N>
+__device__ __forceinline__ void lds_b128_at(u32x4 (&r)[N], const uint32_t (&a)[N]) {
+  if constexpr (N == 2) {
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1])
+        : "v"(a[0]), "v"(a[1])
+        : "memory");
+  } else {
+    static_assert(N == 4, "read count");
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+        : "memory");
+  }
+}
+
+// Two 16-byte LDS writes, at a and a + OFF. Issued from asm like the reads,
+// so the compiler neither orders them behind the direct-to-LDS loads in
+// flight nor counts them: the caller waits (lgkmcnt) before its barrier.
+template <int OFF>
+__device__ __forceinline__ void lds_write2_b128(uint32_t a, const u32x4& x, const u32x4& y) {
   asm volatile(
-      "ds_read_b32 %0, %8 offset:%9\n\t"
-      "ds_read_b32 %1, %8 offset:%10\n\t"
-      "ds_read_b32 %2, %8 offset:%11\n\t"
-      "ds_read_b32 %3, %8 offset:%12\n\t"
-      "ds_read_b32 %4, %8 offset:%13\n\t"
-      "ds_read_b32 %5, %8 offset:%14\n\t"
-      "ds_read_b32 %6, %8 offset:%15\n\t"
-      "ds_read_b32 %7, %8 offset:%16\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-      : "v"(a), "i"(o[0]), "i"(o[1]), "i"(o[2]), "i"(o[3]), "i"(o[4]), "i"(o[5]), "i"(o[6]), "i"(o[7])
+      "ds_write_b128 %0, %1\n\t"
+      "ds_write_b128 %0, %2 offset:%3"
+      :
+      : "v"(a), "v"(x), "v"(y), "i"(OFF)
       : "memory");
 }
 
@@ -234,15 +258,8 @@ __device__ __forceinline__ void read_v(VPieces<C, P_>& v, uint32_t av) {
         v.w[j][x] = a[j][x];
         v.w[j][4 + x] = b[j][x];
       }
-  } else if constexpr (C::VR == 16) {
-    u32x4 a[8];
-    lds_b128<v_off<C, P_, 0>(), v_off<C, P_, 1>(), v_off<C, P_, 2>(), v_off<C, P_, 3>(), v_off<C, P_, 4>(),
-             v_off<C, P_, 5>(), v_off<C, P_, 6>(), v_off<C, P_, 7>()>(a, av);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int x = 0; x < 4; ++x) v.w[j][x] = a[j][x];
-  } else if constexpr (C::VR == 8) {
+  } else {
+    static_assert(C::VR == 8, "V piece");
     u32x2 a[8];
     lds_b64x8<v_off<C, P_, 0>(), v_off<C, P_, 1>(), v_off<C, P_, 2>(), v_off<C, P_, 3>(), v_off<C, P_, 4>(),
               v_off<C, P_, 5>(), v_off<C, P_, 6>(), v_off<C, P_, 7>()>(a, av);
@@ -251,40 +268,20 @@ __device__ __forceinline__ void read_v(VPieces<C, P_>& v, uint32_t av) {
       v.w[j][0] = a[j][0];
       v.w[j][1] = a[j][1];
     }
-  } else {
-    static_assert(C::VR == 4, "V piece");
-    uint32_t a[8];
-    lds_b32x8<v_off<C, P_, 0>(), v_off<C, P_, 1>(), v_off<C, P_, 2>(), v_off<C, P_, 3>(), v_off<C, P_, 4>(),
-              v_off<C, P_, 5>(), v_off<C, P_, 6>(), v_off<C, P_, 7>()>(a, av);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v.w[j][0] = a[j];
   }
 }
 
 // The V^T operand of d-block e: element e of the eight k slots' pieces,
 // gathered with byte permutes (perm(s0, s1, sel): selector bytes 0-3 pick
 // bytes of s1, 4-7 bytes of s0).
-template <bool FP8, typename VP>
+template <typename VP>
 __device__ __forceinline__ bf16x8 v_operand(const VP& v, int e) {
-  if constexpr (FP8) {
-    const int wd = e >> 2, b = e & 3;
-    const uint32_t pick2 = (uint32_t)(((4 + b) << 8) | b);  // byte b of s1, then byte b of s0
-    uint32_t x[2];
+  const int wd = e >> 1;
+  const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of s1 then s0
+  u32x4 r;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t lo = __builtin_amdgcn_perm(v.w[4 * h + 1][wd], v.w[4 * h + 0][wd], pick2);
-      const uint32_t hi = __builtin_amdgcn_perm(v.w[4 * h + 3][wd], v.w[4 * h + 2][wd], pick2);
-      x[h] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-    }
-    return __builtin_bit_cast(bf16x8, dev::fp8x8_to_bf16x8(x[0], x[1]));
-  } else {
-    const int wd = e >> 1;
-    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of s1 then s0
-    u32x4 r;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) r[q] = __builtin_amdgcn_perm(v.w[2 * q + 1][wd], v.w[2 * q][wd], sel);
-    return __builtin_bit_cast(bf16x8, r);
-  }
+  for (int q = 0; q < 4; ++q) r[q] = __builtin_amdgcn_perm(v.w[2 * q + 1][wd], v.w[2 * q][wd], sel);
+  return __builtin_bit_cast(bf16x8, r);
 }
 
 // Maximum over the four 16-lane rows, for every lane (the lane's column
@@ -418,8 +415,9 @@ __device__ __forceinline__ bool merge_parts(const PrefillParams& p, uint32_t& s_
 // head kvh, on the whole workgroup. INL: fp8 rows with their scale inline.
 template <int D, bool FP8, bool INL>
 __device__ __forceinline__ void prefill_item(const PrefillParams& p, const int tile, const int kvh,
-                                             unsigned char (&smem)[2 * Cfg<D, FP8>::STAGE], uint32_t& s_count) {
-  using C = Cfg<D, FP8>;
+                                             unsigned char (&smem)[Cfg<D, FP8>::SMEM], uint32_t& s_count) {
+  using C = Cfg<D, FP8>;     // the staged tiles (loads, fp8 scales)
+  using CC = Cfg<D, false>;  // the bf16 tile the products read (fp8: the widened image)
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, n = lane & 15;
@@ -491,15 +489,14 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, const int t
   }
 
   // Q as the B operand of q.K, zero for columns without a row; the head_dim
-  // order inside a k-step matches the K chunks (bf16: 32 ks + 8 r + j; fp8:
-  // 16-byte chunks hold two k-steps, 64 (ks / 2) + 16 r + 8 (ks mod 2) + j)
+  // order inside a k-step matches the K chunks (32 ks + 8 r + j)
   bf16x8 qop[C::NB][C::KS];
 #pragma unroll
   for (int bb = 0; bb < C::NB; ++bb) {
     const uint16_t* qrow = p.q + (orow[bb] >= 0 ? orow[bb] * D : 0);
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      const int d0 = FP8 ? 64 * (ks >> 1) + 16 * g + 8 * (ks & 1) : 32 * ks + 8 * g;
+      const int d0 = 32 * ks + 8 * g;
       u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + d0);
       if (orow[bb] < 0) raw = u32x4{0u, 0u, 0u, 0u};
       qop[bb][ks] = __builtin_bit_cast(bf16x8, raw);
@@ -672,12 +669,12 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, const int t
   // 4 g + r (+ 32 pp + 16 h, at the immediate offset), d 16 e + 4 q .. + 3,
   // whose 32-byte pair e sits at pair slot e ^ ((4 g + r) mod 8)
   uint32_t trv_off[8];
-  if constexpr (C::TRV) {
+  if constexpr (CC::TRV) {
     const int tr_r = n >> 2, tr_q = n & 3;
     const int tr_x = (4 * g + tr_r) % 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      trv_off[e] = (uint32_t)(C::K_T + (4 * g + tr_r) * C::ROW + 32 * (e ^ tr_x) + 8 * tr_q);
+      trv_off[e] = (uint32_t)(CC::K_T + (4 * g + tr_r) * CC::ROW + 32 * (e ^ tr_x) + 8 * tr_q);
   }
   float m[C::NB], l[C::NB];
   f32x4 acc[C::NB][C::DB];
@@ -690,6 +687,46 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, const int t
   }
 
   const uint32_t lds0 = dev::lds_addr(smem);
+  // fp8: thread t widens 16-byte pieces u = t + 256 i (i < WP) of the staged
+  // K tile and as many of V. K piece u is lane (g', n') of chunk u / 64,
+  // M-block (u / 64) / QK: token n', d 64 ((u / 64) mod QK) + 16 g' .. + 15,
+  // which in bf16 is k-step 2 ((u / 64) mod QK) + g' / 2, lane groups
+  // 2 (g' mod 2) and the next (256 bytes on). V piece u is token u / (D / 16),
+  // d 16 k .. + 15 with k = u mod (D / 16): bf16 chunks 2k and 2k + 1 of the
+  // row, adjacent also where the image swizzles chunks (the swizzle is even).
+  constexpr int WP = FP8 ? C::K_T / (kWaves * 64 * 16) : 1;
+  static_assert(!FP8 || (C::K_T == C::V_T && C::K_T % (kWaves * 64 * 16) == 0 && (WP == 1 || WP == 2)), "pieces");
+  const uint32_t img = lds0 + 2 * C::STAGE;
+  uint32_t w_src[2 * WP], w_dst[2 * WP];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int i = 0; i < WP; ++i) {
+      const int u = i * kWaves * 64 + (int)threadIdx.x;
+      const int q = u >> 6, gg = (u >> 4) & 3, nn = u & 15;
+      const int kq = 2 * (q % C::QK) + (gg >> 1);
+      w_src[i] = (uint32_t)(u * 16);
+      w_dst[i] = img + (uint32_t)((((q / C::QK) * CC::QK + kq) * 64 + 32 * (gg & 1) + nn) * 16);
+      const int t = u / (D / 16), k = u % (D / 16);
+      const int s0 = CC::TRV ? (2 * k) ^ (2 * (t % 8)) : 2 * k;
+      w_src[WP + i] = (uint32_t)(C::K_T + u * 16);
+      w_dst[WP + i] = img + (uint32_t)(CC::K_T + t * CC::ROW + s0 * 16);
+    }
+  }
+  auto widen = [&](uint32_t stage) {
+    uint32_t a[2 * WP];
+#pragma unroll
+    for (int i = 0; i < 2 * WP; ++i) a[i] = stage + w_src[i];
+    u32x4 r[2 * WP];
+    lds_b128_at<2 * WP>(r, a);
+#pragma unroll
+    for (int i = 0; i < 2 * WP; ++i) {
+      const u32x4 lo = dev::fp8x8_to_bf16x8(r[i][0], r[i][1]);
+      const u32x4 hi = dev::fp8x8_to_bf16x8(r[i][2], r[i][3]);
+      if (i < WP) lds_write2_b128<256>(w_dst[i], lo, hi);
+      else lds_write2_b128<16>(w_dst[i], lo, hi);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
   int e0 = 0, e1 = 0;
   if (it0 < it1) {
     load_pages(it0 * C::NT, e0, e1);
@@ -710,37 +747,32 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, const int t
       issue(tb + C::NT, (it + 1) & 1, e0, e1);
       if (it + 2 < it1) load_pages(tb + 2 * C::NT, e0, e1);
     }
-    const uint32_t sb = lds0 + (it & 1) * C::STAGE;
+    const uint32_t st_b = lds0 + (it & 1) * C::STAGE;
+    if constexpr (FP8) {
+      widen(st_b);
+      __syncthreads();  // the image holds tile it
+    }
+    const uint32_t sb = FP8 ? img : st_b;  // the bf16 tile
 
     // the MFMA phases run at raised wave priority, so that the other waves
     // of the SIMD fill the VALU around them instead of competing for issue
     __builtin_amdgcn_s_setprio(1);
     // S^T = K . Q^T
     f32x4 S[C::MB][C::NB];
-    constexpr int KG = 2 * C::QK <= 8 ? 2 : 1;  // M-blocks per LDS wait
-    u32x4 kcg[KG * C::QK];
+    constexpr int KG = 2 * CC::QK <= 8 ? 2 : 1;  // M-blocks per LDS wait
+    u32x4 kcg[KG * CC::QK];
     dev::static_for<0, C::MB>([&](auto mbc) {
       constexpr int mb = decltype(mbc)::value;
-      if constexpr (mb % KG == 0) read_k<C, mb>(kcg, sb + lane * 16, std::make_index_sequence<KG * C::QK>{});
-      const u32x4* kc = kcg + (mb % KG) * C::QK;
+      if constexpr (mb % KG == 0) read_k<CC, mb>(kcg, sb + lane * 16, std::make_index_sequence<KG * CC::QK>{});
+      const u32x4* kc = kcg + (mb % KG) * CC::QK;
 #pragma unroll
       for (int bb = 0; bb < C::NB; ++bb) S[mb][bb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int kq = 0; kq < C::QK; ++kq) {
-        if constexpr (FP8) {
-          const bf16x8 k0 = __builtin_bit_cast(bf16x8, dev::fp8x8_to_bf16x8(kc[kq][0], kc[kq][1]));
-          const bf16x8 k1 = __builtin_bit_cast(bf16x8, dev::fp8x8_to_bf16x8(kc[kq][2], kc[kq][3]));
+      for (int kq = 0; kq < CC::QK; ++kq) {
+        const bf16x8 k0 = __builtin_bit_cast(bf16x8, kc[kq]);
 #pragma unroll
-          for (int bb = 0; bb < C::NB; ++bb) {
-            S[mb][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[bb][2 * kq], S[mb][bb], 0, 0, 0);
-            S[mb][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qop[bb][2 * kq + 1], S[mb][bb], 0, 0, 0);
-          }
-        } else {
-          const bf16x8 k0 = __builtin_bit_cast(bf16x8, kc[kq]);
-#pragma unroll
-          for (int bb = 0; bb < C::NB; ++bb)
-            S[mb][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[bb][kq], S[mb][bb], 0, 0, 0);
-        }
+        for (int bb = 0; bb < C::NB; ++bb)
+          S[mb][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[bb][kq], S[mb][bb], 0, 0, 0);
       }
     });
 
@@ -766,7 +798,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, const int t
       dev::static_for<0, C::MB>([&](auto mbc) {
         constexpr int mb = decltype(mbc)::value;
         u32x4 s2[2];
-        lds_b128<mb * 128, mb * 128 + 64>(s2, sb + C::K_T + C::V_T + 16 * g);
+        lds_b128<mb * 128, mb * 128 + 64>(s2, st_b + C::K_T + C::V_T + 16 * g);
         // __uint_as_float: hipcc mistranslates __builtin_bit_cast applied
         // to one element of a vector (every element reads as element 0)
 #pragma unroll
@@ -862,7 +894,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, const int t
 
     __builtin_amdgcn_s_setprio(1);
     // O^T += V^T . P
-    if constexpr (C::TRV) {
+    if constexpr (CC::TRV) {
       // d-block e, k slots 8 g + j: tokens 32 pp + 16 (j / 4) + 4 g + j mod 4
       // (the P operand's order); the two transposing reads of a block give
       // tokens 32 pp + 4 g .. + 3 and 32 pp + 16 + 4 g .. + 3 of d 16 e + n
@@ -873,8 +905,8 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, const int t
       dev::static_for<0, C::PS>([&](auto ppc) {
         constexpr int pp = decltype(ppc)::value;
         u32x2 t0[8], t1[8];
-        lds_tr8<32 * pp * C::ROW, false>(t0, ab);
-        lds_tr8<(32 * pp + 16) * C::ROW, true>(t1, ab);
+        lds_tr8<32 * pp * CC::ROW, false>(t0, ab);
+        lds_tr8<(32 * pp + 16) * CC::ROW, true>(t1, ab);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const u32x4 vw = {t0[e][0], t0[e][1], t1[e][0], t1[e][1]};
@@ -885,14 +917,14 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, const int t
         }
       });
     } else {
-      const uint32_t av = sb + C::K_T + 4 * g * C::ROW + n * C::VR;
+      const uint32_t av = sb + CC::K_T + 4 * g * CC::ROW + n * CC::VR;
       dev::static_for<0, C::PS>([&](auto ppc) {
         constexpr int pp = decltype(ppc)::value;
-        VPieces<C, pp> vp;
-        read_v<C, pp>(vp, av);
+        VPieces<CC, pp> vp;
+        read_v<CC, pp>(vp, av);
 #pragma unroll
         for (int e = 0; e < C::DB; ++e) {
-          const bf16x8 va = v_operand<FP8>(vp, e);
+          const bf16x8 va = v_operand(vp, e);
 #pragma unroll
           for (int bb = 0; bb < C::NB; ++bb)
             acc[bb][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop[bb][pp], acc[bb][e], 0, 0, 0);
@@ -922,7 +954,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, const int t
     const float lt = l[bb];
     if (orow[bb] < 0) continue;
     float* o = p.out + orow[bb] * D;
-    if constexpr (C::TRV) {
+    if constexpr (CC::TRV) {
       // lane (g, n) holds d 16 e + 4 g + j
       const float inv = lt != 0.0f ? 1.0f / lt : 0.0f;
 #pragma unroll
@@ -954,7 +986,7 @@ template <int D, bool FP8, bool INL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(const PrefillParams p) {
   using C = Cfg<D, FP8>;
   static_assert(FP8 || !INL, "inline scales are an fp8 layout");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
   __shared__ uint32_t s_count;  // a split tile's parts counted in before this one
   prefill_item<D, FP8, INL>(p, blockIdx.x / p.num_kv_heads, blockIdx.x % p.num_kv_heads, smem, s_count);
 }

@@ -289,7 +289,7 @@ struct Tq4Cfg {
   static constexpr int NC = RB;                     // 16-byte chunks of a 16-row tile
   static constexpr int NI = (NC + 63) / 64;         // loads per lane per tile
   static constexpr int BUF = NI * 1024;             // LDS bytes of a wave's tile buffer
-  static constexpr int LDS = 2 * 4 * 256 * kTableCopies + kTq4Waves * BUF;
+  static constexpr int LDS = 2 * 4 * 256 * kTableCopies + kTq4Waves * 2 * BUF;
 };
 
 template <int D>
@@ -299,7 +299,7 @@ void tq4_decode_kernel(const Tq4DecodeParams p) {
   constexpr int H = C::H, RB = C::RB, KB = C::KB, NI = C::NI;
   __shared__ __attribute__((aligned(16))) uint32_t s_ktab[256 * kTableCopies];
   __shared__ __attribute__((aligned(16))) uint32_t s_vtab[256 * kTableCopies];
-  __shared__ __attribute__((aligned(16))) unsigned char s_buf[kTq4Waves][C::BUF];
+  __shared__ __attribute__((aligned(16))) unsigned char s_buf[kTq4Waves][2][C::BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -318,7 +318,8 @@ void tq4_decode_kernel(const Tq4DecodeParams p) {
   const uint32_t* ktab = s_ktab + col;  // copy col of each entry
   const uint32_t* vtab = s_vtab + col;
   auto look = [](const uint32_t* tab, uint32_t byte) -> uint32_t { return tab[byte * kTableCopies]; };
-  unsigned char* buf = s_buf[wave];
+  unsigned char* buf = s_buf[wave][0];
+  unsigned char* buf1 = s_buf[wave][1];
 
   const int G = p.heads_per_kv;
   const int Hkv = p.num_kv_heads;
@@ -484,38 +485,136 @@ void tq4_decode_kernel(const Tq4DecodeParams p) {
       __builtin_amdgcn_wave_barrier();  // the buffer is rewritten by the next tile
     };
 
-    // two tiles in flight: A holds tile t, B tile t + 1. The steady-state
-    // loop issues its loads unconditionally, so that each wait before a
-    // buffer write counts only the older set's loads.
+    // Two tiles as one 32-token step: tile t in buf, tile t + 1 in buf1
+    // (written by stage2, so that their registers take the next loads while
+    // the step computes). One max exchange and one rescale test per step;
+    // p.V on the 16x16x32 MFMA, whose k slot 8 r + j is token 4 r + j of
+    // tile t for j < 4 and token 4 r + j - 4 of tile t + 1 after: the lane's
+    // own probabilities and V lookups of the two tiles, side by side.
+    auto stage2 = [&](const u32x4 (&r0)[NI], const u32x4 (&r1)[NI]) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        *reinterpret_cast<u32x4*>(buf + (64 * i + lane) * 16) = r0[i];
+        *reinterpret_cast<u32x4*>(buf1 + (64 * i + lane) * 16) = r1[i];
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    };
+    auto math2 = [&](int t) {
+      constexpr int VW = KB >= 4 ? KB / 4 : 1;
+      unsigned char* const bufs[2] = {buf, buf1};
+      uint32_t vw[2][4][VW];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const unsigned char* vr = bufs[h] + (4 * grp + jj) * RB + H + 4 + col * KB;
+          if constexpr (KB == 2) {
+            vw[h][jj][0] = *reinterpret_cast<const uint16_t*>(vr);
+          } else {
+#pragma unroll
+            for (int q = 0; q < VW; ++q) vw[h][jj][q] = *reinterpret_cast<const uint32_t*>(vr + 4 * q);
+          }
+        }
+      f32x4 S[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        S[h] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const uint32_t wd = *reinterpret_cast<const uint32_t*>(bufs[h] + col * RB + 4 * (grp * KB + kb));
+          const u32x4 kop = {look(ktab, wd & 0xffu), look(ktab, (wd >> 8) & 0xffu), look(ktab, (wd >> 16) & 0xffu),
+                             look(ktab, wd >> 24)};
+          S[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kop), qop[kb], S[h], 0, 0, 0);
+        }
+      }
+      float x[2][4], vn[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int tok0 = (t + h) * kTileTokens + 4 * grp;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const unsigned char* row = bufs[h] + (4 * grp + j) * RB;
+          const float kn = *reinterpret_cast<const float*>(row + H);
+          vn[h][j] = *reinterpret_cast<const float*>(row + D + 4);
+          const float xs = S[h][j] * kn * p.qk_scale_log2;
+          x[h][j] = tok0 + j < L ? xs : -__builtin_inff();
+        }
+      }
+      const float mx = max_groups(fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                                        fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3]))));
+      const bool up = mx - m_run > 8.0f;
+      const float m_new = up ? mx : m_run;
+      const float m_ref = m_new == -__builtin_inff() ? 0.0f : m_new;
+      if (__any(up)) {
+        asm volatile("; tq4 rescale" ::: "memory");
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+        l_part *= alpha;
+#pragma unroll
+        for (int e = 0; e < 2 * KB; ++e) acc[e] *= alpha;
+      }
+      m_run = m_new;
+      float pw[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int tok0 = (t + h) * kTileTokens + 4 * grp;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float e = __builtin_amdgcn_exp2f(x[h][j] - m_ref);
+          l_part += e;
+          pw[h][j] = tok0 + j < L ? e * vn[h][j] : 0.0f;
+        }
+      }
+      const bf16x8 pop = __builtin_bit_cast(
+          bf16x8, u32x4{pack_bf16(pw[0][0], pw[0][1]), pack_bf16(pw[0][2], pw[0][3]), pack_bf16(pw[1][0], pw[1][1]),
+                        pack_bf16(pw[1][2], pw[1][3])});
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        uint32_t lk[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) lk[h][jj] = look(vtab, (vw[h][jj][i / 4] >> (8 * (i % 4))) & 0xffu);
+        const u32x4 hi = {__builtin_amdgcn_perm(lk[0][1], lk[0][0], 0x05040100u),
+                          __builtin_amdgcn_perm(lk[0][3], lk[0][2], 0x05040100u),
+                          __builtin_amdgcn_perm(lk[1][1], lk[1][0], 0x05040100u),
+                          __builtin_amdgcn_perm(lk[1][3], lk[1][2], 0x05040100u)};
+        const u32x4 lo = {__builtin_amdgcn_perm(lk[0][1], lk[0][0], 0x07060302u),
+                          __builtin_amdgcn_perm(lk[0][3], lk[0][2], 0x07060302u),
+                          __builtin_amdgcn_perm(lk[1][1], lk[1][0], 0x07060302u),
+                          __builtin_amdgcn_perm(lk[1][3], lk[1][2], 0x07060302u)};
+        acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi), pop, acc[2 * i], 0, 0, 0);
+        acc[2 * i + 1] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, lo), pop, acc[2 * i + 1], 0, 0, 0);
+      }
+      __builtin_amdgcn_wave_barrier();  // the buffers are rewritten by the next step
+    };
+
+    // Two tiles in flight: A holds tile t, B tile t + 1. A step writes both
+    // to LDS, loads tiles t + 2 and t + 3 into the freed registers (their
+    // block-table entries were read a step earlier) and computes t, t + 1;
+    // an odd last tile takes the one-tile step.
     u32x4 ra[NI], rb[NI];
-    int e0, e1, n0 = 0, n1 = 0;  // n0, n1: entries of the next tile to load
+    int e0, e1;
+    int a0 = 0, a1 = 0, b0 = 0, b1 = 0;  // entries of tiles t + 2 and t + 3
     pages(t0, e0, e1);
     load_tile(t0, ra, e0, e1);
     if (t0 + 1 < t1) {
       pages(t0 + 1, e0, e1);
       load_tile(t0 + 1, rb, e0, e1);
     }
-    if (t0 + 2 < t1) pages(t0 + 2, n0, n1);
+    if (t0 + 2 < t1) pages(t0 + 2, a0, a1);
+    if (t0 + 3 < t1) pages(t0 + 3, b0, b1);
     int t = t0;
-    for (; t + 4 < t1; t += 2) {
-      compute(t, ra);
-      load_tile(t + 2, ra, n0, n1);
-      pages(t + 3, n0, n1);
-      compute(t + 1, rb);
-      load_tile(t + 3, rb, n0, n1);
-      pages(t + 4, n0, n1);
+    for (; t + 1 < t1; t += 2) {
+      stage2(ra, rb);
+      if (t + 2 < t1) load_tile(t + 2, ra, a0, a1);
+      if (t + 3 < t1) load_tile(t + 3, rb, b0, b1);
+      if (t + 4 < t1) pages(t + 4, a0, a1);
+      if (t + 5 < t1) pages(t + 5, b0, b1);
+      math2(t);
     }
-    for (; t < t1; t += 2) {
-      compute(t, ra);
-      if (t + 2 < t1) {
-        load_tile(t + 2, ra, n0, n1);
-        if (t + 3 < t1) pages(t + 3, n0, n1);
-      }
-      if (t + 1 < t1) {
-        compute(t + 1, rb);
-        if (t + 3 < t1) load_tile(t + 3, rb, n0, n1);
-      }
-    }
+    if (t < t1) compute(t, ra);
 
     // The record (tq4_record_floats(G, D) floats, 16-byte aligned): m[G],
     // l[G], padding to a multiple of 4, then head n's accumulator as the

@@ -37,7 +37,7 @@
 //     a fragment is the same for Q and K, so the contraction is exact.
 //   * softmax on the MFMA result layout (lane: one head, four tokens):
 //     tile max by a 4-way local max and two cross-row exchanges, exp2.
-//   * p . V on the matrix cores (tile_ops.h: the weights as three bf16
+//   * p . V on the matrix cores (tile_ops.h: the weights as two bf16
 //     terms, fp32 accumulation).
 //
 // fp8 pools: e4m3fn bytes are widened in registers (hardware convert, exact

@@ -19,9 +19,9 @@
 //     the product is chosen so that k <-> token r + 4 j, which is where lane
 //     (r, c) already holds column c's weights (A operand) and its V chunk
 //     rows (B operand, V element e of the lane's chunk: n = c stands for
-//     d = c VE + e). Each weight enters as three bf16 terms (hi, mid, lo),
-//     so the product carries it to about 2^-24 relative, as fp32 does; the
-//     normaliser l and lse stay fp32. (On the VALU this product costs
+//     d = c VE + e). Each weight enters as two bf16 terms (hi and the
+//     bf16 of its remainder), so the product carries it to 2^-18 relative;
+//     the normaliser l and lse stay fp32. (On the VALU this product costs
 //     G x d/16 x 4 FMAs per lane per tile, which lengthened every tile
 //     step.)
 //   * the running maximum moves lazily (by more than kRescaleSlack, base
@@ -859,29 +859,21 @@ struct Tile {
 #pragma unroll
       for (int v = 0; v < 4; ++v) pr[v] *= f.vs[v];
     }
-    // p . V on the matrix cores. Each weight enters as three bf16 terms
-    // (hi, mid, lo: about 2^-24 relative, as fp32). One 16x16x32 product per
-    // V element e takes hi and mid: k = 8 row + j carries hi of token
-    // row + 4 j and k = 8 row + 4 + j its mid, against the same V element
-    // twice (B: V element e of tokens row + 4 j, n = col <-> d = col * VE + e);
-    // a second one of the same shape takes lo (its other half zero).
+    // p . V on the matrix cores. Each weight enters as two bf16 terms (hi
+    // and the bf16 of its remainder: within 2^-18 relative). One 16x16x32
+    // product per V element e: k = 8 row + j carries hi of token row + 4 j
+    // and k = 8 row + 4 + j its remainder, against the same V element twice
+    // (B: V element e of tokens row + 4 j, n = col <-> d = col * VE + e).
     bf16x4 vb[VE];
     v_operands(f, vb);
     const bf16x4 ph = {(__bf16)pr[0], (__bf16)pr[1], (__bf16)pr[2], (__bf16)pr[3]};
-    float r1[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) r1[v] = pr[v] - (float)ph[v];
-    const bf16x4 pm = {(__bf16)r1[0], (__bf16)r1[1], (__bf16)r1[2], (__bf16)r1[3]};
-    const bf16x4 pl = {(__bf16)(r1[0] - (float)pm[0]), (__bf16)(r1[1] - (float)pm[1]),
-                       (__bf16)(r1[2] - (float)pm[2]), (__bf16)(r1[3] - (float)pm[3])};
-    const bf16x4 z4 = {(__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f, (__bf16)0.0f};
+    const bf16x4 pm = {(__bf16)(pr[0] - (float)ph[0]), (__bf16)(pr[1] - (float)ph[1]), (__bf16)(pr[2] - (float)ph[2]),
+                       (__bf16)(pr[3] - (float)ph[3])};
     const bf16x8 a8 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(ph, pm, 0, 1, 2, 3, 4, 5, 6, 7));
-    const bf16x8 l8 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(pl, z4, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
       const bf16x8 b8 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vb[e], vb[e], 0, 1, 2, 3, 4, 5, 6, 7));
       s.cacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, s.cacc[e], 0, 0, 0);
-      s.cacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(l8, b8, s.cacc[e], 0, 0, 0);
     }
   }
 

@@ -42,8 +42,9 @@
 //       the elements (fused_tq_attention.cu, the decompress * norm step);
 //       online softmax in base 2 (flash_attention.cu, Online Softmax) with
 //       a lazily moved running max;
-//     * O^T += V^T . P on v_mfma_f32_16x16x16_bf16 (V centroids and the
-//       norm-weighted probabilities in bf16, for the norms' range): the
+//     * O^T += V^T . P on v_mfma_f32_16x16x32_bf16 (V centroids and the
+//       norm-weighted probabilities in bf16, for the norms' range; two tiles
+//       per product, the k slots of the second tile zero for a lone one): the
 //       probabilities are already in B-operand order; lane (d row m, group
 //       r) looks up the code bytes m * d/32 .. of tokens 4 r .. 4 r + 3,
 //       and each lookup feeds the A operands of two d blocks (the high
@@ -468,7 +469,10 @@ void tq4_decode_kernel(const Tq4DecodeParams p) {
         l_part += e;
         pw[j] = tok0 + j < L ? e * vn[j] : 0.0f;
       }
-      const bf16x4 pop = __builtin_bit_cast(bf16x4, u32x2{pack_bf16(pw[0], pw[1]), pack_bf16(pw[2], pw[3])});
+      // the same 16x16x32 shape as the two-tile step (k slots 8 r + 4 ..
+      // 8 r + 7 zero in both operands), so that every product on an
+      // accumulator has one shape
+      const bf16x8 pop = __builtin_bit_cast(bf16x8, u32x4{pack_bf16(pw[0], pw[1]), pack_bf16(pw[2], pw[3]), 0u, 0u});
 
       // O^T += V^T . P
 #pragma unroll
@@ -476,11 +480,13 @@ void tq4_decode_kernel(const Tq4DecodeParams p) {
         uint32_t lk[4];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) lk[jj] = look(vtab, (vw[jj][i / 4] >> (8 * (i % 4))) & 0xffu);
-        const u32x2 hi = {__builtin_amdgcn_perm(lk[1], lk[0], 0x05040100u), __builtin_amdgcn_perm(lk[3], lk[2], 0x05040100u)};
-        const u32x2 lo = {__builtin_amdgcn_perm(lk[1], lk[0], 0x07060302u), __builtin_amdgcn_perm(lk[3], lk[2], 0x07060302u)};
-        acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, hi), pop, acc[2 * i], 0, 0, 0);
+        const u32x4 hi = {__builtin_amdgcn_perm(lk[1], lk[0], 0x05040100u), __builtin_amdgcn_perm(lk[3], lk[2], 0x05040100u),
+                          0u, 0u};
+        const u32x4 lo = {__builtin_amdgcn_perm(lk[1], lk[0], 0x07060302u), __builtin_amdgcn_perm(lk[3], lk[2], 0x07060302u),
+                          0u, 0u};
+        acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi), pop, acc[2 * i], 0, 0, 0);
         acc[2 * i + 1] =
-            __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, lo), pop, acc[2 * i + 1], 0, 0, 0);
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, lo), pop, acc[2 * i + 1], 0, 0, 0);
       }
       __builtin_amdgcn_wave_barrier();  // the buffer is rewritten by the next tile
     };

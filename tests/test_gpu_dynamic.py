@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import synth
-from test_gpu_parity import assert_parity, gpu_run, oracle_run, small, to_dev
+from test_gpu_parity import assert_parity, gpu_run, oracle_run, small, to_dev, two_run_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -171,6 +171,6 @@ def test_graph_replay_matches_eager(balanced):
         out.fill_(float("nan"))
         g.replay()
         torch.cuda.synchronize()
-        assert float((out.cpu() - eager_out).abs().max()) <= 1e-5, rep
+        assert float((out.cpu() - eager_out).abs().max()) <= two_run_bound(inp), rep
         assert float((lse.cpu() - eager_lse).abs().max()) <= 1e-5, rep
         run_with(pl, d, ws)  # eager work between replays

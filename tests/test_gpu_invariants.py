@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import synth
-from test_gpu_parity import assert_parity, gpu_run, oracle_run, small, to_dev
+from test_gpu_parity import assert_parity, gpu_run, oracle_run, small, to_dev, two_run_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -21,13 +21,13 @@ def test_bitwise_deterministic_for_a_fixed_plan():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
-def test_balanced_mode_repeats_to_fp32_rounding():
+def test_balanced_mode_repeats_to_rounding():
     # the split points move with timing; the result moves only by rounding
     inp = synth.make_inputs("llama3_8b")
     a = gpu_run(inp, balanced=True)
     for _ in range(3):
         b = gpu_run(inp, balanced=True)
-        assert float((a[0] - b[0]).abs().max()) <= 1e-5
+        assert float((a[0] - b[0]).abs().max()) <= two_run_bound(inp)
         assert float((a[1] - b[1]).abs().max()) <= 1e-5
 
 
@@ -42,7 +42,7 @@ def test_result_does_not_depend_on_the_split_points():
             assert_parity(out, lse, *ref, tag=f"workers={force} balanced={bal}")
             outs.append((out, lse))
     for out, lse in outs[1:]:
-        assert float((out - outs[0][0]).abs().max()) <= 1e-5
+        assert float((out - outs[0][0]).abs().max()) <= two_run_bound(inp)
         assert float((lse - outs[0][1]).abs().max()) <= 1e-5
 
 

@@ -15,6 +15,7 @@ import torch
 import oracle
 import synth
 from oracle import merge as mg
+from test_gpu_parity import two_run_bound
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -103,7 +104,8 @@ def _piece_tables(bt, lens, P, cuts):
 def test_cascade_merge_equals_whole_decode(name, cuts):
     """Decode each sequence's pages [cuts[i], cuts[i+1]) separately on the
     GPU into stacked partials, merge them on the GPU, and compare with the
-    GPU decode of the whole context (fp32 summation order only) and with the
+    GPU decode of the whole context (the two runs' rounding only: the p.V
+    products' two-term weights and fp32 summation order) and with the
     oracle's decode (the decode tolerances)."""
     pk = _pk()
     inp = synth.make_inputs(name)
@@ -127,7 +129,7 @@ def test_cascade_merge_equals_whole_decode(name, cuts):
                                        context_lens_host=inp["context_lens"], k_scale=d["k_scale"],
                                        v_scale=d["v_scale"])
     torch.cuda.synchronize()
-    assert float((out - whole_o).abs().max()) <= 1e-5, name
+    assert float((out - whole_o).abs().max()) <= two_run_bound(inp), name
     assert float((lse - whole_l).abs().max()) <= 1e-4, name
     ref_o, ref_l = oracle.decode(inp["q"], inp["k_pages"], inp["v_pages"], inp["block_table"], inp["context_lens"],
                                  k_scale=inp["k_scale"], v_scale=inp["v_scale"])

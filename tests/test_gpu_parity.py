@@ -52,6 +52,21 @@ def oracle_run(inp, **kw):
                          inp["context_lens"], k_scale=inp["k_scale"], v_scale=inp["v_scale"], **kw)
 
 
+def two_run_bound(inp):
+    """Bound on the output difference of two GPU decodes of the same rows
+    whose KV ranges are cut differently (split points, cascades, the
+    balanced mode). The p.V products take each weight as two bf16 terms,
+    within 2^-18 relative of it, so each output lies within 2^-18 max |V|
+    of the exact weighted sum of its own pieces and two of them within
+    2^-17 max |V|; 1e-5 covers the fp32 summation order. (lse is formed
+    from fp32 weights and keeps the fp32-order bound.)"""
+    v = inp["v_pages"].float()
+    if inp.get("v_scale") is not None:
+        v = v * inp["v_scale"].float()[..., None]
+    vmax = float(v[torch.isfinite(v)].abs().max())  # unreferenced pages may hold NaN
+    return 2.0 ** -17 * vmax + 1e-5
+
+
 def assert_parity(out, lse, ref_out, ref_lse, fp8=False, tag=""):
     mx_tol, mean_tol = (FP8_MAX, FP8_MEAN) if fp8 else (BF16_MAX, BF16_MEAN)
     diff = (out.to(torch.float64) - ref_out).abs()

@@ -278,3 +278,24 @@ def test_split_argument_checks():
                 P(16), P(16), P(16), None, None) == 1
     assert call(ctypes.byref(prob), 1, None, None, None, None, None, 0, 0, None, 0, None, None, None, None, None,
                 None, None, None, None) == 0
+
+
+def test_prefill_scale_arguments_by_pool_dtype():
+    """Argument checks before any launch: separate-scale fp8 pools need both
+    scale arrays; bf16 and inline-scale fp8 pools (the scale after each
+    row's codes) take none. Every failing call returns
+    PDATTN_ERR_INVALID_ARGUMENT and enqueues nothing."""
+    pk = _pk()
+    import ctypes
+    P = ctypes.c_void_p
+    call = pk._lib.pdattn_prefill
+    for kv, k_scale, v_scale in ((pk.KV_FP8_E4M3, None, None), (pk.KV_FP8_E4M3, P(16), None),
+                                 (pk.KV_FP8_E4M3_INLINE, P(16), P(16)), (pk.KV_FP8_E4M3_INLINE, None, P(16)),
+                                 (pk.KV_BF16, P(16), P(16))):
+        prob = _split_problem(1, max_len=2048)
+        prob.kv_dtype = kv
+        st = call(ctypes.byref(prob), 1, P(16), P(16), P(16), P(16), 3, P(16), P(16), k_scale, v_scale, P(16),
+                  P(16), P(16), None, None)
+        assert st == 1, (kv, st)
+        msg = pk._lib.pdattn_last_error().decode()
+        assert "scale" in msg, msg

@@ -53,6 +53,7 @@
 
 #include <algorithm>
 
+#include "merge_ops.h"
 #include "tile_ops.h"
 
 namespace pdattn {
@@ -306,30 +307,11 @@ constexpr bool merge_fits() {
 // Workgroup size (waves) of the one-pair-per-wave merge.
 constexpr int kMergePairWaves = 4;
 
-// floor(x / d) for 0 <= x, 0 < d: below 2^53 the fp64 quotient, corrected by
-// one step (its error is below one); the integer division beyond
-__device__ __forceinline__ long long floor_div(long long x, long long d) {
-  if (x >= (1ll << 53)) return x / d;
-  long long q = (long long)((double)x / (double)d);
-  if (q * d > x) --q;
-  else if ((q + 1) * d <= x) ++q;
-  return q;
-}
-
-// The split reduce over the (sequence b, kv head) pairs. A pair's tiles
-// [ps, ps + nt) sit in the tile list at ps = Hkv * pre[b] + kvh * nt (nt =
-// pre[b + 1] - pre[b]); with the decode's equal ranges (worker w holds
-// [floor(w T / NW), floor((w + 1) T / NW))), the workers holding its first
-// and last tiles are wf = ceil((ps + 1) NW / T) - 1 and wl = ceil((ps + nt)
-// NW / T) - 1. A pair with wf == wl was finished by the decode. Otherwise
-// workers wf .. wl each left one record of it: wf in slot 0 when its range
-// starts at ps, else in slot 1 (its last piece); every later worker in slot
-// 0 (its first piece; a worker with an empty range holds the empty record
-// m = -inf, l = acc = 0).
+// The split reduce over the (sequence b, kv head) pairs: pair (b, kvh) has
+// its tiles at ps = Hkv * pre[b] + kvh * nt (nt = pre[b + 1] - pre[b]) of the
+// tile list; piece_span (merge_ops.h) finds the workers that hold them.
 struct CutPair {
-  long long wf;  // first worker
-  long long n;   // pieces (workers wf .. wf + n - 1); 0: nothing to merge
-  int slot_first;
+  PieceSpan s;
   int b, kvh;
 };
 
@@ -338,21 +320,11 @@ __device__ __forceinline__ CutPair cut_pair(const MergeParams& p, int pair) {
   const int Hkv = p.num_kv_heads;
   c.b = pair / Hkv;
   c.kvh = pair - c.b * Hkv;
-  c.wf = 0;
-  c.n = 0;
-  c.slot_first = 0;
-  const long long NW = p.num_workers;
   const long long T = p.pre[p.batch] * Hkv;
   const long long pb = p.pre[c.b];
   const long long nt = p.pre[c.b + 1] - pb;
-  if (nt <= 0) return c;  // empty or invalid: written by the decode
-  const long long ps = Hkv * pb + c.kvh * nt;
-  const long long wf = floor_div((ps + 1) * NW + T - 1, T) - 1;
-  const long long wl = floor_div((ps + nt) * NW + T - 1, T) - 1;
-  if (wf == wl) return c;  // one worker finished it
-  c.wf = wf;
-  c.n = wl - wf + 1;
-  c.slot_first = floor_div(wf * T, NW) == ps ? 0 : 1;
+  // an empty or invalid sequence (nt = 0) was written by the decode
+  c.s = piece_span(Hkv * pb + c.kvh * nt, nt, T, p.num_workers);
   return c;
 }
 
@@ -370,56 +342,27 @@ __device__ __forceinline__ void fold_pieces(const MergeParams& p, const CutPair&
   static_assert(EPL >= 1 && D % EPL == 0, "lane slice");
   const int g = lane / LPH;
   const int e0 = lane * EPL;
-  for (long long i = i0; i < c.n; i += (long long)U * S) {
+  for (long long i = i0; i < c.s.n; i += (long long)U * S) {
     float mu[U], lu[U], au[U][EPL];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const long long iu0 = i + (long long)u * S;
-      const long long iu = iu0 < c.n ? iu0 : i;
-      const float* r = p.rec + ((c.wf + iu) * 2 + (iu == 0 ? c.slot_first : 0)) * RF;
+      const long long iu = iu0 < c.s.n ? iu0 : i;
+      const float* r = p.rec + piece_record(c.s, iu) * RF;
       mu[u] = r[g];
       lu[u] = r[G + g];
 #pragma unroll
       for (int k = 0; k < EPL; ++k) au[u][k] = r[2 * G + e0 + k];
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (i + (long long)u * S < c.n) {
-        const float Mn = fmaxf(M, mu[u]);
-        // equal maxima (including both -inf: an empty record) scale by 1
-        const float so = M == Mn ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
-        const float si = mu[u] == Mn ? 1.0f : __builtin_amdgcn_exp2f(mu[u] - Mn);
-        L = L * so + lu[u] * si;
-#pragma unroll
-        for (int k = 0; k < EPL; ++k) A[k] = A[k] * so + au[u][k] * si;
-        M = Mn;
-      }
-    }
+    for (int u = 0; u < U; ++u)
+      if (i + (long long)u * S < c.s.n) fold_piece<EPL>(M, L, A, mu[u], lu[u], au[u]);
   }
 }
 
-// Output row of column c < num_cols of pair (b, kvh): query row c / Gh of
-// head kvh * Gh + c % Gh.
+// Output row of column c < num_cols of pair (b, kvh).
 __device__ __forceinline__ long long merge_row(const MergeParams& p, int b, int kvh, int c) {
-  const int Gh = p.heads_per_kv;
-  return (long long)b * p.q_len * p.num_q_heads + (long long)kvh * Gh + (long long)(c / Gh) * p.num_q_heads + c % Gh;
-}
-
-// A lane's N consecutive output floats at dst (aligned to N floats when N
-// is 2 or a multiple of 4: out is 16-byte aligned and slices start at
-// multiples of N), in the widest stores that alignment allows.
-template <int N>
-__device__ __forceinline__ void store_slice(float* dst, const float (&v)[N]) {
-  if constexpr (N % 4 == 0) {
-#pragma unroll
-    for (int k = 0; k < N; k += 4)
-      *reinterpret_cast<float4*>(dst + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
-  } else if constexpr (N == 2) {
-    *reinterpret_cast<float2*>(dst) = make_float2(v[0], v[1]);
-  } else {
-#pragma unroll
-    for (int k = 0; k < N; ++k) dst[k] = v[k];
-  }
+  return pair_out_row(b, kvh, c, p.q_len, p.num_q_heads, p.heads_per_kv);
 }
 
 // Short pairs: one pair per wave, kMergePairWaves pairs per workgroup; the
@@ -435,20 +378,14 @@ __global__ __launch_bounds__(kMergePairWaves * 64) void merge_wave_kernel(MergeP
   for (int pair = blockIdx.x * kMergePairWaves + wave; pair < p.batch * p.num_kv_heads;
        pair += gridDim.x * kMergePairWaves) {
     const CutPair c = cut_pair(p, pair);
-    if (c.n == 0) continue;
+    if (c.s.n == 0) continue;
     float M = -__builtin_inff(), L = 0.0f, A[EPL];
 #pragma unroll
     for (int k = 0; k < EPL; ++k) A[k] = 0.0f;
     fold_pieces<D, G>(p, c, 0, 1, lane, M, L, A);
     if (g >= p.num_cols) continue;  // padding columns are not written
-    const long long bh = merge_row(p, c.b, c.kvh, g);
-    // a column that saw no token (L = 0) gets 0 and -inf; a NaN sum, from a
-    // poisoned piece, stays NaN
-    float o[EPL];
-#pragma unroll
-    for (int k = 0; k < EPL; ++k) o[k] = L != 0.0f ? A[k] / L : 0.0f;
-    store_slice<EPL>(p.out + bh * D + (e0 % D), o);
-    if (lane % LPH == 0 && p.lse != nullptr) p.lse[bh] = L != 0.0f ? (M + log2f(L)) * kLn2 : -__builtin_inff();
+    write_merged<EPL>(p.out + merge_row(p, c.b, c.kvh, g) * D + (e0 % D),
+                      p.lse != nullptr && lane % LPH == 0 ? p.lse + merge_row(p, c.b, c.kvh, g) : nullptr, M, L, A);
   }
 }
 
@@ -469,7 +406,7 @@ __global__ __launch_bounds__(W * 64) void merge_kernel(MergeParams p) {
   const int e0 = lane * EPL;
   for (int pair = blockIdx.x; pair < p.batch * p.num_kv_heads; pair += gridDim.x) {
     const CutPair c = cut_pair(p, pair);
-    if (c.n == 0) continue;  // uniform over the workgroup
+    if (c.s.n == 0) continue;  // uniform over the workgroup
     float M = -__builtin_inff(), L = 0.0f, A[EPL];
 #pragma unroll
     for (int k = 0; k < EPL; ++k) A[k] = 0.0f;

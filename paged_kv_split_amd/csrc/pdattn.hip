@@ -174,6 +174,12 @@ DynLayout dyn_layout(const pdattn_problem& p, int64_t workers) {
   return d;
 }
 
+// The streaming kernel for a plan with this many workers: it addresses its
+// records with 32-bit buffer offsets (forced worker counts can exceed them).
+bool use_stream_for(const pdattn_problem& p, int64_t workers) {
+  return use_stream(p) && records_bytes(p, workers) < (1ull << 31);
+}
+
 uint64_t workspace_for(const pdattn_problem& p, int64_t workers, int32_t flags) {
   if (!balanced(flags)) return records_bytes(p, workers) + ((uint64_t)p.batch + 1) * 8;
   return dyn_layout(p, workers).total;
@@ -277,7 +283,7 @@ pdattn_status launch_static_decode(const pdattn_plan_t* plan, const void* q, con
   p.head_stride = head_stride_of(pr);
   p.qk_scale_log2 = pr.scale * 1.44269504088896340736f;
 
-  hipError_t e = use_stream(pr) ? pdattn::launch_decode_stream(p, pr.head_dim, group_of(pr), fp8,
+  hipError_t e = use_stream_for(pr, plan->num_workers) ? pdattn::launch_decode_stream(p, pr.head_dim, group_of(pr), fp8,
                                                                 (uint32_t)plan->num_workgroups,
                                                                 static_cast<hipStream_t>(stream))
                                 : pdattn::launch_decode(p, pr.head_dim, group_of(pr), decode_kind(pr),

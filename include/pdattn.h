@@ -33,7 +33,8 @@
  * base 2, fp32 accumulators); pieces of a pair computed by different waves
  * leave (m, l, acc) partials in the workspace and are merged with the
  * log-sum-exp rule. Two modes (plan flags):
- *   default   each wave takes an equal contiguous range of the tile list;
+ *   default   each wave takes a contiguous range of the tile list, sized by
+ *             the plan's worker weights (split_weights);
  *             pdattn_decode writes the pairs one wave covers and
  *             pdattn_reduce merges the others. Bitwise reproducible for a
  *             fixed plan.
@@ -164,7 +165,9 @@ typedef struct pdattn_plan_t {
   int64_t max_context_len;  /* largest host context length planned for */
   uint64_t workspace_bytes; /* partial records and the tile prefix, or counters */
   uint32_t magic;           /* set by pdattn_plan; checked by decode / reduce */
-  uint32_t reserved1;
+  uint32_t split_weights;   /* default mode: worker weights wa << 16 | wb; the first half of
+                               the workers takes wa shares of the tile list each, the rest wb
+                               (1:1, or 5:4 for fp8 pools at the full grid); set by pdattn_plan */
 } pdattn_plan_t;
 
 /* Plan flags (0: static equal ranges + pdattn_reduce; bitwise reproducible). */

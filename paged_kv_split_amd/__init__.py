@@ -66,7 +66,7 @@ class Plan(ctypes.Structure):
         ("max_context_len", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_uint64),
         ("magic", ctypes.c_uint32),
-        ("reserved1", ctypes.c_uint32),
+        ("split_weights", ctypes.c_uint32),
     ]
 
 

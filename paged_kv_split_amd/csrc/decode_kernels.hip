@@ -61,10 +61,11 @@ namespace {
 
 using namespace dev;
 
-// Range [t0, t1) of the tile list owned by worker w of nw, T tiles in all.
+// Range [t0, t1) of the tile list owned by worker w of nw, T tiles in all
+// (the plan gives this kernel equal weights).
 __device__ __forceinline__ void worker_range(long long w, long long nw, long long T, long long& t0, long long& t1) {
-  t0 = w * T / nw;
-  t1 = (w + 1) * T / nw;
+  t0 = worker_start(w, T, nw, 1, 1);
+  t1 = worker_start(w + 1, T, nw, 1, 1);
 }
 
 // fp8 d128 with up to 4 columns: the LDS holds four workgroups per CU; the
@@ -324,7 +325,7 @@ __device__ __forceinline__ CutPair cut_pair(const MergeParams& p, int pair) {
   const long long pb = p.pre[c.b];
   const long long nt = p.pre[c.b + 1] - pb;
   // an empty or invalid sequence (nt = 0) was written by the decode
-  c.s = piece_span(Hkv * pb + c.kvh * nt, nt, T, p.num_workers);
+  c.s = piece_span(Hkv * pb + c.kvh * nt, nt, T, p.num_workers, p.split_wa, p.split_wb);
   return c;
 }
 

@@ -4,12 +4,13 @@
 //
 // The work split is the one of decode_kernel (decode_kernels.hip): all
 // (sequence b, kv head) pairs laid end to end, b major, cut into 16-token
-// tiles, and every wave of a persistent grid takes an equal contiguous range
-// of that tile list (flash-decoding's split of the KV range, FlashQuant wiki
+// tiles, and every wave of a persistent grid takes a contiguous range of
+// that tile list (flash-decoding's split of the KV range, FlashQuant wiki
 // "CUDA Kernels", paged_decode.cu: Grid, Partial Output, with the split
-// points placed by equal work: Atlas "CUDA Kernel Engineering", kernel
-// inventory, adaptive split count). What differs is how a wave walks its
-// range:
+// points placed by work: Atlas "CUDA Kernel Engineering", kernel inventory,
+// adaptive split count), sized by the plan's worker weights (merge_ops.h:
+// equal, or heavier for the first half of the grid, whose workgroups a CU
+// serves first). What differs is how a wave walks its range:
 //   * one table per 64 tiles, one tile per lane: the lane finds its tile's
 //     sequence by a binary search of the workgroup's tile prefix sums, then
 //     the kv head and the tile inside the pair; the tile's block-table entry
@@ -26,6 +27,7 @@
 // leaves the tile prefix the merge walks) are those of decode_kernel, from
 // tile_ops.h.
 
+#include "merge_ops.h"
 #include "tile_ops.h"
 
 namespace pdattn {
@@ -128,18 +130,11 @@ void decode_stream_kernel(DecodeParams p) {
   __syncthreads();
 
   // ---- 2. this wave's range [t0, t1) of the T tiles (T < 2^31: the plan
-  // selects this kernel only then), equal shares.
+  // selects this kernel only then), by the plan's worker weights.
   const long long gw = (long long)blockIdx.x * kStreamWaves + wave;
   if (gw >= NW) return;
   const int T = total * Hkv;
-  // floor(w T / NW) in fp64: exact below 2^53 after one correction step
-  auto range_start = [&](long long w) -> int {
-    const long long x = w * (long long)T;
-    long long q = (long long)((double)x / (double)NW);
-    if (q * NW > x) --q;
-    else if ((q + 1) * NW <= x) ++q;
-    return (int)q;
-  };
+  auto range_start = [&](long long w) -> int { return (int)worker_start(w, T, NW, p.split_wa, p.split_wb); };
   const int t0 = range_start(gw), t1 = range_start(gw + 1);
   const int n = t1 - t0;
   unsigned char* ring = &s_ring[wave][0];

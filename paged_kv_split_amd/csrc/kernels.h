@@ -83,6 +83,7 @@ struct DecodeParams {
   int32_t max_pages_per_seq;
   int32_t num_pages;
   int32_t num_workers;        // waves of the grid that own tile ranges
+  int32_t split_wa, split_wb; // worker weights of the split (merge_ops.h): first half wa, the rest wb
   int32_t q_len;              // query rows per sequence (n)
   int32_t heads_per_kv;       // query heads per kv head (Gh)
   int32_t num_cols;           // valid columns n * Gh (<= the kernel's G; the rest is padding)
@@ -129,6 +130,7 @@ struct MergeParams {
   int32_t num_kv_heads;
   int32_t num_q_heads;
   int32_t num_workers;
+  int32_t split_wa, split_wb; // as in DecodeParams
   int32_t q_len;              // as in DecodeParams
   int32_t heads_per_kv;
   int32_t num_cols;

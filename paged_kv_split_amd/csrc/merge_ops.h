@@ -1,7 +1,6 @@
-// Device helpers of the split reduce shared by the merge kernels
-// (decode_kernels.hip) and the streaming decode's in-kernel merge
-// (decode_stream.hip), so both find a cut pair's pieces the same way and
-// fold them with the same arithmetic.
+// Device helpers of the static split and its reduce: the worker ranges the
+// decode kernels (decode_stream.hip, decode_kernels.hip) stream, and how
+// the merge kernels find a cut pair's pieces in them and fold them.
 //
 // The rule (FlashQuant wiki "CUDA Kernels", split_k_reduce.cu, Algorithm and
 // Numerical Stability, on un-normalised accumulators): for the pieces s of a
@@ -24,33 +23,59 @@ __device__ __forceinline__ long long floor_div(long long x, long long d) {
   return q;
 }
 
+// The static split of the T-tile list over NW workers, by weight: workers
+// 0 .. NW/2 - 1 weigh wa, the others wb (wa = wb: equal shares). With
+// W(w) = the weight of workers 0 .. w - 1, worker w holds
+// [floor(T W(w) / W(NW)), floor(T W(w + 1) / W(NW))).
+__device__ __forceinline__ long long weight_before(long long w, long long NW, long long wa, long long wb) {
+  const long long h = NW / 2;
+  return w <= h ? wa * w : wa * h + wb * (w - h);
+}
+// (Equal weights take the short forms floor(w T / NW) and
+// ceil((g + 1) NW / T) - 1: the same values, fewer divisions.)
+__device__ __forceinline__ long long worker_start(long long w, long long T, long long NW, long long wa, long long wb) {
+  if (wa == wb) return floor_div(w * T, NW);
+  return floor_div(T * weight_before(w, NW, wa, wb), weight_before(NW, NW, wa, wb));
+}
+// The worker holding tile g < T, the last w whose start is <= g: with
+// c = ceil((g + 1) W(NW) / T) - 1, the last w with W(w) <= c.
+__device__ __forceinline__ long long worker_of(long long g, long long T, long long NW, long long wa, long long wb) {
+  if (wa == wb) return floor_div((g + 1) * NW + T - 1, T) - 1;
+  const long long c = floor_div((g + 1) * weight_before(NW, NW, wa, wb) + T - 1, T) - 1;
+  const long long h = NW / 2;
+  // c < 2^24 here (at most 16 times 2^20 workers): 32-bit quotients
+  const long long w = c < wa * h ? (long long)((uint32_t)c / (uint32_t)wa)
+                                 : h + (long long)((uint32_t)(c - wa * h) / (uint32_t)wb);
+  return w < NW - 1 ? w : NW - 1;
+}
+
 // Where the pieces of a pair sit. The pair's tiles are [ps, ps + nt) of the
-// tile list (T tiles), and worker w of NW holds [floor(w T / NW),
-// floor((w + 1) T / NW)). The workers holding its first and last tiles are
-// wf = ceil((ps + 1) NW / T) - 1 and wl = ceil((ps + nt) NW / T) - 1; with
-// wf == wl one worker finished the pair (n = 0 here). Otherwise workers
-// wf .. wl each left one record of it: wf in slot 0 when its range starts
-// at ps, else in slot 1 (its last piece); every later worker in slot 0 (its
-// first piece; a worker with an empty range holds the empty record
-// m = -inf, l = acc = 0).
+// tile list; the workers holding its first and last tiles are
+// wf = worker_of(ps) and wl = worker_of(ps + nt - 1); with wf == wl one
+// worker finished the pair (n = 0 here). Otherwise workers wf .. wl each
+// left one record of it: wf in slot 0 when its range starts at ps, else in
+// slot 1 (its last piece); every later worker in slot 0 (its first piece;
+// a worker with an empty range holds the empty record m = -inf,
+// l = acc = 0).
 struct PieceSpan {
   long long wf;  // first worker
   long long n;   // pieces (workers wf .. wf + n - 1); 0: nothing to merge
   int slot_first;
 };
 
-__device__ __forceinline__ PieceSpan piece_span(long long ps, long long nt, long long T, long long NW) {
+__device__ __forceinline__ PieceSpan piece_span(long long ps, long long nt, long long T, long long NW, long long wa,
+                                                long long wb) {
   PieceSpan s;
   s.wf = 0;
   s.n = 0;
   s.slot_first = 0;
   if (nt <= 0) return s;
-  const long long wf = floor_div((ps + 1) * NW + T - 1, T) - 1;
-  const long long wl = floor_div((ps + nt) * NW + T - 1, T) - 1;
+  const long long wf = worker_of(ps, T, NW, wa, wb);
+  const long long wl = worker_of(ps + nt - 1, T, NW, wa, wb);
   if (wf == wl) return s;
   s.wf = wf;
   s.n = wl - wf + 1;
-  s.slot_first = floor_div(wf * T, NW) == ps ? 0 : 1;
+  s.slot_first = worker_start(wf, T, NW, wa, wb) == ps ? 0 : 1;
   return s;
 }
 

@@ -174,6 +174,18 @@ DynLayout dyn_layout(const pdattn_problem& p, int64_t workers) {
   return d;
 }
 
+// Worker weights of a static plan's split (merge_ops.h), packed wa << 16 | wb.
+int split_wa(const pdattn_plan_t* plan) { return (int)(plan->split_weights >> 16); }
+int split_wb(const pdattn_plan_t* plan) { return (int)(plan->split_weights & 0xffffu); }
+constexpr uint32_t kEqualWeights = (1u << 16) | 1u;
+// fp8 pools: the CU serves its first resident workgroup before its second,
+// and with half-size tiles the second one's waves alone do not keep the HBM
+// busy once the first ones are done; the first half of the grid (each CU's
+// first workgroup) takes 5 shares to the second half's 4 (measured on the
+// FP8 KV step: decode 59.3-59.4 us against 61.1-61.4 with equal shares;
+// bf16 steps gain nothing, their second workgroups alone still saturate).
+constexpr uint32_t kFp8Weights = (5u << 16) | 4u;
+
 // The streaming kernel for a plan with this many workers: it addresses its
 // records with 32-bit buffer offsets (forced worker counts can exceed them).
 bool use_stream_for(const pdattn_problem& p, int64_t workers) {
@@ -226,7 +238,10 @@ pdattn_status check_plan(const pdattn_plan_t* plan) {
       (plan->flags & ~PDATTN_PLAN_BALANCED) != 0 ||
       (balanced(plan->flags) &&
        (qlen_of(plan->problem) > 1 || plan->problem.head_dim == 256 || !pow2_heads(plan->problem))) ||
-      plan->workspace_bytes != workspace_for(plan->problem, plan->num_workers, plan->flags))
+      plan->workspace_bytes != workspace_for(plan->problem, plan->num_workers, plan->flags) ||
+      split_wa(plan) < 1 || split_wa(plan) > 16 || split_wb(plan) < 1 || split_wb(plan) > 16 ||
+      (plan->split_weights != kEqualWeights &&
+       (balanced(plan->flags) || !use_stream_for(plan->problem, plan->num_workers))))
     return fail(PDATTN_ERR_PLAN_MISMATCH, "plan fields are inconsistent");
   return PDATTN_OK;
 }
@@ -276,6 +291,8 @@ pdattn_status launch_static_decode(const pdattn_plan_t* plan, const void* q, con
   p.max_pages_per_seq = pr.max_pages_per_seq;
   p.num_pages = pr.num_pages;
   p.num_workers = plan->num_workers;
+  p.split_wa = split_wa(plan);
+  p.split_wb = split_wb(plan);
   p.q_len = qlen_of(pr);
   p.heads_per_kv = heads_per_kv(pr);
   p.num_cols = cols_of(pr);
@@ -307,14 +324,21 @@ pdattn_status launch_static_reduce(const pdattn_plan_t* plan, const void* worksp
   p.num_kv_heads = pr.num_kv_heads;
   p.num_q_heads = pr.num_q_heads;
   p.num_workers = plan->num_workers;
+  p.split_wa = split_wa(plan);
+  p.split_wb = split_wb(plan);
   p.q_len = qlen_of(pr);
   p.heads_per_kv = heads_per_kv(pr);
   p.num_cols = cols_of(pr);
   // pieces of the longest pair under the host lengths: its tiles span at
   // most floor((nt - 1) NW / T) + 2 worker ranges
   const int64_t nt_max = ceil_div(plan->max_context_len, (int64_t)pdattn::kTileTokens);
-  const int64_t max_pieces =
-      plan->total_tiles > 0 && nt_max > 0 ? (nt_max - 1) * plan->num_workers / plan->total_tiles + 2 : 1;
+  // (the lightest worker holds total_tiles * min(wa, wb) / W of them, W the
+  // weight of all workers)
+  const int64_t wa = split_wa(plan), wb = split_wb(plan);
+  const int64_t wsum = wa * (plan->num_workers / 2) + wb * (plan->num_workers - plan->num_workers / 2);
+  const int64_t max_pieces = plan->total_tiles > 0 && nt_max > 0
+                                 ? (nt_max - 1) * wsum / (plan->total_tiles * std::min(wa, wb)) + 2
+                                 : 1;
   const int waves = pdattn::merge_waves(pr.head_dim, group_of(pr), max_pieces);
   hipError_t e = pdattn::launch_merge(p, pr.head_dim, group_of(pr), waves, (uint32_t)kMaxMergeWorkgroups,
                                       static_cast<hipStream_t>(stream));
@@ -451,6 +475,12 @@ PDATTN_API pdattn_status pdattn_plan(const pdattn_problem* problem, const int32_
   plan.max_context_len = max_len;
   plan.flags = flags;
   plan.workspace_bytes = workspace_for(*problem, workers, flags);
+  // fp8 pools on the streaming kernel at its full grid (two workgroups per
+  // CU, blocks g and g + num_cus on CU g): the weighted split
+  plan.split_weights = !dyn && force_workers == 0 && problem->kv_dtype == PDATTN_KV_FP8_E4M3 && per_cu == 2 &&
+                               workers == capacity && use_stream_for(*problem, workers)
+                           ? kFp8Weights
+                           : kEqualWeights;
   plan.magic = kPlanMagic;
   *out = plan;
   return PDATTN_OK;

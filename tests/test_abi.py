@@ -195,19 +195,59 @@ def test_reduce_validation_rejects_before_launch():
     assert pk._lib.pdattn_reduce(None, P(16), 0, P(16), None, None) == INVALID
 
 
-def test_worker_range_arithmetic():
-    """The kernels place worker w on tiles [w*T/NW, (w+1)*T/NW) and find the
-    first worker reaching tile C as ceil((C+1)*NW/T) - 1; check that formula
-    against a brute-force search."""
-    rng = random.Random(5)
-    for _ in range(3000):
+def _weight_before(w, NW, wa, wb):
+    h = NW // 2
+    return wa * w if w <= h else wa * h + wb * (w - h)
+
+
+@pytest.mark.parametrize("wa,wb", [(1, 1), (5, 4), (3, 2), (2, 1), (16, 15)])
+def test_worker_range_arithmetic(wa, wb):
+    """The kernels place worker w on tiles [T W(w) / W(NW), T W(w+1) / W(NW))
+    with W(w) the weight of workers 0 .. w-1 (the first half wa each, the
+    rest wb), and find the worker holding tile C as the last w with
+    W(w) <= ceil((C+1) W(NW) / T) - 1 (merge_ops.h); check that rule against
+    a brute-force search over the ranges themselves."""
+    rng = random.Random(5 + wa)
+    for _ in range(2000):
         T = rng.randint(1, 5000)
         NW = rng.randint(1, 700)
         C = rng.randrange(T)
-        wf = ((C + 1) * NW + T - 1) // T - 1
-        brute = max(w for w in range(NW) if w * T // NW <= C)
+        om = _weight_before(NW, NW, wa, wb)
+        start = lambda w: T * _weight_before(w, NW, wa, wb) // om
+        c = ((C + 1) * om + T - 1) // T - 1
+        h = NW // 2
+        wf = min(c // wa if c < wa * h else h + (c - wa * h) // wb, NW - 1)
+        brute = max(w for w in range(NW) if start(w) <= C)
         assert wf == brute
-        assert wf * T // NW <= C < (wf + 1) * T // NW
+        assert start(wf) <= C < start(wf + 1)
+        assert start(0) == 0 and start(NW) == T
+
+
+def test_plan_split_weights():
+    """Equal weights unless the plan takes the streaming kernel's full grid
+    for an fp8 pool; forced worker counts, bf16 pools, balanced plans and the
+    general kernel (page size 8) keep equal weights. A plan whose weights do
+    not fit its kernel is refused."""
+    lens = [4000] * 32
+    kw = dict(batch=32, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, max_pages_per_seq=256,
+              num_pages=10 ** 6)
+    equal = (1 << 16) | 1
+    for extra in (dict(kv_dtype=0), dict(kv_dtype=1, force=2048), dict(kv_dtype=0, flags=2),
+                  dict(kv_dtype=1, page_size=8, max_pages_per_seq=512)):
+        st, pl = plan_raw(lens, **{**kw, **extra})
+        assert st == OK, pk._lib.pdattn_last_error()
+        assert pl.split_weights == equal, extra
+    st, pl = plan_raw(lens, **{**kw, "kv_dtype": 1})
+    assert st == OK and pl.split_weights in (equal, (5 << 16) | 4)
+    st, bf = plan_raw(lens, **{**kw, "kv_dtype": 0})
+    for bad_w in (0, (17 << 16) | 1, 1 << 16, 1):    # a weight of 0 or above 16
+        bad = pk.Plan.from_buffer_copy(bytes(bf))
+        bad.split_weights = bad_w
+        assert _decode_raw(bad) == MISMATCH
+    st, gen = plan_raw(lens, **{**kw, "kv_dtype": 1, "page_size": 8, "max_pages_per_seq": 512})
+    bad = pk.Plan.from_buffer_copy(bytes(gen))
+    bad.split_weights = (5 << 16) | 4
+    assert _decode_raw(bad) == MISMATCH               # the general kernel splits equally
 
 
 def test_workspace_init_validation():

@@ -240,3 +240,30 @@ def test_heads_of_a_group_with_equal_q_agree():
     inp["q"][:, 12] = inp["q"][:, 15]
     out, lse = gpu_run(inp, force_workers=11)
     assert torch.equal(out[:, 2], out[:, 3]) and torch.equal(out[:, 12], out[:, 15])
+
+
+@pytest.mark.parametrize("layout", [0, 1], ids=["NHD", "HND"])
+def test_fp8_full_grid_takes_the_weighted_split(layout):
+    """An fp8 pool planned on the device at the streaming kernel's full grid
+    takes the 5:4 worker weights (the first half of the grid heavier); the
+    outputs match the oracle, and an equal-weight plan with the same workers
+    (forced) within the two-cut bound. Ragged lengths with an empty and a
+    one-token sequence; every length spans many worker ranges."""
+    import paged_kv_split_amd as pk
+    lens = [0, 1] + [2100 + 97 * i for i in range(14)]
+    w = synth.Workload("gpu-fp8-weights", "fp8 weighted split", 16, 32, 8, 128, 16, ("fixed", tuple(lens)),
+                       kv_dtype="fp8_e4m3", seed=611)
+    inp = synth.make_inputs(w)
+    data = synth.to_hnd(inp) if layout == pk.LAYOUT_HND else inp
+    dev = to_dev(data)
+    pl = pk.plan(batch=16, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                 max_pages_per_seq=data["block_table"].shape[1], num_pages=data["k_pages"].shape[0],
+                 kv_dtype=pk.KV_FP8_E4M3, context_lens_host=inp["context_lens"], kv_layout=layout)
+    assert pl.split_weights == (5 << 16) | 4, (pl.num_workers, pl.num_workgroups)
+    out, lse = gpu_run(data, dev, layout=layout)
+    assert_parity(out, lse, *oracle_run(inp), fp8=True, tag=f"fp8 weighted split layout={layout}")
+    out_eq, lse_eq = gpu_run(data, dev, layout=layout, force_workers=pl.num_workers)
+    assert float((out - out_eq).abs().max()) <= two_run_bound(inp)
+    fin = torch.isfinite(lse)
+    assert torch.equal(fin, torch.isfinite(lse_eq))      # the empty sequence: -inf in both
+    assert float((lse[fin] - lse_eq[fin]).abs().max()) <= 1e-5

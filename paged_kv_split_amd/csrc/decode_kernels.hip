@@ -543,16 +543,14 @@ hipError_t launch_merge_d(const MergeParams& p, int group, int waves, uint32_t m
 }
 
 // One pair per wave when one step of a wave covers the longest pair; four
-// waves per pair up to six steps' worth; eight beyond (as LDS allows).
+// waves per pair up to four steps' worth; eight beyond (as LDS allows).
 // Measured on MI355X: wider workgroups, or more pieces in flight per wave
-// than a pair has, only lengthen the reduce (the FP8 KV step's reduce, up to
-// 18 pieces per pair: 7.9-8.0 us by events with four waves, 8.1-8.3 with
-// eight).
+// than a pair has, only lengthen the reduce.
 template <int D, int G>
 int merge_waves_g(int64_t max_pieces) {
   constexpr int U = merge_unroll<D, G>();
   if (max_pieces <= U) return 1;
-  if (max_pieces <= 6 * U || !merge_fits<D, G, 8>()) return 4;
+  if (max_pieces <= 4 * U || !merge_fits<D, G, 8>()) return 4;
   return 8;
 }
 

@@ -54,7 +54,7 @@ CSRC = os.path.join(ROOT, "paged_kv_split_amd", "csrc")
 # the sources each mode's decode kernel is built from
 KERNEL_SOURCES = {
     "balanced": ["decode_dynamic.hip", "tile_ops.h", "kernels.h"],
-    "static": ["decode_stream.hip", "tile_ops.h", "kernels.h"],
+    "static": ["decode_stream.hip", "merge_ops.h", "tile_ops.h", "kernels.h"],
 }
 # the static mode's decode kernel for bf16 / fp8 pools with page_size >= 16 and
 # batch <= 512 (every benchmark workload)

@@ -166,26 +166,20 @@ def append(cache, k_new, v_new, token_seq, token_pos, block_table, rotation, k_b
     return c
 
 
-def decode(q, cache, block_table, context_lens, rotation, k_centroids, v_centroids, *, scale=None,
-           return_rotated=False):
-    """Decode attention over a TQ4 cache, fp64.
-
-    q: [B, Hq, d] (bf16 or float; model space). cache: uint8 [num_pages,
-    Hkv, P, d + 8]. Returns (out [B, Hq, d], lse [B, Hq]) in model space as
-    float64 tensors (lse = -inf and out = 0 for an empty sequence); with
-    return_rotated also the output in the sequential rotated space."""
-    qd = _f64(q)
+def _attend_seq(q_seq, cache, block_table, context_lens, k_centroids, v_centroids, scale):
+    """Attention in the sequential rotated space (fused_tq_attention.cu,
+    Decode Path; paged_decode.cu): q_seq [B, Hq, d] fp64 against the
+    decompressed rows of every valid position. Returns (o_seq, lse) fp64
+    arrays; an empty sequence gives o = 0, lse = -inf."""
     rows = np.asarray(cache.detach().cpu().numpy() if isinstance(cache, torch.Tensor) else cache, np.uint8)
     bt = np.asarray(block_table.detach().cpu().numpy() if isinstance(block_table, torch.Tensor) else block_table)
     lens = np.asarray(context_lens.detach().cpu().numpy() if isinstance(context_lens, torch.Tensor) else context_lens)
-    B, Hq, d = qd.shape
+    B, Hq, d = q_seq.shape
     num_pages, Hkv, P, rb = rows.shape
     if rb != d + 8 or Hq % Hkv:
         raise ValueError("shape mismatch")
     G = Hq // Hkv
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    Rs = seq_rotation(rotation)
-    q_seq = qd @ Rs.T                                           # [B, Hq, d]
     o_seq = np.zeros((B, Hq, d))
     lse = np.full((B, Hq), -np.inf)
     for b in range(B):
@@ -208,9 +202,45 @@ def decode(q, cache, block_table, context_lens, rotation, k_centroids, v_centroi
                 w = np.exp(s - m)
                 o_seq[b, hq] = (w[:, None] * V).sum(0) / w.sum()
                 lse[b, hq] = m + math.log(w.sum())
+    return o_seq, lse
+
+
+def decode(q, cache, block_table, context_lens, rotation, k_centroids, v_centroids, *, scale=None,
+           return_rotated=False):
+    """Decode attention over a TQ4 cache, fp64.
+
+    q: [B, Hq, d] (bf16 or float; model space). cache: uint8 [num_pages,
+    Hkv, P, d + 8]. Returns (out [B, Hq, d], lse [B, Hq]) in model space as
+    float64 tensors (lse = -inf and out = 0 for an empty sequence); with
+    return_rotated also the output in the sequential rotated space."""
+    qd = _f64(q)
+    Rs = seq_rotation(rotation)
+    q_seq = qd @ Rs.T                                           # [B, Hq, d]
+    o_seq, lse = _attend_seq(q_seq, cache, block_table, context_lens, k_centroids, v_centroids, scale)
     out = o_seq @ Rs                                            # R_seq^T o_seq, row-wise
     res = (torch.from_numpy(out), torch.from_numpy(lse))
     return res + (torch.from_numpy(o_seq),) if return_rotated else res
+
+
+def decode_rotated(q_rot, cache, block_table, context_lens, k_centroids, v_centroids, *, scale=None):
+    """The fused attention's own boundary (fused_tq_attention.cu,
+    Input/Output): the queries arrive already rotated, q_rot = R q in the
+    rotation's natural coordinate order ([B, Hq, d], any float type), and
+    the output stays in that space (the caller rotates it back). Element i
+    of a decompressed row in natural order is centroid(code i) * norm, code
+    i being nibble i of the row's codes (codes_of), so the sequential
+    layout is only a reordering: q_seq = (q_rot[0::2], q_rot[1::2]) and
+    out[2j] = o_seq[j], out[2j + 1] = o_seq[d/2 + j]. Returns (out [B, Hq,
+    d], lse [B, Hq]) float64 tensors, out = 0 and lse = -inf for an empty
+    sequence."""
+    qr = _f64(q_rot)
+    q_seq = np.concatenate([qr[..., 0::2], qr[..., 1::2]], axis=-1)
+    o_seq, lse = _attend_seq(q_seq, cache, block_table, context_lens, k_centroids, v_centroids, scale)
+    h = qr.shape[-1] // 2
+    out = np.empty_like(o_seq)
+    out[..., 0::2] = o_seq[..., :h]
+    out[..., 1::2] = o_seq[..., h:]
+    return torch.from_numpy(out), torch.from_numpy(lse)
 
 
 def reconstruct_model(cache, rotation, k_centroids, v_centroids):

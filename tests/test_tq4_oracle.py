@@ -175,6 +175,51 @@ def test_distortion_is_the_lloyd_max_error():
 
 # ---- planted mistakes: each must fail a pin above --------------------------
 
+def _natural_rows(cache, k_centroids, v_centroids):
+    """Decompressed rows in the rotation's natural order, straight from the
+    per-element codes (element i = centroid(code i) * norm, compress.cu's
+    packing: byte j holds codes 2j and 2j + 1): (K, V) float64
+    [num_pages, P, Hkv, d]."""
+    rows = np.asarray(cache, np.uint8)
+    kpk, kn, vpk, vn = tq4.unpack_rows(rows)
+    K = np.asarray(k_centroids, np.float64)[tq4.codes_of(kpk)] * np.asarray(kn, np.float64)[..., None]
+    V = np.asarray(v_centroids, np.float64)[tq4.codes_of(vpk)] * np.asarray(vn, np.float64)[..., None]
+    return (torch.from_numpy(np.ascontiguousarray(K.transpose(0, 2, 1, 3))),
+            torch.from_numpy(np.ascontiguousarray(V.transpose(0, 2, 1, 3))))
+
+
+def test_decode_rotated_equals_dense_rotated_space_attention():
+    """fused_tq_attention.cu, Input/Output: q pre-rotated, output in the
+    rotated space; against dense attention over rows rebuilt from the codes
+    alone (no sequential layout, no rotation matrix)."""
+    inp, cache, ck, cv = _small_case(seed=7106, lens=(0, 29, 70))
+    g = torch.Generator().manual_seed(7106)
+    q_rot = torch.randn(inp["q"].shape, generator=g, dtype=torch.float64) * 0.7
+    out, lse = tq4.decode_rotated(q_rot, cache, inp["block_table"], inp["context_lens"], ck, cv)
+    K, V = _natural_rows(cache, ck, cv)
+    ref_o, ref_l = brute.numpy_decode(q_rot, K, V, inp["block_table"], inp["context_lens"])
+    assert float((out - ref_o).abs().max()) <= 1e-9
+    fin = torch.isfinite(ref_l)
+    assert torch.equal(fin, torch.isfinite(lse)) and float((lse[fin] - ref_l[fin]).abs().max()) <= 1e-9
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+
+
+def test_decode_rotated_is_the_model_space_decode_rotated():
+    """R orthogonal: attention on q_rot = R q gives R times the model-space
+    output, and the same lse, up to the float32 rotation's own distance from
+    orthogonality (R R^T - I, ~1e-7 here)."""
+    inp, cache, ck, cv = _small_case(seed=7107)
+    R = tq4._f64(inp["rotation"])
+    defect = float(np.abs(R @ R.T - np.eye(R.shape[0])).max())
+    tol = 4 * R.shape[0] * defect * 4.0 + 1e-12
+    out_m, lse_m = tq4.decode(inp["q"], cache, inp["block_table"], inp["context_lens"], inp["rotation"], ck, cv)
+    q_rot = torch.from_numpy(tq4._f64(inp["q"]) @ R.T)
+    out_r, lse_r = tq4.decode_rotated(q_rot, cache, inp["block_table"], inp["context_lens"], ck, cv)
+    assert defect < 1e-6
+    assert float((out_r - torch.from_numpy(out_m.numpy() @ R.T)).abs().max()) <= tol
+    assert float((lse_r - lse_m).abs().max()) <= tol
+
+
 def test_planted_mistakes_are_caught(monkeypatch):
     inp, cache, ck, cv = _small_case(seed=7105)
     orig_seq, orig_dec = tq4.seq_rotation, tq4.decompress_seq
@@ -200,3 +245,17 @@ def test_planted_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(tq4, "compress", lambda x, R, b, **kw: orig_comp(x, np.asarray(R).T, b, **kw))
     with pytest.raises(AssertionError):
         test_compress_decompress_worked_example(1)
+
+    # 4. nibbles swapped in the decompressor: the rotated-space decode no
+    #    longer matches its dense pin (rows rebuilt from the codes alone)
+    monkeypatch.setattr(tq4, "decompress_seq", swapped)
+    with pytest.raises(AssertionError):
+        test_decode_rotated_equals_dense_rotated_space_attention()
+    monkeypatch.setattr(tq4, "decompress_seq", orig_dec)
+
+    # 5. the sequential rotation's row order dropped: the model-space and
+    #    rotated-space decodes disagree
+    monkeypatch.setattr(tq4, "seq_rotation", lambda R: tq4._f64(R))
+    with pytest.raises(AssertionError):
+        test_decode_rotated_is_the_model_space_decode_rotated()
+    monkeypatch.setattr(tq4, "seq_rotation", orig_seq)

@@ -189,8 +189,10 @@ def time_tq4(pk, flush, dev, reps=20):
     filled by pdattn_tq4_append from the workload's bf16 rows (timed once,
     flushed), with the library's codebook; then the decode step
     (pdattn_tq4_decode: q rotation, the chunk kernel, the merge with the
-    back-rotation; one event pair, caches flushed before every call). GB/s
-    counts the d + 8 cache bytes of every valid (token, kv head) once."""
+    back-rotation; one event pair, caches flushed before every call), and the
+    same step at the fused attention's own boundary (pdattn_tq4_decode_rotated:
+    q pre-rotated, output left rotated). GB/s counts the d + 8 cache bytes of
+    every valid (token, kv head) once."""
     import torch
     import synth
     w = synth.WORKLOADS["llama3_8b"]
@@ -229,11 +231,34 @@ def time_tq4(pk, flush, dev, reps=20):
     us = statistics.fmean(ts)
     if not bool(torch.isfinite(out).all()):
         raise RuntimeError("TQ4 decode produced non-finite outputs")
+    # the same step at the fused attention's own boundary
+    # (pdattn_tq4_decode_rotated: q pre-rotated in fp16, the output left in
+    # the rotated space; the chunk kernel and the merge, no rotation kernels)
+    q_rot = (d["q"].float() @ d["rotation"].t()).to(torch.float16).contiguous()
+    out_r = torch.empty_like(out)
+
+    def step_rot():
+        pk.tq4_decode_rotated(pl, q_rot, cache, ck, ck, d["block_table"], d["context_lens"], ws, out_r, lse)
+    for _ in range(5):
+        step_rot()
+    ts_r = []
+    for i in range(reps):
+        flush.fill_(i & 0xFF)
+        a.record()
+        step_rot()
+        b.record()
+        torch.cuda.synchronize()
+        ts_r.append(a.elapsed_time(b) * 1e3)
+    us_r = statistics.fmean(ts_r)
+    if not bool(torch.isfinite(out_r).all()):
+        raise RuntimeError("TQ4 rotated-space decode produced non-finite outputs")
     tokens = int(inp["context_lens"].sum())
     return {"workload": "Llama-3-8B-shaped TQ4 decode B32, 32 q / 8 kv heads, d128, P16 head-major, L~U[512,4096]",
             "cache_bytes": nbytes, "bf16_equivalent_bytes": synth.kv_bytes(w, inp["context_lens"]),
             "chunk_tiles": int(pl.chunk_tiles), "max_chunks": int(pl.max_chunks),
             "us_per_call": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "rotated_space_us_per_call": round(us_r, 2),
+            "rotated_space_gbs": round(nbytes / (us_r * 1e-6) / 1e9, 1),
             "append_us": round(append_us, 2), "append_tokens": tokens}
 
 

@@ -589,6 +589,22 @@ PDATTN_API pdattn_status pdattn_tq4_decode(const pdattn_tq4_plan_t* plan, const 
                                            const int32_t* context_lens, void* workspace, uint64_t workspace_bytes,
                                            float* out, float* lse, void* stream);
 
+/* The same step at the fused attention's own boundary (fused_tq_attention.cu,
+ * Input/Output: the queries arrive pre-rotated, the output stays in the
+ * rotated space and the caller rotates it back; a caller can fold R into its
+ * q and output projections). q_rot: fp16 [B][Hq][d], 16-byte aligned, in the
+ * rotation's natural order, q_rot = R q (y_i = sum_k R[i][k] q_k; row i of the
+ * `rotation` given to pdattn_tq4_append). out: fp32 [B][Hq][d] in that same
+ * order (the attention output o_rot, with R^T o_rot the model-space output);
+ * lse as in pdattn_tq4_decode. Same plan, workspace, errors and empty /
+ * invalid sequence results as pdattn_tq4_decode. Two kernels on `stream`
+ * (the decode and the merge; no rotation). */
+PDATTN_API pdattn_status pdattn_tq4_decode_rotated(const pdattn_tq4_plan_t* plan, const void* q_rot,
+                                                   const void* cache, const float* k_centroids,
+                                                   const float* v_centroids, const int32_t* block_table,
+                                                   const int32_t* context_lens, void* workspace,
+                                                   uint64_t workspace_bytes, float* out, float* lse, void* stream);
+
 /* Static description of a status code. */
 PDATTN_API const char* pdattn_status_string(pdattn_status status);
 

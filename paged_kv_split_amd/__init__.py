@@ -455,11 +455,14 @@ _lib.pdattn_tq4_plan.argtypes = [ctypes.POINTER(Problem), _P, ctypes.c_int32, ct
 _lib.pdattn_tq4_decode.restype = ctypes.c_int
 _lib.pdattn_tq4_decode.argtypes = [ctypes.POINTER(Tq4Plan), _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint64, _P, _P,
                                    _P]
+_lib.pdattn_tq4_decode_rotated.restype = ctypes.c_int
+_lib.pdattn_tq4_decode_rotated.argtypes = [ctypes.POINTER(Tq4Plan), _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint64, _P,
+                                           _P, _P]
 _lib.pdattn_tq4_plan_size.restype = ctypes.c_uint64
 if _lib.pdattn_tq4_plan_size() != ctypes.sizeof(Tq4Plan):
     raise ImportError("libpdattn.so TQ4 plan layout does not match the binding")
 __all__ += ["KV_TQ4", "Tq4Plan", "tq4_codebook", "tq4_problem", "tq4_append", "tq4_plan", "tq4_decode",
-            "paged_decode_tq4"]
+            "tq4_decode_rotated", "paged_decode_tq4"]
 
 
 def tq4_codebook(head_dim):
@@ -511,6 +514,19 @@ def tq4_decode(pl, q, cache, rotation, k_centroids, v_centroids, block_table, co
     _check(_lib.pdattn_tq4_decode(ctypes.byref(pl), _ptr(q), _ptr(cache), _ptr(rotation), _ptr(k_centroids),
                                   _ptr(v_centroids), _ptr(block_table), _ptr(context_lens), _ptr(ws),
                                   int(ws.numel()), _ptr(out), _ptr(lse), _stream(stream)), "pdattn_tq4_decode")
+
+
+def tq4_decode_rotated(pl, q_rot, cache, k_centroids, v_centroids, block_table, context_lens, ws, out, lse,
+                       stream=None):
+    """pdattn_tq4_decode_rotated: q_rot fp16 [B, Hq, d] (R q, natural order);
+    out fp32 [B, Hq, d] stays in the rotated space. Caller-owned workspace
+    and outputs."""
+    if q_rot.dtype != torch.float16 or not q_rot.is_contiguous():
+        raise ValueError("q_rot must be contiguous fp16")
+    _check(_lib.pdattn_tq4_decode_rotated(ctypes.byref(pl), _ptr(q_rot), _ptr(cache), _ptr(k_centroids),
+                                          _ptr(v_centroids), _ptr(block_table), _ptr(context_lens), _ptr(ws),
+                                          int(ws.numel()), _ptr(out), _ptr(lse), _stream(stream)),
+           "pdattn_tq4_decode_rotated")
 
 
 def paged_decode_tq4(q, cache, block_table, context_lens, rotation, k_centroids, v_centroids, *,

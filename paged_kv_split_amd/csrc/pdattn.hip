@@ -1263,21 +1263,24 @@ PDATTN_API pdattn_status pdattn_tq4_plan(const pdattn_problem* problem, const in
   return PDATTN_OK;
 }
 
-PDATTN_API pdattn_status pdattn_tq4_decode(const pdattn_tq4_plan_t* plan, const void* q, const void* cache,
-                                           const float* rotation, const float* k_centroids,
-                                           const float* v_centroids, const int32_t* block_table,
-                                           const int32_t* context_lens, void* workspace, uint64_t workspace_bytes,
-                                           float* out, float* lse, void* stream) {
+// Both TQ4 decode calls: model space (rotated = false: q rotated in, out
+// rotated back) or the fused attention's own boundary (rotated = true: q
+// arrives rotated as fp16, out stays rotated; no rotation matrix).
+static pdattn_status tq4_decode_call(const pdattn_tq4_plan_t* plan, const void* q, const void* cache,
+                                     const float* rotation, const float* k_centroids, const float* v_centroids,
+                                     const int32_t* block_table, const int32_t* context_lens, void* workspace,
+                                     uint64_t workspace_bytes, float* out, float* lse, void* stream, bool rotated) {
   g_last_error[0] = '\0';
   pdattn_status st = check_tq4_plan(plan);
   if (st != PDATTN_OK) return st;
   const pdattn_problem& pr = plan->problem;
   if (pr.batch == 0) return PDATTN_OK;
-  if (!q || !rotation || !out || !context_lens || !workspace || !block_table)
+  if (!rotated && !rotation) return fail(PDATTN_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if (!q || !out || !context_lens || !workspace || !block_table)
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
   if (pr.num_pages > 0 && (!cache || !k_centroids || !v_centroids))
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "cache and centroids required");
-  if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(rotation, 16) || !aligned(out, 16) ||
+  if (!aligned(q, 16) || !aligned(cache, 16) || (!rotated && !aligned(rotation, 16)) || !aligned(out, 16) ||
       !aligned(workspace, 16))
     return fail(PDATTN_ERR_INVALID_ARGUMENT, "q, cache, rotation, out and workspace must be 16-byte aligned");
   if (!aligned(block_table, 4) || !aligned(context_lens, 4) || !aligned(lse, 4) || !aligned(k_centroids, 4) ||
@@ -1311,9 +1314,28 @@ PDATTN_API pdattn_status pdattn_tq4_decode(const pdattn_tq4_plan_t* plan, const 
   const uint32_t grid = pr.num_pages > 0 && pr.max_pages_per_seq > 0 ? (uint32_t)plan->num_workgroups : 0;
   p.num_waves = (int32_t)(grid * pdattn::kTq4Waves);
   p.qk_scale_log2 = pr.scale * 1.44269504088896340736f;
+  p.q_rotated = rotated ? 1 : 0;
   hipError_t e = pdattn::launch_tq4_decode(p, pr.head_dim, grid, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PDATTN_ERR_DEVICE, "TQ4 decode launch: %s", hipGetErrorString(e));
   return PDATTN_OK;
+}
+
+PDATTN_API pdattn_status pdattn_tq4_decode(const pdattn_tq4_plan_t* plan, const void* q, const void* cache,
+                                           const float* rotation, const float* k_centroids,
+                                           const float* v_centroids, const int32_t* block_table,
+                                           const int32_t* context_lens, void* workspace, uint64_t workspace_bytes,
+                                           float* out, float* lse, void* stream) {
+  return tq4_decode_call(plan, q, cache, rotation, k_centroids, v_centroids, block_table, context_lens, workspace,
+                         workspace_bytes, out, lse, stream, false);
+}
+
+PDATTN_API pdattn_status pdattn_tq4_decode_rotated(const pdattn_tq4_plan_t* plan, const void* q_rot,
+                                                   const void* cache, const float* k_centroids,
+                                                   const float* v_centroids, const int32_t* block_table,
+                                                   const int32_t* context_lens, void* workspace,
+                                                   uint64_t workspace_bytes, float* out, float* lse, void* stream) {
+  return tq4_decode_call(plan, q_rot, cache, nullptr, k_centroids, v_centroids, block_table, context_lens, workspace,
+                         workspace_bytes, out, lse, stream, true);
 }
 
 }  // extern "C"

@@ -41,7 +41,7 @@ struct Tq4AppendParams {
 
 // Decode: q rotation, the chunk kernel, the merge with the back-rotation.
 struct Tq4DecodeParams {
-  const uint16_t* q;           // bf16 bits [B][Hq][D], model space
+  const uint16_t* q;           // bf16 bits [B][Hq][D], model space; with q_rotated: fp16 bits, y = R q
   uint16_t* q_seq;             // workspace: fp16 [B][Hq][D], rotated, sequential order
   const uint8_t* cache;        // [num_pages][Hkv][P][D + 8]
   const float* rotation;       // [D][D]
@@ -63,13 +63,14 @@ struct Tq4DecodeParams {
   int32_t max_chunks;          //  at most max_chunks, splitting its tiles evenly)
   int32_t num_waves;           // waves of the decode grid
   float qk_scale_log2;         // softmax scale * log2(e)
+  int32_t q_rotated;           // 1: q arrives rotated (natural order) and out stays rotated (no rotation kernels)
 };
 
 // Resident decode workgroups per compute unit (runtime occupancy query),
 // 0 when it cannot be asked.
 int tq4_decode_wgs_per_cu(int head_dim);
 hipError_t launch_tq4_append(const Tq4AppendParams& p, int head_dim, uint32_t grid, hipStream_t stream);
-// The three decode launches on one stream.
+// The decode launches on one stream: three, or two with q_rotated.
 hipError_t launch_tq4_decode(const Tq4DecodeParams& p, int head_dim, uint32_t decode_grid, hipStream_t stream);
 
 }  // namespace pdattn

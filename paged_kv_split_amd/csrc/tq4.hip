@@ -345,7 +345,18 @@ void tq4_decode_kernel(const Tq4DecodeParams p) {
     // Q operands: lane (column n, group r), k block kb, slots 2i / 2i + 1 =
     // elements 4 (r KB + kb) + i and d/2 + 4 (r KB + kb) + i
     f16x8 qop[KB];
-    {
+    if (p.q_rotated) {
+      // natural order: those two slots are elements 2 e and 2 e + 1 of y,
+      // so the 8 slots of a k block are 8 consecutive fp16 values
+      const bool live = col < G;
+      const uint16_t* qr = p.q + ((long long)b * p.num_q_heads + kvh * G + (live ? col : 0)) * D;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        u32x4 v = *reinterpret_cast<const u32x4*>(qr + 8 * (grp * KB + kb));
+        if (!live) v = u32x4{0u, 0u, 0u, 0u};
+        qop[kb] = __builtin_bit_cast(f16x8, v);
+      }
+    } else {
       const bool live = col < G;
       const uint16_t* qr = p.q_seq + ((long long)b * p.num_q_heads + kvh * G + (live ? col : 0)) * D;
 #pragma unroll
@@ -803,21 +814,45 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   }
 }
 
+// tq4_merge_rot_kernel: the merge at the fused attention's own boundary
+// (q pre-rotated, output left in the rotated space): one row (sequence, q
+// head) per one-wave workgroup, so that the rows spread over every compute
+// unit; the wave merges its row into LDS in the sequential order and writes
+// it in the rotation's natural order (element 2 j = sequential j, element
+// 2 j + 1 = sequential d/2 + j), one float2 per lane and step.
+template <int D>
+__global__ __launch_bounds__(64) void tq4_merge_rot_kernel(const Tq4DecodeParams p) {
+  constexpr int H = D / 2;
+  __shared__ __attribute__((aligned(16))) float s_o[D];
+  const int lane = threadIdx.x;
+  const long long row = blockIdx.x;
+  merge_row<D>(p, row, lane, s_o);
+  __syncthreads();
+  float* o = p.out + row * D;
+#pragma unroll
+  for (int j = lane; j < H; j += 64) *reinterpret_cast<float2*>(o + 2 * j) = make_float2(s_o[j], s_o[H + j]);
+}
+
 template <int D>
 hipError_t launch_all(const Tq4DecodeParams& p, uint32_t decode_grid, hipStream_t stream) {
   const long long rows = (long long)p.batch * p.num_q_heads;
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(tq4_rotate_q_kernel<D>, dim3((uint32_t)((rows + kRotRows - 1) / kRotRows)), dim3(256), 0,
-                     stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (rows > 0x7fffffffll) return hipErrorInvalidValue;  // one merge workgroup per row in the rotated form
+  hipError_t e = hipSuccess;
+  if (!p.q_rotated) {
+    hipLaunchKernelGGL(tq4_rotate_q_kernel<D>, dim3((uint32_t)((rows + kRotRows - 1) / kRotRows)), dim3(256), 0,
+                       stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (decode_grid > 0) {
     hipLaunchKernelGGL(tq4_decode_kernel<D>, dim3(decode_grid), dim3(kTq4Waves * 64), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(tq4_merge_out_kernel<D>, dim3((uint32_t)((rows + kRotRows - 1) / kRotRows)), dim3(512), 0,
-                     stream, p);
+  const dim3 merge_grid((uint32_t)((rows + kRotRows - 1) / kRotRows));
+  if (p.q_rotated) hipLaunchKernelGGL(tq4_merge_rot_kernel<D>, dim3((uint32_t)rows), dim3(64), 0, stream, p);
+  else hipLaunchKernelGGL(tq4_merge_out_kernel<D>, merge_grid, dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -151,6 +151,53 @@ def test_tq4_decode_matches_oracle(case):
     assert torch.all(out[empty] == 0) and torch.all(torch.isneginf(lse[empty]))
 
 
+def _run_decode_rotated(inp, cache_np, ck, cv, chunk_tiles=0, sample=None):
+    """pdattn_tq4_decode_rotated on q_rot = fp16(R q) (the queries a caller
+    with R folded into its q projection hands over); returns (q_rot, out,
+    lse) on the CPU."""
+    pk = _pk()
+    q_rot = (inp["q"].double() @ inp["rotation"].double().T).to(torch.float16).contiguous()
+    cache, bt, lens = _dev(cache_np), _dev(inp["block_table"]), _dev(inp["context_lens"])
+    pl = pk.tq4_plan(pk.tq4_problem(q_rot, cache, bt), inp["context_lens"], chunk_tiles=chunk_tiles)
+    ws = torch.empty(int(pl.workspace_bytes), dtype=torch.uint8, device=DEV)
+    out = torch.full(q_rot.shape, 7.0, dtype=torch.float32, device=DEV)
+    lse = torch.full(q_rot.shape[:2], 7.0, dtype=torch.float32, device=DEV)
+    pk.tq4_decode_rotated(pl, _dev(q_rot), cache, _dev(ck), _dev(cv), bt, lens, ws, out, lse)
+    torch.cuda.synchronize()
+    return q_rot, out.cpu(), lse.cpu()
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}_G{c[1] // c[2]}_d{c[3]}_P{c[4]}_ct{c[6]}" for c in CASES])
+def test_tq4_decode_rotated_matches_oracle(case):
+    """The fused attention's own boundary (fused_tq_attention.cu,
+    Input/Output): q pre-rotated, the output left in the rotated space."""
+    B, Hq, Hkv, D, P, lens, ct = case
+    inp = synth.make_tq4_inputs(_workload(B, Hq, Hkv, D, P, lens, seed=8200 + D + Hq + P))
+    ck, bk, cv, bv = _tables(D)
+    cache = _oracle_cache(inp, bk, bv)
+    q_rot, out, lse = _run_decode_rotated(inp, cache, ck, cv, chunk_tiles=ct)
+    ref_o, ref_l = otq.decode_rotated(q_rot.double(), cache, inp["block_table"], inp["context_lens"], ck, cv)
+    _compare(out, lse, ref_o, ref_l, "rotated " + str(case))
+    empty = inp["context_lens"] == 0
+    assert torch.all(out[empty] == 0) and torch.all(torch.isneginf(lse[empty]))
+
+
+def test_tq4_decode_rotated_full_size_sampled_sequences():
+    """pdattn_tq4_decode_rotated on the Llama-3-8B-shaped workload at full
+    size in the benchmark's launch configuration, three sequences checked
+    against the oracle."""
+    w = synth.WORKLOADS["llama3_8b"]
+    inp = synth.make_tq4_inputs(w)
+    ck, bk, cv, bv = _tables(w.head_dim)
+    cache = _oracle_cache(inp, bk, bv)
+    q_rot, out, lse = _run_decode_rotated(inp, cache, ck, cv)
+    pick = [0, 13, 31]
+    ref_o, ref_l = otq.decode_rotated(q_rot[pick].double(), cache, inp["block_table"][pick],
+                                      inp["context_lens"][pick], ck, cv)
+    _compare(out[pick], lse[pick], ref_o, ref_l, "llama3_8b tq4 rotated sampled")
+    assert bool(torch.isfinite(out).all())
+
+
 def test_tq4_decode_bad_page_and_overlong_give_nan():
     pk = _pk()
     inp = synth.make_tq4_inputs(_workload(3, 8, 2, 128, 16, (40, 40, 40), seed=8200))
